@@ -1,0 +1,233 @@
+"""CPU oracle for MXFP8 block-scaled quantization and the block-scaled product.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. It is independent of
+the HIP library: it neither imports it nor shares any code, table or helper
+with it. The arithmetic lives in ``mx_oracle.c`` (plain C, fp64); this module
+only marshals numpy arrays into it.
+
+Array conventions (host numpy arrays):
+  * f32 inputs are ``np.float32``; bf16 inputs are their 16-bit patterns as
+    ``np.uint16``;
+  * codes and E8M0 scales are ``np.uint8``;
+  * formats: ``E4M3 = 0``, ``E5M2 = 1``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+E4M3 = 0
+E5M2 = 1
+F32 = 0
+BF16 = 1
+BLOCK = 32
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmxoracle.so")
+_lib = None
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.mxo_decode.restype = ctypes.c_double
+    lib.mxo_decode.argtypes = [ctypes.c_int, ctypes.c_uint]
+    lib.mxo_decode_e8m0.restype = ctypes.c_double
+    lib.mxo_decode_e8m0.argtypes = [ctypes.c_uint]
+    lib.mxo_encode.restype = ctypes.c_uint
+    lib.mxo_encode.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.mxo_scale_code.restype = ctypes.c_uint
+    lib.mxo_scale_code.argtypes = [ctypes.c_int, _p, _i64]
+    lib.mxo_double_to_bf16.restype = ctypes.c_uint16
+    lib.mxo_double_to_bf16.argtypes = [ctypes.c_double]
+    lib.mxo_dequant_value.restype = ctypes.c_double
+    lib.mxo_dequant_value.argtypes = [ctypes.c_int, ctypes.c_uint, ctypes.c_uint]
+    lib.mxo_quantize_rows.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _p, _i64, _p, _i64]
+    lib.mxo_quantize_cols.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _p, _i64, _p, _i64]
+    lib.mxo_kv_quant_write.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _i64]
+    lib.mxo_dequantize.argtypes = [_p, _i64, _p, _i64, ctypes.c_int, _i64, _i64, _p, ctypes.c_int, _i64]
+    lib.mxo_gemm.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, ctypes.c_int, _p, _i64, _p, _i64, ctypes.c_int,
+                             _p, _i64, _p, _i64]
+    lib.mxo_gemm_at.argtypes = [_i64, _p, _i64, _p, _i64, ctypes.c_int, _p, _i64, _p, _i64, ctypes.c_int, _p, _p,
+                                _i64, _p, _p]
+    lib.mxo_num_threads.restype = ctypes.c_int
+    lib.mxo_set_num_threads.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _in_dtype(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs are float32 or bf16 bit patterns (uint16), got %s" % x.dtype)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise ValueError("oracle rejected the shape (status %d)" % rc)
+
+
+# ---- scalar helpers -------------------------------------------------------
+def decode(fmt: int, code: int) -> float:
+    return _load().mxo_decode(fmt, code)
+
+
+def decode_e8m0(e: int) -> float:
+    return _load().mxo_decode_e8m0(e)
+
+
+def encode(fmt: int, y: float) -> int:
+    return _load().mxo_encode(fmt, float(y))
+
+
+def scale_code(fmt: int, block) -> int:
+    v = np.ascontiguousarray(block, dtype=np.float64)
+    return _load().mxo_scale_code(fmt, _ptr(v), v.size)
+
+
+def double_to_bf16(v: float) -> int:
+    return _load().mxo_double_to_bf16(float(v))
+
+
+def dequant_value(fmt: int, code: int, scale: int) -> float:
+    return _load().mxo_dequant_value(fmt, code, scale)
+
+
+def decode_table(fmt: int) -> np.ndarray:
+    return np.array([decode(fmt, c) for c in range(256)], dtype=np.float64)
+
+
+# ---- array operations -----------------------------------------------------
+def quantize_rows(x: np.ndarray, fmt: int):
+    """Rowwise MXFP8: returns (codes [R, C] uint8, scales [R, C/32] uint8)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // BLOCK), np.uint8)
+    _check(_load().mxo_quantize_rows(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, _ptr(q), cols, _ptr(s),
+                                     cols // BLOCK))
+    return q, s
+
+
+def quantize_cols(x: np.ndarray, fmt: int):
+    """Colwise MXFP8 (blocks down columns), stored transposed:
+    returns (codes^T [C, R] uint8, scales^T [C, R/32] uint8)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    qt = np.empty((cols, rows), np.uint8)
+    st = np.empty((cols, rows // BLOCK), np.uint8)
+    _check(_load().mxo_quantize_cols(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, _ptr(qt), rows, _ptr(st),
+                                     rows // BLOCK))
+    return qt, st
+
+
+def kv_quant_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, page_size: int, num_pages: int,
+                   k_cache=None, k_scale=None, v_cache=None, v_scale=None):
+    """Fused quantize + paged write of K and V [T, H, D] into the caches.
+
+    Caches are [num_pages, page_size, H, D] uint8 and scales
+    [num_pages, page_size, H, D/32] uint8; pass existing arrays to update them
+    in place (slots not named by slot_mapping keep their contents)."""
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    assert k.shape == v.shape and k.dtype == v.dtype
+    T, H, D = k.shape
+    shape_c = (num_pages, page_size, H, D)
+    shape_s = (num_pages, page_size, H, D // BLOCK)
+    k_cache = np.zeros(shape_c, np.uint8) if k_cache is None else k_cache
+    v_cache = np.zeros(shape_c, np.uint8) if v_cache is None else v_cache
+    k_scale = np.zeros(shape_s, np.uint8) if k_scale is None else k_scale
+    v_scale = np.zeros(shape_s, np.uint8) if v_scale is None else v_scale
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    _check(_load().mxo_kv_quant_write(_ptr(k), _ptr(v), _in_dtype(k), T, H, D, H * D, _ptr(sm), _ptr(k_cache),
+                                      _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), page_size, num_pages))
+    return k_cache, k_scale, v_cache, v_scale
+
+
+def dequantize(q: np.ndarray, s: np.ndarray, fmt: int, out: str = "f32") -> np.ndarray:
+    """x_hat = s * q rounded to f32 (np.float32) or bf16 (np.uint16 patterns)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    rows, cols = q.shape
+    if out == "f32":
+        y = np.empty((rows, cols), np.float32)
+        ydt = F32
+    else:
+        y = np.empty((rows, cols), np.uint16)
+        ydt = BF16
+    _check(_load().mxo_dequantize(_ptr(q), cols, _ptr(s), s.shape[1], fmt, rows, cols, _ptr(y), ydt, cols))
+    return y
+
+
+def gemm(a: np.ndarray, sa: np.ndarray, afmt: int, b: np.ndarray, sb: np.ndarray, bfmt: int):
+    """Block-scaled product y = A * B^T with A [M, K], B [N, K] codes.
+
+    Returns (y [M, N] float64, t [M, N] float64) with t = sum_k |a_k b_k|."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.uint8)
+    sb = np.ascontiguousarray(sb, dtype=np.uint8)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K and sa.shape == (M, K // BLOCK) and sb.shape == (N, K // BLOCK)
+    y = np.empty((M, N), np.float64)
+    t = np.empty((M, N), np.float64)
+    _check(_load().mxo_gemm(M, N, K, _ptr(a), K, _ptr(sa), K // BLOCK, afmt, _ptr(b), K, _ptr(sb), K // BLOCK,
+                            bfmt, _ptr(y), N, _ptr(t), N))
+    return y, t
+
+
+def gemm_at(a: np.ndarray, sa: np.ndarray, afmt: int, b: np.ndarray, sb: np.ndarray, bfmt: int,
+            mi: np.ndarray, ni: np.ndarray):
+    """The block-scaled product at output coordinates (mi[i], ni[i]) only."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.uint8)
+    sb = np.ascontiguousarray(sb, dtype=np.uint8)
+    K = a.shape[1]
+    mi = np.ascontiguousarray(mi, dtype=np.int64)
+    ni = np.ascontiguousarray(ni, dtype=np.int64)
+    assert mi.shape == ni.shape
+    assert mi.size == 0 or (0 <= mi.min() and mi.max() < a.shape[0] and 0 <= ni.min() and ni.max() < b.shape[0])
+    y = np.empty(mi.shape, np.float64)
+    t = np.empty(mi.shape, np.float64)
+    _check(_load().mxo_gemm_at(K, _ptr(a), a.shape[1], _ptr(sa), sa.shape[1], afmt, _ptr(b), b.shape[1], _ptr(sb),
+                               sb.shape[1], bfmt, _ptr(mi), _ptr(ni), mi.size, _ptr(y), _ptr(t)))
+    return y, t
+
+
+def paged_scores_at(q_codes, q_scales, k_cache, k_scale, page_table, seq_len, page_size, head, seq, i, j):
+    """QK^T score of query token i against key token j of sequence `seq`, head
+    `head`, reading K through the page table. q_codes [T, H, D] with token
+    index seq*seq_len + i; k_cache [P, page_size, H, D]."""
+    D = q_codes.shape[2]
+    page = page_table[seq, j // page_size]
+    krow = k_cache[page, j % page_size, head][None, :]
+    ks = k_scale[page, j % page_size, head][None, :]
+    qrow = q_codes[seq * seq_len + i, head][None, :]
+    qs = q_scales[seq * seq_len + i, head][None, :]
+    y, t = gemm(qrow, qs, E4M3, krow, ks, E4M3)
+    return float(y[0, 0]), float(t[0, 0])
+
+
+def num_threads() -> int:
+    return _load().mxo_num_threads()
+
+
+def set_num_threads(n: int):
+    _load().mxo_set_num_threads(n)

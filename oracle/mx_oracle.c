@@ -1,0 +1,369 @@
+/*
+ * mx_oracle.c -- plain CPU reference for MXFP8 block-scaled quantization and
+ * the block-scaled matrix product.
+ *
+ * TEST INFRASTRUCTURE. This file is the yardstick the HIP library is checked
+ * against. It shares no code, header, table or helper with that library, and
+ * only the test suite, the package smoke check and the benchmark's CPU-baseline
+ * leg may load it. Nothing on the product path calls it.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [SM120]  "MXFP8 SM120 software support" (xuesongtap.github.io, 2026-09-22)
+ *   [GLOSS]  "MXFP8 quantization" glossary (robocikowo.com)
+ *   [FP8DS]  "FP8 训练为什么能稳：把缩放因子的粒度与累加精度算清楚" (magicnetworld.com)
+ *   [NVFP4]  "NVFP4 如何用 4 bit 实现高精度" (theluyuan.com)
+ *
+ * Precision. Every quantity is held in IEEE double. All of them are exact
+ * there: bf16/f32 inputs, their power-of-two rescalings, FP8 code values,
+ * E8M0 scales, and products of two decoded codes. Rounding happens only where
+ * the method rounds: the element encode (to E4M3/E5M2), the dequantize output
+ * (to f32/bf16), and the fp64 summation of the matrix product.
+ *
+ * Readings taken where the pages leave a step open:
+ *   - scale rule: X = 2^(floor(log2 amax) - emax_elem), emax_elem = 8 (E4M3),
+ *     15 (E5M2); E8M0 code = that exponent + 127 clamped to [0, 254];
+ *   - element rounding: round to nearest, ties to even, saturating at the
+ *     largest finite magnitude (448 / 57344);
+ *   - amax == 0 gives scale code 0 and all-zero codes;
+ *   - a block holding NaN or Inf gets scale code 0xFF and element codes 0x7F;
+ *   - the sign of x is kept, so negative values that round to zero give 0x80.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#include "mx_oracle.h"
+
+/* ---------------------------------------------------------------------------
+ * Element formats. [SM120 §0.1, table of element encodings]: E4M3 has 1 sign,
+ * 4 exponent and 3 mantissa bits, largest finite 448, smallest subnormal 2^-9;
+ * E5M2 has 1/5/2 bits, largest finite 57344, smallest subnormal 2^-16.
+ * [FP8DS §4.1]: the smallest E4M3 normal is 2^-6; [FP8DS §三]: the E5M2 normal
+ * range is 57344 * 2^14, so its smallest normal is 2^-14. Together these fix
+ * the exponent biases at 7 and 15.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    int mbits;        /* stored mantissa bits */
+    int emin;         /* exponent of the smallest normal */
+    int bias;         /* exponent bias */
+    double maxfinite; /* largest finite magnitude */
+    int emax_elem;    /* floor(log2(maxfinite)), used by the scale rule */
+} fp8_format;
+
+static const fp8_format FMT_E4M3 = {3, -6, 7, 448.0, 8};
+static const fp8_format FMT_E5M2 = {2, -14, 15, 57344.0, 15};
+
+static const fp8_format* fmt_of(int fmt) {
+    return fmt == MXO_E5M2 ? &FMT_E5M2 : &FMT_E4M3;
+}
+
+/* Value of an E4M3 code: exponent field 0 is subnormal (m * 2^-9); the one
+ * pattern S.1111.111 is NaN and there is no infinity [FP8DS §三]. */
+double mxo_decode_e4m3(unsigned code) {
+    unsigned s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, (int)e - 7);
+    return s ? -v : v;
+}
+
+/* Value of an E5M2 code: IEEE-style, exponent field 31 holds Inf (m = 0) and
+ * NaN (m != 0) [FP8DS §三]; exponent field 0 is subnormal (m * 2^-16). */
+double mxo_decode_e5m2(unsigned code) {
+    unsigned s = (code >> 7) & 1, e = (code >> 2) & 31, m = code & 3;
+    double v;
+    if (e == 31) {
+        if (m != 0) return NAN;
+        v = INFINITY;
+    } else if (e == 0) {
+        v = ldexp((double)m, -16);
+    } else {
+        v = ldexp(1.0 + m / 4.0, (int)e - 15);
+    }
+    return s ? -v : v;
+}
+
+double mxo_decode(int fmt, unsigned code) {
+    return fmt == MXO_E5M2 ? mxo_decode_e5m2(code & 0xFF) : mxo_decode_e4m3(code & 0xFF);
+}
+
+/* E8M0 scale: no sign, no mantissa; finite values 2^k for -127 <= k <= 127
+ * plus one NaN encoding [SM120 §0.1]; value 2^(e-127) [NVFP4 §5.3]. */
+double mxo_decode_e8m0(unsigned e) {
+    e &= 0xFF;
+    if (e == 255) return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* ---------------------------------------------------------------------------
+ * Rounding to a binary grid.
+ *
+ * Round a >= 0 (finite) to the nearest multiple of the local grid spacing of a
+ * binary format with `mbits` fraction bits whose smallest normal exponent is
+ * `emin` (below it the spacing stays at 2^(emin - mbits): subnormals). Ties go
+ * to the even multiple, i.e. to the value whose last mantissa bit is 0.
+ * [SM120 §0.1]: elements are rounded to nearest; [FP8DS §4.1] works the
+ * subnormal spacing 2^-9 and the half-spacing zero threshold 2^-10 for E4M3.
+ * No upper bound is applied here.
+ * ------------------------------------------------------------------------- */
+static double round_to_grid(double a, int mbits, int emin) {
+    if (a == 0.0) return 0.0;
+    int e = ilogb(a);
+    if (e < emin) e = emin;
+    double spacing = ldexp(1.0, e - mbits);
+    double units = a / spacing; /* exact: division by a power of two */
+    double n = floor(units);
+    double rem = units - n;     /* exact */
+    if (rem > 0.5 || (rem == 0.5 && fmod(n, 2.0) != 0.0)) n += 1.0;
+    return n * spacing;
+}
+
+/* Bit pattern of a finite magnitude r that lies on the format's grid. */
+static unsigned grid_bits(double r, int mbits, int emin, int bias) {
+    if (r < ldexp(1.0, emin)) /* zero or subnormal: exponent field 0 */
+        return (unsigned)(r / ldexp(1.0, emin - mbits));
+    int e = ilogb(r);
+    unsigned m = (unsigned)((ldexp(r, -e) - 1.0) * (double)(1 << mbits));
+    return ((unsigned)(e + bias) << mbits) | m;
+}
+
+/* Code of the FP8 value nearest to y (ties to even), saturating at the largest
+ * finite magnitude; the sign bit is taken from y. */
+unsigned mxo_encode(int fmt, double y) {
+    const fp8_format* f = fmt_of(fmt);
+    unsigned sign = signbit(y) ? 0x80u : 0u;
+    if (isnan(y)) return 0x7Fu;
+    double a = fabs(y);
+    double r = a >= f->maxfinite ? f->maxfinite : round_to_grid(a, f->mbits, f->emin);
+    if (r > f->maxfinite) r = f->maxfinite;
+    return sign | grid_bits(r, f->mbits, f->emin, f->bias);
+}
+
+/* ---------------------------------------------------------------------------
+ * Scale selection for one block. [GLOSS]: one shared E8M0 factor per block of
+ * 32, usually derived from the block's largest absolute value; [SM120 §0.2]:
+ * take the amax of 32 values, choose a power of two that E8M0 can hold, then
+ * round x / scale to FP8. The rule itself is left to the implementation
+ * [SM120 §0.1]; this file uses X = 2^(floor(log2 amax) - emax_elem).
+ * ------------------------------------------------------------------------- */
+unsigned mxo_scale_code(int fmt, const double* x, int64_t n) {
+    const fp8_format* f = fmt_of(fmt);
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!isfinite(x[i])) return 0xFFu;
+        double a = fabs(x[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0) return 0u;
+    int k = ilogb(amax) - f->emax_elem + 127; /* ilogb is floor(log2) exactly */
+    if (k < 0) k = 0;
+    if (k > 254) k = 254;
+    return (unsigned)k;
+}
+
+/* Quantize one block: scale code, then q_i = Q_FP8(x_i / s) [SM120 §0.1]. */
+static void quantize_block(int fmt, const double* x, int64_t n, uint8_t* codes, int64_t code_stride,
+                           uint8_t* scale) {
+    unsigned s = mxo_scale_code(fmt, x, n);
+    *scale = (uint8_t)s;
+    for (int64_t i = 0; i < n; ++i) {
+        unsigned c = (s == 0xFFu) ? 0x7Fu : mxo_encode(fmt, ldexp(x[i], -((int)s - 127)));
+        codes[i * code_stride] = (uint8_t)c;
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Input element access: f32, or bf16 given as its 16-bit pattern.
+ * ------------------------------------------------------------------------- */
+static double load_elem(const void* x, int dt, int64_t idx) {
+    if (dt == MXO_F32) return (double)((const float*)x)[idx];
+    uint32_t u = (uint32_t)((const uint16_t*)x)[idx] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Rowwise: blocks of 32 consecutive elements along each row (the contiguous
+ * axis) [GLOSS]; codes and scales in separate arrays [SM120 §0.1]. */
+int mxo_quantize_rows(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                      int64_t ldq, uint8_t* s, int64_t lds) {
+    if (cols % MXO_BLOCK != 0 || rows < 0 || cols < 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double v[MXO_BLOCK];
+        for (int64_t b = 0; b < cols / MXO_BLOCK; ++b) {
+            for (int i = 0; i < MXO_BLOCK; ++i) v[i] = load_elem(x, xdt, r * ldx + b * MXO_BLOCK + i);
+            quantize_block(fmt, v, MXO_BLOCK, q + r * ldq + b * MXO_BLOCK, 1, s + r * lds + b);
+        }
+    }
+    return 0;
+}
+
+/* Colwise: blocks of 32 consecutive elements down each column. Blocks are
+ * directional, so this is a second quantization from the high-precision input,
+ * not a transpose of the rowwise codes [SM120 §1.2; GLOSS]. The result is
+ * stored transposed: qt[c][r] (row pitch ldq), st[c][r/32] (row pitch lds). */
+int mxo_quantize_cols(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* qt,
+                      int64_t ldq, uint8_t* st, int64_t lds) {
+    if (rows % MXO_BLOCK != 0 || rows < 0 || cols < 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; ++c) {
+        double v[MXO_BLOCK];
+        for (int64_t b = 0; b < rows / MXO_BLOCK; ++b) {
+            for (int i = 0; i < MXO_BLOCK; ++i) v[i] = load_elem(x, xdt, (b * MXO_BLOCK + i) * ldx + c);
+            quantize_block(fmt, v, MXO_BLOCK, qt + c * ldq + b * MXO_BLOCK, 1, st + c * lds + b);
+        }
+    }
+    return 0;
+}
+
+/* Fused KV-cache write [SM120 §0.2]: for each token t and head h, the D values
+ * are quantized to E4M3 in blocks of 32 along the head dimension and written
+ * to the cache slot slot_mapping[t]; page = slot / page_size, offset = slot %
+ * page_size. Cache layout [page][offset][h][d], scales [page][offset][h][d/32].
+ * A negative slot marks a padding token and is skipped. */
+int mxo_kv_quant_write(const void* k, const void* v, int dt, int64_t T, int64_t H, int64_t D, int64_t ld_token,
+                       const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* k_scale, uint8_t* v_cache,
+                       uint8_t* v_scale, int64_t page_size, int64_t num_pages) {
+    if (D % MXO_BLOCK != 0 || T < 0 || H < 0 || D < 0 || page_size <= 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= page_size * num_pages) continue;
+        int64_t page = slot / page_size, off = slot % page_size;
+        int64_t cache_row = (page * page_size + off) * H; /* first (slot, h=0) row */
+        double buf[MXO_BLOCK];
+        for (int which = 0; which < 2; ++which) {
+            const void* src = which == 0 ? k : v;
+            uint8_t* cache = which == 0 ? k_cache : v_cache;
+            uint8_t* scale = which == 0 ? k_scale : v_scale;
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t b = 0; b < D / MXO_BLOCK; ++b) {
+                    for (int i = 0; i < MXO_BLOCK; ++i) buf[i] = load_elem(src, dt, t * ld_token + h * D + b * MXO_BLOCK + i);
+                    quantize_block(MXO_E4M3, buf, MXO_BLOCK, cache + (cache_row + h) * D + b * MXO_BLOCK, 1,
+                                   scale + (cache_row + h) * (D / MXO_BLOCK) + b);
+                }
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Dequantize: x_hat = s_b * q_i [SM120 §0.1], in double (exact), then rounded
+ * to the output type. f32 output uses C's double-to-float conversion (round to
+ * nearest even, overflow to infinity). bf16 output is rounded here directly
+ * from the double, to 8 significant bits with subnormals below 2^-126.
+ * ------------------------------------------------------------------------- */
+uint16_t mxo_double_to_bf16(double v) {
+    if (isnan(v)) return 0x7FC0u;
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (isinf(a)) return sign | 0x7F80u;
+    double r = round_to_grid(a, 7, -126);
+    if (r >= ldexp(1.0, 128)) return sign | 0x7F80u; /* past the largest finite bf16 */
+    return sign | (uint16_t)grid_bits(r, 7, -126, 127);
+}
+
+double mxo_dequant_value(int fmt, unsigned code, unsigned scale) {
+    if ((scale & 0xFF) == 0xFF) return NAN; /* a NaN scale makes the whole block NaN */
+    return mxo_decode(fmt, code) * mxo_decode_e8m0(scale);
+}
+
+int mxo_dequantize(const uint8_t* q, int64_t ldq, const uint8_t* s, int64_t lds, int fmt, int64_t rows, int64_t cols,
+                   void* y, int ydt, int64_t ldy) {
+    if (cols % MXO_BLOCK != 0 || rows < 0 || cols < 0) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            double v = mxo_dequant_value(fmt, q[r * ldq + c], s[r * lds + c / MXO_BLOCK]);
+            if (ydt == MXO_F32)
+                ((float*)y)[r * ldy + c] = (float)v;
+            else
+                ((uint16_t*)y)[r * ldy + c] = mxo_double_to_bf16(v);
+        }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Block-scaled matrix product [SM120 §0.3; NVFP4 §7.1, §7.4]:
+ *   y[m][n] = sum_b sA[m][b] * sB[n][b] * sum_{i<32} qA[m][32b+i] * qB[n][32b+i]
+ * with A codes [M x K] and B codes [N x K], both K-contiguous (y = A * B^T).
+ * Each block's inner sum is formed in double, multiplied by the two block
+ * scales, and added to the running double total in block order, exactly the
+ * shape of the equation. t[m][n] = sum_k |a_hat_k * b_hat_k| is returned
+ * beside it: the magnitude against which a tolerance is stated.
+ * ------------------------------------------------------------------------- */
+static void gemm_one(int64_t K, const uint8_t* a, const uint8_t* sa, const double* lut_a, const uint8_t* b,
+                     const uint8_t* sb, const double* lut_b, double* y_out, double* t_out) {
+    double y = 0.0, t = 0.0;
+    for (int64_t blk = 0; blk < K / MXO_BLOCK; ++blk) {
+        double inner = 0.0, inner_abs = 0.0;
+        for (int i = 0; i < MXO_BLOCK; ++i) {
+            double p = lut_a[a[blk * MXO_BLOCK + i]] * lut_b[b[blk * MXO_BLOCK + i]];
+            inner += p;
+            inner_abs += fabs(p);
+        }
+        double ss = mxo_decode_e8m0(sa[blk]) * mxo_decode_e8m0(sb[blk]);
+        y += ss * inner;
+        t += ss * inner_abs;
+    }
+    *y_out = y;
+    *t_out = t;
+}
+
+static void build_lut(int fmt, double* lut) {
+    for (unsigned c = 0; c < 256; ++c) lut[c] = mxo_decode(fmt, c);
+}
+
+int mxo_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t ldsa,
+             int afmt, const uint8_t* b, int64_t ldb, const uint8_t* sb, int64_t ldsb, int bfmt, double* y,
+             int64_t ldy, double* t, int64_t ldt) {
+    if (K % MXO_BLOCK != 0 || M < 0 || N < 0 || K < 0) return -2;
+    double lut_a[256], lut_b[256];
+    build_lut(afmt, lut_a);
+    build_lut(bfmt, lut_b);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            gemm_one(K, a + m * lda, sa + m * ldsa, lut_a, b + n * ldb, sb + n * ldsb, lut_b, &y[m * ldy + n],
+                     &t[m * ldt + n]);
+    return 0;
+}
+
+/* The same product at a list of (m, n) output coordinates only. */
+int mxo_gemm_at(int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t ldsa, int afmt, const uint8_t* b,
+                int64_t ldb, const uint8_t* sb, int64_t ldsb, int bfmt, const int64_t* mi, const int64_t* ni,
+                int64_t count, double* y, double* t) {
+    if (K % MXO_BLOCK != 0 || count < 0) return -2;
+    double lut_a[256], lut_b[256];
+    build_lut(afmt, lut_a);
+    build_lut(bfmt, lut_b);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        gemm_one(K, a + mi[i] * lda, sa + mi[i] * ldsa, lut_a, b + ni[i] * ldb, sb + ni[i] * ldsb, lut_b, &y[i],
+                 &t[i]);
+    return 0;
+}
+
+int mxo_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void mxo_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

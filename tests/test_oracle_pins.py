@@ -1,0 +1,422 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each test compares the oracle with something other than itself: values the
+pages print (tests/golden, each with its citation), an independent
+nearest-value search over the format's grid, closed forms, library routines
+(numpy matmul, torch's bfloat16 cast), invariants, and exact rational
+arithmetic on tiny inputs. A plausible slip in the oracle (a wrong bias, tie
+rule, saturation, scale rule, sign, index or operand order, a dropped term)
+fails at least one of them.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from conftest import load_golden
+from microscaling_block_scaled_amd import inputs
+
+E4M3, E5M2 = 0, 1
+EMAX = {E4M3: 8, E5M2: 15}
+MAXF = {E4M3: 448.0, E5M2: 57344.0}
+
+
+# ---------------------------------------------------------------------------
+# Independent descriptions of the formats, written from the facts the pages
+# give (the element table, the subnormal step and the normal minimum). They
+# enumerate values; they do not share the oracle's bit arithmetic.
+# ---------------------------------------------------------------------------
+def positive_grid(fmt):
+    """Sorted non-negative finite values; index i is the code's low 7 bits."""
+    if fmt == E4M3:
+        mb, emin, maxf = 3, -6, 448.0
+    else:
+        mb, emin, maxf = 2, -14, 57344.0
+    vals = [k * 2.0 ** (emin - mb) for k in range(2 ** mb)]
+    e = emin
+    while True:
+        row = [(1 + m / 2 ** mb) * 2.0 ** e for m in range(2 ** mb)]
+        vals.extend(v for v in row if v <= maxf)
+        if row[-1] >= maxf:
+            break
+        e += 1
+    return np.array(vals)
+
+
+def nearest_code(y, fmt):
+    """Nearest grid value (ties to the even index), clamped to the largest
+    finite value; sign bit from y."""
+    g = positive_grid(fmt)
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(g, a), 1, len(g) - 1)
+    lo = hi - 1
+    dlo = a - g[lo]
+    dhi = g[hi] - a
+    take_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    idx = np.where(take_hi, hi, lo)
+    idx = np.where(a >= g[-1], len(g) - 1, idx)
+    return (idx | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def value_of(code, fmt):
+    """Exact value of a code as a Fraction (finite codes only)."""
+    s = -1 if code & 0x80 else 1
+    g = positive_grid(fmt)
+    return s * Fraction(float(g[code & 0x7F]))
+
+
+# ---------------------------------------------------------------------------
+# Worked example [MXFP8 SM120 software support, section 0.1]
+# ---------------------------------------------------------------------------
+def test_worked_example_per_block_scales(oracle):
+    ex = load_golden("worked_example_v64.json")
+    v64 = inputs.tiny()["v64"]
+    assert v64[0, 0] == ex["input"]["first_32"] and v64[0, 63] == ex["input"]["last_32"]
+    q, s = oracle.quantize_rows(v64, E4M3)
+    scale_values = [oracle.decode_e8m0(int(c)) for c in s[0]]
+    assert scale_values == ex["per_block"]["scale_values"]
+    # E8M0 value 2^(e - 127) [NVFP4 page, section 5.3]
+    assert [int(c) - 127 for c in s[0]] == ex["per_block"]["scale_exponents"]
+    assert all(oracle.decode(E4M3, int(c)) == ex["per_block"]["q_value"] for c in q[0])
+    deq = oracle.dequantize(q, s, E4M3, "f32")
+    assert np.array_equal(deq, v64), "the page says both blocks decode exactly"
+
+
+def test_worked_example_shared_scale_flushes_small_half(oracle):
+    ex = load_golden("worked_example_v64.json")["shared_scale"]
+    s = ex["scale_value"]
+    big = oracle.encode(E4M3, 1024.0 / s)
+    small = oracle.encode(E4M3, 2.0 ** -12 / s)
+    assert 2.0 ** -12 / s == ex["scaled_last_32"]
+    assert oracle.decode(E4M3, big) == ex["q_first_32"]
+    assert oracle.decode(E4M3, small) == ex["q_last_32"]
+
+
+# ---------------------------------------------------------------------------
+# Format facts
+# ---------------------------------------------------------------------------
+def test_format_facts(oracle):
+    f = load_golden("fp8_format_facts.json")
+    for fmt, key in ((E4M3, "E4M3"), (E5M2, "E5M2")):
+        t = oracle.decode_table(fmt)
+        fin = t[np.isfinite(t)]
+        pos = np.unique(fin[fin > 0])
+        assert pos.max() == f[key]["max_finite"]
+        assert pos.min() == f[key]["min_subnormal"]
+        ones = pos[(pos >= 1) & (pos < 2)]
+        assert np.all(np.diff(ones) == f[key]["spacing_in_1_2"])
+        assert len(ones) * f[key]["spacing_in_1_2"] == 1.0
+        # the smallest normal: the first value after which spacing stops being the subnormal step
+        assert pos[pos < f[key]["min_normal"]].size == round(f[key]["min_normal"] / f[key]["min_subnormal"]) - 1
+        assert np.isinf(t).any() == f[key]["has_inf"]
+        # codes are ordered by magnitude and the sign is the top bit
+        assert np.all(np.diff(t[:0x7F][np.isfinite(t[:0x7F])]) > 0)
+        assert all(t[c | 0x80] == -t[c] for c in range(0x7F) if np.isfinite(t[c]) and t[c] != 0)
+    # E4M3: 7 non-zero subnormals, exactly one NaN pattern per sign, no Inf
+    t4 = oracle.decode_table(E4M3)
+    assert f["E4M3"]["nonzero_subnormals"] == 7
+    assert np.sum((t4 > 0) & (t4 < f["E4M3"]["min_normal"])) == 7
+    assert [c for c in range(256) if np.isnan(t4[c])] == [0x7F, 0xFF]
+    # E8M0
+    assert oracle.decode_e8m0(0) == 2.0 ** f["E8M0"]["min_exponent"]
+    assert oracle.decode_e8m0(254) == 2.0 ** f["E8M0"]["max_exponent"]
+    assert math.isnan(oracle.decode_e8m0(255))
+    assert all(oracle.decode_e8m0(e) == 2.0 ** (e - 127) for e in range(255))
+    # 8.25 bits per element: 32 one-byte codes + one one-byte scale per block
+    q, s = oracle.quantize_rows(np.ones((1, 32), np.float32), E4M3)
+    assert (q.nbytes + s.nbytes) * 8 == f["block"]["bits"]
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_encode_decode_round_trip_all_codes(oracle, fmt):
+    n_finite = 0
+    for c in range(256):
+        v = oracle.decode(fmt, c)
+        if not math.isfinite(v):
+            continue
+        n_finite += 1
+        assert oracle.encode(fmt, v) == c, hex(c)
+    assert n_finite == (254 if fmt == E4M3 else 248)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_encode_matches_nearest_grid_value_for_all_bf16_and_scales(oracle, fmt):
+    """Every finite bf16 input under every scale code the rule can produce:
+    the quantizer's element codes equal the nearest grid value (ties to even,
+    clamped at the largest finite), and the chosen scale is the anchor's."""
+    emax = EMAX[fmt]
+    bits = np.arange(0x8000, dtype=np.uint16)  # non-negative finite patterns (and Inf/NaN, dropped below)
+    mag = inputs.bf16_bits_to_f32(bits).astype(np.float64)
+    keep = np.isfinite(mag)
+    bits, mag = bits[keep], mag[keep]
+    rows, expect_codes, expect_scale = [], [], []
+    max_code = 127 + 127 - emax  # largest bf16 amax exponent is 127
+    for c in range(0, max_code + 1):
+        anchor = 2.0 ** (c - 127 + emax)
+        sel = bits[mag < 2 * anchor]
+        sel = np.concatenate([sel, sel | np.uint16(0x8000)])  # both signs
+        pad = (-len(sel)) % 31
+        sel = np.concatenate([sel, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        anc = np.full((sel.shape[0], 1), inputs.f32_to_bf16_bits(np.float32([anchor]))[0], np.uint16)
+        blk = np.concatenate([anc, sel], axis=1)
+        rows.append(blk)
+        y = inputs.bf16_bits_to_f32(blk).astype(np.float64) / 2.0 ** (c - 127)
+        expect_codes.append(nearest_code(y, fmt))
+        expect_scale.append(np.full(blk.shape[0], c, np.uint8))
+    x = np.concatenate(rows)
+    q, s = oracle.quantize_rows(x, fmt)
+    assert np.array_equal(s[:, 0], np.concatenate(expect_scale))
+    exp = np.concatenate(expect_codes)
+    bad = np.argwhere(q != exp)
+    assert bad.size == 0, "first mismatch at %s: x=%r code=%#x expected %#x" % (
+        bad[0], inputs.bf16_bits_to_f32(x[tuple(bad[0])]), q[tuple(bad[0])], exp[tuple(bad[0])])
+
+
+# ---------------------------------------------------------------------------
+# Scale rule edge cases and invariants
+# ---------------------------------------------------------------------------
+def test_scale_rule_edges(oracle):
+    z = np.zeros((1, 32), np.float32)
+    q, s = oracle.quantize_rows(z, E4M3)
+    assert s[0, 0] == 0 and not q.any()                      # amax == 0
+    tiny = np.full((1, 32), 2.0 ** -140, np.float32)           # below 2^-119: clamps at code 0
+    q, s = oracle.quantize_rows(tiny, E4M3)
+    assert s[0, 0] == 0 and not q.any()                       # 2^-140 / 2^-127 = 2^-13 -> 0
+    big = np.full((1, 32), 2.0 ** 127, np.float32)
+    _, s = oracle.quantize_rows(big, E4M3)
+    assert s[0, 0] == 127 + 127 - 8
+    _, s = oracle.quantize_rows(big, E5M2)
+    assert s[0, 0] == 127 + 127 - 15
+    for bad in (np.nan, np.inf, -np.inf):
+        x = np.ones((1, 32), np.float32)
+        x[0, 7] = bad
+        q, s = oracle.quantize_rows(x, E4M3)
+        assert s[0, 0] == 0xFF and np.all(q == 0x7F)
+    neg = np.full((1, 32), -(2.0 ** -30), np.float32)
+    neg[0, 0] = 1.0                                           # the rest round to zero, keeping the sign
+    q, _ = oracle.quantize_rows(neg, E4M3)
+    assert np.all(q[0, 1:] == 0x80)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_top_binade_and_sign_symmetry_and_equivariance(oracle, fmt):
+    x = inputs.normal_bf16(77, (64, 256))
+    q, s = oracle.quantize_rows(x, fmt)
+    blocks = q.reshape(64, 8, 32)
+    top_field = 15 if fmt == E4M3 else 30
+    shift = 3 if fmt == E4M3 else 2
+    assert np.all(((blocks & 0x7F).max(axis=2) >> shift) == top_field)
+    qn, sn = oracle.quantize_rows(x ^ np.uint16(0x8000), fmt)
+    assert np.array_equal(sn, s) and np.array_equal(qn, q ^ np.uint8(0x80))
+    for j in (-9, 5):
+        xf = inputs.bf16_bits_to_f32(x) * np.float32(2.0 ** j)
+        qj, sj = oracle.quantize_rows(xf, fmt)
+        assert np.array_equal(qj, q) and np.array_equal(sj.astype(int), s.astype(int) + j)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_relative_error_bound_and_zero_threshold(oracle, fmt):
+    """[FP8 训练为什么能稳, sections 四 and 4.1]: inside the normal range the
+    rounding error is at most 2^-p relative; below half the smallest
+    subnormal step a value becomes zero."""
+    f = load_golden("fp8_format_facts.json")["E4M3" if fmt == E4M3 else "E5M2"]
+    g = inputs.rng(91)
+    x = (g.standard_normal((256, 512)) * np.exp2(g.integers(-20, 20, (256, 1)))).astype(np.float32)
+    x[:, ::97] *= np.float32(2.0 ** 13)  # outliers push many block members out of the normal range
+    q, s = oracle.quantize_rows(x, fmt)
+    xhat = oracle.dequantize(q, s, fmt, "f32").astype(np.float64)
+    X = np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+    r = np.abs(x.astype(np.float64)) / X
+    normal = (r >= f["min_normal"]) & (r <= f["max_finite"])
+    err = np.abs(xhat - x)
+    assert np.all(err[normal] <= f["relative_error_bound"] * np.abs(x[normal]))
+    half_step = f["min_subnormal"] / 2
+    assert np.array_equal(xhat == 0, r <= half_step)
+    if fmt == E4M3:
+        assert half_step == f["zero_threshold"]
+
+
+def test_colwise_is_rowwise_of_transpose_and_differs_from_transposed_codes(oracle):
+    """Blocks are directional [MXFP8 quantization glossary; MXFP8 SM120 software
+    support, section 1.2]: the colwise result is the rowwise quantization of
+    X^T, and in general not the transpose of X's rowwise codes."""
+    x = inputs.normal_bf16(5, (96, 160))
+    x[:, 3] = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(x[:, 3]) * np.float32(4096))
+    qt, st = oracle.quantize_cols(x, E4M3)
+    qr, sr = oracle.quantize_rows(np.ascontiguousarray(x.T), E4M3)
+    assert np.array_equal(qt, qr) and np.array_equal(st, sr)
+    q_row, _ = oracle.quantize_rows(x, E4M3)
+    assert not np.array_equal(qt, q_row.T)
+
+
+def test_kv_write_is_rowwise_of_token_head_rows_scattered(oracle):
+    T, H, D, P, page = 96, 3, 64, 4, 32
+    k = inputs.normal_bf16(11, (T, H, D))
+    v = inputs.normal_bf16(12, (T, H, D))
+    slots = inputs.rng(13).permutation(P * page)[:T].astype(np.int64)
+    slots[5] = -1  # a padding token is skipped
+    kc, ks, vc, vs = oracle.kv_quant_write(k, v, slots, page, P)
+    for src, cache, scale in ((k, kc, ks), (v, vc, vs)):
+        q, s = oracle.quantize_rows(src.reshape(T * H, D), E4M3)
+        q = q.reshape(T, H, D)
+        s = s.reshape(T, H, D // 32)
+        flat_c = cache.reshape(P * page, H, D)
+        flat_s = scale.reshape(P * page, H, D // 32)
+        for t in range(T):
+            if slots[t] < 0:
+                continue
+            assert np.array_equal(flat_c[slots[t]], q[t]) and np.array_equal(flat_s[slots[t]], s[t])
+        untouched = np.setdiff1d(np.arange(P * page), slots[slots >= 0])
+        assert not flat_c[untouched].any() and not flat_s[untouched].any()
+
+
+# ---------------------------------------------------------------------------
+# Dequantize
+# ---------------------------------------------------------------------------
+def test_dequantize_exact_and_bf16_rounding(oracle):
+    import torch
+    g = inputs.rng(21)
+    codes = g.integers(0, 256, (64, 128), dtype=np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes[codes == 0xFF] = 0xFE
+    scales = g.integers(0, 255, (64, 4), dtype=np.uint8)
+    scales[0, 0] = 0      # 2^-127: f32 subnormal outputs
+    scales[1, 0] = 254    # 2^127: overflow to infinity
+    y32 = oracle.dequantize(codes, scales, E4M3, "f32")
+    exact = np.array([[value_of(int(codes[r, c]), E4M3) * Fraction(2) ** (int(scales[r, c // 32]) - 127)
+                       for c in range(128)] for r in range(64)], dtype=object)
+    for r in range(64):
+        for c in range(128):
+            v = exact[r, c]
+            want = np.float32(float(v)) if abs(v) < Fraction(2) ** 128 else np.float32(np.inf) * (1 if v > 0 else -1)
+            assert y32[r, c] == want or (np.isinf(want) and y32[r, c] == want)
+    ybf = oracle.dequantize(codes, scales, E4M3, "bf16")
+    ref = torch.from_numpy(y32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ybf, ref)
+    nan_s = scales.copy()
+    nan_s[2, 1] = 0xFF
+    y = oracle.dequantize(codes, nan_s, E4M3, "f32")
+    assert np.all(np.isnan(y[2, 32:64])) and not np.isnan(y[2, :32]).any()
+
+
+def test_dequant_of_quant_is_identity_on_grid(oracle):
+    g = inputs.rng(31)
+    codes = g.integers(0, 0x7F, (32, 64), dtype=np.uint8) | (g.integers(0, 2, (32, 64), dtype=np.uint8) << 7)
+    codes[:, ::32] = 0x7E  # each block's top element sits in the top binade, so requantizing keeps the scale
+    sc = g.integers(100, 150, (32, 2), dtype=np.uint8)
+    x = oracle.dequantize(codes, sc, E4M3, "f32")
+    q, s = oracle.quantize_rows(x, E4M3)
+    assert np.array_equal(s, sc)
+    assert np.array_equal(q[q != 0x80], codes[q != 0x80])  # -0 and +0 are the same grid point
+    assert np.array_equal(oracle.dequantize(q, s, E4M3, "f32"), x)
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled matrix product [MXFP8 SM120 software support, section 0.3;
+# NVFP4 page, sections 7.1-7.4]
+# ---------------------------------------------------------------------------
+def _codes_of(vals, fmt=E4M3):
+    return np.array([oracle_free_code(v, fmt) for v in vals], np.uint8)
+
+
+def oracle_free_code(v, fmt):
+    return int(nearest_code(np.array([v], np.float64), fmt)[0])
+
+
+def test_block_dot_example(oracle):
+    ex = load_golden("block_dot_example.json")
+    a = np.zeros((1, 32), np.uint8)
+    b = np.zeros((1, 32), np.uint8)
+    a[0, :4] = _codes_of(ex["q"])
+    b[0, :4] = _codes_of(ex["p"])
+    y, t = oracle.gemm(a, np.array([[127]], np.uint8), E4M3, b, np.array([[127]], np.uint8), E4M3)
+    assert y[0, 0] == ex["dot"]
+    y, _ = oracle.gemm(a, np.array([[128]], np.uint8), E4M3, b, np.array([[128]], np.uint8), E4M3)
+    assert y[0, 0] == ex["dot"] * 4
+    assert ex["dot"] * ex["page_scale"] == ex["scaled_dot"]
+
+
+def test_block_scales_do_not_factor_out_of_the_whole_sum(oracle):
+    a = np.zeros((1, 64), np.uint8)
+    b = np.zeros((1, 64), np.uint8)
+    a[0, 0] = a[0, 32] = _codes_of([1.0])[0]
+    b[0, 0] = b[0, 32] = _codes_of([1.0])[0]
+    sa = np.array([[130, 120]], np.uint8)
+    sb = np.array([[127, 127]], np.uint8)
+    y, _ = oracle.gemm(a, sa, E4M3, b, sb, E4M3)
+    assert y[0, 0] == 2.0 ** 3 + 2.0 ** -7
+    assert y[0, 0] != 2.0 * 2.0 ** 3  # one pair of scales for the whole sum would give this
+
+
+def test_worked_vector_self_product_closed_form(oracle):
+    v64 = inputs.tiny()["v64"]
+    q, s = oracle.quantize_rows(v64, E4M3)
+    y, t = oracle.gemm(q, s, E4M3, q, s, E4M3)
+    assert y[0, 0] == 2.0 ** 25 + 2.0 ** -19 == t[0, 0]
+    shared = np.full((1, 2), 129, np.uint8)  # one scale s = 4 for both blocks
+    qs = np.array([[oracle.encode(E4M3, float(x) / 4) for x in v64[0]]], np.uint8)
+    y, _ = oracle.gemm(qs, shared, E4M3, qs, shared, E4M3)
+    assert y[0, 0] == 2.0 ** 25
+
+
+@pytest.mark.parametrize("afmt,bfmt", [(E4M3, E4M3), (E5M2, E4M3)])
+def test_unit_scales_reduce_to_numpy_matmul(oracle, afmt, bfmt):
+    g = inputs.rng(41)
+    M, N, K = 24, 40, 256
+    a = g.integers(0, 256, (M, K), dtype=np.uint8)
+    b = g.integers(0, 256, (N, K), dtype=np.uint8)
+    for arr, fmt in ((a, afmt), (b, bfmt)):
+        t = oracle.decode_table(fmt)
+        arr[~np.isfinite(t[arr])] = 0x41
+    if afmt == E5M2:
+        a[(a & 0x7F) > 0x6F] &= 0x6F  # keep products inside the range where fp64 sums stay exact
+    ones_a = np.full((M, K // 32), 127, np.uint8)
+    ones_b = np.full((N, K // 32), 127, np.uint8)
+    y, t = oracle.gemm(a, ones_a, afmt, b, ones_b, bfmt)
+    A = oracle.decode_table(afmt)[a]
+    B = oracle.decode_table(bfmt)[b]
+    assert np.array_equal(y, A @ B.T)
+    assert np.array_equal(t, np.abs(A) @ np.abs(B).T)
+
+
+@pytest.mark.parametrize("K", [32, 64, 128])
+@pytest.mark.parametrize("afmt", [E4M3, E5M2])
+def test_gemm_matches_exact_rational_sum(oracle, K, afmt):
+    g = inputs.rng(50 + K + afmt)
+    M, N = 3, 4
+    def pick(shape, fmt):
+        c = g.integers(0, 256, shape, dtype=np.uint8)
+        ok = np.array([[np.isfinite(oracle.decode(fmt, int(x))) for x in row] for row in c])
+        c[~ok] = 0x03  # a subnormal
+        c[:, 1] = 0x02  # make sure subnormals appear
+        return c
+    a, b = pick((M, K), afmt), pick((N, K), E4M3)
+    sa = g.integers(100, 150, (M, K // 32), dtype=np.uint8)
+    sb = g.integers(100, 150, (N, K // 32), dtype=np.uint8)
+    y, t = oracle.gemm(a, sa, afmt, b, sb, E4M3)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(value_of(int(a[m, k]), afmt) * Fraction(2) ** (int(sa[m, k // 32]) - 127)
+                        * value_of(int(b[n, k]), E4M3) * Fraction(2) ** (int(sb[n, k // 32]) - 127)
+                        for k in range(K))
+            tabs = sum(abs(value_of(int(a[m, k]), afmt) * value_of(int(b[n, k]), E4M3))
+                       * Fraction(2) ** (int(sa[m, k // 32]) + int(sb[n, k // 32]) - 254) for k in range(K))
+            assert abs(Fraction(y[m, n]) - exact) <= Fraction(2) ** -50 * tabs
+            assert abs(Fraction(t[m, n]) - tabs) <= Fraction(2) ** -50 * tabs
+
+
+def test_gemm_at_equals_full_product(oracle):
+    g = inputs.rng(61)
+    x = inputs.normal_bf16(62, (40, 96))
+    w = inputs.normal_bf16(63, (24, 96))
+    a, sa = oracle.quantize_rows(x, E4M3)
+    b, sb = oracle.quantize_rows(w, E4M3)
+    y, t = oracle.gemm(a, sa, E4M3, b, sb, E4M3)
+    mi = g.integers(0, 40, 50)
+    ni = g.integers(0, 24, 50)
+    ys, ts = oracle.gemm_at(a, sa, E4M3, b, sb, E4M3, mi, ni)
+    assert np.array_equal(ys, y[mi, ni]) and np.array_equal(ts, t[mi, ni])
+    # y = A B^T: swapping the operands transposes the result
+    y2, _ = oracle.gemm(b, sb, E4M3, a, sa, E4M3)
+    assert np.array_equal(y2, y.T)
