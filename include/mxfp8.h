@@ -1,0 +1,206 @@
+/*
+ * mxfp8.h -- C ABI of libmxfp8: MXFP8 block-scaled quantization and the
+ * block-scaled matrix product on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [SM120]  "MXFP8 SM120 software support" (xuesongtap.github.io, 2026-09-22)
+ *   [GLOSS]  "MXFP8 quantization" glossary (robocikowo.com)
+ *   [FP8DS]  "FP8 训练为什么能稳：把缩放因子的粒度与累加精度算清楚" (magicnetworld.com)
+ *   [NVFP4]  "NVFP4 如何用 4 bit 实现高精度" (theluyuan.com)
+ *
+ * Format. An MXFP8 block is 32 consecutive FP8 elements (E4M3 or E5M2) that
+ * share one E8M0 scale 2^(e-127); decoded value x_hat_i = s_b * q_i
+ * [SM120 §0.1]. Codes and scales live in separate arrays [SM120 §0.1]:
+ * codes are one byte per element, scales one byte per block.
+ *
+ * Scale rule (the pages leave it to the implementation [SM120 §0.1]; this
+ * library fixes it): X = 2^(floor(log2 amax) - emax_elem), emax_elem = 8 for
+ * E4M3 and 15 for E5M2, code = clamp(floor(log2 amax) - emax_elem + 127, 0,
+ * 254); amax == 0 gives code 0; a block holding NaN or Inf gets code 0xFF and
+ * element codes 0x7F. Elements: q = RNE(x / X) with ties to even and
+ * saturation at +-448 (E4M3) / +-57344 (E5M2); the sign of x is kept, so
+ * negative values that round to zero give 0x80.
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller. The library
+ *     allocates no memory, keeps no pointer after returning, and holds no
+ *     mutable global state; calls on different streams may run concurrently.
+ *   - Work is enqueued on `stream` (asynchronous; no implicit sync). Argument
+ *     errors are detected on the host before anything is launched and are
+ *     returned synchronously; then nothing is written. A launch failure
+ *     returns MX_ERR_HIP. Device-side faults surface at the caller's next
+ *     synchronization.
+ *   - Sizes and leading dimensions ("ld", row pitches) are in elements of the
+ *     array they describe (bytes for codes and scales). Matrices are
+ *     row-major: element (r, c) of an array with pitch ld is at r * ld + c.
+ *   - A blocked dimension must be a multiple of 32 (MX_ERR_SHAPE otherwise).
+ *   - Alignment (MX_ERR_ALIGN otherwise): the base address and the byte pitch
+ *     of every high-precision input, of the dequantize output and of every
+ *     code array must be multiples of 16 bytes. Scale arrays have no
+ *     alignment requirement; the mx_gemm output needs only the natural
+ *     alignment of its element type.
+ *   - Zero-sized problems are valid and launch nothing.
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mx_status_t;
+#define MX_OK          0
+#define MX_ERR_NULL   -1 /* a required pointer is NULL */
+#define MX_ERR_SHAPE  -2 /* negative size, pitch smaller than the row, blocked dim not a multiple of 32 */
+#define MX_ERR_ALIGN  -3 /* base address or pitch breaks the 16-byte rule above */
+#define MX_ERR_FORMAT -4 /* unknown element format or data type */
+#define MX_ERR_DEVICE -5 /* current device is not gfx950 */
+#define MX_ERR_HIP    -6 /* the HIP runtime reported an error at launch */
+
+/* Element encodings [SM120 §0.1 table; GLOSS]: E4M3 (448 max, used for
+ * activations and weights), E5M2 (57344 max, used for gradients). */
+typedef enum { MX_E4M3 = 0, MX_E5M2 = 1 } mx_fmt_t;
+/* High-precision data types of inputs and outputs. */
+typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype_t;
+
+/*
+ * mx_quantize -- rowwise (1 x 32) MXFP8 quantization.
+ * [SM120 §0.1, §0.2; GLOSS]: per block of 32 consecutive values along a row,
+ * find amax, choose a power-of-two E8M0 scale, round x / scale to FP8.
+ *
+ *   x    [rows x cols] input (xdt), pitch ldx >= cols
+ *   q    [rows x cols] codes out, pitch ldq >= cols
+ *   s    [rows x cols/32] scales out, pitch lds >= cols/32
+ * cols % 32 == 0.
+ */
+mx_status_t mx_quantize(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx, mx_fmt_t fmt,
+                        uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, hipStream_t stream);
+
+/*
+ * mx_quantize_colwise -- columnwise (32 x 1) MXFP8 quantization, stored
+ * transposed. Blocks are directional, so the second representation the
+ * backward pass needs is quantized again from the high-precision input; a
+ * transpose of the rowwise codes is not equivalent [SM120 §1.2, §1.3; GLOSS].
+ *
+ *   x    [rows x cols] input (xdt), pitch ldx >= cols
+ *   qt   [cols x rows] codes out (qt[c][r] is element (r, c)), pitch ldq >= rows
+ *   st   [cols x rows/32] scales out (st[c][r/32]), pitch lds >= rows/32
+ * rows % 32 == 0. The result equals mx_quantize applied to x^T, so it is
+ * directly a K-contiguous operand of mx_gemm with K = rows.
+ */
+mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                                mx_fmt_t fmt, uint8_t* qt, int64_t ldq, uint8_t* st, int64_t lds,
+                                hipStream_t stream);
+
+/*
+ * mx_dequantize -- x_hat = s_b * q_i [SM120 §0.1], exact in f32, then
+ * rounded to nearest-even for bf16 output. A scale code 0xFF (NaN) makes its
+ * whole block NaN; NaN results are written as the canonical quiet NaN
+ * (0x7FC00000 / 0x7FC0).
+ *
+ *   q    [rows x cols] codes, pitch ldq;  s [rows x cols/32] scales, pitch lds
+ *   y    [rows x cols] output (ydt), pitch ldy
+ * cols % 32 == 0.
+ */
+mx_status_t mx_dequantize(const uint8_t* q, int64_t ldq, const uint8_t* s, int64_t lds, mx_fmt_t fmt, int64_t rows,
+                          int64_t cols, void* y, mx_dtype_t ydt, int64_t ldy, hipStream_t stream);
+
+/*
+ * mx_kv_quant_write -- fused E4M3 quantization and paged KV-cache write
+ * [SM120 §0.2]: for every token t and head h, the D values of K and of V are
+ * quantized in blocks of 32 along the head dimension and written to cache
+ * slot slot_mapping[t]: page = slot / page_size, offset = slot % page_size.
+ *
+ *   k, v           [T x H x D] inputs (dt); token t, head h starts at t*ld_token + h*D
+ *   slot_mapping   [T] int64 (device); a negative slot marks a padding token
+ *                  and is skipped; slots >= page_size * num_pages are ignored
+ *   k_cache, v_cache [num_pages x page_size x H x D] codes out
+ *   k_scale, v_scale [num_pages x page_size x H x D/32] scales out
+ * D % 32 == 0, ld_token >= H*D. Slots not named by slot_mapping are left
+ * untouched.
+ */
+mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_t dt, int64_t T, int64_t H, int64_t D,
+                              int64_t ld_token, const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* k_scale,
+                              uint8_t* v_cache, uint8_t* v_scale, int64_t page_size, int64_t num_pages,
+                              hipStream_t stream);
+
+/*
+ * mx_gemm -- block-scaled matrix product [SM120 §0.3; NVFP4 §7.1, §7.4]:
+ *
+ *   y[m][n] = sum_b sa[m][b] * sb[n][b] * sum_{i<32} a[m][32b+i] * b[n][32b+i]
+ *
+ * with both operands K-contiguous (y = A * B^T; the "TN" call of a
+ * column-major GEMM interface [SM120 §1.1, §1.2]). The per-block scale
+ * products stay inside the sum over blocks; accumulation is in FP32. Other
+ * transpositions are obtained by quantizing the operand colwise, which
+ * yields a K-contiguous array directly.
+ *
+ * Batching: the problem is repeated for p = 0 .. batch_outer*batch_inner-1,
+ * with o = p / batch_inner and i = p % batch_inner; operand X of problem
+ * (o, i) starts at X + o*stride_X_outer + i*stride_X_inner (elements).
+ * Zero batch sizes mean 1.
+ *
+ * Paged B: when b_page_table != NULL, row n of B in problem (o, i) is read
+ * from page P = b_page_table[o * b_pages_per_seq + n / b_page_rows] at
+ *   b  + P*b_page_stride   + (n % b_page_rows)*ldb  + i*stride_b_inner
+ *   sb + P*b_page_stride_s + (n % b_page_rows)*ldsb + i*stride_sb_inner
+ * (stride_b_outer and stride_sb_outer are then unused). The page table is a
+ * device int32 array of batch_outer * b_pages_per_seq entries whose values
+ * must index valid pages; the caller guarantees that.
+ *
+ * K % 32 == 0. Output y is f32 or bf16 (round to nearest even); y needs only
+ * the natural alignment of its element type (wider stores are used when the
+ * pitch allows them).
+ *
+ * Accumulation (field `accum`). The sum over blocks is FP32 in every mode;
+ * the modes differ inside one matrix instruction:
+ *   MX_ACCUM_FP8  -- v_mfma_scale_f32_16x16x128_f8f6f4 on the codes, peak
+ *                    rate. On gfx950 this instruction adds the products of
+ *                    each group of 8 consecutive k with only about 14
+ *                    significant bits, aligned to the group's largest product
+ *                    (measured), i.e. a per-group error up to ~2^-13 of that
+ *                    product. [FP8DS §6.1-§6.3] discusses the same kind of
+ *                    limited-precision accumulation in FP8 tensor cores.
+ *   MX_ACCUM_FP32 -- codes decoded exactly to bf16 with the block scale
+ *                    folded in (exact for scale codes 3..246 with E4M3 and
+ *                    10..239 with E5M2), then bf16 MFMA with FP32-level
+ *                    accumulation; half the peak rate of MX_ACCUM_FP8.
+ *   MX_ACCUM_AUTO -- MX_ACCUM_FP8 when both operands are E4M3 and K >= 2048,
+ *                    where the grouped error stays far below 1e-5 * sum|a b|
+ *                    for data of Gaussian-like spread; MX_ACCUM_FP32 otherwise.
+ */
+typedef enum { MX_ACCUM_AUTO = 0, MX_ACCUM_FP8 = 1, MX_ACCUM_FP32 = 2 } mx_accum_t;
+
+typedef struct mx_gemm_desc {
+    int64_t M, N, K;
+    const uint8_t* a;  int64_t lda;  const uint8_t* sa; int64_t ldsa; mx_fmt_t a_fmt;
+    const uint8_t* b;  int64_t ldb;  const uint8_t* sb; int64_t ldsb; mx_fmt_t b_fmt;
+    void* y;           int64_t ldy;  mx_dtype_t y_dtype;
+    int64_t batch_outer, batch_inner;
+    int64_t stride_a_outer, stride_a_inner, stride_sa_outer, stride_sa_inner;
+    int64_t stride_b_outer, stride_b_inner, stride_sb_outer, stride_sb_inner;
+    int64_t stride_y_outer, stride_y_inner;
+    const int32_t* b_page_table;
+    int64_t b_pages_per_seq, b_page_rows, b_page_stride, b_page_stride_s;
+    mx_accum_t accum;
+} mx_gemm_desc_t;
+
+mx_status_t mx_gemm(const mx_gemm_desc_t* desc, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* mx_status_string(mx_status_t status);
+
+/*
+ * mx_query_support -- can this library run on `device`? Returns MX_OK, or an
+ * error code with *reason (if reason != NULL) set to a static explanation:
+ * the (bool, reason) shape of an availability check [SM120 §2].
+ */
+mx_status_t mx_query_support(int device, const char** reason);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXFP8_H */

@@ -1,0 +1,208 @@
+"""libmxfp8 for MI355X: MXFP8 block-scaled quantization and the block-scaled
+matrix product, as hand-written HIP kernels behind a C ABI (include/mxfp8.h).
+
+This package is the thin Python binding: each function has the name of the C
+entry point it calls, takes torch tensors on the GPU (torch provides device
+memory and the current stream), allocates outputs when none are given, and
+raises MXError on any non-OK status. Nothing here computes; there is no CPU
+fallback.
+
+Layouts (row-major, unit stride along the last dimension):
+  * codes  uint8 [rows, cols]; E8M0 scales uint8 [rows, cols/32];
+  * mx_quantize_colwise returns the codes and scales of X^T (blocks down the
+    columns of X), i.e. [cols, rows] and [cols, rows/32];
+  * mx_gemm(a, sa, b, sb) computes y = A * B^T for A [M, K], B [N, K].
+"""
+import ctypes
+
+from ._lib import (BLOCK, MX_ACCUM_AUTO, MX_ACCUM_FP8, MX_ACCUM_FP32, MX_BF16, MX_E4M3, MX_E5M2, MX_F32, MXError,
+                   check, lib, mx_gemm_desc_t)
+
+__all__ = [
+    "MX_E4M3", "MX_E5M2", "MX_F32", "MX_BF16", "BLOCK", "MXError",
+    "MX_ACCUM_AUTO", "MX_ACCUM_FP8", "MX_ACCUM_FP32",
+    "mx_quantize", "mx_quantize_colwise", "mx_dequantize", "mx_kv_quant_write", "mx_gemm",
+    "mx_gemm_desc", "mx_paged_scores", "mx_status_string", "mx_query_support",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MX_F32
+    if t.dtype == torch.bfloat16:
+        return MX_BF16
+    raise TypeError("expected float32 or bfloat16, got %s" % t.dtype)
+
+
+def _rowmajor(t, name, ndim=2):
+    if t.dim() != ndim:
+        raise ValueError("%s must be %d-D" % (name, ndim))
+    if t.stride(-1) != 1 and t.numel() > 0:
+        raise ValueError("%s must have unit stride along its last dimension" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t):
+    """Row pitch of a 2-D tensor; a single row may carry any stride, so its
+    pitch is taken as its length."""
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def mx_quantize(x, fmt=MX_E4M3, q=None, s=None, stream=None):
+    """Rowwise MXFP8 quantization of x [rows, cols] -> (codes, scales)."""
+    torch = _torch()
+    _rowmajor(x, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    s = torch.empty((rows, cols // BLOCK), dtype=torch.uint8, device=x.device) if s is None else s
+    check("mx_quantize", lib().mx_quantize(_p(x), _dtype_code(x), rows, cols, _ld(x), fmt, _p(q), _ld(q),
+                                           _p(s), _ld(s), _stream(stream)))
+    return q, s
+
+
+def mx_quantize_colwise(x, fmt=MX_E4M3, qt=None, st=None, stream=None):
+    """Colwise MXFP8 quantization of x [rows, cols] (blocks of 32 down each
+    column), stored transposed -> (codes [cols, rows], scales [cols, rows/32])."""
+    torch = _torch()
+    _rowmajor(x, "x")
+    rows, cols = x.shape
+    qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if qt is None else qt
+    st = torch.empty((cols, rows // BLOCK), dtype=torch.uint8, device=x.device) if st is None else st
+    check("mx_quantize_colwise", lib().mx_quantize_colwise(_p(x), _dtype_code(x), rows, cols, _ld(x), fmt,
+                                                           _p(qt), _ld(qt), _p(st), _ld(st),
+                                                           _stream(stream)))
+    return qt, st
+
+
+def mx_dequantize(q, s, fmt=MX_E4M3, out_dtype=None, y=None, stream=None):
+    """x_hat = scale * code -> y [rows, cols] in float32 or bfloat16."""
+    torch = _torch()
+    _rowmajor(q, "q")
+    rows, cols = q.shape
+    if y is None:
+        y = torch.empty((rows, cols), dtype=out_dtype or torch.float32, device=q.device)
+    check("mx_dequantize", lib().mx_dequantize(_p(q), _ld(q), _p(s), _ld(s), fmt, rows, cols, _p(y),
+                                               _dtype_code(y), _ld(y), _stream(stream)))
+    return y
+
+
+def mx_kv_quant_write(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale, stream=None):
+    """Fused E4M3 quantize + paged write of k, v [T, H, D] into
+    k_cache / v_cache [pages, page_size, H, D] and k_scale / v_scale
+    [pages, page_size, H, D/32] at slot_mapping [T] (int64)."""
+    torch = _torch()
+    if k.shape != v.shape or k.dim() != 3 or k.stride() != v.stride():
+        raise ValueError("k and v must be [T, H, D] with equal strides")
+    T, H, D = k.shape
+    if k.stride(2) != 1 or k.stride(1) != D:
+        raise ValueError("k/v must be contiguous within a token")
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    for c, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if tuple(c.shape) != (pages, page_size, H, D) or not c.is_contiguous():
+            raise ValueError("%s must be contiguous [pages, page_size, H, D]" % n)
+    for c, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if tuple(c.shape) != (pages, page_size, H, D // BLOCK) or not c.is_contiguous():
+            raise ValueError("%s must be contiguous [pages, page_size, H, D/32]" % n)
+    check("mx_kv_quant_write", lib().mx_kv_quant_write(_p(k), _p(v), _dtype_code(k), T, H, D, k.stride(0),
+                                                       _p(slot_mapping), _p(k_cache), _p(k_scale), _p(v_cache),
+                                                       _p(v_scale), page_size, pages, _stream(stream)))
+
+
+def mx_gemm_desc(desc, stream=None):
+    """Call mx_gemm with a filled mx_gemm_desc_t."""
+    check("mx_gemm", lib().mx_gemm(ctypes.byref(desc), _stream(stream)))
+
+
+def mx_gemm(a, sa, b, sb, a_fmt=MX_E4M3, b_fmt=MX_E4M3, out_dtype=None, y=None, stream=None, accum=MX_ACCUM_AUTO):
+    """y [M, N] = block-scaled A [M, K] * B [N, K]^T with FP32 accumulation
+    (accum selects the matrix-instruction path; see include/mxfp8.h)."""
+    torch = _torch()
+    for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
+        _rowmajor(t, n)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or sa.shape != (M, K // BLOCK) or sb.shape != (N, K // BLOCK):
+        raise ValueError("shape mismatch: a %s sa %s b %s sb %s" % (tuple(a.shape), tuple(sa.shape), tuple(b.shape),
+                                                                    tuple(sb.shape)))
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    d = mx_gemm_desc_t()
+    d.M, d.N, d.K = M, N, K
+    d.a, d.lda, d.sa, d.ldsa, d.a_fmt = a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), a_fmt
+    d.b, d.ldb, d.sb, d.ldsb, d.b_fmt = b.data_ptr(), _ld(b), sb.data_ptr(), _ld(sb), b_fmt
+    d.y, d.ldy, d.y_dtype = y.data_ptr(), _ld(y), _dtype_code(y)
+    d.accum = accum
+    mx_gemm_desc(d, stream)
+    return y
+
+
+def mx_paged_scores(q_codes, q_scales, k_cache, k_scale, page_table, seq_len, out=None, stream=None,
+                    accum=MX_ACCUM_AUTO):
+    """QK^T scores per (sequence, head) with K read through a page table.
+
+    q_codes [S*seq_len, H, D] / q_scales [S*seq_len, H, D/32] (rowwise E4M3
+    along D); k_cache [pages, page_size, H, D] / k_scale [..., D/32];
+    page_table int32 [S, seq_len/page_size]. Returns f32 [S, H, seq_len,
+    seq_len] with out[s, h, i, j] = q(s, i, h) . k(s, j, h), the block-scaled
+    product over D."""
+    torch = _torch()
+    tokens, H, D = q_codes.shape
+    S = page_table.shape[0]
+    page_size = k_cache.shape[1]
+    if tokens != S * seq_len or page_table.shape[1] * page_size < seq_len:
+        raise ValueError("inconsistent query/page-table sizes")
+    if not (q_codes.is_contiguous() and q_scales.is_contiguous() and k_cache.is_contiguous()
+            and k_scale.is_contiguous() and page_table.is_contiguous()):
+        raise ValueError("inputs must be contiguous")
+    if page_table.dtype != torch.int32:
+        raise TypeError("page_table must be int32")
+    if out is None:
+        out = torch.empty((S, H, seq_len, seq_len), dtype=torch.float32, device=q_codes.device)
+    d = mx_gemm_desc_t()
+    d.M, d.N, d.K = seq_len, seq_len, D
+    d.a, d.lda, d.sa, d.ldsa, d.a_fmt = q_codes.data_ptr(), H * D, q_scales.data_ptr(), H * (D // BLOCK), MX_E4M3
+    d.b, d.ldb, d.sb, d.ldsb, d.b_fmt = k_cache.data_ptr(), H * D, k_scale.data_ptr(), H * (D // BLOCK), MX_E4M3
+    d.y, d.ldy, d.y_dtype = out.data_ptr(), seq_len, MX_F32
+    d.batch_outer, d.batch_inner = S, H
+    d.stride_a_outer, d.stride_a_inner = seq_len * H * D, D
+    d.stride_sa_outer, d.stride_sa_inner = seq_len * H * (D // BLOCK), D // BLOCK
+    d.stride_b_inner, d.stride_sb_inner = D, D // BLOCK
+    d.stride_y_outer, d.stride_y_inner = H * seq_len * seq_len, seq_len * seq_len
+    d.b_page_table = page_table.data_ptr()
+    d.b_pages_per_seq = page_table.shape[1]
+    d.b_page_rows = page_size
+    d.b_page_stride = page_size * H * D
+    d.b_page_stride_s = page_size * H * (D // BLOCK)
+    d.accum = accum
+    mx_gemm_desc(d, stream)
+    return out
+
+
+def mx_status_string(status):
+    return lib().mx_status_string(status).decode()
+
+
+def mx_query_support(device=0):
+    """(ok: bool, reason: str) for `device`."""
+    r = ctypes.c_char_p()
+    st = lib().mx_query_support(device, ctypes.byref(r))
+    return st == 0, (r.value.decode() if r.value else "")

@@ -1,0 +1,82 @@
+"""ctypes binding of libmxfp8 (include/mxfp8.h).
+
+Argument marshalling only: every step runs in the HIP library. torch supplies
+device memory and the current stream. There is no fallback: if the library is
+not built, or a call returns an error, this module raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxfp8.so")
+
+MX_OK = 0
+MX_E4M3 = 0
+MX_E5M2 = 1
+MX_F32 = 0
+MX_BF16 = 1
+MX_ACCUM_AUTO = 0
+MX_ACCUM_FP8 = 1
+MX_ACCUM_FP32 = 2
+BLOCK = 32
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+
+
+class MXError(RuntimeError):
+    def __init__(self, func, status, text):
+        super().__init__("%s failed: %s (%d)" % (func, text, status))
+        self.status = status
+
+
+class mx_gemm_desc_t(ctypes.Structure):
+    _fields_ = [
+        ("M", _i64), ("N", _i64), ("K", _i64),
+        ("a", _p), ("lda", _i64), ("sa", _p), ("ldsa", _i64), ("a_fmt", ctypes.c_int),
+        ("b", _p), ("ldb", _i64), ("sb", _p), ("ldsb", _i64), ("b_fmt", ctypes.c_int),
+        ("y", _p), ("ldy", _i64), ("y_dtype", ctypes.c_int),
+        ("batch_outer", _i64), ("batch_inner", _i64),
+        ("stride_a_outer", _i64), ("stride_a_inner", _i64), ("stride_sa_outer", _i64), ("stride_sa_inner", _i64),
+        ("stride_b_outer", _i64), ("stride_b_inner", _i64), ("stride_sb_outer", _i64), ("stride_sb_inner", _i64),
+        ("stride_y_outer", _i64), ("stride_y_inner", _i64),
+        ("b_page_table", _p),
+        ("b_pages_per_seq", _i64), ("b_page_rows", _i64), ("b_page_stride", _i64), ("b_page_stride_s", _i64),
+        ("accum", ctypes.c_int),
+    ]
+
+
+_lib = None
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "mx_quantize": (_i32, [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _p, _i64, _p, _i64, _p]),
+    "mx_quantize_colwise": (_i32, [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _p, _i64, _p, _i64, _p]),
+    "mx_dequantize": (_i32, [_p, _i64, _p, _i64, ctypes.c_int, _i64, _i64, _p, ctypes.c_int, _i64, _p]),
+    "mx_kv_quant_write": (_i32, [_p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p]),
+    "mx_gemm": (_i32, [ctypes.POINTER(mx_gemm_desc_t), _p]),
+    "mx_status_string": (ctypes.c_char_p, [_i32]),
+    "mx_query_support": (_i32, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p)]),
+}
+
+
+def lib():
+    """Load libmxfp8.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmxfp8.so is not built: run `python -m microscaling_block_scaled_amd.build` "
+                              "(or __graft_entry__.build())")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def check(func, status):
+    if status != MX_OK:
+        raise MXError(func, status, lib().mx_status_string(status).decode())

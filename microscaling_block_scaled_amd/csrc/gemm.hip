@@ -1,0 +1,367 @@
+// gemm.hip -- block-scaled matrix product on gfx950 scaled-FP8 MFMA.
+//
+//   y[m][n] = sum_b sa[m][b] * sb[n][b] * sum_{i<32} a[m][32b+i] * b[n][32b+i]
+//
+// [MXFP8 SM120 software support, §0.3; NVFP4 如何用 4 bit 实现高精度, §7.1,
+// §7.4]: every 32-element block carries its own pair of scales, so the scales
+// cannot be pulled out of the whole sum; the matrix instruction applies them
+// per block inside the multiply-accumulate. On gfx950 that instruction is
+// v_mfma_scale_f32_16x16x128_f8f6f4: 128 K per issue = 4 blocks, with each
+// lane supplying the E8M0 scale of one (row, block) pair; accumulation is
+// FP32.
+//
+// Tiling: a workgroup of 4 waves computes a BM x BN tile; the waves form a
+// 2 x 2 grid of (BM/2) x (BN/2) sub-tiles built from 16 x 16 MFMA tiles.
+// K advances 128 bytes (4 blocks) per step through a double-buffered LDS
+// stage. The MFMA's first operand is the B fragment and its second the A
+// fragment, so each lane ends up owning 4 consecutive output columns of one
+// row and the epilogue stores 8 (bf16) or 16 (f32) contiguous bytes.
+// LDS rows are 128 bytes; their 16-byte chunks are XOR-swizzled by row so
+// that the fragment reads (16 rows at one K offset) hit distinct banks.
+//
+// Two accumulation modes share the staging:
+//  * kModeFP8: one v_mfma_scale_f32_16x16x128_f8f6f4 per 128 K on the raw
+//    codes. Inside the instruction each group of 8 consecutive k is summed
+//    with only ~14 significant bits aligned to the group's largest product.
+//  * kModeBF16: per 32-K block, the codes are decoded to bf16 with the block
+//    scale folded in (v_cvt_scalef32_pk_bf16_{fp8,bf8}; exact for the scale
+//    range the quantizer produces), then v_mfma_f32_16x16x32_bf16, whose
+//    accumulation is FP32-level. Half the peak rate.
+#include "mx_common.hpp"
+
+namespace {
+using namespace mx;
+
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+
+constexpr int kModeFP8 = 0;
+constexpr int kModeBF16 = 1;
+
+constexpr int kThreads = 256;
+constexpr int kBK = 128;  // K bytes per step = 4 MX blocks
+
+struct GemmArgs {
+  int64_t M, N, K;
+  const uint8_t* a; int64_t lda; const uint8_t* sa; int64_t ldsa;
+  const uint8_t* b; int64_t ldb; const uint8_t* sb; int64_t ldsb;
+  void* y; int64_t ldy;
+  int64_t batch_inner;
+  int64_t sa_o, sa_i, ssa_o, ssa_i, sb_o, sb_i, ssb_o, ssb_i, sy_o, sy_i;
+  const int32_t* page_table; int64_t pages_per_seq, page_rows, page_stride, page_stride_s;
+  uint32_t tiles_m, tiles_n;
+  uint32_t scales_dword;  // 1: every row's 4 scale bytes of a K step can be read as one aligned dword
+  uint32_t y_vec;         // 1: output rows allow 8/16-byte vector stores
+};
+
+// 2^(code - 127) as an f32 multiplier; code 0xFF (NaN scale) gives NaN.
+__device__ __forceinline__ float scale_value(uint32_t code) {
+  return code == 0xFFu ? __uint_as_float(0x7FC00000u) : __uint_as_float(code ? (code << 23) : 0x00400000u);
+}
+
+// Eight codes (two dwords) -> eight bf16 values times the block scale.
+template <int FMT>
+__device__ __forceinline__ v8bf16 decode8_bf16(uint2 w, float scale) {
+  v2bf16 r0, r1, r2, r3;
+  if constexpr (FMT == MX_E5M2) {
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.x, scale, false);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.x, scale, true);
+    r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.y, scale, false);
+    r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.y, scale, true);
+  } else {
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, scale, false);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, scale, true);
+    r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, scale, false);
+    r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, scale, true);
+  }
+  return v8bf16{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
+  return row * kBK + (((chunk ^ row) & 7u) << 4);
+}
+
+// Four E8M0 scale bytes (blocks 4kt .. 4kt+3) of one operand row; blocks
+// past K read as 127 (scale 1.0) so the zero codes there contribute 0.
+__device__ __forceinline__ uint32_t load_scales4(const uint8_t* p, int64_t kt, int64_t kblocks, bool dword_ok) {
+  const int64_t b0 = 4 * kt;
+  if (dword_ok && b0 + 4 <= kblocks) return *(const uint32_t*)(p + b0);
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v |= (b0 + j < kblocks ? (uint32_t)p[b0 + j] : 127u) << (8 * j);
+  return v;
+}
+
+template <int BM, int BN, int AFMT, int BFMT, bool BF16OUT, bool PAGED, int MODE>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+  constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-tile
+  constexpr int FM = WM / 16, FN = WN / 16; // MFMA tiles per wave
+  constexpr int CA = BM * 8 / kThreads;     // 16-byte A chunks per thread per step
+  constexpr int CB = BN * 8 / kThreads;
+  static_assert(CA >= 1 && CB >= 1, "tile too small");
+
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * kBK];
+  __shared__ uint32_t sAs[2][BM];
+  __shared__ uint32_t sBs[2][BN];
+
+  // ---- which tile: groups of 8 tile rows, walked column-major inside a group
+  const uint32_t pid = blockIdx.x;
+  const uint32_t group_size = 8;
+  const uint32_t per_group = group_size * g.tiles_n;
+  const uint32_t first_m = (pid / per_group) * group_size;
+  const uint32_t gm = min(g.tiles_m - first_m, group_size);
+  const uint32_t tile_m = first_m + (pid % per_group) % gm;
+  const uint32_t tile_n = (pid % per_group) / gm;
+  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+
+  // ---- which problem of the batch
+  const int64_t p = blockIdx.y;
+  const int64_t po = p / g.batch_inner, pi = p % g.batch_inner;
+  const uint8_t* A = g.a + po * g.sa_o + pi * g.sa_i;
+  const uint8_t* SA = g.sa + po * g.ssa_o + pi * g.ssa_i;
+  const uint8_t* B = g.b + pi * g.sb_i;
+  const uint8_t* SB = g.sb + pi * g.ssb_i;
+  if (!PAGED) {
+    B += po * g.sb_o;
+    SB += po * g.ssb_o;
+  }
+
+  const int tid = threadIdx.x;
+  const int64_t kblocks = g.K / kBlock;
+  const int64_t ksteps = (g.K + kBK - 1) / kBK;
+  const bool dword_ok = g.scales_dword != 0;
+
+  // ---- per-thread global row pointers (fixed for the whole K loop)
+  const uint8_t* a_row[CA];
+  const uint8_t* b_row[CB];
+  uint32_t a_lds[CA], b_lds[CB], a_ch[CA], b_ch[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const uint32_t id = tid + kThreads * i, row = id >> 3, ch = id & 7;
+    a_row[i] = (m0 + row < g.M) ? A + (m0 + row) * g.lda : nullptr;
+    a_lds[i] = swz(row, ch);
+    a_ch[i] = ch;
+  }
+  auto b_row_ptr = [&](int64_t n, const uint8_t* base, int64_t ld, int64_t pstride) -> const uint8_t* {
+    if (PAGED) {
+      const int32_t page = g.page_table[po * g.pages_per_seq + n / g.page_rows];
+      return base + (int64_t)page * pstride + (n % g.page_rows) * ld;
+    }
+    return base + n * ld;
+  };
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const uint32_t id = tid + kThreads * i, row = id >> 3, ch = id & 7;
+    b_row[i] = (n0 + row < g.N) ? b_row_ptr(n0 + row, B, g.ldb, g.page_stride) : nullptr;
+    b_lds[i] = swz(row, ch);
+    b_ch[i] = ch;
+  }
+  // scale rows: thread t serves A row t (t < BM) and B row t (t < BN)
+  const uint8_t* sa_row = (tid < BM && m0 + tid < g.M) ? SA + (m0 + tid) * g.ldsa : nullptr;
+  const uint8_t* sb_row = (tid < BN && n0 + tid < g.N) ? b_row_ptr(n0 + tid, SB, g.ldsb, g.page_stride_s) : nullptr;
+
+  uint4 ra[CA], rb[CB];
+  uint32_t rsa = 0, rsb = 0;
+  auto load_global = [&](int64_t kt) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int64_t k0 = kt * kBK + a_ch[i] * 16;
+      ra[i] = (a_row[i] && k0 < g.K) ? *(const uint4*)(a_row[i] + k0) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int64_t k0 = kt * kBK + b_ch[i] * 16;
+      rb[i] = (b_row[i] && k0 < g.K) ? *(const uint4*)(b_row[i] + k0) : make_uint4(0, 0, 0, 0);
+    }
+    rsa = sa_row ? load_scales4(sa_row, kt, kblocks, dword_ok) : 0x7F7F7F7Fu;
+    rsb = sb_row ? load_scales4(sb_row, kt, kblocks, dword_ok) : 0x7F7F7F7Fu;
+  };
+  auto store_lds = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) *(uint4*)(&As[buf][a_lds[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) *(uint4*)(&Bs[buf][b_lds[i]]) = rb[i];
+    if (tid < BM) sAs[buf][tid] = rsa;
+    if (tid < BN) sBs[buf][tid] = rsb;
+  };
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lr = lane & 15, lg = lane >> 4;
+
+  v4f32 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4f32{0.f, 0.f, 0.f, 0.f};
+
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+
+  for (int64_t kt = 0; kt < ksteps; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ksteps) load_global(kt + 1);
+
+    if constexpr (MODE == kModeFP8) {
+      v8i32 bf[FN];
+      int bsc[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const uint32_t row = wn * WN + j * 16 + lr;
+        const uint4 lo = *(const uint4*)(&Bs[buf][swz(row, lg)]);
+        const uint4 hi = *(const uint4*)(&Bs[buf][swz(row, lg + 4)]);
+        bf[j] = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        bsc[j] = (int)(sBs[buf][row] >> (8 * lg));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint32_t row = wm * WM + i * 16 + lr;
+        const uint4 lo = *(const uint4*)(&As[buf][swz(row, lg)]);
+        const uint4 hi = *(const uint4*)(&As[buf][swz(row, lg + 4)]);
+        const v8i32 af = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const int asc = (int)(sAs[buf][row] >> (8 * lg));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], BFMT, AFMT, 0, bsc[j], 0, asc);
+      }
+    } else {
+      // one 32-K block per MFMA: lane (r, g) takes k = 32*kb + 8g .. +7, i.e.
+      // bytes 8*(g & 1) .. +7 of 16-byte chunk 2*kb + g/2 of its row
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint32_t chunk = 2 * kb + (lg >> 1), off = 8 * (lg & 1);
+        v8bf16 bf[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint32_t row = wn * WN + j * 16 + lr;
+          const uint2 w = *(const uint2*)(&Bs[buf][swz(row, chunk) + off]);
+          bf[j] = decode8_bf16<BFMT>(w, scale_value((sBs[buf][row] >> (8 * kb)) & 0xFFu));
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const uint32_t row = wm * WM + i * 16 + lr;
+          const uint2 w = *(const uint2*)(&As[buf][swz(row, chunk) + off]);
+          const v8bf16 af = decode8_bf16<AFMT>(w, scale_value((sAs[buf][row] >> (8 * kb)) & 0xFFu));
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+    if (kt + 1 < ksteps) store_lds(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane owns y[m][n .. n+3]
+  uint8_t* Y = (uint8_t*)g.y + (po * g.sy_o + pi * g.sy_i) * (BF16OUT ? 2 : 4);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t m = m0 + wm * WM + i * 16 + lr;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn * WN + j * 16 + 4 * lg;
+      const v4f32 v = acc[i][j];
+      if constexpr (BF16OUT) {
+        uint16_t* row = (uint16_t*)Y + m * g.ldy;
+        if (g.y_vec && n + 3 < g.N) {
+          *(uint2*)(row + n) = make_uint2(f32_to_bf16_rne(canon_nan(v[0])) | (f32_to_bf16_rne(canon_nan(v[1])) << 16),
+                                          f32_to_bf16_rne(canon_nan(v[2])) | (f32_to_bf16_rne(canon_nan(v[3])) << 16));
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (n + e < g.N) row[n + e] = (uint16_t)f32_to_bf16_rne(canon_nan(v[e]));
+        }
+      } else {
+        float* row = (float*)Y + m * g.ldy;
+        if (g.y_vec && n + 3 < g.N) {
+          *(float4*)(row + n) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (n + e < g.N) row[n + e] = v[e];
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, bool PAGED, int MODE>
+mx_status_t launch(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, int64_t batch, hipStream_t st) {
+  const dim3 grid(g.tiles_m * g.tiles_n, (uint32_t)batch);
+#define MX_GEMM_LAUNCH(AF, BF, OUT) \
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, AF, BF, OUT, PAGED, MODE>), grid, dim3(kThreads), 0, st, g)
+#define MX_GEMM_OUT(AF, BF) \
+  do { if (bf16out) MX_GEMM_LAUNCH(AF, BF, true); else MX_GEMM_LAUNCH(AF, BF, false); } while (0)
+  if (af == MX_E4M3 && bf == MX_E4M3) MX_GEMM_OUT(MX_E4M3, MX_E4M3);
+  else if (af == MX_E5M2 && bf == MX_E4M3) MX_GEMM_OUT(MX_E5M2, MX_E4M3);
+  else if (af == MX_E4M3 && bf == MX_E5M2) MX_GEMM_OUT(MX_E4M3, MX_E5M2);
+  else MX_GEMM_OUT(MX_E5M2, MX_E5M2);
+#undef MX_GEMM_OUT
+#undef MX_GEMM_LAUNCH
+  return mx_host::launch_status();
+}
+
+}  // namespace
+
+extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
+  if (!d) return MX_ERR_NULL;
+  if (d->a_fmt != MX_E4M3 && d->a_fmt != MX_E5M2) return MX_ERR_FORMAT;
+  if (d->b_fmt != MX_E4M3 && d->b_fmt != MX_E5M2) return MX_ERR_FORMAT;
+  if (d->y_dtype != MX_F32 && d->y_dtype != MX_BF16) return MX_ERR_FORMAT;
+  const int64_t M = d->M, N = d->N, K = d->K;
+  if (M < 0 || N < 0 || K < 0 || K % kBlock != 0) return MX_ERR_SHAPE;
+  const int64_t bo = d->batch_outer > 0 ? d->batch_outer : 1;
+  const int64_t bi = d->batch_inner > 0 ? d->batch_inner : 1;
+  if (d->batch_outer < 0 || d->batch_inner < 0) return MX_ERR_SHAPE;
+  const bool paged = d->b_page_table != nullptr;
+  if (M == 0 || N == 0) return mx_host::check_device();
+  if (!d->y) return MX_ERR_NULL;
+  if (K > 0 && (!d->a || !d->b || !d->sa || !d->sb)) return MX_ERR_NULL;
+  if (d->lda < K || d->ldb < K || d->ldsa < K / kBlock || d->ldsb < K / kBlock || d->ldy < N) return MX_ERR_SHAPE;
+  if (paged && (d->b_page_rows <= 0 || d->b_pages_per_seq <= 0 || (N + d->b_page_rows - 1) / d->b_page_rows > d->b_pages_per_seq))
+    return MX_ERR_SHAPE;
+  if (d->accum != MX_ACCUM_AUTO && d->accum != MX_ACCUM_FP8 && d->accum != MX_ACCUM_FP32) return MX_ERR_FORMAT;
+  const int64_t ysz = d->y_dtype == MX_F32 ? 4 : 2;
+  if (!mx_host::aligned16(d->a) || !mx_host::aligned16(d->b) || d->lda % 16 || d->ldb % 16 ||
+      ((uintptr_t)d->y % ysz) != 0)
+    return MX_ERR_ALIGN;
+  if (d->stride_a_outer % 16 || d->stride_a_inner % 16 || d->stride_b_inner % 16 || (!paged && d->stride_b_outer % 16) ||
+      (paged && d->b_page_stride % 16))
+    return MX_ERR_ALIGN;
+  mx_status_t st;
+  if ((st = mx_host::check_device()) != MX_OK) return st;
+  if (bo * bi >= 65536) return MX_ERR_SHAPE;
+
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.a = d->a; g.lda = d->lda; g.sa = d->sa; g.ldsa = d->ldsa;
+  g.b = d->b; g.ldb = d->ldb; g.sb = d->sb; g.ldsb = d->ldsb;
+  g.y = d->y; g.ldy = d->ldy;
+  g.batch_inner = bi;
+  g.sa_o = d->stride_a_outer; g.sa_i = d->stride_a_inner; g.ssa_o = d->stride_sa_outer; g.ssa_i = d->stride_sa_inner;
+  g.sb_o = d->stride_b_outer; g.sb_i = d->stride_b_inner; g.ssb_o = d->stride_sb_outer; g.ssb_i = d->stride_sb_inner;
+  g.sy_o = d->stride_y_outer; g.sy_i = d->stride_y_inner;
+  g.page_table = d->b_page_table; g.pages_per_seq = d->b_pages_per_seq; g.page_rows = d->b_page_rows;
+  g.page_stride = d->b_page_stride; g.page_stride_s = d->b_page_stride_s;
+  // dword scale reads need 4-byte aligned scale rows in every problem and page
+  const bool sa4 = ((uintptr_t)d->sa % 4 == 0) && d->ldsa % 4 == 0 && d->stride_sa_outer % 4 == 0 && d->stride_sa_inner % 4 == 0;
+  const bool sb4 = ((uintptr_t)d->sb % 4 == 0) && d->ldsb % 4 == 0 && d->stride_sb_inner % 4 == 0 &&
+                   (paged ? d->b_page_stride_s % 4 == 0 : d->stride_sb_outer % 4 == 0);
+  g.scales_dword = (sa4 && sb4) ? 1u : 0u;
+  g.y_vec = (mx_host::aligned16(d->y) && (d->ldy * ysz) % 16 == 0 && (d->stride_y_outer * ysz) % 16 == 0 &&
+             (d->stride_y_inner * ysz) % 16 == 0) ? 1u : 0u;
+  const bool fp8 = d->accum == MX_ACCUM_FP8 ||
+                   (d->accum == MX_ACCUM_AUTO && d->a_fmt == MX_E4M3 && d->b_fmt == MX_E4M3 && K >= 2048);
+
+  constexpr int BM = 128, BN = 128;
+  g.tiles_m = (uint32_t)((M + BM - 1) / BM);
+  g.tiles_n = (uint32_t)((N + BN - 1) / BN);
+  if ((int64_t)g.tiles_m * g.tiles_n >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
+  const bool bf16out = d->y_dtype == MX_BF16;
+  if (fp8)
+    return paged ? launch<BM, BN, true, kModeFP8>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream)
+                 : launch<BM, BN, false, kModeFP8>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
+  return paged ? launch<BM, BN, true, kModeBF16>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream)
+               : launch<BM, BN, false, kModeBF16>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
+}

@@ -1,0 +1,166 @@
+// mx_common.hpp -- helpers shared by the libmxfp8 kernels (gfx950 only).
+//
+// Hardware facts these helpers rely on (established by exhaustive on-device
+// checks over every bf16 input pattern and every E8M0 scale):
+//  * v_cvt_scalef32_pk_{fp8,bf8}_{bf16,f32} compute RNE(x / scale) exactly,
+//    subnormal results and signed zeros included, but do NOT saturate: a
+//    magnitude past the largest finite value becomes NaN (E4M3) or Inf
+//    (E5M2). fix_overflow_* below turns those bytes into the saturated code.
+//  * v_cvt_scalef32_pk_f32_{fp8,bf8} compute code * scale exactly in f32.
+//  * v_mfma_scale_f32_16x16x128_f8f6f4 takes, per lane l (row r = l % 16,
+//    group g = l / 16), 32 bytes: bytes 0-15 hold k = 16g .. 16g+15 and bytes
+//    16-31 hold k = 64+16g .. 64+16g+15 of the 128-wide K slice; the 32-bit
+//    scale operand of lane l is the E8M0 scale of (row r, k-block g). The
+//    result D[i][j] sits in lane j + 16*(i/4), element i % 4.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxfp8.h"
+
+namespace mx {
+
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+typedef float v2f32 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 32;  // elements per MX block
+
+// ---------------------------------------------------------------- scales
+// E8M0 code from the largest |x| bit pattern of a block, for the rule
+// X = 2^(floor(log2 amax) - emax_elem): code = max(E - emax_elem, 0) with E
+// the biased exponent field of amax (subnormal and zero amax have E = 0, so
+// they clamp to code 0); E = 255 (Inf/NaN present) gives 0xFF.
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_code_from_exp(uint32_t E) {
+  constexpr uint32_t emax = FMT == MX_E5M2 ? 15u : 8u;
+  uint32_t c = E > emax ? E - emax : 0u;
+  return E == 255u ? 0xFFu : c;
+}
+
+// The divisor 2^(code - 127) as an f32 (code 0 -> the subnormal 2^-127).
+__device__ __forceinline__ float scale_divisor(uint32_t code) {
+  return __uint_as_float(code ? (code << 23) : 0x00400000u);
+}
+
+// ---------------------------------------------------------------- encode
+// Saturate the bytes the conversion overflowed: E4M3 NaN (0x7F/0xFF) becomes
+// +-448 (0x7E/0xFE); E5M2 Inf (0x7C/0xFC) becomes +-57344 (0x7B/0xFB). Only
+// valid for codes of finite inputs (no other byte reaches these patterns).
+__device__ __forceinline__ uint32_t fix_overflow_e4m3(uint32_t d) {
+  uint32_t t = (d & 0x7F7F7F7Fu) + 0x01010101u;
+  return d - ((t >> 7) & 0x01010101u);
+}
+__device__ __forceinline__ uint32_t fix_overflow_e5m2(uint32_t d) {
+  uint32_t t = (d & 0x7F7F7F7Fu) + 0x04040404u;
+  return d - ((t >> 7) & 0x01010101u);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t fix_overflow(uint32_t d) {
+  return FMT == MX_E5M2 ? fix_overflow_e5m2(d) : fix_overflow_e4m3(d);
+}
+
+// Four bf16 values (two packed words) -> four codes in one dword.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4_bf16(uint32_t w01, uint32_t w23, float div) {
+  v2i16 r = {0, 0};
+  if constexpr (FMT == MX_E5M2) {
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(v2bf16, w01), div, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(v2bf16, w23), div, true);
+  } else {
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf16, w01), div, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf16, w23), div, true);
+  }
+  return fix_overflow<FMT>(__builtin_bit_cast(uint32_t, r));
+}
+
+// Four f32 values -> four codes in one dword.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4_f32(float a, float b, float c, float d, float div) {
+  v2i16 r = {0, 0};
+  if constexpr (FMT == MX_E5M2) {
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, a, b, div, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, c, d, div, true);
+  } else {
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, a, b, div, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, div, true);
+  }
+  return fix_overflow<FMT>(__builtin_bit_cast(uint32_t, r));
+}
+
+// ---------------------------------------------------------------- reductions
+// Packed 16-bit unsigned max of two words (v_pk_max_u16).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  u16x2 r = __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b));
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// DPP lane moves inside a row of 16 lanes.
+#define MX_DPP_QUAD_XOR1 0xB1   // quad_perm [1,0,3,2]
+#define MX_DPP_QUAD_XOR2 0x4E   // quad_perm [2,3,0,1]
+#define MX_DPP_HALF_MIRROR 0x141  // reverse within each group of 8 lanes
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+// max over the 4 lanes of a quad (32-bit values)
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  v = umax(v, dpp<MX_DPP_QUAD_XOR1>(v));
+  return umax(v, dpp<MX_DPP_QUAD_XOR2>(v));
+}
+// packed-u16 max over the 8 lanes of an aligned group of 8
+__device__ __forceinline__ uint32_t oct_max_pk_u16(uint32_t v) {
+  v = pk_max_u16(v, dpp<MX_DPP_QUAD_XOR1>(v));
+  v = pk_max_u16(v, dpp<MX_DPP_QUAD_XOR2>(v));
+  return pk_max_u16(v, dpp<MX_DPP_HALF_MIRROR>(v));
+}
+__device__ __forceinline__ uint32_t oct_max_u32(uint32_t v) {
+  v = umax(v, dpp<MX_DPP_QUAD_XOR1>(v));
+  v = umax(v, dpp<MX_DPP_QUAD_XOR2>(v));
+  return umax(v, dpp<MX_DPP_HALF_MIRROR>(v));
+}
+
+// ---------------------------------------------------------------- division
+// n / d for 0 <= n < 2^31 and 1 <= d < 2^31 by multiply-high: for d not a
+// power of two, l = ceil(log2 d), m = ceil(2^(31+l) / d) (fits in 32 bits)
+// and n / d = mulhi(n, m) >> (l - 1); powers of two use a shift.
+struct FastDiv {
+  uint32_t d, m, s;  // m == 0 -> shift by s
+  __host__ static FastDiv make(uint32_t d) {
+    FastDiv f{d, 0, 0};
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    if ((1ull << l) == d) {
+      f.s = l;
+    } else {
+      unsigned __int128 num = (unsigned __int128)1 << (31 + l);
+      f.m = (uint32_t)((num + d - 1) / d);
+      f.s = l - 1;
+    }
+    return f;
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    return m ? (__umulhi(n, m) >> s) : (n >> s);
+  }
+};
+
+// ---------------------------------------------------------------- bf16 out
+// f32 -> bf16, round to nearest even; NaN inputs must already be canonical.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float canon_nan(float f) { return f != f ? __uint_as_float(0x7FC00000u) : f; }
+
+}  // namespace mx
+
+// ---------------------------------------------------------------- host side
+namespace mx_host {
+mx_status_t check_device();  // MX_OK when the current device is gfx950
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline mx_status_t launch_status() {
+  return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_HIP;
+}
+}  // namespace mx_host

@@ -1,0 +1,382 @@
+// quantize.hip -- MXFP8 quantization kernels for gfx950:
+//   rowwise (1 x 32 blocks), the fused paged KV-cache write, and colwise
+//   (32 x 1 blocks, stored transposed through an LDS tile).
+//
+// Method [MXFP8 SM120 software support, §0.1-§0.2; MXFP8 quantization
+// glossary]: each block of 32 consecutive values gets one E8M0 scale chosen
+// from its amax, X = 2^(floor(log2 amax) - emax_elem), and every element is
+// rounded to nearest-even FP8 of x / X, saturating at the largest finite
+// value. All three kernels are HBM-bound: they read the input once with
+// 16-byte loads and write codes with 8- or 16-byte stores.
+#include "mx_common.hpp"
+
+namespace {
+
+using namespace mx;
+
+constexpr int kThreads = 256;
+constexpr int kRowUnroll = 4;  // 8-element chunks per thread in the rowwise kernel
+
+// ---------------------------------------------------------------------------
+// Rowwise. One thread handles chunks of 8 consecutive elements; the 4 lanes
+// of a quad hold one 32-element block, reduce its amax with two DPP steps,
+// convert with the scaled-FP8 instruction and store 8 codes each. Chunk g of
+// a workgroup pass maps to row = g / (cols/8), chunk-in-row = g % (cols/8).
+// ---------------------------------------------------------------------------
+struct RowArgs {
+  const void* x;      // input base
+  uint8_t* q;         // codes base
+  uint8_t* s;         // scales base
+  int64_t ldx, ldq, lds;
+  uint32_t nchunks;   // rows * cols / 8 of this launch (< 2^31)
+  FastDiv per_row;    // divide by cols / 8
+  // fused KV write: a row is (token, head); src/dst rows are remapped
+  const int64_t* slot_mapping;
+  FastDiv heads;      // divide by H
+  int64_t ld_token;   // elements between tokens
+  int64_t head_dim;   // D
+  int64_t capacity;   // page_size * num_pages
+  const void* x2;     // second tensor (V) for the fused KV write
+  uint8_t* q2;
+  uint8_t* s2;
+};
+
+template <typename InT>
+struct Chunk;  // 8 input elements as raw words
+template <>
+struct Chunk<uint16_t> { uint4 w; };
+template <>
+struct Chunk<float> { uint4 w0, w1; };
+
+template <typename InT>
+__device__ __forceinline__ void load_chunk(Chunk<InT>& c, const InT* p) {
+  if constexpr (sizeof(InT) == 2) {
+    c.w = *(const uint4*)p;
+  } else {
+    c.w0 = *(const uint4*)p;
+    c.w1 = *(const uint4*)(p + 4);
+  }
+}
+
+// |x| bit patterns' maximum over the 8 elements (bf16: 16-bit field, f32: 31-bit)
+template <typename InT>
+__device__ __forceinline__ uint32_t chunk_amax_bits(const Chunk<InT>& c) {
+  if constexpr (sizeof(InT) == 2) {
+    uint32_t m = pk_max_u16(pk_max_u16(c.w.x & 0x7FFF7FFFu, c.w.y & 0x7FFF7FFFu),
+                            pk_max_u16(c.w.z & 0x7FFF7FFFu, c.w.w & 0x7FFF7FFFu));
+    return umax(m & 0xFFFFu, m >> 16);
+  } else {
+    uint32_t a = umax(umax(c.w0.x & 0x7FFFFFFFu, c.w0.y & 0x7FFFFFFFu), umax(c.w0.z & 0x7FFFFFFFu, c.w0.w & 0x7FFFFFFFu));
+    uint32_t b = umax(umax(c.w1.x & 0x7FFFFFFFu, c.w1.y & 0x7FFFFFFFu), umax(c.w1.z & 0x7FFFFFFFu, c.w1.w & 0x7FFFFFFFu));
+    return umax(a, b);
+  }
+}
+
+template <typename InT>
+__device__ __forceinline__ uint32_t exp_field(uint32_t amax_bits) {
+  return sizeof(InT) == 2 ? (amax_bits >> 7) : (amax_bits >> 23);
+}
+
+template <typename InT, int FMT>
+__device__ __forceinline__ uint2 encode_chunk(const Chunk<InT>& c, float div) {
+  if constexpr (sizeof(InT) == 2) {
+    return make_uint2(encode4_bf16<FMT>(c.w.x, c.w.y, div), encode4_bf16<FMT>(c.w.z, c.w.w, div));
+  } else {
+    return make_uint2(encode4_f32<FMT>(__uint_as_float(c.w0.x), __uint_as_float(c.w0.y), __uint_as_float(c.w0.z),
+                                       __uint_as_float(c.w0.w), div),
+                      encode4_f32<FMT>(__uint_as_float(c.w1.x), __uint_as_float(c.w1.y), __uint_as_float(c.w1.z),
+                                       __uint_as_float(c.w1.w), div));
+  }
+}
+
+template <typename InT, int FMT, bool KV>
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(RowArgs a) {
+  const InT* x = (const InT*)a.x;
+  uint8_t* q = a.q;
+  uint8_t* s = a.s;
+  if (KV && blockIdx.y == 1) {
+    x = (const InT*)a.x2;
+    q = a.q2;
+    s = a.s2;
+  }
+  const uint32_t base = blockIdx.x * (kThreads * kRowUnroll) + threadIdx.x;
+  Chunk<InT> c[kRowUnroll];
+  int64_t dst_row[kRowUnroll];
+  uint32_t col8[kRowUnroll];
+  bool ok[kRowUnroll];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    const uint32_t g = base + u * kThreads;
+    ok[u] = g < a.nchunks;
+    const uint32_t row = a.per_row.div(g);
+    col8[u] = g - row * a.per_row.d;
+    int64_t src;
+    if (KV) {
+      const uint32_t t = a.heads.div(row);
+      const uint32_t h = row - t * a.heads.d;
+      int64_t slot = ok[u] ? a.slot_mapping[t] : -1;
+      ok[u] = ok[u] && slot >= 0 && slot < a.capacity;
+      src = (int64_t)t * a.ld_token + (int64_t)h * a.head_dim;
+      dst_row[u] = slot * (int64_t)a.heads.d + h;
+    } else {
+      src = (int64_t)row * a.ldx;
+      dst_row[u] = row;
+    }
+    if (ok[u]) load_chunk<InT>(c[u], x + src + (int64_t)col8[u] * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    // whole quads share `ok` (cols % 32 == 0 and the chunk base is quad aligned)
+    if (!ok[u]) continue;
+    const uint32_t amax = quad_max_u32(chunk_amax_bits<InT>(c[u]));
+    const uint32_t code = scale_code_from_exp<FMT>(exp_field<InT>(amax));
+    uint2 out = encode_chunk<InT, FMT>(c[u], scale_divisor(code));
+    if (code == 0xFFu) out = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    const int64_t ldq = KV ? a.head_dim : a.ldq;
+    const int64_t lds = KV ? a.head_dim / kBlock : a.lds;
+    *(uint2*)(q + dst_row[u] * ldq + (int64_t)col8[u] * 8) = out;
+    if ((threadIdx.x & 3) == 0) s[dst_row[u] * lds + col8[u] / 4] = (uint8_t)code;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Colwise. A workgroup owns a 128-row x 64-column tile. Wave w takes rows
+// 32w .. 32w+31 (one block row). Lane j takes the 8 columns 8*(j/8) .. +7
+// and the 4 rows 4*(j%8) .. +3, so a column's 32 values sit in the 8 lanes
+// of one DPP group of 8. The codes of a column (4 per lane) go to an LDS tile
+// [64 columns][128 bytes] and leave as 128-byte rows of the transposed output.
+// LDS chunks of 16 bytes are XOR-swizzled by column group to keep the
+// transposing writes free of bank conflicts.
+// ---------------------------------------------------------------------------
+constexpr int kColTileRows = 128;
+constexpr int kColTileCols = 64;
+
+__device__ __forceinline__ uint32_t col_lds_offset(uint32_t c, uint32_t rbyte) {
+  return c * 128u + ((((rbyte >> 4) ^ (c >> 3)) & 7u) << 4) + (rbyte & 15u);
+}
+
+template <typename InT, int FMT>
+__global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restrict__ x, int64_t rows, int64_t cols,
+                                                              int64_t ldx, uint8_t* __restrict__ qt, int64_t ldq,
+                                                              uint8_t* __restrict__ st, int64_t lds,
+                                                              uint32_t col_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kColTileCols * kColTileRows];
+  const uint32_t tile_r = blockIdx.x / col_tiles, tile_c = blockIdx.x % col_tiles;
+  const int64_t r0 = (int64_t)tile_r * kColTileRows, c0 = (int64_t)tile_c * kColTileCols;
+  const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t k = lane >> 3, b = lane & 7;
+  const int64_t rblk = r0 + 32 * wave;   // first row of this wave's block row
+  const bool wave_ok = rblk < rows;      // rows % 32 == 0
+  const int64_t cc = c0 + 8 * k;         // first of this lane's 8 columns
+  const int ncol = cols - cc >= 8 ? 8 : (cols > cc ? (int)(cols - cc) : 0);
+
+  if (wave_ok) {
+    // v[i][p]: row 4b+i, column pair p (bf16) or column p (f32)
+    constexpr int W = sizeof(InT) == 2 ? 4 : 8;
+    uint32_t v[4][W];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const InT* p = x + (rblk + 4 * b + i) * ldx + cc;
+      if (ncol == 8) {
+        uint4 t = *(const uint4*)p;
+        v[i][0] = t.x; v[i][1] = t.y; v[i][2] = t.z; v[i][3] = t.w;
+        if constexpr (W == 8) {
+          uint4 t2 = *(const uint4*)(p + 4);
+          v[i][4] = t2.x; v[i][5] = t2.y; v[i][6] = t2.z; v[i][7] = t2.w;
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < W; ++w) v[i][w] = 0;
+        for (int e = 0; e < ncol; ++e) {
+          if constexpr (W == 4) {
+            uint32_t h = ((const uint16_t*)p)[e];
+            v[i][e >> 1] |= h << (16 * (e & 1));
+          } else {
+            v[i][e] = ((const uint32_t*)p)[e];
+          }
+        }
+      }
+    }
+    // per-column amax over the 4 rows, then over the 8 lanes of the group
+    uint32_t codes[8];
+    if constexpr (W == 4) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t m = pk_max_u16(pk_max_u16(v[0][p] & 0x7FFF7FFFu, v[1][p] & 0x7FFF7FFFu),
+                                pk_max_u16(v[2][p] & 0x7FFF7FFFu, v[3][p] & 0x7FFF7FFFu));
+        m = oct_max_pk_u16(m);
+        codes[2 * p] = scale_code_from_exp<FMT>((m & 0xFFFFu) >> 7);
+        codes[2 * p + 1] = scale_code_from_exp<FMT>(m >> 23);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        uint32_t m = umax(umax(v[0][p] & 0x7FFFFFFFu, v[1][p] & 0x7FFFFFFFu),
+                          umax(v[2][p] & 0x7FFFFFFFu, v[3][p] & 0x7FFFFFFFu));
+        m = oct_max_u32(m);
+        codes[p] = scale_code_from_exp<FMT>(m >> 23);
+      }
+    }
+    // encode: column c gets one dword = rows 4b .. 4b+3
+#pragma unroll
+    for (int ci = 0; ci < 8; ++ci) {
+      const float div = scale_divisor(codes[ci]);
+      uint32_t d;
+      if constexpr (W == 4) {
+        const int p = ci >> 1;
+        const uint32_t sel = (ci & 1) ? 0x07060302u : 0x05040100u;  // pick the high or low halves
+        uint32_t r01 = __builtin_amdgcn_perm(v[1][p], v[0][p], sel);
+        uint32_t r23 = __builtin_amdgcn_perm(v[3][p], v[2][p], sel);
+        d = encode4_bf16<FMT>(r01, r23, div);
+      } else {
+        d = encode4_f32<FMT>(__uint_as_float(v[0][ci]), __uint_as_float(v[1][ci]), __uint_as_float(v[2][ci]),
+                             __uint_as_float(v[3][ci]), div);
+      }
+      if (codes[ci] == 0xFFu) d = 0x7F7F7F7Fu;
+      const uint32_t c = 8 * k + ci;
+      *(uint32_t*)(tile + col_lds_offset(c, 32 * wave + 4 * b)) = d;
+      if (b == 0 && ci < ncol) st[(cc + ci) * lds + rblk / 32] = (uint8_t)codes[ci];
+    }
+  }
+  __syncthreads();
+  // write out: 64 columns x 128 bytes = 512 chunks of 16 bytes
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const uint32_t id = threadIdx.x + kThreads * it;
+    const uint32_t c = id >> 3, m = id & 7;
+    const int64_t r = r0 + 16 * m;
+    if (c0 + c < cols && r < rows) {
+      uint4 val = *(const uint4*)(tile + col_lds_offset(c, 16 * m));
+      *(uint4*)(qt + (c0 + c) * ldq + r) = val;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+mx_status_t check_common(const void* x, mx_dtype_t xdt, mx_fmt_t fmt, int64_t rows, int64_t cols, int64_t ldx) {
+  if (xdt != MX_F32 && xdt != MX_BF16) return MX_ERR_FORMAT;
+  if (fmt != MX_E4M3 && fmt != MX_E5M2) return MX_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || ldx < cols) return MX_ERR_SHAPE;
+  const int64_t esz = xdt == MX_F32 ? 4 : 2;
+  if (!mx_host::aligned16(x) || (ldx * esz) % 16 != 0) return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+template <typename InT, int FMT, bool KV>
+mx_status_t launch_rows(RowArgs a, int64_t rows, int64_t cols, hipStream_t stream) {
+  // split into launches of < 2^31 chunks so chunk indices stay 32-bit
+  const int64_t cpr = cols / 8;
+  const int64_t rows_per_launch = std::max<int64_t>(1, ((int64_t)1 << 30) / std::max<int64_t>(cpr, 1));
+  for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
+    const int64_t nr = std::min(rows_per_launch, rows - r0);
+    RowArgs b = a;
+    b.nchunks = (uint32_t)(nr * cpr);
+    if (KV) {
+      b.slot_mapping = a.slot_mapping + r0 / a.heads.d;  // KV launches always start at a token boundary
+    } else {
+      b.x = (const InT*)a.x + r0 * a.ldx;
+      b.q = a.q + r0 * a.ldq;
+      b.s = a.s + r0 * a.lds;
+    }
+    const uint32_t blocks = (b.nchunks + kThreads * kRowUnroll - 1) / (kThreads * kRowUnroll);
+    hipLaunchKernelGGL((quant_rows_kernel<InT, FMT, KV>), dim3(blocks, KV ? 2 : 1), dim3(kThreads), 0, stream, b);
+    if (mx_host::launch_status() != MX_OK) return MX_ERR_HIP;
+  }
+  return MX_OK;
+}
+
+template <typename InT>
+mx_status_t dispatch_rows(mx_fmt_t fmt, RowArgs a, int64_t rows, int64_t cols, hipStream_t st) {
+  return fmt == MX_E5M2 ? launch_rows<InT, MX_E5M2, false>(a, rows, cols, st)
+                        : launch_rows<InT, MX_E4M3, false>(a, rows, cols, st);
+}
+
+}  // namespace
+
+extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                                   mx_fmt_t fmt, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                                   hipStream_t stream) {
+  if (!x || !q || !s) return MX_ERR_NULL;
+  mx_status_t st = check_common(x, xdt, fmt, rows, cols, ldx);
+  if (st != MX_OK) return st;
+  if (cols % kBlock != 0 || ldq < cols || lds < cols / kBlock) return MX_ERR_SHAPE;
+  if (!mx_host::aligned16(q) || ldq % 16 != 0) return MX_ERR_ALIGN;
+  if ((st = mx_host::check_device()) != MX_OK) return st;
+  if (rows == 0 || cols == 0) return MX_OK;
+  RowArgs a{};
+  a.x = x; a.q = q; a.s = s; a.ldx = ldx; a.ldq = ldq; a.lds = lds;
+  a.per_row = FastDiv::make((uint32_t)(cols / 8));
+  if (cols / 8 >= ((int64_t)1 << 30)) return MX_ERR_SHAPE;
+  return xdt == MX_BF16 ? dispatch_rows<uint16_t>(fmt, a, rows, cols, stream)
+                        : dispatch_rows<float>(fmt, a, rows, cols, stream);
+}
+
+extern "C" mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_t dt, int64_t T, int64_t H, int64_t D,
+                                         int64_t ld_token, const int64_t* slot_mapping, uint8_t* k_cache,
+                                         uint8_t* k_scale, uint8_t* v_cache, uint8_t* v_scale, int64_t page_size,
+                                         int64_t num_pages, hipStream_t stream) {
+  if (!k || !v || !slot_mapping || !k_cache || !k_scale || !v_cache || !v_scale) return MX_ERR_NULL;
+  if (dt != MX_F32 && dt != MX_BF16) return MX_ERR_FORMAT;
+  if (T < 0 || H < 0 || D < 0 || page_size <= 0 || num_pages < 0 || D % kBlock != 0 || ld_token < H * D)
+    return MX_ERR_SHAPE;
+  if (H >= ((int64_t)1 << 31) || D >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
+  const int64_t esz = dt == MX_F32 ? 4 : 2;
+  if (!mx_host::aligned16(k) || !mx_host::aligned16(v) || (ld_token * esz) % 16 != 0 || (D * esz) % 16 != 0 ||
+      !mx_host::aligned16(k_cache) || !mx_host::aligned16(v_cache) || D % 16 != 0)
+    return MX_ERR_ALIGN;
+  mx_status_t st;
+  if ((st = mx_host::check_device()) != MX_OK) return st;
+  if (T == 0 || H == 0 || D == 0) return MX_OK;
+  RowArgs a{};
+  a.x = k; a.x2 = v; a.q = k_cache; a.q2 = v_cache; a.s = k_scale; a.s2 = v_scale;
+  a.slot_mapping = slot_mapping;
+  a.heads = FastDiv::make((uint32_t)H);
+  a.per_row = FastDiv::make((uint32_t)(D / 8));
+  a.ld_token = ld_token;
+  a.head_dim = D;
+  a.capacity = page_size * num_pages;
+  // rows of the launch are (token, head) pairs; split at token boundaries
+  const int64_t cpr = D / 8;
+  const int64_t tok_per_launch = std::max<int64_t>(1, ((int64_t)1 << 30) / (cpr * H));
+  for (int64_t t0 = 0; t0 < T; t0 += tok_per_launch) {
+    const int64_t nt = std::min(tok_per_launch, T - t0);
+    RowArgs b = a;
+    b.x = (const uint8_t*)k + t0 * ld_token * esz;
+    b.x2 = (const uint8_t*)v + t0 * ld_token * esz;
+    b.slot_mapping = slot_mapping + t0;
+    b.nchunks = (uint32_t)(nt * H * cpr);
+    const uint32_t blocks = (b.nchunks + kThreads * kRowUnroll - 1) / (kThreads * kRowUnroll);
+    if (dt == MX_BF16)
+      hipLaunchKernelGGL((quant_rows_kernel<uint16_t, MX_E4M3, true>), dim3(blocks, 2), dim3(kThreads), 0, stream, b);
+    else
+      hipLaunchKernelGGL((quant_rows_kernel<float, MX_E4M3, true>), dim3(blocks, 2), dim3(kThreads), 0, stream, b);
+    if (mx_host::launch_status() != MX_OK) return MX_ERR_HIP;
+  }
+  return MX_OK;
+}
+
+extern "C" mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                                           mx_fmt_t fmt, uint8_t* qt, int64_t ldq, uint8_t* st, int64_t lds,
+                                           hipStream_t stream) {
+  if (!x || !qt || !st) return MX_ERR_NULL;
+  mx_status_t rc = check_common(x, xdt, fmt, rows, cols, ldx);
+  if (rc != MX_OK) return rc;
+  if (rows % kBlock != 0 || ldq < rows || lds < rows / kBlock) return MX_ERR_SHAPE;
+  if (!mx_host::aligned16(qt) || ldq % 16 != 0) return MX_ERR_ALIGN;
+  if ((rc = mx_host::check_device()) != MX_OK) return rc;
+  if (rows == 0 || cols == 0) return MX_OK;
+  const int64_t row_tiles = (rows + kColTileRows - 1) / kColTileRows;
+  const int64_t col_tiles = (cols + kColTileCols - 1) / kColTileCols;
+  if (row_tiles * col_tiles >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
+  const dim3 grid((uint32_t)(row_tiles * col_tiles));
+#define MX_COLS_LAUNCH(T, F)                                                                                        \
+  hipLaunchKernelGGL((quant_cols_kernel<T, F>), grid, dim3(kThreads), 0, stream, (const T*)x, rows, cols, ldx, qt, \
+                     ldq, st, lds, (uint32_t)col_tiles)
+  if (xdt == MX_BF16) {
+    if (fmt == MX_E5M2) MX_COLS_LAUNCH(uint16_t, MX_E5M2); else MX_COLS_LAUNCH(uint16_t, MX_E4M3);
+  } else {
+    if (fmt == MX_E5M2) MX_COLS_LAUNCH(float, MX_E5M2); else MX_COLS_LAUNCH(float, MX_E4M3);
+  }
+#undef MX_COLS_LAUNCH
+  return mx_host::launch_status();
+}

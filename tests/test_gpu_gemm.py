@@ -1,0 +1,287 @@
+"""GPU parity of the block-scaled matrix product against the oracle.
+
+Bound (per output element): |y_gpu - y_ref| <= 1e-5 * sum_k |a_k b_k| for
+f32 output; bf16 output adds its own rounding, 2^-8 of the magnitude. The
+oracle quantizes the bf16 inputs itself and computes y_ref in fp64; the GPU
+quantizes the same inputs with its own kernels (the codes are compared
+bit for bit as well) and multiplies.
+"""
+import numpy as np
+import pytest
+
+from conftest import load_golden
+from gpu_util import FP8_GROUPED_REL, assert_bitexact, assert_gemm_bound, bf16_to_f64, dev, host
+from microscaling_block_scaled_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+AUTO, FP8, FP32 = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import torch
+    import microscaling_block_scaled_amd as m
+    assert torch.cuda.is_available()
+    ok, reason = m.mx_query_support(0)
+    assert ok, reason
+    return m
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def sample_coords(M, N, n, seed, tile=128):
+    """Random outputs plus the corners of the first, a middle and the last
+    tile in each direction."""
+    g = inputs.rng(seed)
+    mi = list(g.integers(0, M, n))
+    ni = list(g.integers(0, N, n))
+    edges_m = sorted({0, 1, min(tile - 1, M - 1), min(tile, M - 1), M // 2, M - 2 if M > 1 else 0, M - 1})
+    edges_n = sorted({0, 1, min(tile - 1, N - 1), min(tile, N - 1), N // 2, N - 2 if N > 1 else 0, N - 1})
+    for m in edges_m:
+        for nn in edges_n:
+            mi.append(m)
+            ni.append(nn)
+    return np.array(mi, np.int64), np.array(ni, np.int64)
+
+
+# --------------------------------------------------------------------------- page examples
+@pytest.mark.parametrize("accum", [FP8, FP32])
+def test_block_dot_example(mx, oracle, accum):
+    """[NVFP4 page, section 7.2] q . p = 5.25, and with s_A s_B = 4, 21."""
+    torch = _torch()
+    ex = load_golden("block_dot_example.json")
+    a = np.zeros((1, 128), np.uint8)
+    b = np.zeros((1, 128), np.uint8)
+    a[0, :4] = [oracle.encode(E4M3, v) for v in ex["q"]]
+    b[0, :4] = [oracle.encode(E4M3, v) for v in ex["p"]]
+    for sc, want in ((127, ex["dot"]), (128, ex["dot"] * 4)):
+        s = np.full((1, 4), sc, np.uint8)
+        y = host(mx.mx_gemm(dev(a), dev(s), dev(b), dev(s), out_dtype=torch.float32, accum=accum))
+        assert y[0, 0] == want
+
+
+@pytest.mark.parametrize("accum", [FP8, FP32])
+def test_scales_stay_inside_the_sum(mx, oracle, accum):
+    """[MXFP8 SM120 software support, section 0.3]: with different scales
+    per block, the result is sum_b s_A s_B d_b, not one scale pair applied
+    to the whole sum."""
+    torch = _torch()
+    a = np.zeros((16, 128), np.uint8)
+    b = np.zeros((16, 128), np.uint8)
+    one = oracle.encode(E4M3, 1.0)
+    a[:, 0::32] = one
+    b[:, 0::32] = one
+    sa = np.tile(np.array([[130, 120, 127, 140]], np.uint8), (16, 1))
+    sb = np.tile(np.array([[127, 127, 100, 110]], np.uint8), (16, 1))
+    y = host(mx.mx_gemm(dev(a), dev(sa), dev(b), dev(sb), out_dtype=torch.float32, accum=accum))
+    want = 2.0 ** 3 + 2.0 ** -7 + 2.0 ** -27 + 2.0 ** -4
+    assert np.all(y == np.float32(want))
+
+
+# --------------------------------------------------------------------------- tiny config
+def test_tiny_config(mx, oracle):
+    """v64 and A [64, 128] x B [128, 64] f32 ~ N(0,1): A rowwise, B colwise
+    (blocks along K = 128), every output checked."""
+    torch = _torch()
+    t = inputs.tiny()
+    A, B = t["A"], t["B"]
+    qa, sa = mx.mx_quantize(dev(A), E4M3)
+    qb, sb = mx.mx_quantize_colwise(dev(B), E4M3)
+    qa_o, sa_o = oracle.quantize_rows(A, E4M3)
+    qb_o, sb_o = oracle.quantize_cols(B, E4M3)
+    assert_bitexact(host(qa), qa_o, "A codes")
+    assert_bitexact(host(sa), sa_o, "A scales")
+    assert_bitexact(host(qb), qb_o, "B^T codes")
+    assert_bitexact(host(sb), sb_o, "B^T scales")
+    y_ref, t_ref = oracle.gemm(qa_o, sa_o, E4M3, qb_o, sb_o, E4M3)
+    y32 = host(mx.mx_gemm(qa, sa, qb, sb, out_dtype=torch.float32))
+    assert_gemm_bound(y32, y_ref, t_ref, "tiny f32")
+    ybf = host(mx.mx_gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16))
+    assert_gemm_bound(bf16_to_f64(ybf), y_ref, t_ref, "tiny bf16", bf16_out=True)
+    # the worked vector against itself: 2^25 + 2^-19, which rounds to 2^25 in f32
+    v = t["v64"]
+    qv, sv = mx.mx_quantize(dev(v), E4M3)
+    pad_q = torch.zeros((1, 128), dtype=torch.uint8, device="cuda")
+    pad_s = torch.full((1, 4), 127, dtype=torch.uint8, device="cuda")
+    pad_q[:, :64] = qv
+    pad_s[:, :2] = sv
+    yv = host(mx.mx_gemm(pad_q, pad_s, pad_q, pad_s, out_dtype=torch.float32))
+    assert yv[0, 0] == np.float32(2.0 ** 25 + 2.0 ** -19)
+
+
+# --------------------------------------------------------------------------- ragged shapes
+SHAPES = [(1, 1, 32), (17, 33, 96), (130, 129, 160), (64, 64, 128), (257, 300, 416), (128, 256, 1024),
+          (300, 17, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("afmt,bfmt", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)])
+@pytest.mark.parametrize("accum", [AUTO, FP8, FP32])
+def test_ragged_shapes(mx, oracle, M, N, K, afmt, bfmt, accum):
+    torch = _torch()
+    xa = inputs.normal_bf16(100 + M, (M, K))
+    xb = inputs.normal_bf16(200 + N, (N, K), sigma=0.02)
+    qa, sa = mx.mx_quantize(dev(xa, bf16=True), afmt)
+    qb, sb = mx.mx_quantize(dev(xb, bf16=True), bfmt)
+    qa_o, sa_o = oracle.quantize_rows(xa, afmt)
+    qb_o, sb_o = oracle.quantize_rows(xb, bfmt)
+    assert_bitexact(host(qa), qa_o, "A codes")
+    assert_bitexact(host(qb), qb_o, "B codes")
+    y_ref, t_ref = oracle.gemm(qa_o, sa_o, afmt, qb_o, sb_o, bfmt)
+    rel = FP8_GROUPED_REL if accum == FP8 else 1e-5
+    y = host(mx.mx_gemm(qa, sa, qb, sb, afmt, bfmt, out_dtype=torch.float32, accum=accum))
+    assert_gemm_bound(y, y_ref, t_ref, "f32 %s" % ((M, N, K),), rel=rel)
+    yb = host(mx.mx_gemm(qa, sa, qb, sb, afmt, bfmt, out_dtype=torch.bfloat16, accum=accum))
+    assert_gemm_bound(bf16_to_f64(yb), y_ref, t_ref, "bf16 %s" % ((M, N, K),), bf16_out=True, rel=rel)
+
+
+def test_padded_pitches_and_unaligned_scale_rows(mx, oracle):
+    """Leading dimensions larger than the rows, and K/32 not a multiple of 4
+    (scale rows not dword aligned)."""
+    torch = _torch()
+    M, N, K = 70, 50, 224
+    xa = inputs.normal_bf16(5, (M, K))
+    xb = inputs.normal_bf16(6, (N, K))
+    qa_o, sa_o = oracle.quantize_rows(xa, E4M3)
+    qb_o, sb_o = oracle.quantize_rows(xb, E4M3)
+    A = torch.zeros((M, K + 32), dtype=torch.uint8, device="cuda")
+    B = torch.zeros((N, K + 48), dtype=torch.uint8, device="cuda")
+    SA = torch.zeros((M, K // 32 + 3), dtype=torch.uint8, device="cuda")
+    SB = torch.zeros((N, K // 32 + 1), dtype=torch.uint8, device="cuda")
+    A[:, :K] = dev(qa_o); B[:, :K] = dev(qb_o); SA[:, :K // 32] = dev(sa_o); SB[:, :K // 32] = dev(sb_o)
+    Y = torch.full((M, N + 12), -7.0, dtype=torch.float32, device="cuda")
+    mx.mx_gemm(A[:, :K], SA[:, :K // 32], B[:, :K], SB[:, :K // 32], y=Y[:, :N])
+    y_ref, t_ref = oracle.gemm(qa_o, sa_o, E4M3, qb_o, sb_o, E4M3)
+    Yh = host(Y)
+    assert_gemm_bound(Yh[:, :N], y_ref, t_ref, "padded")
+    assert np.all(Yh[:, N:] == -7.0)
+
+
+def test_batched_paged_scores_small(mx, oracle):
+    """Paged QK^T: 3 sequences x 2 heads, seq_len 96 on pages of 32 rows."""
+    torch = _torch()
+    S, L, H, D, page = 3, 96, 2, 64, 32
+    n_pages = 12
+    pages_per_seq = L // page
+    k = inputs.normal_bf16(71, (S * L, H, D))
+    q = inputs.normal_bf16(72, (S * L, H, D))
+    perm = inputs.rng(73).permutation(n_pages)
+    table = perm[:S * pages_per_seq].reshape(S, pages_per_seq).astype(np.int32)
+    t = np.arange(S * L)
+    slots = (table[t // L, (t % L) // page].astype(np.int64) * page + (t % L) % page)
+    kc = torch.zeros((n_pages, page, H, D), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((n_pages, page, H, D // 32), dtype=torch.uint8, device="cuda")
+    vc, vs = torch.zeros_like(kc), torch.zeros_like(ks)
+    mx.mx_kv_quant_write(dev(k, bf16=True), dev(k, bf16=True), dev(slots), kc, ks, vc, vs)
+    qq, qs = mx.mx_quantize(dev(q.reshape(S * L * H, D), bf16=True), E4M3)
+    out = host(mx.mx_paged_scores(qq.view(S * L, H, D), qs.view(S * L, H, D // 32), kc, ks, dev(table), L))
+    qo, qso = oracle.quantize_rows(q.reshape(S * L * H, D), E4M3)
+    ko, kso = oracle.quantize_rows(k.reshape(S * L * H, D), E4M3)
+    qo = qo.reshape(S, L, H, D); qso = qso.reshape(S, L, H, D // 32)
+    ko = ko.reshape(S, L, H, D); kso = kso.reshape(S, L, H, D // 32)
+    for s in range(S):
+        for h in range(H):
+            y_ref, t_ref = oracle.gemm(qo[s, :, h], qso[s, :, h], E4M3, ko[s, :, h], kso[s, :, h], E4M3)
+            assert_gemm_bound(out[s, h], y_ref, t_ref, "scores s=%d h=%d" % (s, h))
+
+
+# --------------------------------------------------------------------------- workload sizes
+def _check_sampled(y_dev, qa_o, sa_o, afmt, qb_o, sb_o, bfmt, what, n=3000, seed=1, bf16_out=False):
+    M, N = y_dev.shape
+    mi, ni = sample_coords(M, N, n, seed)
+    import oracle as o
+    y_ref, t_ref = o.gemm_at(qa_o, sa_o, afmt, qb_o, sb_o, bfmt, mi, ni)
+    torch = _torch()
+    yg = y_dev[dev(mi), dev(ni)]
+    yg = bf16_to_f64(host(yg)) if y_dev.dtype == torch.bfloat16 else host(yg).astype(np.float64)
+    return assert_gemm_bound(yg, y_ref, t_ref, what, bf16_out=bf16_out)
+
+
+@pytest.mark.slow
+def test_gemm_8192_cubed(mx, oracle):
+    """M = N = K = 8192, E4M3 x E4M3, inputs ~ N(0,1) quantized rowwise along
+    K; bf16 output (the timed configuration) and an f32 output run."""
+    torch = _torch()
+    xa, xb = inputs.gemm_inputs()
+    qa, sa = mx.mx_quantize(dev(xa, bf16=True), E4M3)
+    qb, sb = mx.mx_quantize(dev(xb, bf16=True), E4M3)
+    qa_o, sa_o = oracle.quantize_rows(xa, E4M3)
+    qb_o, sb_o = oracle.quantize_rows(xb, E4M3)
+    assert_bitexact(host(qa), qa_o, "A codes")
+    assert_bitexact(host(qb), qb_o, "B codes")
+    y = mx.mx_gemm(qa, sa, qb, sb, out_dtype=torch.bfloat16)
+    _check_sampled(y, qa_o, sa_o, E4M3, qb_o, sb_o, E4M3, "8192^3 bf16", bf16_out=True)
+    y32 = mx.mx_gemm(qa, sa, qb, sb, out_dtype=torch.float32)
+    worst = _check_sampled(y32, qa_o, sa_o, E4M3, qb_o, sb_o, E4M3, "8192^3 f32", seed=2, n=20000)
+    print("8192^3 worst |err|/T = %.3g" % worst)
+    # bf16 output is the f32 result rounded once
+    assert torch.equal(y, y32.to(torch.bfloat16))
+    y_exact = mx.mx_gemm(qa, sa, qb, sb, out_dtype=torch.float32, accum=FP32)
+    worst_e = _check_sampled(y_exact, qa_o, sa_o, E4M3, qb_o, sb_o, E4M3, "8192^3 f32 FP32-accum", seed=3)
+    print("8192^3 FP32-accumulation worst |err|/T = %.3g" % worst_e)
+
+
+@pytest.mark.slow
+def test_training_linear_fwd_and_dgrad(mx, oracle):
+    """fwd Y = X W^T: X [16384, 4096] E4M3, W [14336, 4096] E4M3 (rowwise);
+    dgrad dX = G W: G [16384, 14336] E5M2 rowwise x W colwise E4M3."""
+    torch = _torch()
+    x, w, g = inputs.training_inputs()
+    xd, wd = dev(x, bf16=True), dev(w, bf16=True)
+    qx, sx = mx.mx_quantize(xd, E4M3)
+    qw, sw = mx.mx_quantize(wd, E4M3)
+    qx_o, sx_o = oracle.quantize_rows(x, E4M3)
+    qw_o, sw_o = oracle.quantize_rows(w, E4M3)
+    y = mx.mx_gemm(qx, sx, qw, sw, out_dtype=torch.float32)
+    worst_f = _check_sampled(y, qx_o, sx_o, E4M3, qw_o, sw_o, E4M3, "fwd f32")
+    del y, qx, sx, qx_o, sx_o, qw, sw, qw_o, sw_o
+    gd = dev(g, bf16=True)
+    qg, sg = mx.mx_quantize(gd, E5M2)
+    qwt, swt = mx.mx_quantize_colwise(wd, E4M3)
+    qg_o, sg_o = oracle.quantize_rows(g, E5M2)
+    qwt_o, swt_o = oracle.quantize_cols(w, E4M3)
+    assert_bitexact(host(swt), swt_o, "W colwise scales")
+    dx = mx.mx_gemm(qg, sg, qwt, swt, E5M2, E4M3, out_dtype=torch.float32)
+    worst_d = _check_sampled(dx, qg_o, sg_o, E5M2, qwt_o, swt_o, E4M3, "dgrad f32", n=20000)
+    print("fwd worst |err|/T = %.3g, dgrad worst |err|/T = %.3g" % (worst_f, worst_d))
+
+
+@pytest.mark.slow
+def test_kv_cache_scores_full_size(mx, oracle):
+    """32768 tokens x 8 heads x 128 written to 256 pages of 128, then QK^T
+    for 64 sequences x 512 tokens per head, f32 output; sampled check."""
+    torch = _torch()
+    k, v, q = inputs.kv_inputs()
+    slots, table = inputs.kv_layout()
+    kc = torch.empty((256, 128, 8, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((256, 128, 8, 4), dtype=torch.uint8, device="cuda")
+    vc, vs = torch.empty_like(kc), torch.empty_like(ks)
+    mx.mx_kv_quant_write(dev(k, bf16=True), dev(v, bf16=True), dev(slots), kc, ks, vc, vs)
+    qq, qs = mx.mx_quantize(dev(q.reshape(-1, 128), bf16=True), E4M3)
+    scores = mx.mx_paged_scores(qq.view(32768, 8, 128), qs.view(32768, 8, 4), kc, ks, dev(table), 512)
+    qo, qso = oracle.quantize_rows(q.reshape(-1, 128), E4M3)
+    ko, kso = oracle.quantize_rows(k.reshape(-1, 128), E4M3)
+    g = inputs.rng(9)
+    n = 4000
+    s_i, h_i, i_i, j_i = g.integers(0, 64, n), g.integers(0, 8, n), g.integers(0, 512, n), g.integers(0, 512, n)
+    # query row (s*512 + i, h) and key row (s*512 + j, h) in the token-major quantized arrays
+    y_ref, t_ref = oracle.gemm_at(qo, qso, E4M3, ko, kso, E4M3, (s_i * 512 + i_i) * 8 + h_i, (s_i * 512 + j_i) * 8 + h_i)
+    got = host(scores[dev(s_i), dev(h_i), dev(i_i), dev(j_i)]).astype(np.float64)
+    assert_gemm_bound(got, y_ref, t_ref, "kv scores")
+
+
+def test_gemm_repeat_runs_identical(mx):
+    torch = _torch()
+    g = inputs.rng(3)
+    a = torch.from_numpy(g.integers(0, 0x7E, (384, 512), dtype=np.uint8)).cuda()
+    b = torch.from_numpy(g.integers(0, 0x7E, (256, 512), dtype=np.uint8)).cuda()
+    sa = torch.full((384, 16), 120, dtype=torch.uint8, device="cuda")
+    sb = torch.full((256, 16), 125, dtype=torch.uint8, device="cuda")
+    y1 = mx.mx_gemm(a, sa, b, sb, out_dtype=torch.float32)
+    y2 = mx.mx_gemm(a, sa, b, sb, out_dtype=torch.float32)
+    assert torch.equal(y1, y2)

@@ -1,0 +1,261 @@
+"""GPU parity of the quantize / KV-write / dequantize kernels against the
+oracle: codes, scales and dequantized values must match bit for bit."""
+import numpy as np
+import pytest
+
+from conftest import load_golden
+from gpu_util import assert_bitexact, dev, host
+from microscaling_block_scaled_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import torch
+    import microscaling_block_scaled_amd as m
+    assert torch.cuda.is_available()
+    ok, reason = m.mx_query_support(0)
+    assert ok, reason
+    return m
+
+
+def assorted_bits(seed, rows, cols):
+    """bf16 patterns mixing normal data, per-block magnitude jumps, exact
+    ties, zeros, subnormals, huge values, and raw random bit patterns
+    (which include NaN/Inf, so some blocks take the NaN path)."""
+    width = cols
+    cols = (cols + 31) // 32 * 32
+    g = inputs.rng(seed)
+    x = (g.standard_normal((rows, cols)) * np.exp2(g.integers(-30, 30, (rows, cols // 32)).repeat(32, 1)))
+    bits = inputs.f32_to_bf16_bits(x.astype(np.float32))
+    kind = g.integers(0, 10, (rows, cols // 32)).repeat(32, 1)
+    raw = g.integers(0, 1 << 16, (rows, cols), dtype=np.uint32).astype(np.uint16)
+    bits = np.where(kind == 0, raw, bits)                                   # random patterns
+    bits = np.where(kind == 1, np.uint16(0), bits)                          # all-zero blocks
+    bits = np.where((kind == 2) & (g.random((rows, cols)) < 0.5), np.uint16(0x8000), bits)  # -0
+    bits = np.where(kind == 3, (raw & np.uint16(0x807F)), bits)             # bf16 subnormals
+    bits = np.where(kind == 4, (raw | np.uint16(0x7E00)) & np.uint16(0xFF7F), bits)  # near the bf16 max
+    # ties: values exactly halfway between E4M3 grid points relative to a power-of-two amax
+    tie = inputs.f32_to_bf16_bits(np.float32(1.0625) * np.ones((rows, cols), np.float32))
+    bits = np.where((kind == 5) & (g.random((rows, cols)) < 0.3), tie, bits)
+    return np.ascontiguousarray(bits[:, :width])
+
+
+def f32_from(bits, seed=0):
+    """f32 values with the given bf16 top halves and random low mantissa bits
+    (zeros stay zero), so the f32 path sees full-precision inputs."""
+    low = inputs.rng(seed).integers(0, 1 << 16, bits.shape, dtype=np.uint32)
+    hi = bits.astype(np.uint32) << np.uint32(16)
+    keep_exact = (bits & np.uint16(0x7FFF)) == 0
+    return np.where(keep_exact, hi, hi | low).view(np.float32)
+
+
+# --------------------------------------------------------------------------- worked example
+def test_worked_example_on_gpu(mx, oracle):
+    ex = load_golden("worked_example_v64.json")
+    v = inputs.tiny()["v64"]
+    q, s = mx.mx_quantize(dev(v), E4M3)
+    q, s = host(q), host(s)
+    qo, so = oracle.quantize_rows(v, E4M3)
+    assert_bitexact(q, qo, "codes")
+    assert_bitexact(s, so, "scales")
+    assert [int(c) - 127 for c in s[0]] == ex["per_block"]["scale_exponents"]
+    back = host(mx.mx_dequantize(dev(q), dev(s), E4M3))
+    assert np.array_equal(back, v)
+
+
+# --------------------------------------------------------------------------- rowwise
+ROW_SHAPES = [(1, 32, 0), (3, 96, 8), (7, 160, 0), (33, 4096 + 32, 24), (130, 512, 0), (257, 96, 64)]
+
+
+@pytest.mark.parametrize("rows,cols,pad", ROW_SHAPES)
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_rowwise_matches_oracle(mx, oracle, rows, cols, pad, fmt, dt):
+    bits = assorted_bits(1000 + rows + cols + fmt, rows, cols + pad)
+    x = bits if dt == "bf16" else f32_from(bits, rows)
+    xd = dev(x, bf16=(dt == "bf16"))[:, :cols]
+    q, s = mx.mx_quantize(xd, fmt)
+    qo, so = oracle.quantize_rows(np.ascontiguousarray(x[:, :cols]), fmt)
+    assert_bitexact(host(s), so, "scales")
+    assert_bitexact(host(q), qo, "codes")
+
+
+def test_rowwise_writes_only_its_region(mx, oracle):
+    import torch
+    rows, cols = 40, 96
+    x = inputs.normal_bf16(3, (rows, cols))
+    q = torch.full((rows, 128), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.full((rows, 8), 0x5A, dtype=torch.uint8, device="cuda")
+    mx.mx_quantize(dev(x, bf16=True), E4M3, q=q[:, :cols], s=s[:, :3])
+    qh, sh = host(q), host(s)
+    qo, so = oracle.quantize_rows(x, E4M3)
+    assert_bitexact(qh[:, :cols], qo, "codes")
+    assert_bitexact(sh[:, :3], so, "scales")
+    assert np.all(qh[:, cols:] == 0xA5) and np.all(sh[:, 3:] == 0x5A)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_every_bf16_input_under_every_scale(mx, oracle, fmt):
+    """Every finite bf16 magnitude (both signs) under every scale code the
+    rule can choose, each block anchored so that it selects that code."""
+    emax = 8 if fmt == E4M3 else 15
+    bits = np.arange(0x7F80, dtype=np.uint16)
+    mag = inputs.bf16_bits_to_f32(bits).astype(np.float64)
+    rows = []
+    for c in range(0, 127 + 127 - emax + 1):
+        anchor = 2.0 ** (c - 127 + emax)
+        sel = bits[mag < 2 * anchor]
+        sel = np.concatenate([sel, sel | np.uint16(0x8000)])
+        sel = np.concatenate([sel, np.zeros((-len(sel)) % 31, np.uint16)]).reshape(-1, 31)
+        anc = np.full((sel.shape[0], 1), inputs.f32_to_bf16_bits(np.float32([anchor]))[0], np.uint16)
+        rows.append(np.concatenate([anc, sel], axis=1))
+    x = np.concatenate(rows)
+    pad = (-x.shape[0]) % 4
+    x = np.concatenate([x, np.zeros((pad, 32), np.uint16)]).reshape(-1, 128)
+    q, s = mx.mx_quantize(dev(x, bf16=True), fmt)
+    qo, so = oracle.quantize_rows(x, fmt)
+    assert_bitexact(host(s), so, "scales")
+    assert_bitexact(host(q), qo, "codes")
+
+
+# --------------------------------------------------------------------------- colwise
+COL_SHAPES = [(32, 1, 8), (64, 7, 1), (96, 65, 7), (160, 100, 4), (128, 64, 0), (256, 1000, 8), (4096, 96, 0)]
+
+
+@pytest.mark.parametrize("rows,cols,pad", COL_SHAPES)
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_colwise_matches_oracle(mx, oracle, rows, cols, pad, fmt, dt):
+    bits = assorted_bits(2000 + rows + cols + fmt, rows, cols + pad)
+    x = bits if dt == "bf16" else f32_from(bits, cols)
+    ld_align = 8 if dt == "bf16" else 4
+    ld = (cols + pad + ld_align - 1) // ld_align * ld_align
+    xp = np.zeros((rows, ld), x.dtype)
+    xp[:, :cols] = x[:, :cols]
+    xd = dev(xp, bf16=(dt == "bf16"))[:, :cols]
+    qt, st = mx.mx_quantize_colwise(xd, fmt)
+    qo, so = oracle.quantize_cols(np.ascontiguousarray(x[:, :cols]), fmt)
+    assert_bitexact(host(st), so, "scales")
+    assert_bitexact(host(qt), qo, "codes")
+
+
+# --------------------------------------------------------------------------- workload sizes
+@pytest.mark.slow
+def test_quantize_workload_full_size(mx, oracle):
+    """X bf16 [8192, 4096] ~ N(0,1) with 4 outlier channels x 2^12, E4M3,
+    rowwise and colwise, every code and scale compared."""
+    x, channels = inputs.quantize_input()
+    xd = dev(x, bf16=True)
+    q, s = mx.mx_quantize(xd, E4M3)
+    qt, st = mx.mx_quantize_colwise(xd, E4M3)
+    qo, so = oracle.quantize_rows(x, E4M3)
+    assert_bitexact(host(s), so, "rowwise scales")
+    assert_bitexact(host(q), qo, "rowwise codes")
+    qto, sto = oracle.quantize_cols(x, E4M3)
+    assert_bitexact(host(st), sto, "colwise scales")
+    assert_bitexact(host(qt), qto, "colwise codes")
+    # the outlier channels' colwise scales sit 12 binades above their neighbours'
+    assert np.all(host(st)[channels].astype(int).mean(axis=1) > host(st)[channels ^ 1].astype(int).mean(axis=1) + 10)
+
+
+@pytest.mark.slow
+def test_training_quantize_full_size(mx, oracle):
+    """Training linear layer: X and W rowwise E4M3, W colwise E4M3 (the
+    dgrad operand), G rowwise E5M2, each compared in full."""
+    x, w, g = inputs.training_inputs()
+    for name, arr, fmt in (("X", x, E4M3), ("W", w, E4M3), ("G", g, E5M2)):
+        q, s = mx.mx_quantize(dev(arr, bf16=True), fmt)
+        qo, so = oracle.quantize_rows(arr, fmt)
+        assert_bitexact(host(s), so, name + " scales")
+        assert_bitexact(host(q), qo, name + " codes")
+        del q, s, qo, so
+    qt, st = mx.mx_quantize_colwise(dev(w, bf16=True), E4M3)
+    qto, sto = oracle.quantize_cols(w, E4M3)
+    assert_bitexact(host(st), sto, "W colwise scales")
+    assert_bitexact(host(qt), qto, "W colwise codes")
+
+
+# --------------------------------------------------------------------------- KV write
+def _kv_run(mx, k, v, slots, pages, page_size):
+    import torch
+    T, H, D = k.shape
+    kc = torch.full((pages, page_size, H, D), 0x33, dtype=torch.uint8, device="cuda")
+    vc = torch.full_like(kc, 0x33)
+    ks = torch.full((pages, page_size, H, D // 32), 0x44, dtype=torch.uint8, device="cuda")
+    vs = torch.full_like(ks, 0x44)
+    mx.mx_kv_quant_write(dev(k, bf16=True), dev(v, bf16=True), dev(slots), kc, ks, vc, vs)
+    return host(kc), host(ks), host(vc), host(vs)
+
+
+def test_kv_write_small_with_padding_and_bad_slots(mx, oracle):
+    T, H, D, pages, page_size = 200, 3, 96, 5, 64
+    k = assorted_bits(31, T * H, D).reshape(T, H, D)
+    v = assorted_bits(32, T * H, D).reshape(T, H, D)
+    slots = inputs.rng(33).permutation(pages * page_size)[:T].astype(np.int64)
+    slots[::17] = -1                 # padding tokens
+    slots[5] = pages * page_size + 3  # out of range: ignored
+    got = _kv_run(mx, k, v, slots, pages, page_size)
+    ok_slots = np.where((slots >= 0) & (slots < pages * page_size), slots, -1)
+    init = [np.full((pages, page_size, H, D), 0x33, np.uint8), np.full((pages, page_size, H, D // 32), 0x44, np.uint8)]
+    want = oracle.kv_quant_write(k, v, ok_slots, page_size, pages, k_cache=init[0].copy(), k_scale=init[1].copy(),
+                                 v_cache=init[0].copy(), v_scale=init[1].copy())
+    for g_, w_, n in zip(got, want, ("k_cache", "k_scale", "v_cache", "v_scale")):
+        assert_bitexact(g_, w_, n)
+
+
+@pytest.mark.slow
+def test_kv_write_full_size(mx, oracle):
+    k, v, _ = inputs.kv_inputs()
+    slots, _ = inputs.kv_layout()
+    got = _kv_run(mx, k, v, slots, 256, 128)
+    want = oracle.kv_quant_write(k, v, slots, 128, 256)
+    for g_, w_, n in zip(got, want, ("k_cache", "k_scale", "v_cache", "v_scale")):
+        assert_bitexact(g_, w_, n)
+
+
+# --------------------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 96), (256, 1024)])
+def test_dequantize_matches_oracle(mx, oracle, fmt, out, rows, cols):
+    import torch
+    g = inputs.rng(40 + rows + fmt)
+    q = g.integers(0, 256, (rows, cols), dtype=np.uint8)
+    s = g.integers(0, 256, (rows, cols // 32), dtype=np.uint8)  # every code incl. 0xFF (NaN) and the extremes
+    y = host(mx.mx_dequantize(dev(q), dev(s), fmt, out_dtype=torch.float32 if out == "f32" else torch.bfloat16))
+    want = oracle.dequantize(q, s, fmt, out)
+    if out == "f32":
+        assert_bitexact(y.view(np.uint32), want.view(np.uint32), "dequant f32 bits")
+    else:
+        assert_bitexact(y, want, "dequant bf16 bits")
+
+
+# --------------------------------------------------------------------------- determinism, errors
+def test_repeat_runs_are_byte_identical(mx):
+    x = dev(inputs.normal_bf16(7, (512, 1024)), bf16=True)
+    a = [host(t) for t in mx.mx_quantize(x, E4M3)] + [host(t) for t in mx.mx_quantize_colwise(x, E4M3)]
+    b = [host(t) for t in mx.mx_quantize(x, E4M3)] + [host(t) for t in mx.mx_quantize_colwise(x, E4M3)]
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+
+
+def test_argument_errors_are_returned_not_launched(mx):
+    import torch
+    x = torch.zeros((64, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mx.MXError) as e:
+        mx.mx_quantize(x[:, :40], E4M3)                 # cols % 32 != 0
+    assert e.value.status == -2
+    with pytest.raises(mx.MXError) as e:
+        mx.mx_quantize(x[:, 1:33], E4M3)                # base not 16-byte aligned
+    assert e.value.status == -3
+    with pytest.raises(mx.MXError) as e:
+        mx.mx_quantize(x, 7)                            # unknown format
+    assert e.value.status == -4
+    with pytest.raises(mx.MXError) as e:
+        mx.mx_quantize_colwise(x[:48], E4M3)            # rows % 32 != 0
+    assert e.value.status == -2
+    torch.cuda.synchronize()
