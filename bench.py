@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP8 hot path on one MI355X (gfx950).
+
+One step = one pass of the metric's workload with inputs resident in HBM:
+  1. mx_quantize          bf16 X [8192, 4096] -> E4M3 codes + E8M0 scales (rowwise)
+  2. mx_quantize_colwise  the same X, blocks down the columns, stored transposed
+  3. mx_gemm              8192 x 8192 x 8192, E4M3 x E4M3 (pre-quantized rowwise
+                          along K), FP32 accumulation, bf16 output
+Before each kernel a 512 MiB fill evicts the caches (MALL included), outside
+the kernel's timing. Kernel durations come from HIP events recorded on the
+stream the kernels run on; ms_per_step is wall time per step including the
+fills.
+
+`value` is the GEMM's TFLOP/s (2*M*N*K per launch / mean launch time); the
+quantizers' GB/s (algorithmic bytes: read 2RC, write RC + RC/32) are reported
+beside it, and the other rows of the path (paged KV write, paged QK^T scores,
+dequantize, training linear fwd/dgrad) unless --quick. cpu_baseline times
+the CPU oracle on a bounded sample of the same GEMM.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+       [--no-cpu-baseline] [--copy-calibration]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 GEMM TFLOP/s @8192³ + quantize GB/s, each as % of MI355X peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 matrix peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_8192_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "microscaling_block_scaled_amd", "csrc", "gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Accumulates HIP-event durations of kernels launched on one stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, {}
+
+    def run(self, name, fn, record=True):
+        if not record:
+            fn()
+            return
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        fn()
+        e1.record(self.stream)
+        self.pairs.setdefault(name, []).append((e0, e1))
+
+    def mean_ms(self, name):
+        ts = [a.elapsed_time(b) for a, b in self.pairs[name]]
+        return sum(ts) / len(ts)
+
+
+def dev_bf16(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def copy_calibration(torch, steps):
+    """Plain device copy of a known size, for scaling the HBM byte counters."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": steps}}))
+
+
+def gemm_traffic():
+    """HBM bytes per 8192^3 GEMM launch from the committed counter summary,
+    or None if the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(GEMM_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        return t["bytes_per_launch"] if t.get("gemm_source_sha256") == sha else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(xa, xb, xq, budget_s=10.0):
+    """The oracle, as it is, on a bounded sample of the 8192^3 GEMM: quantize
+    the sampled rows of A and B and compute a square block of outputs over
+    the full K; plus the oracle's rowwise quantize of the full 8192 x 4096
+    input."""
+    import numpy as np
+    import oracle
+    K = xa.shape[1]
+
+    def run(n):
+        qa, sa = oracle.quantize_rows(np.ascontiguousarray(xa[:n]), oracle.E4M3)
+        qb, sb = oracle.quantize_rows(np.ascontiguousarray(xb[:n]), oracle.E4M3)
+        t0 = time.perf_counter()
+        oracle.gemm(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3)
+        return time.perf_counter() - t0
+
+    n = 32
+    t = run(n)
+    n = int(min(4096, max(32, n * (budget_s / max(t, 1e-3)) ** 0.5)))
+    t = run(n)
+    flop = 2.0 * n * n * K
+    t0 = time.perf_counter()
+    oracle.quantize_rows(xq, oracle.E4M3)
+    tq = time.perf_counter() - t0
+    R, C = xq.shape
+    qbytes = 2 * R * C + R * C + R * C // 32
+    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d x %d outputs of the 8192^3 product over the full K=%d (%.2f s, fp64); quantize: the "
+                      "full 8192 x 4096 input rowwise (%.2f s)" % (n, n, K, t, tq),
+            "quantize_GB/s": round(qbytes / tq / 1e9, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--quick", action="store_true", help="only the metric's workload (quantize + 8192^3 GEMM)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each rank's work is the "
+              "single-GPU kernel at its full shape); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import microscaling_block_scaled_amd as mx
+    from microscaling_block_scaled_amd import inputs
+
+    if args.copy_calibration:
+        copy_calibration(torch, args.steps)
+        return
+    ok, reason = mx.mx_query_support(0)
+    if not ok:
+        raise SystemExit("libmxfp8 cannot run here: " + reason)
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        flush_buf.zero_()
+
+    # ---- inputs (generated on the host, resident in HBM before timing)
+    log("generating inputs")
+    xq, _ = inputs.quantize_input()
+    xa, xb = inputs.gemm_inputs()
+    X = dev_bf16(torch, xq)
+    R, C = X.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    s = torch.empty((R, C // 32), dtype=torch.uint8, device="cuda")
+    qt = torch.empty((C, R), dtype=torch.uint8, device="cuda")
+    st = torch.empty((C, R // 32), dtype=torch.uint8, device="cuda")
+    A, SA = mx.mx_quantize(dev_bf16(torch, xa), mx.MX_E4M3)
+    B, SB = mx.mx_quantize(dev_bf16(torch, xb), mx.MX_E4M3)
+    M, K = A.shape
+    N = B.shape[0]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    tm = Timer(torch, stream)
+
+    def step(record):
+        flush()
+        tm.run("quantize_rowwise", lambda: mx.mx_quantize(X, mx.MX_E4M3, q=q, s=s), record)
+        flush()
+        tm.run("quantize_colwise", lambda: mx.mx_quantize_colwise(X, mx.MX_E4M3, qt=qt, st=st), record)
+        flush()
+        tm.run("gemm_8192", lambda: mx.mx_gemm(A, SA, B, SB, y=Y), record)
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    gemm_ms = tm.mean_ms("gemm_8192")
+    gemm_tflops = 2.0 * M * N * K / (gemm_ms * 1e-3) / 1e12
+    qbytes = 2 * R * C + R * C + R * C // 32
+    quant = {}
+    for name in ("quantize_rowwise", "quantize_colwise"):
+        ms = tm.mean_ms(name)
+        gbps = qbytes / (ms * 1e-3) / 1e9
+        quant[name] = {"us": round(ms * 1e3, 2), "GB/s": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                       "algorithmic_bytes": qbytes}
+
+    result = {
+        "metric": METRIC, "value": round(gemm_tflops, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic (seeded N(0,1) bf16, quantized to MXFP8 E4M3 on the GPU)",
+        "config": {"workload": "MXFP8 GEMM M=N=K=8192 E4M3 x E4M3, FP32 accumulate, bf16 out; "
+                               "quantize bf16 [8192 x 4096] (4 outlier channels x 2^12) to E4M3 rowwise and colwise",
+                   "gemm_accumulation": "AUTO -> scaled FP8 MFMA (E4M3 x E4M3, K >= 2048)"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+                     "traffic": gemm_traffic()},
+        "roofline_quantize": {"bound": "hbm", "achieved": quant["quantize_rowwise"]["GB/s"], "peak": HBM_PEAK_GBPS,
+                              "unit": "GB/s", "frac": quant["quantize_rowwise"]["frac_of_hbm_peak"],
+                              "traffic": None},
+        "gemm_us": round(gemm_ms * 1e3, 2),
+        "quantize": quant,
+    }
+
+    if not args.quick:
+        result["other_rows"] = other_rows(torch, mx, inputs, np, flush, stream, args.steps)
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(xa, xb, xq)
+    print(json.dumps(result))
+
+
+def other_rows(torch, mx, inputs, np, flush, stream, steps):
+    """The remaining rows of the path, each timed like the metric's kernels."""
+    out = {}
+    tm = Timer(torch, stream)
+    reps = max(3, steps // 4)
+
+    def timed(name, fn, n=reps):
+        fn()
+        torch.cuda.synchronize()
+        for _ in range(n):
+            flush()
+            tm.run(name, fn)
+        torch.cuda.synchronize()
+        return tm.mean_ms(name)
+
+    # paged KV write + paged QK^T scores (32768 tokens x 8 heads x 128, pages of 128)
+    log("kv rows")
+    k, v, qv = inputs.kv_inputs()
+    slots, table = inputs.kv_layout()
+    T, H, D = k.shape
+    Kd, Vd = dev_bf16(torch, k), dev_bf16(torch, v)
+    slots_d = torch.from_numpy(slots).cuda()
+    kc = torch.empty((256, 128, H, D), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((256, 128, H, D // 32), dtype=torch.uint8, device="cuda")
+    vc, vs = torch.empty_like(kc), torch.empty_like(ks)
+    ms = timed("kv_write", lambda: mx.mx_kv_quant_write(Kd, Vd, slots_d, kc, ks, vc, vs))
+    kv_bytes = 2 * T * H * D * 2 + T * 8 + 2 * (T * H * D + T * H * D // 32)
+    out["kv_quant_write"] = {"us": round(ms * 1e3, 2), "GB/s": round(kv_bytes / ms / 1e6, 1),
+                             "frac_of_hbm_peak": round(kv_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                             "algorithmic_bytes": kv_bytes}
+    Qc, Qs = mx.mx_quantize(dev_bf16(torch, qv.reshape(-1, D)), mx.MX_E4M3)
+    Qc, Qs = Qc.view(T, H, D), Qs.view(T, H, D // 32)
+    table_d = torch.from_numpy(table).cuda()
+    S = torch.empty((64, H, 512, 512), dtype=torch.float32, device="cuda")
+    ms = timed("paged_scores", lambda: mx.mx_paged_scores(Qc, Qs, kc, ks, table_d, 512, out=S))
+    sc_bytes = 2 * T * H * (D + D // 32) + 64 * H * 512 * 512 * 4
+    sc_flop = 2.0 * 64 * H * 512 * 512 * D
+    out["paged_scores"] = {"us": round(ms * 1e3, 2), "GB/s": round(sc_bytes / ms / 1e6, 1),
+                           "frac_of_hbm_peak": round(sc_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                           "TFLOP/s": round(sc_flop / ms / 1e9, 1), "algorithmic_bytes": sc_bytes,
+                           "accumulation": "AUTO -> bf16 MFMA (K = 128)"}
+    del S, Qc, Qs, Kd, Vd, kc, ks, vc, vs
+    # dequantize the 8192 x 4096 codes to bf16
+    log("dequant row")
+    xq, _ = inputs.quantize_input()
+    q, s = mx.mx_quantize(dev_bf16(torch, xq), mx.MX_E4M3)
+    yd = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    ms = timed("dequant", lambda: mx.mx_dequantize(q, s, mx.MX_E4M3, y=yd))
+    dq_bytes = q.numel() + s.numel() + 2 * q.numel()
+    out["dequantize_bf16"] = {"us": round(ms * 1e3, 2), "GB/s": round(dq_bytes / ms / 1e6, 1),
+                              "frac_of_hbm_peak": round(dq_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                              "algorithmic_bytes": dq_bytes}
+    del q, s, yd
+    # training linear layer: fwd (E4M3 x E4M3, K = 4096) and dgrad (E5M2 x E4M3, K = 14336)
+    log("training rows")
+    x, w, g = inputs.training_inputs()
+    Xd, Wd, Gd = dev_bf16(torch, x), dev_bf16(torch, w), dev_bf16(torch, g)
+    del x, w, g
+    M, Kf = Xd.shape
+    N = Wd.shape[0]
+    qg = torch.empty(Gd.shape, dtype=torch.uint8, device="cuda")
+    sg = torch.empty((Gd.shape[0], Gd.shape[1] // 32), dtype=torch.uint8, device="cuda")
+    ms = timed("quantize_G_e5m2", lambda: mx.mx_quantize(Gd, mx.MX_E5M2, q=qg, s=sg))
+    g_bytes = 3 * Gd.numel() + Gd.numel() // 32
+    out["quantize_G_e5m2_rowwise"] = {"us": round(ms * 1e3, 2), "GB/s": round(g_bytes / ms / 1e6, 1),
+                                      "frac_of_hbm_peak": round(g_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                      "algorithmic_bytes": g_bytes}
+    qwt = torch.empty((Wd.shape[1], Wd.shape[0]), dtype=torch.uint8, device="cuda")
+    swt = torch.empty((Wd.shape[1], Wd.shape[0] // 32), dtype=torch.uint8, device="cuda")
+    ms = timed("quantize_W_colwise", lambda: mx.mx_quantize_colwise(Wd, mx.MX_E4M3, qt=qwt, st=swt))
+    w_bytes = 3 * Wd.numel() + Wd.numel() // 32
+    out["quantize_W_colwise"] = {"us": round(ms * 1e3, 2), "GB/s": round(w_bytes / ms / 1e6, 1),
+                                 "frac_of_hbm_peak": round(w_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                 "algorithmic_bytes": w_bytes}
+    qx, sx = mx.mx_quantize(Xd, mx.MX_E4M3)
+    qw, sw = mx.mx_quantize(Wd, mx.MX_E4M3)
+    Yf = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ms = timed("fwd", lambda: mx.mx_gemm(qx, sx, qw, sw, y=Yf))
+    flop = 2.0 * M * N * Kf
+    out["training_fwd"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flop / ms / 1e9, 1),
+                           "frac_of_fp8_peak": round(flop / ms / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4),
+                           "shape": [M, N, Kf], "accumulation": "AUTO -> scaled FP8 MFMA"}
+    del Yf
+    dX = torch.empty((M, Kf), dtype=torch.bfloat16, device="cuda")
+    ms = timed("dgrad", lambda: mx.mx_gemm(qg, sg, qwt, swt, mx.MX_E5M2, mx.MX_E4M3, y=dX))
+    out["training_dgrad"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flop / ms / 1e9, 1),
+                             "frac_of_bf16_peak": round(flop / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "frac_of_fp8_peak": round(flop / ms / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4),
+                             "shape": [M, Kf, N], "accumulation": "AUTO -> bf16 MFMA (E5M2 operand)"}
+    return out
+
+
+if __name__ == "__main__":
+    main()

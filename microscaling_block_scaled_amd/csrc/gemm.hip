@@ -286,6 +286,266 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Main-loop kernel for large aligned problems (FP8 accumulation path).
+//
+// Tile 256 x 256 per workgroup, 4 waves of 128 x 128, built from
+// v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 per issue = 2 MX blocks). K
+// advances 64 bytes per stage through a ring of 4 LDS stages (32 KB of codes
+// + 2 KB of scales each) filled by direct global->LDS loads issued two
+// stages before the stage is published, so each load has about two stages
+// of MFMA work to land.
+// K must be a multiple of 256 (the ring depth times the stage).
+// Rows are 64 bytes; their 16-byte chunks are XOR-swizzled by (row >> 1) & 3,
+// which keeps every group of 8 fragment-reading lanes on distinct banks.
+// Operand layout of the 32x32x64 instruction: lane l (row l % 32, half
+// g = l / 32) holds k = 16g .. 16g+15 in bytes 0-15 and k = 32+16g .. +15 in
+// bytes 16-31, and supplies the scale of (row, block g). The result D[i][j]
+// sits in lane j + 32 * ((i / 4) % 2), element 4 * (i / 8) + i % 4.
+// Rows past M or N are clamped to the last row for loading and skipped on
+// store. Work-groups are dealt round-robin to the 8 XCDs, so tile ids are
+// remapped to give each XCD a contiguous band of tiles (shared panels stay
+// in that XCD's L2).
+// ---------------------------------------------------------------------------
+constexpr int kFBM = 256, kFBN = 256, kFBK = 64, kStages = 4;
+
+typedef float v16f32 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t fswz(uint32_t row, uint32_t chunk) {
+  return row * kFBK + ((chunk ^ ((row >> 1) & 3u)) << 4);
+}
+
+// LDS byte offset of a __shared__ object (the low half of its flat address).
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct global->LDS loads: lane i's 16 bytes land at M0 + 16i; a 2-byte load
+// lands zero-extended in the 4-byte slot at M0 + 4i.
+// They are issued as inline assembly so that the compiler does not add its
+// own drain of every outstanding load before each LDS read; completion is
+// tracked explicitly with wait_vmcnt before the barrier that publishes a
+// stage. Nothing else in these kernels uses M0.
+// The address is a wave-uniform base (SGPR pair) plus a per-lane 32-bit offset.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t off, const void* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+}
+__device__ __forceinline__ void dma2(uint32_t lds, uint32_t off, const void* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ushort %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int AFMT, int BFMT, bool BF16OUT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As[kStages][kFBM * kFBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs[kStages][kFBN * kFBK];
+  // the 2-byte scale loads land zero-extended in 4-byte slots: [row][4]
+  __shared__ __attribute__((aligned(16))) uint8_t sAs[kStages][kFBM * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sBs[kStages][kFBN * 4];
+
+  // ---- tile id: XCD-contiguous bands, then groups of 4 tile rows
+  const uint32_t ntiles = g.tiles_m * g.tiles_n;
+  uint32_t lid = blockIdx.x;
+  if (ntiles % 8 == 0) lid = (lid % 8) * (ntiles / 8) + lid / 8;
+  const uint32_t group = 4;
+  const uint32_t per_group = group * g.tiles_n;
+  const uint32_t first_m = (lid / per_group) * group;
+  const uint32_t gm = min(g.tiles_m - first_m, group);
+  const uint32_t tile_m = first_m + (lid % per_group) % gm;
+  const uint32_t tile_n = (lid % per_group) / gm;
+  const int64_t m0 = (int64_t)tile_m * kFBM, n0 = (int64_t)tile_n * kFBN;
+
+  const int64_t p = blockIdx.y;
+  const int64_t po = p / g.batch_inner, pi = p % g.batch_inner;
+  const uint8_t* A = g.a + po * g.sa_o + pi * g.sa_i;
+  const uint8_t* SA = g.sa + po * g.ssa_o + pi * g.ssa_i;
+  const uint8_t* B = g.b + po * g.sb_o + pi * g.sb_i;
+  const uint8_t* SB = g.sb + po * g.ssb_o + pi * g.ssb_i;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int64_t nsteps = g.K / kFBK;
+
+  // ---- loads: a wave-uniform base per operand (advanced by 64 bytes of K
+  // per stage) plus per-lane offsets fixed over K. Codes: 4 instructions per
+  // operand, 16 rows of 64 bytes each; scales: one instruction per operand,
+  // 64 rows of 2 bytes. Rows past M / N are clamped to the last row.
+  const uint8_t* a_base = A + m0 * g.lda;
+  const uint8_t* b_base = B + n0 * g.ldb;
+  const uint8_t* sa_base = SA + m0 * g.ldsa;
+  const uint8_t* sb_base = SB + n0 * g.ldsb;
+  uint32_t a_off[4], b_off[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t row = wave * 64 + t * 16 + (lane >> 2);
+    const uint32_t chunk = (lane & 3) ^ ((row >> 1) & 3u);
+    const uint32_t ra = (uint32_t)min((int64_t)row, g.M - 1 - m0), rb = (uint32_t)min((int64_t)row, g.N - 1 - n0);
+    a_off[t] = ra * (uint32_t)g.lda + chunk * 16;
+    b_off[t] = rb * (uint32_t)g.ldb + chunk * 16;
+  }
+  const uint32_t sa_off = (uint32_t)min((int64_t)(wave * 64 + lane), g.M - 1 - m0) * (uint32_t)g.ldsa;
+  const uint32_t sb_off = (uint32_t)min((int64_t)(wave * 64 + lane), g.N - 1 - n0) * (uint32_t)g.ldsb;
+
+  // LDS destinations are wave-uniform (one 1 KB / 128 B run per instruction)
+  const uint32_t a_dst0 = lds_off(&As[0][0]) + wave * 64 * kFBK, b_dst0 = lds_off(&Bs[0][0]) + wave * 64 * kFBK;
+  const uint32_t sa_dst0 = lds_off(&sAs[0][0]) + wave * 256, sb_dst0 = lds_off(&sBs[0][0]) + wave * 256;
+  constexpr uint32_t kCodeStage = kFBM * kFBK, kScaleStage = kFBM * 4;
+  auto issue = [&](int64_t ks) {
+    const uint32_t buf = (uint32_t)(ks % kStages);
+    const uint8_t* ab = a_base + ks * kFBK;
+    const uint8_t* bb = b_base + ks * kFBK;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dma16(a_dst0 + buf * kCodeStage + t * 16 * kFBK, a_off[t], ab);
+      dma16(b_dst0 + buf * kCodeStage + t * 16 * kFBK, b_off[t], bb);
+    }
+    dma2(sa_dst0 + buf * kScaleStage, sa_off, sa_base + ks * 2);
+    dma2(sb_dst0 + buf * kScaleStage, sb_off, sb_base + ks * 2);
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lr = lane & 31, lg = lane >> 5;
+
+  // operand fragments: B (the MFMA's first operand, rows n) for a whole stage,
+  // A (rows m) one 32-row block at a time
+  auto read_b = [&](v8i32 (&bf)[4], int (&bs)[4], int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t row = wn * 128 + j * 32 + lr;
+      const uint4 lo = *(const uint4*)(&Bs[buf][fswz(row, lg)]);
+      const uint4 hi = *(const uint4*)(&Bs[buf][fswz(row, lg + 2)]);
+      bf[j] = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      bs[j] = sBs[buf][row * 4 + lg];
+    }
+  };
+  auto read_a = [&](v8i32& af, int& as, int buf, int i) {
+    const uint32_t row = wm * 128 + i * 32 + lr;
+    const uint4 lo = *(const uint4*)(&As[buf][fswz(row, lg)]);
+    const uint4 hi = *(const uint4*)(&As[buf][fswz(row, lg + 2)]);
+    af = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    as = sAs[buf][row * 4 + lg];
+  };
+
+  v16f32 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Pipeline. LDS holds 4 stages: stage ks is being read, stage ks+1 is
+  // published, stage ks+2 is in flight, and at the top of step ks the buffer
+  // of stage ks-1 (fully read by every wave before the barrier) is refilled
+  // with stage ks+3. During step ks the B fragments of stage ks+1 and the
+  // next A fragment are read while the MFMAs of stage ks run. Each wave
+  // issues 10 loads per stage, so "stage ks+1 landed" is vmcnt <= 10 once
+  // stage ks+2 has been issued. The K loop is unrolled by the ring depth so
+  // every LDS offset is a constant.
+  constexpr int kLoadsPerStage = 10;
+  issue(0);
+  issue(1);
+  issue(2);
+  wait_vmcnt<2 * kLoadsPerStage>();
+  barrier();
+  v8i32 bcur[4], bnext[4];
+  int bscur[4], bsnext[4];
+  v8i32 acur, anext;
+  int ascur, asnext;
+  read_b(bcur, bscur, 0);
+  read_a(acur, ascur, 0, 0);
+
+  for (int64_t ks0 = 0; ks0 < nsteps; ks0 += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      const int64_t ks = ks0 + u;
+      const bool more = ks + 1 < nsteps;
+      if (more) {
+        if (ks + 2 < nsteps) wait_vmcnt<kLoadsPerStage>();
+        else wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        barrier();
+        if (ks + 3 < nsteps) issue(ks + 3);
+        read_b(bnext, bsnext, (u + 1) % kStages);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < 3) read_a(anext, asnext, u, i + 1);
+        else if (more) read_a(anext, asnext, (u + 1) % kStages, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[j], acur, acc[i][j], BFMT, AFMT, 0, bscur[j],
+                                                                       0, ascur);
+        acur = anext;
+        ascur = asnext;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bcur[j] = bnext[j];
+        bscur[j] = bsnext[j];
+      }
+    }
+  }
+
+  // ---- epilogue: lane owns y[m][n .. n+3] for 4 groups of n
+  uint8_t* Y = (uint8_t*)g.y + (po * g.sy_o + pi * g.sy_i) * (BF16OUT ? 2 : 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + wm * 128 + i * 32 + lr;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + wn * 128 + j * 32 + 8 * q + 4 * lg;
+        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if constexpr (BF16OUT) {
+          uint16_t* row = (uint16_t*)Y + m * g.ldy;
+          if (g.y_vec && n + 3 < g.N) {
+            *(uint2*)(row + n) = make_uint2(f32_to_bf16_rne(canon_nan(v0)) | (f32_to_bf16_rne(canon_nan(v1)) << 16),
+                                            f32_to_bf16_rne(canon_nan(v2)) | (f32_to_bf16_rne(canon_nan(v3)) << 16));
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+            for (int e = 0; e < 4; ++e)
+              if (n + e < g.N) row[n + e] = (uint16_t)f32_to_bf16_rne(canon_nan(vv[e]));
+          }
+        } else {
+          float* row = (float*)Y + m * g.ldy;
+          if (g.y_vec && n + 3 < g.N) {
+            *(float4*)(row + n) = make_float4(v0, v1, v2, v3);
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+            for (int e = 0; e < 4; ++e)
+              if (n + e < g.N) row[n + e] = vv[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+mx_status_t launch_fp8_big(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, int64_t batch, hipStream_t st) {
+  const dim3 grid(g.tiles_m * g.tiles_n, (uint32_t)batch);
+#define MX_BIG_LAUNCH(AF, BF, OUT) \
+  hipLaunchKernelGGL((gemm_fp8_big_kernel<AF, BF, OUT>), grid, dim3(kThreads), 0, st, g)
+#define MX_BIG_OUT(AF, BF) \
+  do { if (bf16out) MX_BIG_LAUNCH(AF, BF, true); else MX_BIG_LAUNCH(AF, BF, false); } while (0)
+  if (af == MX_E4M3 && bf == MX_E4M3) MX_BIG_OUT(MX_E4M3, MX_E4M3);
+  else if (af == MX_E5M2 && bf == MX_E4M3) MX_BIG_OUT(MX_E5M2, MX_E4M3);
+  else if (af == MX_E4M3 && bf == MX_E5M2) MX_BIG_OUT(MX_E4M3, MX_E5M2);
+  else MX_BIG_OUT(MX_E5M2, MX_E5M2);
+#undef MX_BIG_OUT
+#undef MX_BIG_LAUNCH
+  return mx_host::launch_status();
+}
+
 template <int BM, int BN, bool PAGED, int MODE>
 mx_status_t launch(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, int64_t batch, hipStream_t st) {
   const dim3 grid(g.tiles_m * g.tiles_n, (uint32_t)batch);
@@ -359,6 +619,17 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   g.tiles_n = (uint32_t)((N + BN - 1) / BN);
   if ((int64_t)g.tiles_m * g.tiles_n >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const bool bf16out = d->y_dtype == MX_BF16;
+  // large aligned problems: the 256 x 256 pipelined FP8 kernel
+  const bool big_ok = fp8 && !paged && K % 256 == 0 && K > 0 && d->lda % 16 == 0 && d->ldb % 16 == 0 &&
+                      ((uintptr_t)d->sa % 2 == 0) && ((uintptr_t)d->sb % 2 == 0) && d->ldsa % 2 == 0 &&
+                      d->ldsb % 2 == 0 && d->stride_sa_outer % 2 == 0 && d->stride_sa_inner % 2 == 0 &&
+                      d->stride_sb_outer % 2 == 0 && d->stride_sb_inner % 2 == 0 && M >= 256 && N >= 256;
+  if (big_ok) {
+    GemmArgs gb = g;
+    gb.tiles_m = (uint32_t)((M + kFBM - 1) / kFBM);
+    gb.tiles_n = (uint32_t)((N + kFBN - 1) / kFBN);
+    return launch_fp8_big(gb, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
+  }
   if (fp8)
     return paged ? launch<BM, BN, true, kModeFP8>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream)
                  : launch<BM, BN, false, kModeFP8>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);

@@ -140,6 +140,57 @@ def test_ragged_shapes(mx, oracle, M, N, K, afmt, bfmt, accum):
     assert_gemm_bound(bf16_to_f64(yb), y_ref, t_ref, "bf16 %s" % ((M, N, K),), bf16_out=True, rel=rel)
 
 
+# shapes that take the 256 x 256 pipelined kernel (M, N >= 256, K % 256 == 0),
+# including ragged M / N, a single K ring, odd ring counts and batching
+BIG_SHAPES = [(256, 256, 256), (300, 257, 512), (513, 1000, 1280), (1024, 512, 2048), (640, 384, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", BIG_SHAPES)
+@pytest.mark.parametrize("afmt,bfmt", [(E4M3, E4M3), (E5M2, E4M3)])
+def test_large_tile_kernel(mx, oracle, M, N, K, afmt, bfmt):
+    torch = _torch()
+    xa = inputs.normal_bf16(300 + M, (M, K))
+    xb = inputs.normal_bf16(400 + N, (N, K))
+    qa_o, sa_o = oracle.quantize_rows(xa, afmt)
+    qb_o, sb_o = oracle.quantize_rows(xb, bfmt)
+    y_ref, t_ref = oracle.gemm(qa_o, sa_o, afmt, qb_o, sb_o, bfmt)
+    qa, sa, qb, sb = dev(qa_o), dev(sa_o), dev(qb_o), dev(sb_o)
+    y = host(mx.mx_gemm(qa, sa, qb, sb, afmt, bfmt, out_dtype=torch.float32, accum=FP8))
+    assert_gemm_bound(y, y_ref, t_ref, "fp8 f32 %s" % ((M, N, K),), rel=FP8_GROUPED_REL)
+    yb = host(mx.mx_gemm(qa, sa, qb, sb, afmt, bfmt, out_dtype=torch.bfloat16, accum=FP8))
+    assert_gemm_bound(bf16_to_f64(yb), y_ref, t_ref, "fp8 bf16 %s" % ((M, N, K),), bf16_out=True, rel=FP8_GROUPED_REL)
+    if afmt == E4M3 and K >= 2048:
+        assert_gemm_bound(y, y_ref, t_ref, "fp8 auto-range %s" % ((M, N, K),))
+
+
+def test_large_tile_kernel_batched(mx, oracle):
+    """Two problems of 256 x 512 x 512 in one call (batch strides)."""
+    torch = _torch()
+    Bt, M, N, K = 2, 256, 512, 512
+    xa = inputs.normal_bf16(51, (Bt * M, K))
+    xb = inputs.normal_bf16(52, (Bt * N, K))
+    qa_o, sa_o = oracle.quantize_rows(xa, E4M3)
+    qb_o, sb_o = oracle.quantize_rows(xb, E4M3)
+    qa, sa, qb, sb = dev(qa_o), dev(sa_o), dev(qb_o), dev(sb_o)
+    y = torch.empty((Bt, M, N), dtype=torch.float32, device="cuda")
+    d = mx.mx_gemm_desc_t()
+    d.M, d.N, d.K = M, N, K
+    d.a, d.lda, d.sa, d.ldsa, d.a_fmt = qa.data_ptr(), K, sa.data_ptr(), K // 32, E4M3
+    d.b, d.ldb, d.sb, d.ldsb, d.b_fmt = qb.data_ptr(), K, sb.data_ptr(), K // 32, E4M3
+    d.y, d.ldy, d.y_dtype = y.data_ptr(), N, mx.MX_F32
+    d.batch_outer, d.batch_inner = Bt, 1
+    d.stride_a_outer, d.stride_sa_outer = M * K, M * K // 32
+    d.stride_b_outer, d.stride_sb_outer = N * K, N * K // 32
+    d.stride_y_outer = M * N
+    d.accum = FP8
+    mx.mx_gemm_desc(d)
+    yh = host(y)
+    for b in range(Bt):
+        y_ref, t_ref = oracle.gemm(qa_o[b * M:(b + 1) * M], sa_o[b * M:(b + 1) * M], E4M3,
+                                   qb_o[b * N:(b + 1) * N], sb_o[b * N:(b + 1) * N], E4M3)
+        assert_gemm_bound(yh[b], y_ref, t_ref, "batch %d" % b, rel=FP8_GROUPED_REL)
+
+
 def test_padded_pitches_and_unaligned_scale_rows(mx, oracle):
     """Leading dimensions larger than the rows, and K/32 not a multiple of 4
     (scale rows not dword aligned)."""
