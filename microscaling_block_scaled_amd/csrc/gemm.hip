@@ -291,47 +291,55 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 //
 // Tile 256 x 256 per workgroup, 4 waves of 128 x 128, built from
 // v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 per issue = 2 MX blocks). K
-// advances 64 bytes per stage through a ring of 4 LDS stages (32 KB of codes
-// + 2 KB of scales each) filled by direct global->LDS loads issued two
-// stages before the stage is published, so each load has about two stages
-// of MFMA work to land.
-// K must be a multiple of 256 (the ring depth times the stage).
-// Rows are 64 bytes; their 16-byte chunks are XOR-swizzled by (row >> 1) & 3,
-// which keeps every group of 8 fragment-reading lanes on distinct banks.
+// advances 128 bytes per stage -- whole 128-byte cache lines of every operand
+// row -- through two LDS stages of 64 KB (A and B) filled by direct
+// global->LDS loads; scales arrive 16 bytes per row (4 stages' worth) at a
+// time into two 8 KB buffers, so a scale line is fetched once per 4 stages.
 // Operand layout of the 32x32x64 instruction: lane l (row l % 32, half
 // g = l / 32) holds k = 16g .. 16g+15 in bytes 0-15 and k = 32+16g .. +15 in
 // bytes 16-31, and supplies the scale of (row, block g). The result D[i][j]
 // sits in lane j + 32 * ((i / 4) % 2), element 4 * (i / 8) + i % 4.
-// Rows past M or N are clamped to the last row for loading and skipped on
-// store. Work-groups are dealt round-robin to the 8 XCDs, so tile ids are
-// remapped to give each XCD a contiguous band of tiles (shared panels stay
-// in that XCD's L2).
+// Rows are 128 bytes; their 16-byte chunks are XOR-permuted by row (fperm)
+// so the fragment reads are free of bank conflicts. Rows past M or N are
+// clamped to the last row for loading and skipped on store. Work-groups are
+// dealt round-robin to the 8 XCDs, so tile ids are remapped to give each XCD
+// a contiguous band of tiles (shared panels stay in that XCD's L2).
+// Requires K % 512 == 0 and 16-byte aligned scale rows.
 // ---------------------------------------------------------------------------
-constexpr int kFBM = 256, kFBN = 256, kFBK = 64, kStages = 4;
+constexpr int kFBM = 256, kFBN = 256, kFBK = 128;
+constexpr uint32_t kCodeStage = kFBM * kFBK;   // bytes per operand per stage
+constexpr uint32_t kScaleRow = 16;             // scale bytes per row per group of 4 stages
+constexpr uint32_t kScaleBuf = kFBM * kScaleRow;
 
 typedef float v16f32 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ uint32_t fswz(uint32_t row, uint32_t chunk) {
-  return row * kFBK + ((chunk ^ ((row >> 1) & 3u)) << 4);
-}
+// 16-byte chunk permutation of a 128-byte LDS row: chunk ^ fperm(row) with
+// fperm = ((row >> 1) & 7) ^ ((row & 1) << 2). The 16 (or 8) lanes that a
+// ds_read_b128 serves together read 16 (8) consecutive rows at one logical
+// chunk; fperm gives them distinct bank groups whether the LDS serves 16
+// lanes over 64 banks or 8 lanes over 32 banks. It depends only on row bits
+// 0-3, so rows 32 apart share it.
+__device__ __forceinline__ uint32_t fperm(uint32_t row) { return ((row >> 1) & 7u) ^ ((row & 1u) << 2); }
 
 // LDS byte offset of a __shared__ object (the low half of its flat address).
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Direct global->LDS loads: lane i's 16 bytes land at M0 + 16i; a 2-byte load
-// lands zero-extended in the 4-byte slot at M0 + 4i.
+// Direct global->LDS 16-byte loads: lane i's bytes land at M0 + 16i. The
+// address is a wave-uniform base (SGPR pair) plus a per-lane 32-bit offset.
 // They are issued as inline assembly so that the compiler does not add its
 // own drain of every outstanding load before each LDS read; completion is
 // tracked explicitly with wait_vmcnt before the barrier that publishes a
-// stage. Nothing else in these kernels uses M0.
-// The address is a wave-uniform base (SGPR pair) plus a per-lane 32-bit offset.
+// stage. Nothing else in this kernel uses M0.
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t off, const void* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
-}
-__device__ __forceinline__ void dma2(uint32_t lds, uint32_t off, const void* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ushort %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+  // the base is wave-uniform by construction; readfirstlane makes that
+  // visible to the compiler so the pair is kept in SGPRs
+  const uint64_t b = (uint64_t)base;
+  const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"((const void*)ub)
+               : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -343,11 +351,10 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 
 template <int AFMT, int BFMT, bool BF16OUT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t As[kStages][kFBM * kFBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t Bs[kStages][kFBN * kFBK];
-  // the 2-byte scale loads land zero-extended in 4-byte slots: [row][4]
-  __shared__ __attribute__((aligned(16))) uint8_t sAs[kStages][kFBM * 4];
-  __shared__ __attribute__((aligned(16))) uint8_t sBs[kStages][kFBN * 4];
+  __shared__ __attribute__((aligned(1024))) uint8_t As[2][kCodeStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs[2][kCodeStage];
+  __shared__ __attribute__((aligned(16))) uint8_t sAs[2][kScaleBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t sBs[2][kScaleBuf];
 
   // ---- tile id: XCD-contiguous bands, then groups of 4 tile rows
   const uint32_t ntiles = g.tiles_m * g.tiles_n;
@@ -371,66 +378,67 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int64_t nsteps = g.K / kFBK;
+  const int64_t nsteps = g.K / kFBK;  // a multiple of 4
 
-  // ---- loads: a wave-uniform base per operand (advanced by 64 bytes of K
-  // per stage) plus per-lane offsets fixed over K. Codes: 4 instructions per
-  // operand, 16 rows of 64 bytes each; scales: one instruction per operand,
-  // 64 rows of 2 bytes. Rows past M / N are clamped to the last row.
+  // ---- loads. Codes: per stage and operand, 8 instructions per wave, each
+  // 8 rows x 128 bytes (lane i: row i / 8, LDS chunk i % 8, which holds the
+  // row's logical chunk (i % 8) ^ fperm(row)). Scales: per group of 4
+  // stages and operand, one instruction per wave, 64 rows x 16 bytes. Rows
+  // past M / N are clamped to the last row.
   const uint8_t* a_base = A + m0 * g.lda;
   const uint8_t* b_base = B + n0 * g.ldb;
   const uint8_t* sa_base = SA + m0 * g.ldsa;
   const uint8_t* sb_base = SB + n0 * g.ldsb;
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[8], b_off[8];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t row = wave * 64 + t * 16 + (lane >> 2);
-    const uint32_t chunk = (lane & 3) ^ ((row >> 1) & 3u);
-    const uint32_t ra = (uint32_t)min((int64_t)row, g.M - 1 - m0), rb = (uint32_t)min((int64_t)row, g.N - 1 - n0);
-    a_off[t] = ra * (uint32_t)g.lda + chunk * 16;
-    b_off[t] = rb * (uint32_t)g.ldb + chunk * 16;
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t row = wave * 64 + t * 8 + (lane >> 3);
+    const uint32_t chunk16 = (((uint32_t)lane & 7u) ^ fperm(row)) << 4;
+    a_off[t] = (uint32_t)min((int64_t)row, g.M - 1 - m0) * (uint32_t)g.lda + chunk16;
+    b_off[t] = (uint32_t)min((int64_t)row, g.N - 1 - n0) * (uint32_t)g.ldb + chunk16;
   }
-  const uint32_t sa_off = (uint32_t)min((int64_t)(wave * 64 + lane), g.M - 1 - m0) * (uint32_t)g.ldsa;
-  const uint32_t sb_off = (uint32_t)min((int64_t)(wave * 64 + lane), g.N - 1 - n0) * (uint32_t)g.ldsb;
-
-  // LDS destinations are wave-uniform (one 1 KB / 128 B run per instruction)
-  const uint32_t a_dst0 = lds_off(&As[0][0]) + wave * 64 * kFBK, b_dst0 = lds_off(&Bs[0][0]) + wave * 64 * kFBK;
-  const uint32_t sa_dst0 = lds_off(&sAs[0][0]) + wave * 256, sb_dst0 = lds_off(&sBs[0][0]) + wave * 256;
-  constexpr uint32_t kCodeStage = kFBM * kFBK, kScaleStage = kFBM * 4;
-  auto issue = [&](int64_t ks) {
-    const uint32_t buf = (uint32_t)(ks % kStages);
-    const uint8_t* ab = a_base + ks * kFBK;
-    const uint8_t* bb = b_base + ks * kFBK;
+  const uint32_t srow = wave * 64 + lane;
+  const uint32_t sa_off = (uint32_t)min((int64_t)srow, g.M - 1 - m0) * (uint32_t)g.ldsa;
+  const uint32_t sb_off = (uint32_t)min((int64_t)srow, g.N - 1 - n0) * (uint32_t)g.ldsb;
+  const uint32_t a_dst = lds_off(&As[0][0]) + wave * 64 * kFBK, b_dst = lds_off(&Bs[0][0]) + wave * 64 * kFBK;
+  const uint32_t sa_dst = lds_off(&sAs[0][0]) + wave * 64 * kScaleRow;
+  const uint32_t sb_dst = lds_off(&sBs[0][0]) + wave * 64 * kScaleRow;
+  auto issue_codes = [&](int64_t s) {
+    const uint32_t buf = (uint32_t)(s & 1);
+    const uint8_t* ab = a_base + s * kFBK;
+    const uint8_t* bb = b_base + s * kFBK;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      dma16(a_dst0 + buf * kCodeStage + t * 16 * kFBK, a_off[t], ab);
-      dma16(b_dst0 + buf * kCodeStage + t * 16 * kFBK, b_off[t], bb);
+    for (int t = 0; t < 8; ++t) {
+      dma16(a_dst + buf * kCodeStage + t * 8 * kFBK, a_off[t], ab);
+      dma16(b_dst + buf * kCodeStage + t * 8 * kFBK, b_off[t], bb);
     }
-    dma2(sa_dst0 + buf * kScaleStage, sa_off, sa_base + ks * 2);
-    dma2(sb_dst0 + buf * kScaleStage, sb_off, sb_base + ks * 2);
+  };
+  auto issue_scales = [&](int64_t grp) {
+    const uint32_t buf = (uint32_t)(grp & 1);
+    dma16(sa_dst + buf * kScaleBuf, sa_off, sa_base + grp * kScaleRow);
+    dma16(sb_dst + buf * kScaleBuf, sb_off, sb_base + grp * kScaleRow);
   };
 
+  // ---- fragment reads: lane (lr, lg) of fragment f reads row base + 32 f;
+  // the permutation term depends only on lr, so every read is a per-lane
+  // base address plus a compile-time offset (carried as an immediate).
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lr = lane & 31, lg = lane >> 5;
-
-  // operand fragments: B (the MFMA's first operand, rows n) for a whole stage,
-  // A (rows m) one 32-row block at a time
-  auto read_b = [&](v8i32 (&bf)[4], int (&bs)[4], int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t row = wn * 128 + j * 32 + lr;
-      const uint4 lo = *(const uint4*)(&Bs[buf][fswz(row, lg)]);
-      const uint4 hi = *(const uint4*)(&Bs[buf][fswz(row, lg + 2)]);
-      bf[j] = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      bs[j] = sBs[buf][row * 4 + lg];
-    }
-  };
-  auto read_a = [&](v8i32& af, int& as, int buf, int i) {
-    const uint32_t row = wm * 128 + i * 32 + lr;
-    const uint4 lo = *(const uint4*)(&As[buf][fswz(row, lg)]);
-    const uint4 hi = *(const uint4*)(&As[buf][fswz(row, lg + 2)]);
-    af = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    as = sAs[buf][row * 4 + lg];
+  const uint32_t fp = fperm(lr);
+  const uint8_t* a_row = &As[0][0] + (wm * 128 + lr) * kFBK;
+  const uint8_t* b_row = &Bs[0][0] + (wn * 128 + lr) * kFBK;
+  const uint8_t* a_sc = &sAs[0][0] + (wm * 128 + lr) * kScaleRow + lg;
+  const uint8_t* b_sc = &sBs[0][0] + (wn * 128 + lr) * kScaleRow + lg;
+  // K half h of stage buffer buf: logical chunks 4h + lg and 4h + 2 + lg
+  const uint32_t c_lo[2] = {((0 + lg) ^ fp) << 4, ((4 + lg) ^ fp) << 4};
+  const uint32_t c_hi[2] = {((2 + lg) ^ fp) << 4, ((6 + lg) ^ fp) << 4};
+  auto read_frag = [&](const uint8_t* row_base, const uint8_t* sc_base, int buf, int sbuf, int sub, int h, int f,
+                       v8i32& fr, int& sc) {
+    const uint8_t* r = row_base + buf * kCodeStage + f * 32 * kFBK;
+    const uint4 lo = *(const uint4*)(r + c_lo[h]);
+    const uint4 hi = *(const uint4*)(r + c_hi[h]);
+    fr = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    sc = sc_base[sbuf * kScaleBuf + f * 32 * kScaleRow + sub * 4 + 2 * h];
   };
 
   v16f32 acc[4][4];
@@ -441,50 +449,84 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // Pipeline. LDS holds 4 stages: stage ks is being read, stage ks+1 is
-  // published, stage ks+2 is in flight, and at the top of step ks the buffer
-  // of stage ks-1 (fully read by every wave before the barrier) is refilled
-  // with stage ks+3. During step ks the B fragments of stage ks+1 and the
-  // next A fragment are read while the MFMAs of stage ks run. Each wave
-  // issues 10 loads per stage, so "stage ks+1 landed" is vmcnt <= 10 once
-  // stage ks+2 has been issued. The K loop is unrolled by the ring depth so
-  // every LDS offset is a constant.
-  constexpr int kLoadsPerStage = 10;
-  issue(0);
-  issue(1);
-  issue(2);
-  wait_vmcnt<2 * kLoadsPerStage>();
+  // Pipeline. Stage s lives in buffer s % 2. The DMA of stage s+2 is issued
+  // right after the barrier near the end of stage s that publishes stage s+1
+  // (at that point every wave has finished reading stage s), so each stage
+  // has about one stage of MFMA work to land. Fragments of the next K half
+  // (and of stage s+1's first half, right after that barrier) are read while
+  // the current MFMAs run. The loop is unrolled by 4 stages so that buffer,
+  // scale-slot and half offsets are all constants.
+  issue_scales(0);
+  issue_codes(0);
+  if (nsteps > 1) issue_codes(1);
+  if (nsteps > 1) wait_vmcnt<16>();
+  else wait_vmcnt<0>();
   barrier();
-  v8i32 bcur[4], bnext[4];
-  int bscur[4], bsnext[4];
-  v8i32 acur, anext;
-  int ascur, asnext;
-  read_b(bcur, bscur, 0);
-  read_a(acur, ascur, 0, 0);
-
-  for (int64_t ks0 = 0; ks0 < nsteps; ks0 += kStages) {
+  v8i32 bcur[4], bnext[4], acur, anext;
+  int bscur[4], bsnext[4], ascur, asnext;
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      const int64_t ks = ks0 + u;
-      const bool more = ks + 1 < nsteps;
-      if (more) {
-        if (ks + 2 < nsteps) wait_vmcnt<kLoadsPerStage>();
-        else wait_vmcnt<0>();
-        wait_lgkmcnt0();
-        barrier();
-        if (ks + 3 < nsteps) issue(ks + 3);
-        read_b(bnext, bsnext, (u + 1) % kStages);
-      }
+  for (int j = 0; j < 4; ++j) read_frag(b_row, b_sc, 0, 0, 0, 0, j, bcur[j], bscur[j]);
+  read_frag(a_row, a_sc, 0, 0, 0, 0, 0, acur, ascur);
+
+  for (int64_t s0 = 0; s0 < nsteps; s0 += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t s = s0 + u;
+      const int buf = u & 1, sbuf = (int)((s0 / 4) & 1);
+      // ---- first K half: fetch the second half's B fragments
+#pragma unroll
+      for (int j = 0; j < 4; ++j) read_frag(b_row, b_sc, buf, sbuf, u, 1, j, bnext[j], bsnext[j]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (i < 3) read_a(anext, asnext, u, i + 1);
-        else if (more) read_a(anext, asnext, (u + 1) % kStages, 0);
+        if (i < 3) read_frag(a_row, a_sc, buf, sbuf, u, 0, i + 1, anext, asnext);
+        else read_frag(a_row, a_sc, buf, sbuf, u, 1, 0, anext, asnext);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[j], acur, acc[i][j], BFMT, AFMT, 0, bscur[j],
                                                                        0, ascur);
         acur = anext;
         ascur = asnext;
+        // keep each group's fragment reads next to the MFMAs that hide them
+        // (hoisting all of a stage's reads would exhaust the registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bcur[j] = bnext[j];
+        bscur[j] = bsnext[j];
+      }
+      // ---- second K half
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < 3) {
+          read_frag(a_row, a_sc, buf, sbuf, u, 1, i + 1, anext, asnext);
+        } else {
+          // publish stage s+1; every wave is done reading stage s. This runs
+          // on the last stage too (its reads of the other buffer are unused):
+          // with a barrier on every path, the compiler cannot carry fragment
+          // values from one stage to a later one that reads the same buffer.
+          wait_vmcnt<0>();
+          wait_lgkmcnt0();
+          barrier();
+          // The last two stages reload stage nsteps-1 into a buffer nobody
+          // reads again: the loop body stays free of branches, which would
+          // let the compiler sink the MFMAs past the barrier.
+          if (((u + 2) & 3) == 0) issue_scales(min((s + 2) >> 2, nsteps / 4 - 1));
+          issue_codes(min(s + 2, nsteps - 1));
+          const int nbuf = buf ^ 1, nsbuf = u == 3 ? sbuf ^ 1 : sbuf, nsub = (u + 1) & 3;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) read_frag(b_row, b_sc, nbuf, nsbuf, nsub, 0, j, bnext[j], bsnext[j]);
+          read_frag(a_row, a_sc, nbuf, nsbuf, nsub, 0, 0, anext, asnext);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[j], acur, acc[i][j], BFMT, AFMT, 0, bscur[j],
+                                                                       0, ascur);
+        acur = anext;
+        ascur = asnext;
+        // keep each group's fragment reads next to the MFMAs that hide them
+        // (hoisting all of a stage's reads would exhaust the registers)
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -493,6 +535,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
       }
     }
   }
+
+  wait_vmcnt<0>();  // no load may still be writing LDS when the group ends
 
   // ---- epilogue: lane owns y[m][n .. n+3] for 4 groups of n
   uint8_t* Y = (uint8_t*)g.y + (po * g.sy_o + pi * g.sy_i) * (BF16OUT ? 2 : 4);
@@ -620,10 +664,11 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   if ((int64_t)g.tiles_m * g.tiles_n >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const bool bf16out = d->y_dtype == MX_BF16;
   // large aligned problems: the 256 x 256 pipelined FP8 kernel
-  const bool big_ok = fp8 && !paged && K % 256 == 0 && K > 0 && d->lda % 16 == 0 && d->ldb % 16 == 0 &&
-                      ((uintptr_t)d->sa % 2 == 0) && ((uintptr_t)d->sb % 2 == 0) && d->ldsa % 2 == 0 &&
-                      d->ldsb % 2 == 0 && d->stride_sa_outer % 2 == 0 && d->stride_sa_inner % 2 == 0 &&
-                      d->stride_sb_outer % 2 == 0 && d->stride_sb_inner % 2 == 0 && M >= 256 && N >= 256;
+  const bool big_ok = fp8 && !paged && K % 512 == 0 && K > 0 && d->lda % 16 == 0 && d->ldb % 16 == 0 &&
+                      mx_host::aligned16(d->sa) && mx_host::aligned16(d->sb) && d->ldsa % 16 == 0 &&
+                      d->ldsb % 16 == 0 && d->stride_sa_outer % 16 == 0 && d->stride_sa_inner % 16 == 0 &&
+                      d->stride_sb_outer % 16 == 0 && d->stride_sb_inner % 16 == 0 && M >= 256 && N >= 256 &&
+                      (M * d->lda) < ((int64_t)1 << 32) && (N * d->ldb) < ((int64_t)1 << 32);
   if (big_ok) {
     GemmArgs gb = g;
     gb.tiles_m = (uint32_t)((M + kFBM - 1) / kFBM);

@@ -16,7 +16,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/mxfp8.h"
+#include "mxfp8.h"
 
 namespace mx {
 

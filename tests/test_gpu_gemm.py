@@ -140,9 +140,11 @@ def test_ragged_shapes(mx, oracle, M, N, K, afmt, bfmt, accum):
     assert_gemm_bound(bf16_to_f64(yb), y_ref, t_ref, "bf16 %s" % ((M, N, K),), bf16_out=True, rel=rel)
 
 
-# shapes that take the 256 x 256 pipelined kernel (M, N >= 256, K % 256 == 0),
-# including ragged M / N, a single K ring, odd ring counts and batching
-BIG_SHAPES = [(256, 256, 256), (300, 257, 512), (513, 1000, 1280), (1024, 512, 2048), (640, 384, 8192)]
+# shapes that take the 256 x 256 pipelined kernel (M, N >= 256, K % 512 == 0,
+# 16-byte aligned scale rows), including ragged M / N, a single scale group
+# and odd group counts; K = 256 falls back to the general kernel
+BIG_SHAPES = [(256, 256, 256), (256, 256, 512), (300, 257, 512), (513, 1000, 1536), (1024, 512, 2048),
+              (640, 384, 8192)]
 
 
 @pytest.mark.parametrize("M,N,K", BIG_SHAPES)
