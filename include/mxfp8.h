@@ -157,8 +157,9 @@ mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_t dt, int64
  *
  * Accumulation (field `accum`). The sum over blocks is FP32 in every mode;
  * the modes differ inside one matrix instruction:
- *   MX_ACCUM_FP8  -- v_mfma_scale_f32_16x16x128_f8f6f4 on the codes, peak
- *                    rate. On gfx950 this instruction adds the products of
+ *   MX_ACCUM_FP8  -- the scaled FP8 matrix instructions on the codes
+ *                    (v_mfma_scale_f32_16x16x128_f8f6f4 / _32x32x64_), peak
+ *                    rate. On gfx950 these instructions add the products of
  *                    each group of 8 consecutive k with only about 14
  *                    significant bits, aligned to the group's largest product
  *                    (measured), i.e. a per-group error up to ~2^-13 of that

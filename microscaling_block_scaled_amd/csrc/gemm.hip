@@ -427,18 +427,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   const uint32_t fp = fperm(lr);
   const uint8_t* a_row = &As[0][0] + (wm * 128 + lr) * kFBK;
   const uint8_t* b_row = &Bs[0][0] + (wn * 128 + lr) * kFBK;
-  const uint8_t* a_sc = &sAs[0][0] + (wm * 128 + lr) * kScaleRow + lg;
-  const uint8_t* b_sc = &sBs[0][0] + (wn * 128 + lr) * kScaleRow + lg;
+  const uint8_t* a_sc = &sAs[0][0] + (wm * 128 + lr) * kScaleRow;
+  const uint8_t* b_sc = &sBs[0][0] + (wn * 128 + lr) * kScaleRow;
   // K half h of stage buffer buf: logical chunks 4h + lg and 4h + 2 + lg
   const uint32_t c_lo[2] = {((0 + lg) ^ fp) << 4, ((4 + lg) ^ fp) << 4};
   const uint32_t c_hi[2] = {((2 + lg) ^ fp) << 4, ((6 + lg) ^ fp) << 4};
-  auto read_frag = [&](const uint8_t* row_base, const uint8_t* sc_base, int buf, int sbuf, int sub, int h, int f,
-                       v8i32& fr, int& sc) {
+  // Scales: once per group of 4 stages each lane reads the 16 scale bytes of
+  // its 4 rows per operand (16-byte reads of consecutive rows, free of bank
+  // conflicts, where byte reads of a 16-byte-pitch array are not). Word w of
+  // row f holds blocks 4w .. 4w+3 of the group; shifting it right by 8 * lg
+  // puts block 4w + lg in byte 0 and block 4w + 2 + lg in byte 2, so the
+  // scale of (stage w, half h) is the word shifted right by 16 h (the
+  // instruction reads byte 0).
+  uint4 sa4[4], sb4[4];
+  auto read_scales = [&](int sbuf) {
+    const uint32_t sh = 8 * lg;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      uint4 va = *(const uint4*)(a_sc + sbuf * kScaleBuf + f * 32 * kScaleRow);
+      uint4 vb = *(const uint4*)(b_sc + sbuf * kScaleBuf + f * 32 * kScaleRow);
+      sa4[f] = make_uint4(va.x >> sh, va.y >> sh, va.z >> sh, va.w >> sh);
+      sb4[f] = make_uint4(vb.x >> sh, vb.y >> sh, vb.z >> sh, vb.w >> sh);
+    }
+  };
+  auto scale_of = [&](const uint4& w4, int sub, int h) -> int {
+    const uint32_t w = sub == 0 ? w4.x : sub == 1 ? w4.y : sub == 2 ? w4.z : w4.w;
+    return (int)(w >> (16 * h));
+  };
+  auto read_frag = [&](const uint8_t* row_base, const uint4* s4, int buf, int sub, int h, int f, v8i32& fr,
+                       int& sc) {
     const uint8_t* r = row_base + buf * kCodeStage + f * 32 * kFBK;
     const uint4 lo = *(const uint4*)(r + c_lo[h]);
     const uint4 hi = *(const uint4*)(r + c_hi[h]);
     fr = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    sc = sc_base[sbuf * kScaleBuf + f * 32 * kScaleRow + sub * 4 + 2 * h];
+    sc = scale_of(s4[f], sub, h);
   };
 
   v16f32 acc[4][4];
@@ -464,9 +486,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   barrier();
   v8i32 bcur[4], bnext[4], acur, anext;
   int bscur[4], bsnext[4], ascur, asnext;
+  read_scales(0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) read_frag(b_row, b_sc, 0, 0, 0, 0, j, bcur[j], bscur[j]);
-  read_frag(a_row, a_sc, 0, 0, 0, 0, 0, acur, ascur);
+  for (int j = 0; j < 4; ++j) read_frag(b_row, sb4, 0, 0, 0, j, bcur[j], bscur[j]);
+  read_frag(a_row, sa4, 0, 0, 0, 0, acur, ascur);
 
   for (int64_t s0 = 0; s0 < nsteps; s0 += 4) {
 #pragma unroll
@@ -475,11 +498,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
       const int buf = u & 1, sbuf = (int)((s0 / 4) & 1);
       // ---- first K half: fetch the second half's B fragments
 #pragma unroll
-      for (int j = 0; j < 4; ++j) read_frag(b_row, b_sc, buf, sbuf, u, 1, j, bnext[j], bsnext[j]);
+      for (int j = 0; j < 4; ++j) read_frag(b_row, sb4, buf, u, 1, j, bnext[j], bsnext[j]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (i < 3) read_frag(a_row, a_sc, buf, sbuf, u, 0, i + 1, anext, asnext);
-        else read_frag(a_row, a_sc, buf, sbuf, u, 1, 0, anext, asnext);
+        if (i < 3) read_frag(a_row, sa4, buf, u, 0, i + 1, anext, asnext);
+        else read_frag(a_row, sa4, buf, u, 1, 0, anext, asnext);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[j], acur, acc[i][j], BFMT, AFMT, 0, bscur[j],
@@ -499,7 +522,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i < 3) {
-          read_frag(a_row, a_sc, buf, sbuf, u, 1, i + 1, anext, asnext);
+          read_frag(a_row, sa4, buf, u, 1, i + 1, anext, asnext);
         } else {
           // publish stage s+1; every wave is done reading stage s. This runs
           // on the last stage too (its reads of the other buffer are unused):
@@ -513,10 +536,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
           // let the compiler sink the MFMAs past the barrier.
           if (((u + 2) & 3) == 0) issue_scales(min((s + 2) >> 2, nsteps / 4 - 1));
           issue_codes(min(s + 2, nsteps - 1));
-          const int nbuf = buf ^ 1, nsbuf = u == 3 ? sbuf ^ 1 : sbuf, nsub = (u + 1) & 3;
+          const int nbuf = buf ^ 1, nsub = (u + 1) & 3;
+          if (u == 3) read_scales(sbuf ^ 1);  // the next group's scales were published by this barrier
 #pragma unroll
-          for (int j = 0; j < 4; ++j) read_frag(b_row, b_sc, nbuf, nsbuf, nsub, 0, j, bnext[j], bsnext[j]);
-          read_frag(a_row, a_sc, nbuf, nsbuf, nsub, 0, 0, anext, asnext);
+          for (int j = 0; j < 4; ++j) read_frag(b_row, sb4, nbuf, nsub, 0, j, bnext[j], bsnext[j]);
+          read_frag(a_row, sa4, nbuf, nsub, 0, 0, anext, asnext);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
