@@ -341,6 +341,15 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t off, const void* ba
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"((const void*)ub)
                : "memory");
 }
+// 4-byte variant (lane i's dword lands at M0 + 4i); used to pull lines into
+// L2 ahead of the 16-byte loads, into a scratch area nobody reads.
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t off, const void* base) {
+  const uint64_t b = (uint64_t)base;
+  const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"((const void*)ub)
+               : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -355,6 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[2][kCodeStage];
   __shared__ __attribute__((aligned(16))) uint8_t sAs[2][kScaleBuf];
   __shared__ __attribute__((aligned(16))) uint8_t sBs[2][kScaleBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t l2warm[kThreads * 4];
 
   // ---- tile id: XCD-contiguous bands, then groups of 4 tile rows
   const uint32_t ntiles = g.tiles_m * g.tiles_n;
@@ -389,24 +399,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   const uint8_t* b_base = B + n0 * g.ldb;
   const uint8_t* sa_base = SA + m0 * g.ldsa;
   const uint8_t* sb_base = SB + n0 * g.ldsb;
+  const int64_t a_last = g.M - 1 - m0, b_last = g.N - 1 - n0;
   uint32_t a_off[8], b_off[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const uint32_t row = wave * 64 + t * 8 + (lane >> 3);
     const uint32_t chunk16 = (((uint32_t)lane & 7u) ^ fperm(row)) << 4;
-    a_off[t] = (uint32_t)min((int64_t)row, g.M - 1 - m0) * (uint32_t)g.lda + chunk16;
-    b_off[t] = (uint32_t)min((int64_t)row, g.N - 1 - n0) * (uint32_t)g.ldb + chunk16;
+    a_off[t] = (uint32_t)min((int64_t)row, a_last) * (uint32_t)g.lda + chunk16;
+    b_off[t] = (uint32_t)min((int64_t)row, b_last) * (uint32_t)g.ldb + chunk16;
   }
   const uint32_t srow = wave * 64 + lane;
-  const uint32_t sa_off = (uint32_t)min((int64_t)srow, g.M - 1 - m0) * (uint32_t)g.ldsa;
-  const uint32_t sb_off = (uint32_t)min((int64_t)srow, g.N - 1 - n0) * (uint32_t)g.ldsb;
+  const uint32_t sa_off = (uint32_t)min((int64_t)srow, a_last) * (uint32_t)g.ldsa;
+  const uint32_t sb_off = (uint32_t)min((int64_t)srow, b_last) * (uint32_t)g.ldsb;
+  const uint32_t pa_off = (uint32_t)min((int64_t)srow, a_last) * (uint32_t)g.lda;
+  const uint32_t pb_off = (uint32_t)min((int64_t)srow, b_last) * (uint32_t)g.ldb;
   const uint32_t a_dst = lds_off(&As[0][0]) + wave * 64 * kFBK, b_dst = lds_off(&Bs[0][0]) + wave * 64 * kFBK;
   const uint32_t sa_dst = lds_off(&sAs[0][0]) + wave * 64 * kScaleRow;
   const uint32_t sb_dst = lds_off(&sBs[0][0]) + wave * 64 * kScaleRow;
-  auto issue_codes = [&](int64_t s) {
-    const uint32_t buf = (uint32_t)(s & 1);
-    const uint8_t* ab = a_base + s * kFBK;
-    const uint8_t* bb = b_base + s * kFBK;
+  const uint32_t warm_dst = lds_off(&l2warm[0]) + wave * 256;
+  // codes of stage `src` into LDS buffer `buf`
+  auto issue_codes = [&](int64_t src, uint32_t buf) {
+    const uint8_t* ab = a_base + src * kFBK;
+    const uint8_t* bb = b_base + src * kFBK;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       dma16(a_dst + buf * kCodeStage + t * 8 * kFBK, a_off[t], ab);
@@ -417,6 +431,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
     const uint32_t buf = (uint32_t)(grp & 1);
     dma16(sa_dst + buf * kScaleBuf, sa_off, sa_base + grp * kScaleRow);
     dma16(sb_dst + buf * kScaleBuf, sb_off, sb_base + grp * kScaleRow);
+  };
+  // one dword of each row's 128-byte line of stage `src`: brings the lines
+  // into L2 one stage before their 16-byte loads are issued
+  auto warm_l2 = [&](int64_t src) {
+    dma4(warm_dst, pa_off, a_base + src * kFBK);
+    dma4(warm_dst, pb_off, b_base + src * kFBK);
   };
 
   // ---- fragment reads: lane (lr, lg) of fragment f reads row base + 32 f;
@@ -429,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   const uint8_t* b_row = &Bs[0][0] + (wn * 128 + lr) * kFBK;
   const uint8_t* a_sc = &sAs[0][0] + (wm * 128 + lr) * kScaleRow;
   const uint8_t* b_sc = &sBs[0][0] + (wn * 128 + lr) * kScaleRow;
-  // K half h of stage buffer buf: logical chunks 4h + lg and 4h + 2 + lg
+  // K half h of a stage: logical chunks 4h + lg and 4h + 2 + lg
   const uint32_t c_lo[2] = {((0 + lg) ^ fp) << 4, ((4 + lg) ^ fp) << 4};
   const uint32_t c_hi[2] = {((2 + lg) ^ fp) << 4, ((6 + lg) ^ fp) << 4};
   // Scales: once per group of 4 stages each lane reads the 16 scale bytes of
@@ -471,95 +491,76 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // Pipeline. Stage s lives in buffer s % 2. The DMA of stage s+2 is issued
-  // right after the barrier near the end of stage s that publishes stage s+1
-  // (at that point every wave has finished reading stage s), so each stage
-  // has about one stage of MFMA work to land. Fragments of the next K half
-  // (and of stage s+1's first half, right after that barrier) are read while
-  // the current MFMAs run. The loop is unrolled by 4 stages so that buffer,
-  // scale-slot and half offsets are all constants.
+  // Fragments of one K half (4 A + 4 B) live in register set 0 (first half
+  // of a stage) or 1 (second half). While one set feeds 16 MFMAs, the other
+  // is refilled one A and one B fragment per group of 4 MFMAs, so LDS reads
+  // are spread evenly over the stage.
+  v8i32 fa[2][4], fb[2][4];
+  int sa[2][4], sb[2][4];
+  auto mfma_group = [&](int set, int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], BFMT, AFMT, 0,
+                                                                   sb[set][j], 0, sa[set][i]);
+  };
+
+  // Pipeline. Stage s lives in LDS buffer s % 2. In the middle of stage s
+  // (its second-half fragments are already in registers) one barrier
+  // publishes stage s+1 and frees buffer s % 2, and the loads of stage s+2
+  // go out into it at once, so each stage has one stage of MFMA work to
+  // land; the L2 warm-up of stage s+3 goes out with them. The loop body has
+  // no branches (a branch lets the compiler sink MFMAs past the barrier):
+  // past the last stage the loads repeat the last stage into the free
+  // buffer and the extra fragment reads are discarded.
+  const int64_t last = nsteps - 1;
   issue_scales(0);
-  issue_codes(0);
-  if (nsteps > 1) issue_codes(1);
-  if (nsteps > 1) wait_vmcnt<16>();
-  else wait_vmcnt<0>();
+  issue_codes(0, 0);
+  issue_codes(1, 1);
+  warm_l2(min((int64_t)2, last));
+  wait_vmcnt<18>();  // scales and stage 0 landed; stage 1 and the warm-up may still be in flight
   barrier();
-  v8i32 bcur[4], bnext[4], acur, anext;
-  int bscur[4], bsnext[4], ascur, asnext;
   read_scales(0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) read_frag(b_row, sb4, 0, 0, 0, j, bcur[j], bscur[j]);
-  read_frag(a_row, sa4, 0, 0, 0, 0, acur, ascur);
+  for (int f = 0; f < 4; ++f) {
+    read_frag(a_row, sa4, 0, 0, 0, f, fa[0][f], sa[0][f]);
+    read_frag(b_row, sb4, 0, 0, 0, f, fb[0][f], sb[0][f]);
+  }
 
   for (int64_t s0 = 0; s0 < nsteps; s0 += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t s = s0 + u;
       const int buf = u & 1, sbuf = (int)((s0 / 4) & 1);
-      // ---- first K half: fetch the second half's B fragments
-#pragma unroll
-      for (int j = 0; j < 4; ++j) read_frag(b_row, sb4, buf, u, 1, j, bnext[j], bsnext[j]);
+      // ---- first half: MFMAs on set 0; set 1 <- second half of stage s
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (i < 3) read_frag(a_row, sa4, buf, u, 0, i + 1, anext, asnext);
-        else read_frag(a_row, sa4, buf, u, 1, 0, anext, asnext);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[j], acur, acc[i][j], BFMT, AFMT, 0, bscur[j],
-                                                                       0, ascur);
-        acur = anext;
-        ascur = asnext;
-        // keep each group's fragment reads next to the MFMAs that hide them
-        // (hoisting all of a stage's reads would exhaust the registers)
+        read_frag(a_row, sa4, buf, u, 1, i, fa[1][i], sa[1][i]);
+        read_frag(b_row, sb4, buf, u, 1, i, fb[1][i], sb[1][i]);
+        mfma_group(0, i);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bcur[j] = bnext[j];
-        bscur[j] = bsnext[j];
-      }
-      // ---- second K half
+      // ---- publish stage s+1 (its loads were issued one stage ago); every
+      // wave holds the rest of stage s in registers, so buffer s % 2 is free
+      wait_vmcnt<2>();
+      wait_lgkmcnt0();
+      barrier();
+      if (((u + 2) & 3) == 0) issue_scales(min((s + 2) >> 2, nsteps / 4 - 1));
+      issue_codes(min(s + 2, last), (uint32_t)buf);
+      warm_l2(min(s + 3, last));
+      // the next scale group was published by this barrier
+      if (u == 3) read_scales(sbuf ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- second half: MFMAs on set 1; set 0 <- first half of stage s+1
+      const int nbuf = buf ^ 1, nsub = (u + 1) & 3;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (i < 3) {
-          read_frag(a_row, sa4, buf, u, 1, i + 1, anext, asnext);
-        } else {
-          // publish stage s+1; every wave is done reading stage s. This runs
-          // on the last stage too (its reads of the other buffer are unused):
-          // with a barrier on every path, the compiler cannot carry fragment
-          // values from one stage to a later one that reads the same buffer.
-          wait_vmcnt<0>();
-          wait_lgkmcnt0();
-          barrier();
-          // The last two stages reload stage nsteps-1 into a buffer nobody
-          // reads again: the loop body stays free of branches, which would
-          // let the compiler sink the MFMAs past the barrier.
-          if (((u + 2) & 3) == 0) issue_scales(min((s + 2) >> 2, nsteps / 4 - 1));
-          issue_codes(min(s + 2, nsteps - 1));
-          const int nbuf = buf ^ 1, nsub = (u + 1) & 3;
-          if (u == 3) read_scales(sbuf ^ 1);  // the next group's scales were published by this barrier
-#pragma unroll
-          for (int j = 0; j < 4; ++j) read_frag(b_row, sb4, nbuf, nsub, 0, j, bnext[j], bsnext[j]);
-          read_frag(a_row, sa4, nbuf, nsub, 0, 0, anext, asnext);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bcur[j], acur, acc[i][j], BFMT, AFMT, 0, bscur[j],
-                                                                       0, ascur);
-        acur = anext;
-        ascur = asnext;
-        // keep each group's fragment reads next to the MFMAs that hide them
-        // (hoisting all of a stage's reads would exhaust the registers)
+        read_frag(a_row, sa4, nbuf, nsub, 0, i, fa[0][i], sa[0][i]);
+        read_frag(b_row, sb4, nbuf, nsub, 0, i, fb[0][i], sb[0][i]);
+        mfma_group(1, i);
         __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bcur[j] = bnext[j];
-        bscur[j] = bsnext[j];
       }
     }
   }
-
   wait_vmcnt<0>();  // no load may still be writing LDS when the group ends
 
   // ---- epilogue: lane owns y[m][n .. n+3] for 4 groups of n
