@@ -341,15 +341,6 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t off, const void* ba
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"((const void*)ub)
                : "memory");
 }
-// 4-byte variant (lane i's dword lands at M0 + 4i); used to pull lines into
-// L2 ahead of the 16-byte loads, into a scratch area nobody reads.
-__device__ __forceinline__ void dma4(uint32_t lds, uint32_t off, const void* base) {
-  const uint64_t b = (uint64_t)base;
-  const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
-                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"((const void*)ub)
-               : "memory");
-}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -364,7 +355,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[2][kCodeStage];
   __shared__ __attribute__((aligned(16))) uint8_t sAs[2][kScaleBuf];
   __shared__ __attribute__((aligned(16))) uint8_t sBs[2][kScaleBuf];
-  __shared__ __attribute__((aligned(16))) uint8_t l2warm[kThreads * 4];
 
   // ---- tile id: XCD-contiguous bands, then groups of 4 tile rows
   const uint32_t ntiles = g.tiles_m * g.tiles_n;
@@ -411,12 +401,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   const uint32_t srow = wave * 64 + lane;
   const uint32_t sa_off = (uint32_t)min((int64_t)srow, a_last) * (uint32_t)g.ldsa;
   const uint32_t sb_off = (uint32_t)min((int64_t)srow, b_last) * (uint32_t)g.ldsb;
-  const uint32_t pa_off = (uint32_t)min((int64_t)srow, a_last) * (uint32_t)g.lda;
-  const uint32_t pb_off = (uint32_t)min((int64_t)srow, b_last) * (uint32_t)g.ldb;
   const uint32_t a_dst = lds_off(&As[0][0]) + wave * 64 * kFBK, b_dst = lds_off(&Bs[0][0]) + wave * 64 * kFBK;
   const uint32_t sa_dst = lds_off(&sAs[0][0]) + wave * 64 * kScaleRow;
   const uint32_t sb_dst = lds_off(&sBs[0][0]) + wave * 64 * kScaleRow;
-  const uint32_t warm_dst = lds_off(&l2warm[0]) + wave * 256;
   // codes of stage `src` into LDS buffer `buf`
   auto issue_codes = [&](int64_t src, uint32_t buf) {
     const uint8_t* ab = a_base + src * kFBK;
@@ -427,16 +414,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
       dma16(b_dst + buf * kCodeStage + t * 8 * kFBK, b_off[t], bb);
     }
   };
+  // a quarter of the codes of stage `src` (rows 16q .. 16q+15 of each wave's 64)
+  auto issue_codes_part = [&](int64_t src, uint32_t buf, int q) {
+    const uint8_t* ab = a_base + src * kFBK;
+    const uint8_t* bb = b_base + src * kFBK;
+#pragma unroll
+    for (int t = 2 * q; t < 2 * q + 2; ++t) {
+      dma16(a_dst + buf * kCodeStage + t * 8 * kFBK, a_off[t], ab);
+      dma16(b_dst + buf * kCodeStage + t * 8 * kFBK, b_off[t], bb);
+    }
+  };
   auto issue_scales = [&](int64_t grp) {
     const uint32_t buf = (uint32_t)(grp & 1);
     dma16(sa_dst + buf * kScaleBuf, sa_off, sa_base + grp * kScaleRow);
     dma16(sb_dst + buf * kScaleBuf, sb_off, sb_base + grp * kScaleRow);
-  };
-  // one dword of each row's 128-byte line of stage `src`: brings the lines
-  // into L2 one stage before their 16-byte loads are issued
-  auto warm_l2 = [&](int64_t src) {
-    dma4(warm_dst, pa_off, a_base + src * kFBK);
-    dma4(warm_dst, pb_off, b_base + src * kFBK);
   };
 
   // ---- fragment reads: lane (lr, lg) of fragment f reads row base + 32 f;
@@ -507,8 +498,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   // Pipeline. Stage s lives in LDS buffer s % 2. In the middle of stage s
   // (its second-half fragments are already in registers) one barrier
   // publishes stage s+1 and frees buffer s % 2, and the loads of stage s+2
-  // go out into it at once, so each stage has one stage of MFMA work to
-  // land; the L2 warm-up of stage s+3 goes out with them. The loop body has
+  // go out into it during the following MFMA groups, so each stage has most
+  // of a stage of MFMA work to land. The loop body has
   // no branches (a branch lets the compiler sink MFMAs past the barrier):
   // past the last stage the loads repeat the last stage into the free
   // buffer and the extra fragment reads are discarded.
@@ -516,8 +507,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   issue_scales(0);
   issue_codes(0, 0);
   issue_codes(1, 1);
-  warm_l2(min((int64_t)2, last));
-  wait_vmcnt<18>();  // scales and stage 0 landed; stage 1 and the warm-up may still be in flight
+  wait_vmcnt<16>();  // scales and stage 0 landed; stage 1 may still be in flight
   barrier();
   read_scales(0);
 #pragma unroll
@@ -541,19 +531,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
       }
       // ---- publish stage s+1 (its loads were issued one stage ago); every
       // wave holds the rest of stage s in registers, so buffer s % 2 is free
-      wait_vmcnt<2>();
+      wait_vmcnt<0>();
       wait_lgkmcnt0();
       barrier();
       if (((u + 2) & 3) == 0) issue_scales(min((s + 2) >> 2, nsteps / 4 - 1));
-      issue_codes(min(s + 2, last), (uint32_t)buf);
-      warm_l2(min(s + 3, last));
       // the next scale group was published by this barrier
       if (u == 3) read_scales(sbuf ^ 1);
       __builtin_amdgcn_sched_barrier(0);
-      // ---- second half: MFMAs on set 1; set 0 <- first half of stage s+1
+      // ---- second half: MFMAs on set 1; set 0 <- first half of stage s+1.
+      // The loads of stage s+2 are issued a quarter per MFMA group: a wave
+      // issues in order, and 18 loads in a row would hold back its MFMAs.
       const int nbuf = buf ^ 1, nsub = (u + 1) & 3;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        issue_codes_part(min(s + 2, last), (uint32_t)buf, i);
         read_frag(a_row, sa4, nbuf, nsub, 0, i, fa[0][i], sa[0][i]);
         read_frag(b_row, sb4, nbuf, nsub, 0, i, fb[0][i], sb[0][i]);
         mfma_group(1, i);
