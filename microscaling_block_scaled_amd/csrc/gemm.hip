@@ -333,13 +333,14 @@ __device__ __forceinline__ uint32_t lds_off(const void* p) {
 // tracked explicitly with wait_vmcnt before the barrier that publishes a
 // stage. Nothing else in this kernel uses M0.
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t off, const void* base) {
-  // the base is wave-uniform by construction; readfirstlane makes that
-  // visible to the compiler so the pair is kept in SGPRs
-  const uint64_t b = (uint64_t)base;
-  const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
-                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"((const void*)ub)
-               : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+}
+// A pointer that is the same in every lane, moved to SGPRs once, so that
+// the per-stage address arithmetic stays on the scalar unit.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t b = (uint64_t)p;
+  return (const uint8_t*)((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32));
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -385,10 +386,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   // row's logical chunk (i % 8) ^ fperm(row)). Scales: per group of 4
   // stages and operand, one instruction per wave, 64 rows x 16 bytes. Rows
   // past M / N are clamped to the last row.
-  const uint8_t* a_base = A + m0 * g.lda;
-  const uint8_t* b_base = B + n0 * g.ldb;
-  const uint8_t* sa_base = SA + m0 * g.ldsa;
-  const uint8_t* sb_base = SB + n0 * g.ldsb;
+  const uint8_t* a_base = uniform_ptr(A + m0 * g.lda);
+  const uint8_t* b_base = uniform_ptr(B + n0 * g.ldb);
+  const uint8_t* sa_base = uniform_ptr(SA + m0 * g.ldsa);
+  const uint8_t* sb_base = uniform_ptr(SB + n0 * g.ldsb);
   const int64_t a_last = g.M - 1 - m0, b_last = g.N - 1 - n0;
   uint32_t a_off[8], b_off[8];
 #pragma unroll
