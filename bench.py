@@ -6,8 +6,9 @@ One step = one pass of the metric's workload with inputs resident in HBM:
   2. mx_quantize_colwise  the same X, blocks down the columns, stored transposed
   3. mx_gemm              8192 x 8192 x 8192, E4M3 x E4M3 (pre-quantized rowwise
                           along K), FP32 accumulation, bf16 output
-Before each kernel a 512 MiB fill evicts the caches (MALL included), outside
-the kernel's timing. Kernel durations come from HIP events recorded on the
+Before each kernel a 512 MiB read evicts the caches (L2 and MALL) with clean
+lines, outside the kernel's timing: the inputs come from HBM and no write-back
+of unrelated data lands in the kernel's time. Kernel durations come from HIP events recorded on the
 stream the kernels run on; ms_per_step is wall time per step including the
 fills.
 
@@ -34,8 +35,9 @@ METRIC = "MXFP8 GEMM TFLOP/s @8192³ + quantize GB/s, each as % of MI355X peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 matrix peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_8192_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_8192_quantize_8192x4096.json")
 GEMM_SOURCE = os.path.join(ROOT, "microscaling_block_scaled_amd", "csrc", "gemm.hip")
+QUANT_SOURCE = os.path.join(ROOT, "microscaling_block_scaled_amd", "csrc", "quantize.hip")
 
 
 def log(*a):
@@ -80,15 +82,20 @@ def copy_calibration(torch, steps):
     print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": steps}}))
 
 
-def gemm_traffic():
-    """HBM bytes per 8192^3 GEMM launch from the committed counter summary,
-    or None if the kernel source changed since it was taken."""
+def _sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def committed_traffic(key, source, sha_field):
+    """HBM bytes per launch of one kernel from the committed counter summary,
+    or None if that kernel's source changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(GEMM_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        return t["bytes_per_launch"] if t.get("gemm_source_sha256") == sha else None
+        if t.get(sha_field) != _sha256(source):
+            return None
+        return t[key]["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
         return None
 
@@ -151,10 +158,10 @@ def main():
     if not ok:
         raise SystemExit("libmxfp8 cannot run here: " + reason)
     stream = torch.cuda.current_stream()
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush_buf = torch.ones((512 << 20) // 4, dtype=torch.float32, device="cuda")
 
     def flush():
-        flush_buf.zero_()
+        flush_buf.sum()
 
     # ---- inputs (generated on the host, resident in HBM before timing)
     log("generating inputs")
@@ -214,10 +221,11 @@ def main():
                    "gemm_accumulation": "AUTO -> scaled FP8 MFMA (E4M3 x E4M3, K >= 2048)"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_FP8_PEAK_TFLOPS, 4),
-                     "traffic": gemm_traffic()},
+                     "traffic": committed_traffic("gemm_fp8_big_kernel 8192^3", GEMM_SOURCE, "gemm_source_sha256")},
         "roofline_quantize": {"bound": "hbm", "achieved": quant["quantize_rowwise"]["GB/s"], "peak": HBM_PEAK_GBPS,
                               "unit": "GB/s", "frac": quant["quantize_rowwise"]["frac_of_hbm_peak"],
-                              "traffic": None},
+                              "traffic": committed_traffic("quant_rows_kernel 8192x4096 bf16 E4M3", QUANT_SOURCE,
+                                                           "quantize_source_sha256")},
         "gemm_us": round(gemm_ms * 1e3, 2),
         "quantize": quant,
     }
