@@ -116,6 +116,11 @@ __device__ __forceinline__ uint32_t oct_max_pk_u16(uint32_t v) {
   v = pk_max_u16(v, dpp<MX_DPP_QUAD_XOR2>(v));
   return pk_max_u16(v, dpp<MX_DPP_HALF_MIRROR>(v));
 }
+// packed-u16 max over the 4 lanes of a quad
+__device__ __forceinline__ uint32_t quad_max_pk_u16(uint32_t v) {
+  v = pk_max_u16(v, dpp<MX_DPP_QUAD_XOR1>(v));
+  return pk_max_u16(v, dpp<MX_DPP_QUAD_XOR2>(v));
+}
 __device__ __forceinline__ uint32_t oct_max_u32(uint32_t v) {
   v = umax(v, dpp<MX_DPP_QUAD_XOR1>(v));
   v = umax(v, dpp<MX_DPP_QUAD_XOR2>(v));

@@ -140,43 +140,60 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Colwise. A workgroup owns a 128-row x 64-column tile. Wave w takes rows
-// 32w .. 32w+31 (one block row). Lane j takes the 8 columns 8*(j/8) .. +7
-// and the 4 rows 4*(j%8) .. +3, so a column's 32 values sit in the 8 lanes
-// of one DPP group of 8. The codes of a column (4 per lane) go to an LDS tile
-// [64 columns][128 bytes] and leave as 128-byte rows of the transposed output.
-// LDS chunks of 16 bytes are XOR-swizzled by column group to keep the
-// transposing writes free of bank conflicts.
+// Colwise. A workgroup owns a 128-row x 128-column tile; wave w takes the
+// 32-row block row w. Lane j takes the 8 columns 8*(j/4) .. +7 and the 8 rows
+// 8*(j%4) .. +7, so one load instruction covers 4 rows x 16 column groups
+// (256 contiguous bytes of bf16 per row) and a column's 32 values sit in the
+// 4 lanes of a quad (two DPP steps reduce the amax). The codes of a column
+// (8 per lane) go to an LDS tile [128 columns][128 bytes] and leave as
+// 128-byte rows of the transposed output; the 4 scales of a column (one per
+// block row) are gathered in LDS and leave as one 4-byte store.
+// Work-groups are dealt round-robin to the 8 XCDs; when the column-tile
+// count allows, all row tiles of a column tile go to one XCD, so each XCD's
+// L2 assembles whole lines of the transposed codes and of the scales.
 // ---------------------------------------------------------------------------
 constexpr int kColTileRows = 128;
-constexpr int kColTileCols = 64;
+constexpr int kColTileCols = 128;
 
+// LDS byte offset of row byte `rbyte` of column `c`: the 16-byte chunk index
+// is XORed with 2 * (c / 8), which keeps both the 8-byte writes (16 lanes:
+// 4 column groups x 4 row groups) and the 16-byte row reads free of bank
+// conflicts.
 __device__ __forceinline__ uint32_t col_lds_offset(uint32_t c, uint32_t rbyte) {
-  return c * 128u + ((((rbyte >> 4) ^ (c >> 3)) & 7u) << 4) + (rbyte & 15u);
+  return c * 128u + ((((rbyte >> 4) ^ (2u * (c >> 3))) & 7u) << 4) + (rbyte & 15u);
 }
 
 template <typename InT, int FMT>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restrict__ x, int64_t rows, int64_t cols,
                                                               int64_t ldx, uint8_t* __restrict__ qt, int64_t ldq,
                                                               uint8_t* __restrict__ st, int64_t lds,
-                                                              uint32_t col_tiles) {
+                                                              uint32_t row_tiles, uint32_t col_tiles) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kColTileCols * kColTileRows];
-  const uint32_t tile_r = blockIdx.x / col_tiles, tile_c = blockIdx.x % col_tiles;
+  __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 4];
+  uint32_t tile_r, tile_c;
+  if (col_tiles % 8 == 0) {
+    const uint32_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+    tile_c = xcd + 8 * (local / row_tiles);
+    tile_r = local % row_tiles;
+  } else {
+    tile_r = blockIdx.x / col_tiles;
+    tile_c = blockIdx.x % col_tiles;
+  }
   const int64_t r0 = (int64_t)tile_r * kColTileRows, c0 = (int64_t)tile_c * kColTileCols;
   const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t k = lane >> 3, b = lane & 7;
+  const uint32_t k = lane >> 2, b = lane & 3;
   const int64_t rblk = r0 + 32 * wave;   // first row of this wave's block row
   const bool wave_ok = rblk < rows;      // rows % 32 == 0
   const int64_t cc = c0 + 8 * k;         // first of this lane's 8 columns
   const int ncol = cols - cc >= 8 ? 8 : (cols > cc ? (int)(cols - cc) : 0);
 
   if (wave_ok) {
-    // v[i][p]: row 4b+i, column pair p (bf16) or column p (f32)
+    // v[i][p]: row 8b+i, column pair p (bf16) or column p (f32)
     constexpr int W = sizeof(InT) == 2 ? 4 : 8;
-    uint32_t v[4][W];
+    uint32_t v[8][W];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const InT* p = x + (rblk + 4 * b + i) * ldx + cc;
+    for (int i = 0; i < 8; ++i) {
+      const InT* p = x + (rblk + 8 * b + i) * ldx + cc;
       if (ncol == 8) {
         uint4 t = *(const uint4*)p;
         v[i][0] = t.x; v[i][1] = t.y; v[i][2] = t.z; v[i][3] = t.w;
@@ -197,57 +214,75 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
         }
       }
     }
-    // per-column amax over the 4 rows, then over the 8 lanes of the group
+    // per-column amax over the lane's 8 rows, then over the 4 lanes of the quad
     uint32_t codes[8];
     if constexpr (W == 4) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        uint32_t m = pk_max_u16(pk_max_u16(v[0][p] & 0x7FFF7FFFu, v[1][p] & 0x7FFF7FFFu),
-                                pk_max_u16(v[2][p] & 0x7FFF7FFFu, v[3][p] & 0x7FFF7FFFu));
-        m = oct_max_pk_u16(m);
+        uint32_t m = v[0][p] & 0x7FFF7FFFu;
+#pragma unroll
+        for (int i = 1; i < 8; ++i) m = pk_max_u16(m, v[i][p] & 0x7FFF7FFFu);
+        m = quad_max_pk_u16(m);
         codes[2 * p] = scale_code_from_exp<FMT>((m & 0xFFFFu) >> 7);
         codes[2 * p + 1] = scale_code_from_exp<FMT>(m >> 23);
       }
     } else {
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        uint32_t m = umax(umax(v[0][p] & 0x7FFFFFFFu, v[1][p] & 0x7FFFFFFFu),
-                          umax(v[2][p] & 0x7FFFFFFFu, v[3][p] & 0x7FFFFFFFu));
-        m = oct_max_u32(m);
+        uint32_t m = v[0][p] & 0x7FFFFFFFu;
+#pragma unroll
+        for (int i = 1; i < 8; ++i) m = umax(m, v[i][p] & 0x7FFFFFFFu);
+        m = quad_max_u32(m);
         codes[p] = scale_code_from_exp<FMT>(m >> 23);
       }
     }
-    // encode: column c gets one dword = rows 4b .. 4b+3
+    // encode: column c gets two dwords = rows 8b .. 8b+3 and 8b+4 .. 8b+7
 #pragma unroll
     for (int ci = 0; ci < 8; ++ci) {
       const float div = scale_divisor(codes[ci]);
-      uint32_t d;
-      if constexpr (W == 4) {
-        const int p = ci >> 1;
-        const uint32_t sel = (ci & 1) ? 0x07060302u : 0x05040100u;  // pick the high or low halves
-        uint32_t r01 = __builtin_amdgcn_perm(v[1][p], v[0][p], sel);
-        uint32_t r23 = __builtin_amdgcn_perm(v[3][p], v[2][p], sel);
-        d = encode4_bf16<FMT>(r01, r23, div);
-      } else {
-        d = encode4_f32<FMT>(__uint_as_float(v[0][ci]), __uint_as_float(v[1][ci]), __uint_as_float(v[2][ci]),
-                             __uint_as_float(v[3][ci]), div);
+      uint32_t d[2];
+#pragma unroll
+      for (int hgrp = 0; hgrp < 2; ++hgrp) {
+        const int i0 = 4 * hgrp;
+        if constexpr (W == 4) {
+          const int p = ci >> 1;
+          const uint32_t sel = (ci & 1) ? 0x07060302u : 0x05040100u;  // pick the high or low halves
+          uint32_t r01 = __builtin_amdgcn_perm(v[i0 + 1][p], v[i0][p], sel);
+          uint32_t r23 = __builtin_amdgcn_perm(v[i0 + 3][p], v[i0 + 2][p], sel);
+          d[hgrp] = encode4_bf16<FMT>(r01, r23, div);
+        } else {
+          d[hgrp] = encode4_f32<FMT>(__uint_as_float(v[i0][ci]), __uint_as_float(v[i0 + 1][ci]),
+                                     __uint_as_float(v[i0 + 2][ci]), __uint_as_float(v[i0 + 3][ci]), div);
+        }
+        if (codes[ci] == 0xFFu) d[hgrp] = 0x7F7F7F7Fu;
       }
-      if (codes[ci] == 0xFFu) d = 0x7F7F7F7Fu;
       const uint32_t c = 8 * k + ci;
-      *(uint32_t*)(tile + col_lds_offset(c, 32 * wave + 4 * b)) = d;
-      if (b == 0 && ci < ncol) st[(cc + ci) * lds + rblk / 32] = (uint8_t)codes[ci];
+      *(uint2*)(tile + col_lds_offset(c, 32 * wave + 8 * b)) = make_uint2(d[0], d[1]);
+      if (b == 0) stile[c * 4 + wave] = (uint8_t)codes[ci];
     }
   }
   __syncthreads();
-  // write out: 64 columns x 128 bytes = 512 chunks of 16 bytes
+  // codes: 128 columns x 128 bytes = 1024 chunks of 16 bytes
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
+  for (int it = 0; it < 4; ++it) {
     const uint32_t id = threadIdx.x + kThreads * it;
     const uint32_t c = id >> 3, m = id & 7;
     const int64_t r = r0 + 16 * m;
     if (c0 + c < cols && r < rows) {
       uint4 val = *(const uint4*)(tile + col_lds_offset(c, 16 * m));
       *(uint4*)(qt + (c0 + c) * ldq + r) = val;
+    }
+  }
+  // scales: column c's 4 block rows are 4 consecutive bytes of st row c0 + c
+  if (threadIdx.x < kColTileCols && c0 + threadIdx.x < cols) {
+    const uint32_t c = threadIdx.x;
+    const int64_t nb = min((rows - r0) / kBlock, (int64_t)4);
+    uint8_t* dst = st + (c0 + c) * lds + r0 / kBlock;
+    const uint32_t sv = *(const uint32_t*)(stile + 4 * c);
+    if (nb == 4 && ((uintptr_t)dst & 3u) == 0) {
+      *(uint32_t*)dst = sv;
+    } else {
+      for (int64_t j = 0; j < nb; ++j) dst[j] = (uint8_t)(sv >> (8 * j));
     }
   }
 }
@@ -371,7 +406,7 @@ extern "C" mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_
   const dim3 grid((uint32_t)(row_tiles * col_tiles));
 #define MX_COLS_LAUNCH(T, F)                                                                                        \
   hipLaunchKernelGGL((quant_cols_kernel<T, F>), grid, dim3(kThreads), 0, stream, (const T*)x, rows, cols, ldx, qt, \
-                     ldq, st, lds, (uint32_t)col_tiles)
+                     ldq, st, lds, (uint32_t)row_tiles, (uint32_t)col_tiles)
   if (xdt == MX_BF16) {
     if (fmt == MX_E5M2) MX_COLS_LAUNCH(uint16_t, MX_E5M2); else MX_COLS_LAUNCH(uint16_t, MX_E4M3);
   } else {

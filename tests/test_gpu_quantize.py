@@ -123,7 +123,8 @@ def test_every_bf16_input_under_every_scale(mx, oracle, fmt):
 
 
 # --------------------------------------------------------------------------- colwise
-COL_SHAPES = [(32, 1, 8), (64, 7, 1), (96, 65, 7), (160, 100, 4), (128, 64, 0), (256, 1000, 8), (4096, 96, 0)]
+COL_SHAPES = [(32, 1, 8), (64, 7, 1), (96, 65, 7), (160, 100, 4), (128, 64, 0), (256, 1000, 8), (4096, 96, 0),
+              (160, 1024, 0), (96, 2043, 5), (384, 1032, 0)]
 
 
 @pytest.mark.parametrize("rows,cols,pad", COL_SHAPES)
