@@ -45,25 +45,60 @@ def log(*a):
 
 
 class Timer:
-    """Accumulates HIP-event durations of kernels launched on one stream."""
+    """Accumulates HIP-event durations of kernels launched on one stream.
+
+    The events are created through the HIP runtime with
+    hipEventDisableSystemFence: recording them then skips the system-scope
+    cache release, which adds ~1-2 us to every recorded interval and would
+    distort kernels that run for ~20 us."""
+
+    HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, torch, stream):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.torch, self.stream, self.pairs = torch, stream, {}
+        self.sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def _event(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
 
     def run(self, name, fn, record=True):
         if not record:
             fn()
             return
-        e0 = self.torch.cuda.Event(enable_timing=True)
-        e1 = self.torch.cuda.Event(enable_timing=True)
-        e0.record(self.stream)
+        e0, e1 = self._event(), self._event()
+        if self.hip.hipEventRecord(e0, self.sp) != 0:
+            raise RuntimeError("hipEventRecord failed")
         fn()
-        e1.record(self.stream)
+        if self.hip.hipEventRecord(e1, self.sp) != 0:
+            raise RuntimeError("hipEventRecord failed")
         self.pairs.setdefault(name, []).append((e0, e1))
 
     def mean_ms(self, name):
-        ts = [a.elapsed_time(b) for a, b in self.pairs[name]]
+        self.torch.cuda.synchronize()
+        ts = []
+        for e0, e1 in self.pairs[name]:
+            ms = self.ct.c_float()
+            if self.hip.hipEventElapsedTime(self.ct.byref(ms), e0, e1) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            ts.append(ms.value)
         return sum(ts) / len(ts)
+
+    def release(self):
+        for pairs in self.pairs.values():
+            for e0, e1 in pairs:
+                self.hip.hipEventDestroy(e0)
+                self.hip.hipEventDestroy(e1)
+        self.pairs = {}
 
 
 def dev_bf16(torch, bits):

@@ -560,25 +560,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + wm * 128 + i * 32 + lr;
-    if (m >= g.M) continue;
+    const bool mok = m < g.M;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const int64_t nb = n0 + wn * 128 + j * 32;  // the lane's columns: nb + 8 q + 4 lg + 0..3
+      if constexpr (BF16OUT) {
+        uint16_t* row = (uint16_t*)Y + m * g.ldy;
+        uint32_t w[4][2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * 128 + j * 32 + 8 * q + 4 * lg;
-        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if constexpr (BF16OUT) {
-          uint16_t* row = (uint16_t*)Y + m * g.ldy;
-          if (g.y_vec && n + 3 < g.N) {
-            *(uint2*)(row + n) = make_uint2(f32_to_bf16_rne(canon_nan(v0)) | (f32_to_bf16_rne(canon_nan(v1)) << 16),
-                                            f32_to_bf16_rne(canon_nan(v2)) | (f32_to_bf16_rne(canon_nan(v3)) << 16));
-          } else {
-            const float vv[4] = {v0, v1, v2, v3};
-            for (int e = 0; e < 4; ++e)
-              if (n + e < g.N) row[n + e] = (uint16_t)f32_to_bf16_rne(canon_nan(vv[e]));
+        for (int q = 0; q < 4; ++q) {
+          w[q][0] = f32_to_bf16_rne(canon_nan(acc[i][j][4 * q])) |
+                    (f32_to_bf16_rne(canon_nan(acc[i][j][4 * q + 1])) << 16);
+          w[q][1] = f32_to_bf16_rne(canon_nan(acc[i][j][4 * q + 2])) |
+                    (f32_to_bf16_rne(canon_nan(acc[i][j][4 * q + 3])) << 16);
+        }
+        if (g.y_vec && nb + 32 <= g.N) {
+          // Lanes l and l + 32 (same row) hold columns 16p + 4 lg .. and
+          // 16p + 8 + 4 lg ..; one lane swap per dword gives lane lg the 8
+          // consecutive columns 16p + 8 lg .. +7, stored as 16 bytes.
+#pragma unroll
+          for (int pq = 0; pq < 2; ++pq) {
+            const auto r0 = __builtin_amdgcn_permlane32_swap(w[2 * pq][0], w[2 * pq + 1][0], false, false);
+            const auto r1 = __builtin_amdgcn_permlane32_swap(w[2 * pq][1], w[2 * pq + 1][1], false, false);
+            if (mok) *(uint4*)(row + nb + 16 * pq + 8 * lg) = make_uint4(r0[0], r1[0], r0[1], r1[1]);
           }
-        } else {
-          float* row = (float*)Y + m * g.ldy;
+        } else if (mok) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = nb + 8 * q + 4 * lg;
+            if (g.y_vec && n + 3 < g.N) {
+              *(uint2*)(row + n) = make_uint2(w[q][0], w[q][1]);
+            } else {
+              for (int e = 0; e < 4; ++e)
+                if (n + e < g.N) row[n + e] = (uint16_t)(w[q][e >> 1] >> (16 * (e & 1)));
+            }
+          }
+        }
+      } else if (mok) {
+        float* row = (float*)Y + m * g.ldy;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = nb + 8 * q + 4 * lg;
+          const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
+                      v3 = acc[i][j][4 * q + 3];
           if (g.y_vec && n + 3 < g.N) {
             *(float4*)(row + n) = make_float4(v0, v1, v2, v3);
           } else {
