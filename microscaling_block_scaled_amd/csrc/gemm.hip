@@ -287,6 +287,165 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// Row-panel kernel for short reductions (K <= 128, FP32-accumulation mode),
+// e.g. attention scores over one head: the output is large and the work per
+// output small, so the kernel is bound by writing y. A work-group takes 256
+// rows of A and up to 512 rows of B of one problem: B (codes and scales,
+// gathered through the page table when paged) is loaded into LDS once,
+// each wave keeps its 64 rows of A decoded in registers, and then walks the
+// columns in chunks of 64, storing each chunk as soon as it is computed.
+// Each wave holds 64 rows of A (4 MFMA row tiles), so every decoded B
+// fragment feeds 4 MFMAs.
+// No load follows the first store, so the stores stream out without being
+// waited on. Work-groups of one problem are placed on one XCD so its B rows
+// are read from that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kRPTiles = 4;                  // 16-row MFMA tiles of A per wave
+constexpr int kRPRows = 4 * 16 * kRPTiles;   // A rows per work-group
+constexpr int kRPMaxN = 512;   // B rows held in LDS
+
+template <int AFMT, int BFMT, bool BF16OUT, bool PAGED>
+__global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uint32_t row_blocks, uint32_t nprob) {
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[kRPMaxN * kBK];
+  __shared__ uint32_t sBs[kRPMaxN];
+
+  // work-group -> (problem, row block); with 8 or more problems and a
+  // problem count divisible by 8, the row blocks of problem p run on XCD p % 8
+  uint32_t prob, rb;
+  if (nprob % 8 == 0) {
+    const uint32_t x = blockIdx.x % 8, r = blockIdx.x / 8;
+    prob = x + 8 * (r / row_blocks);
+    rb = r % row_blocks;
+  } else {
+    prob = blockIdx.x / row_blocks;
+    rb = blockIdx.x % row_blocks;
+  }
+  const int64_t po = prob / g.batch_inner, pi = prob % g.batch_inner;
+  const uint8_t* A = g.a + po * g.sa_o + pi * g.sa_i;
+  const uint8_t* SA = g.sa + po * g.ssa_o + pi * g.ssa_i;
+  const uint8_t* B = g.b + pi * g.sb_i;
+  const uint8_t* SB = g.sb + pi * g.ssb_i;
+  if (!PAGED) {
+    B += po * g.sb_o;
+    SB += po * g.ssb_o;
+  }
+  auto b_row_ptr = [&](int64_t n, const uint8_t* base, int64_t ld, int64_t pstride) -> const uint8_t* {
+    if (PAGED) {
+      const int32_t page = g.page_table[po * g.pages_per_seq + n / g.page_rows];
+      return base + (int64_t)page * pstride + (n % g.page_rows) * ld;
+    }
+    return base + n * ld;
+  };
+  const int tid = threadIdx.x;
+  const int64_t kblocks = g.K / kBlock;  // 1 .. 4
+  const bool dword_ok = g.scales_dword != 0;
+
+  // ---- B into LDS: row n, 16-byte chunk c at swz(n, c); chunks past K are
+  // zero. All of a thread's loads are issued before any LDS store.
+  const int64_t nrows = g.N;  // <= kRPMaxN
+  constexpr int kPer = kRPMaxN * 8 / kThreads;  // 16 chunks per thread
+  uint4 bv[kPer];
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const uint32_t id = tid + kThreads * it, c = id & 7;
+    const int64_t n = id >> 3;
+    bv[it] = make_uint4(0, 0, 0, 0);
+    if (n < nrows && (int64_t)c * 16 < g.K) bv[it] = *(const uint4*)(b_row_ptr(n, B, g.ldb, g.page_stride) + c * 16);
+  }
+  uint32_t sv[kRPMaxN / kThreads];
+#pragma unroll
+  for (int it = 0; it < kRPMaxN / kThreads; ++it) {
+    const int64_t n = tid + kThreads * it;
+    sv[it] = n < nrows ? load_scales4(b_row_ptr(n, SB, g.ldsb, g.page_stride_s), 0, kblocks, dword_ok) : 0u;
+  }
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const uint32_t id = tid + kThreads * it;
+    if ((int64_t)(id >> 3) < nrows) *(uint4*)(&Bs[swz(id >> 3, id & 7)]) = bv[it];
+  }
+#pragma unroll
+  for (int it = 0; it < kRPMaxN / kThreads; ++it) {
+    const int64_t n = tid + kThreads * it;
+    if (n < nrows) sBs[n] = sv[it];
+  }
+
+  // ---- this wave's 64 rows of A, decoded: lane (r, q) of tile t takes row
+  // 16 t + r and, for block kb, k = 32 kb + 8 q .. +7
+  const int wave = tid >> 6, lane = tid & 63;
+  const uint32_t lr = lane & 15, lg = lane >> 4;
+  const int64_t mw = (int64_t)rb * kRPRows + wave * 16 * kRPTiles + lr;  // + 16 t
+  v8bf16 af[kRPTiles][4];
+#pragma unroll
+  for (int t = 0; t < kRPTiles; ++t) {
+    const int64_t m = mw + 16 * t;
+    const bool mok = m < g.M;
+    const uint8_t* arow = A + (mok ? m : 0) * g.lda;
+    const uint32_t sa4 = mok ? load_scales4(SA + m * g.ldsa, 0, kblocks, dword_ok) : 0x7F7F7F7Fu;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      uint2 w = make_uint2(0, 0);
+      if (mok && kb < kblocks) w = *(const uint2*)(arow + 32 * kb + 8 * lg);
+      af[t][kb] = decode8_bf16<AFMT>(w, scale_value((sa4 >> (8 * kb)) & 0xFFu));
+    }
+  }
+  __syncthreads();
+
+  // ---- columns in chunks of 64 (4 tiles of 16); lane owns y[m][n .. n+3]
+  uint8_t* Y = (uint8_t*)g.y + (po * g.sy_o + pi * g.sy_i) * (BF16OUT ? 2 : 4);
+  for (int64_t n0 = 0; n0 < nrows; n0 += 64) {
+    v4f32 acc[kRPTiles][4];
+#pragma unroll
+    for (int t = 0; t < kRPTiles; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[t][j] = v4f32{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb < kblocks) {
+        const uint32_t chunk = 2 * kb + (lg >> 1), off = 8 * (lg & 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t row = (uint32_t)min(n0 + j * 16 + lr, (int64_t)kRPMaxN - 1);
+          const uint2 w = *(const uint2*)(&Bs[swz(row, chunk) + off]);
+          const v8bf16 bf = decode8_bf16<BFMT>(w, scale_value((sBs[row] >> (8 * kb)) & 0xFFu));
+#pragma unroll
+          for (int t = 0; t < kRPTiles; ++t)
+            acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[t][kb], acc[t][j], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kRPTiles; ++t) {
+      const int64_t m = mw + 16 * t;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + j * 16 + 4 * lg;
+        const v4f32 v = acc[t][j];
+        if constexpr (BF16OUT) {
+          uint16_t* row = (uint16_t*)Y + m * g.ldy;
+          if (g.y_vec && n + 3 < g.N) {
+            *(uint2*)(row + n) =
+                make_uint2(f32_to_bf16_rne(canon_nan(v[0])) | (f32_to_bf16_rne(canon_nan(v[1])) << 16),
+                           f32_to_bf16_rne(canon_nan(v[2])) | (f32_to_bf16_rne(canon_nan(v[3])) << 16));
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (n + e < g.N) row[n + e] = (uint16_t)f32_to_bf16_rne(canon_nan(v[e]));
+          }
+        } else {
+          float* row = (float*)Y + m * g.ldy;
+          if (g.y_vec && n + 3 < g.N) {
+            *(float4*)(row + n) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (n + e < g.N) row[n + e] = v[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Main-loop kernel for large aligned problems (FP8 accumulation path).
 //
 // Tile 256 x 256 per workgroup, 4 waves of 128 x 128, built from
@@ -631,6 +790,25 @@ mx_status_t launch_fp8_big(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf1
   return mx_host::launch_status();
 }
 
+template <bool PAGED>
+mx_status_t launch_rowpanel(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, int64_t batch, hipStream_t st) {
+  const int64_t row_blocks = (g.M + kRPRows - 1) / kRPRows;
+  if (row_blocks * batch >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
+  const dim3 grid((uint32_t)(row_blocks * batch));
+  const uint32_t rbs = (uint32_t)row_blocks, np = (uint32_t)batch;
+#define MX_RP_LAUNCH(AF, BF, OUT) \
+  hipLaunchKernelGGL((gemm_rowpanel_kernel<AF, BF, OUT, PAGED>), grid, dim3(kThreads), 0, st, g, rbs, np)
+#define MX_RP_OUT(AF, BF) \
+  do { if (bf16out) MX_RP_LAUNCH(AF, BF, true); else MX_RP_LAUNCH(AF, BF, false); } while (0)
+  if (af == MX_E4M3 && bf == MX_E4M3) MX_RP_OUT(MX_E4M3, MX_E4M3);
+  else if (af == MX_E5M2 && bf == MX_E4M3) MX_RP_OUT(MX_E5M2, MX_E4M3);
+  else if (af == MX_E4M3 && bf == MX_E5M2) MX_RP_OUT(MX_E4M3, MX_E5M2);
+  else MX_RP_OUT(MX_E5M2, MX_E5M2);
+#undef MX_RP_OUT
+#undef MX_RP_LAUNCH
+  return mx_host::launch_status();
+}
+
 template <int BM, int BN, bool PAGED, int MODE>
 mx_status_t launch(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, int64_t batch, hipStream_t st) {
   const dim3 grid(g.tiles_m * g.tiles_n, (uint32_t)batch);
@@ -716,6 +894,13 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
     gb.tiles_n = (uint32_t)((N + kFBN - 1) / kFBN);
     return launch_fp8_big(gb, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
   }
+  // short reductions with at most 512 B rows: the row-panel kernel
+  const bool rowpanel_ok = !fp8 && K <= kBK && N <= kRPMaxN && d->lda % 8 == 0 && d->ldb % 16 == 0 &&
+                           (paged ? d->b_page_stride % 16 == 0 : d->stride_b_outer % 16 == 0) &&
+                           d->stride_b_inner % 16 == 0 && d->stride_a_outer % 8 == 0 && d->stride_a_inner % 8 == 0;
+  if (rowpanel_ok)
+    return paged ? launch_rowpanel<true>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream)
+                 : launch_rowpanel<false>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
   if (fp8)
     return paged ? launch<BM, BN, true, kModeFP8>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream)
                  : launch<BM, BN, false, kModeFP8>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
