@@ -509,8 +509,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int AFMT, int BFMT, bool BF16OUT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
+template <int AFMT, int BFMT, bool BF16OUT, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t As[2][kCodeStage];
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[2][kCodeStage];
   __shared__ __attribute__((aligned(16))) uint8_t sAs[2][kScaleBuf];
@@ -610,9 +610,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   // puts block 4w + lg in byte 0 and block 4w + 2 + lg in byte 2, so the
   // scale of (stage w, half h) is the word shifted right by 16 h (the
   // instruction reads byte 0).
+  // (FP32-accumulation mode: no shift; the lane needs both blocks 2h and
+  // 2h + 1, found in bytes 0 and 1 of the word shifted right by 16 h.)
   uint4 sa4[4], sb4[4];
   auto read_scales = [&](int sbuf) {
-    const uint32_t sh = 8 * lg;
+    const uint32_t sh = MODE == kModeFP8 ? 8 * lg : 0;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       uint4 va = *(const uint4*)(a_sc + sbuf * kScaleBuf + f * 32 * kScaleRow);
@@ -648,11 +650,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   // are spread evenly over the stage.
   v8i32 fa[2][4], fb[2][4];
   int sa[2][4], sb[2][4];
+  // One of the 4 MFMA groups of a K half. FP8 mode: group i is the 4
+  // scaled MFMAs of A fragment i. FP32-accumulation mode: group t is K step
+  // t of the half (8 of each lane's 32 codes, bytes 8t .. 8t+7, the same
+  // k positions in A and B), decoded exactly to bf16 with the block scale
+  // folded in (blocks 2h for t < 2, 2h + 1 after), then 16
+  // v_mfma_f32_32x32x16_bf16; each decoded B fragment feeds 4 of them.
   auto mfma_group = [&](int set, int i) {
+    if constexpr (MODE == kModeFP8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], BFMT, AFMT, 0,
-                                                                   sb[set][j], 0, sa[set][i]);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], BFMT, AFMT, 0,
+                                                                     sb[set][j], 0, sa[set][i]);
+    } else {
+      const int t = i;
+      v8bf16 bb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bb[j] = decode8_bf16<BFMT>(make_uint2((uint32_t)fb[set][j][2 * t], (uint32_t)fb[set][j][2 * t + 1]),
+                                   scale_value(((uint32_t)sb[set][j] >> (8 * (t >> 1))) & 0xFFu));
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const v8bf16 aa = decode8_bf16<AFMT>(make_uint2((uint32_t)fa[set][a][2 * t], (uint32_t)fa[set][a][2 * t + 1]),
+                                             scale_value(((uint32_t)sa[set][a] >> (8 * (t >> 1))) & 0xFFu));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[j], aa, acc[a][j], 0, 0, 0);
+      }
+    }
   };
 
   // Pipeline. Stage s lives in LDS buffer s % 2. In the middle of stage s
@@ -775,10 +799,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_big_kernel(GemmArgs g) {
   }
 }
 
-mx_status_t launch_fp8_big(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, int64_t batch, hipStream_t st) {
+template <int MODE>
+mx_status_t launch_big(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, int64_t batch, hipStream_t st) {
   const dim3 grid(g.tiles_m * g.tiles_n, (uint32_t)batch);
 #define MX_BIG_LAUNCH(AF, BF, OUT) \
-  hipLaunchKernelGGL((gemm_fp8_big_kernel<AF, BF, OUT>), grid, dim3(kThreads), 0, st, g)
+  hipLaunchKernelGGL((gemm_big_kernel<AF, BF, OUT, MODE>), grid, dim3(kThreads), 0, st, g)
 #define MX_BIG_OUT(AF, BF) \
   do { if (bf16out) MX_BIG_LAUNCH(AF, BF, true); else MX_BIG_LAUNCH(AF, BF, false); } while (0)
   if (af == MX_E4M3 && bf == MX_E4M3) MX_BIG_OUT(MX_E4M3, MX_E4M3);
@@ -882,8 +907,8 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   g.tiles_n = (uint32_t)((N + BN - 1) / BN);
   if ((int64_t)g.tiles_m * g.tiles_n >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const bool bf16out = d->y_dtype == MX_BF16;
-  // large aligned problems: the 256 x 256 pipelined FP8 kernel
-  const bool big_ok = fp8 && !paged && K % 512 == 0 && K > 0 && d->lda % 16 == 0 && d->ldb % 16 == 0 &&
+  // large aligned problems: the 256 x 256 pipelined kernel (either mode)
+  const bool big_ok = !paged && K % 512 == 0 && K > 0 && d->lda % 16 == 0 && d->ldb % 16 == 0 &&
                       mx_host::aligned16(d->sa) && mx_host::aligned16(d->sb) && d->ldsa % 16 == 0 &&
                       d->ldsb % 16 == 0 && d->stride_sa_outer % 16 == 0 && d->stride_sa_inner % 16 == 0 &&
                       d->stride_sb_outer % 16 == 0 && d->stride_sb_inner % 16 == 0 && M >= 256 && N >= 256 &&
@@ -892,7 +917,8 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
     GemmArgs gb = g;
     gb.tiles_m = (uint32_t)((M + kFBM - 1) / kFBM);
     gb.tiles_n = (uint32_t)((N + kFBN - 1) / kFBN);
-    return launch_fp8_big(gb, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
+    return fp8 ? launch_big<kModeFP8>(gb, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream)
+               : launch_big<kModeBF16>(gb, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
   }
   // short reductions with at most 512 B rows: the row-panel kernel
   const bool rowpanel_ok = !fp8 && K <= kBK && N <= kRPMaxN && d->lda % 8 == 0 && d->ldb % 16 == 0 &&

@@ -163,6 +163,11 @@ def test_large_tile_kernel(mx, oracle, M, N, K, afmt, bfmt):
     assert_gemm_bound(bf16_to_f64(yb), y_ref, t_ref, "fp8 bf16 %s" % ((M, N, K),), bf16_out=True, rel=FP8_GROUPED_REL)
     if afmt == E4M3 and K >= 2048:
         assert_gemm_bound(y, y_ref, t_ref, "fp8 auto-range %s" % ((M, N, K),))
+    # the same kernel in FP32-accumulation mode (bf16 MFMA on decoded codes)
+    y = host(mx.mx_gemm(qa, sa, qb, sb, afmt, bfmt, out_dtype=torch.float32, accum=FP32))
+    assert_gemm_bound(y, y_ref, t_ref, "fp32-accum f32 %s" % ((M, N, K),))
+    yb = host(mx.mx_gemm(qa, sa, qb, sb, afmt, bfmt, out_dtype=torch.bfloat16, accum=FP32))
+    assert_gemm_bound(bf16_to_f64(yb), y_ref, t_ref, "fp32-accum bf16 %s" % ((M, N, K),), bf16_out=True)
 
 
 def test_large_tile_kernel_batched(mx, oracle):
