@@ -656,6 +656,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   // k positions in A and B), decoded exactly to bf16 with the block scale
   // folded in (blocks 2h for t < 2, 2h + 1 after), then 16
   // v_mfma_f32_32x32x16_bf16; each decoded B fragment feeds 4 of them.
+  auto mfma_pair = [&](int set, int i, int j0) {
+#pragma unroll
+    for (int j = j0; j < j0 + 2; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], BFMT, AFMT, 0,
+                                                                   sb[set][j], 0, sa[set][i]);
+  };
   auto mfma_group = [&](int set, int i) {
     if constexpr (MODE == kModeFP8) {
 #pragma unroll
@@ -728,10 +734,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
       const int nbuf = buf ^ 1, nsub = (u + 1) & 3;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        issue_codes_part(min(s + 2, last), (uint32_t)buf, i);
         read_frag(a_row, sa4, nbuf, nsub, 0, i, fa[0][i], sa[0][i]);
         read_frag(b_row, sb4, nbuf, nsub, 0, i, fb[0][i], sb[0][i]);
-        mfma_group(1, i);
+        if constexpr (MODE == kModeFP8) {
+          // the loads go out between two pairs of MFMAs, so the matrix unit
+          // has queued work while the wave issues them
+          mfma_pair(1, i, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          issue_codes_part(min(s + 2, last), (uint32_t)buf, i);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_pair(1, i, 2);
+        } else {
+          issue_codes_part(min(s + 2, last), (uint32_t)buf, i);
+          mfma_group(1, i);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
