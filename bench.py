@@ -15,7 +15,7 @@ fills.
 `value` is the GEMM's TFLOP/s (2*M*N*K per launch / mean launch time); the
 quantizers' GB/s (algorithmic bytes: read 2RC, write RC + RC/32) are reported
 beside it, and the other rows of the path (paged KV write, paged QK^T scores,
-dequantize, training linear fwd/dgrad) unless --quick. cpu_baseline times
+dequantize, training linear fwd / dgrad / wgrad) unless --quick. cpu_baseline times
 the CPU oracle on a bounded sample of the same GEMM.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
@@ -363,6 +363,22 @@ def other_rows(torch, mx, inputs, np, flush, stream, steps):
                              "frac_of_bf16_peak": round(flop / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
                              "frac_of_fp8_peak": round(flop / ms / 1e9 / MFMA_FP8_PEAK_TFLOPS, 4),
                              "shape": [M, Kf, N], "accumulation": "AUTO -> bf16 MFMA (E5M2 operand)"}
+    del dX, qwt, swt, qx, sx, qw, sw
+    # wgrad dW = G^T X: both quantized colwise (blocks along the 16384 tokens)
+    qgt = torch.empty((Gd.shape[1], Gd.shape[0]), dtype=torch.uint8, device="cuda")
+    sgt = torch.empty((Gd.shape[1], Gd.shape[0] // 32), dtype=torch.uint8, device="cuda")
+    qxt = torch.empty((Xd.shape[1], Xd.shape[0]), dtype=torch.uint8, device="cuda")
+    sxt = torch.empty((Xd.shape[1], Xd.shape[0] // 32), dtype=torch.uint8, device="cuda")
+    ms = timed("quantize_G_colwise", lambda: mx.mx_quantize_colwise(Gd, mx.MX_E5M2, qt=qgt, st=sgt))
+    out["quantize_G_e5m2_colwise"] = {"us": round(ms * 1e3, 2), "GB/s": round(g_bytes / ms / 1e6, 1),
+                                      "frac_of_hbm_peak": round(g_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                      "algorithmic_bytes": g_bytes}
+    mx.mx_quantize_colwise(Xd, mx.MX_E4M3, qt=qxt, st=sxt)
+    dW = torch.empty((N, Kf), dtype=torch.bfloat16, device="cuda")
+    ms = timed("wgrad", lambda: mx.mx_gemm(qgt, sgt, qxt, sxt, mx.MX_E5M2, mx.MX_E4M3, y=dW))
+    out["training_wgrad"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flop / ms / 1e9, 1),
+                             "frac_of_bf16_peak": round(flop / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "shape": [N, Kf, M], "accumulation": "AUTO -> bf16 MFMA (E5M2 operand)"}
     return out
 
 

@@ -310,6 +310,25 @@ def test_training_linear_fwd_and_dgrad(mx, oracle):
 
 
 @pytest.mark.slow
+def test_training_linear_wgrad(mx, oracle):
+    """wgrad dW = G^T X [14336, 4096]: G [16384, 14336] quantized colwise in
+    E5M2 and X [16384, 4096] colwise in E4M3 (blocks along the 16384 tokens,
+    the reduction), then the block-scaled product over K = 16384."""
+    torch = _torch()
+    x, _, g = inputs.training_inputs()
+    qgt, sgt = mx.mx_quantize_colwise(dev(g, bf16=True), E5M2)
+    qxt, sxt = mx.mx_quantize_colwise(dev(x, bf16=True), E4M3)
+    qgt_o, sgt_o = oracle.quantize_cols(g, E5M2)
+    qxt_o, sxt_o = oracle.quantize_cols(x, E4M3)
+    assert_bitexact(host(sgt), sgt_o, "G colwise scales")
+    assert_bitexact(host(sxt), sxt_o, "X colwise scales")
+    assert_bitexact(host(qxt), qxt_o, "X colwise codes")
+    dw = mx.mx_gemm(qgt, sgt, qxt, sxt, E5M2, E4M3, out_dtype=torch.float32)
+    worst = _check_sampled(dw, qgt_o, sgt_o, E5M2, qxt_o, sxt_o, E4M3, "wgrad f32", n=20000)
+    print("wgrad worst |err|/T = %.3g" % worst)
+
+
+@pytest.mark.slow
 def test_kv_cache_scores_full_size(mx, oracle):
     """32768 tokens x 8 heads x 128 written to 256 pages of 128, then QK^T
     for 64 sequences x 512 tokens per head, f32 output; sampled check."""
