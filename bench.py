@@ -256,7 +256,7 @@ def main():
                    "gemm_accumulation": "AUTO -> scaled FP8 MFMA (E4M3 x E4M3, K >= 2048)"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MFMA_FP8_PEAK_TFLOPS, 4),
-                     "traffic": committed_traffic("gemm_fp8_big_kernel 8192^3", GEMM_SOURCE, "gemm_source_sha256")},
+                     "traffic": committed_traffic("gemm_big_kernel (FP8 mode) 8192^3", GEMM_SOURCE, "gemm_source_sha256")},
         "roofline_quantize": {"bound": "hbm", "achieved": quant["quantize_rowwise"]["GB/s"], "peak": HBM_PEAK_GBPS,
                               "unit": "GB/s", "frac": quant["quantize_rowwise"]["frac_of_hbm_peak"],
                               "traffic": committed_traffic("quant_rows_kernel 8192x4096 bf16 E4M3", QUANT_SOURCE,
