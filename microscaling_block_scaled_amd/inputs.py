@@ -21,6 +21,10 @@ Workloads (sizes as given for the method's headline runs):
               5002 / 5003); 64 sequences of 512 tokens on pages of 128 tokens;
               sequence s owns logical pages 4s..4s+3, mapped to physical pages
               by a seeded permutation of 0..255 (5004).
+  * attention: the kv workload read back as paged attention: the query of
+              every token (seed 5003) attends over its sequence's 512 cached
+              keys. Smaller cases (`attention_case`) draw a ragged mix of
+              sequence lengths and a shuffled page table from one seed.
 All sizes can be scaled down (same distributions) for tests that must finish
 quickly on the CPU.
 """
@@ -118,3 +122,20 @@ def kv_inputs(tokens: int = 32768, heads: int = 8, head_dim: int = 128):
     v = normal_bf16(5002, (tokens, heads, head_dim))
     q = normal_bf16(5003, (tokens, heads, head_dim))
     return k, v, q
+
+
+def attention_case(seed: int, n_seqs: int, q_len: int, kv_lens, page_size: int, q_heads: int, kv_heads: int,
+                   head_dim: int, spare_pages: int = 3):
+    """Inputs of a paged-attention case: bf16 queries [n_seqs*q_len, q_heads,
+    head_dim], bf16 cache contents for every slot [pages, page_size, kv_heads,
+    head_dim] (K and V), an int32 page table [n_seqs, pages_per_seq] drawn as a
+    shuffled subset of the pages, and int32 kv_lens. All values ~ N(0, 1)."""
+    kv_lens = np.asarray(kv_lens, dtype=np.int32)
+    assert kv_lens.shape == (n_seqs,)
+    pps = max(1, -(-int(kv_lens.max(initial=0)) // page_size))
+    n_pages = n_seqs * pps + spare_pages
+    table = rng(seed).permutation(n_pages)[: n_seqs * pps].reshape(n_seqs, pps).astype(np.int32)
+    q = normal_bf16(seed + 1, (n_seqs * q_len, q_heads, head_dim))
+    k = normal_bf16(seed + 2, (n_pages, page_size, kv_heads, head_dim))
+    v = normal_bf16(seed + 3, (n_pages, page_size, kv_heads, head_dim))
+    return q, k, v, table, kv_lens

@@ -59,6 +59,8 @@ def _load():
                              _p, _i64, _p, _i64]
     lib.mxo_gemm_at.argtypes = [_i64, _p, _i64, _p, _i64, ctypes.c_int, _p, _i64, _p, _i64, ctypes.c_int, _p, _p,
                                 _i64, _p, _p]
+    lib.mxo_paged_attention.argtypes = [_p, _p, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _i64,
+                                        _i64, _i64, ctypes.c_double, ctypes.c_int, _p, _i64, _p, _p, _p, _p]
     lib.mxo_num_threads.restype = ctypes.c_int
     lib.mxo_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
@@ -223,6 +225,49 @@ def paged_scores_at(q_codes, q_scales, k_cache, k_scale, page_table, seq_len, pa
     qs = q_scales[seq * seq_len + i, head][None, :]
     y, t = gemm(qrow, qs, E4M3, krow, ks, E4M3)
     return float(y[0, 0]), float(t[0, 0])
+
+
+def paged_attention(q_codes, q_scales, k_cache, k_scale, v_cache, v_scale, page_table, kv_lens, q_len,
+                    sm_scale, causal=False, rows=None):
+    """Attention of MXFP8 queries over the paged MXFP8 KV cache (see
+    mxo_paged_attention in mx_oracle.c for the definition).
+
+    q_codes [S*q_len, Hq, D] / q_scales [S*q_len, Hq, D/32]; k_cache, v_cache
+    [pages, page_size, Hkv, D] / k_scale, v_scale [pages, page_size, Hkv,
+    D/32]; page_table int32 [S, pages_per_seq]; kv_lens int32 [S]. `rows`:
+    optional flat (token * Hq + head) indices to evaluate; default all.
+
+    Returns (o, w, lse, tmax): o and w [n, D] float64 (w = sum_j P_j |Vb_j|),
+    lse and tmax [n] float64, n = len(rows) or S*q_len*Hq (token-major)."""
+    q_codes = np.ascontiguousarray(q_codes, dtype=np.uint8)
+    q_scales = np.ascontiguousarray(q_scales, dtype=np.uint8)
+    k_cache = np.ascontiguousarray(k_cache, dtype=np.uint8)
+    k_scale = np.ascontiguousarray(k_scale, dtype=np.uint8)
+    v_cache = np.ascontiguousarray(v_cache, dtype=np.uint8)
+    v_scale = np.ascontiguousarray(v_scale, dtype=np.uint8)
+    page_table = np.ascontiguousarray(page_table, dtype=np.int32)
+    kv_lens = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    T, Hq, D = q_codes.shape
+    n_pages, page_size, Hkv, D2 = k_cache.shape
+    S, pps = page_table.shape
+    assert D2 == D and v_cache.shape == k_cache.shape and T == S * q_len and kv_lens.shape == (S,)
+    assert q_scales.shape == (T, Hq, D // BLOCK) and k_scale.shape == v_scale.shape == (n_pages, page_size, Hkv, D // BLOCK)
+    assert page_table.size == 0 or (page_table.min() >= 0 and page_table.max() < n_pages)
+    if rows is None:
+        n, rp = T * Hq, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        assert rows.size == 0 or (rows.min() >= 0 and rows.max() < T * Hq)
+        n, rp = rows.size, _ptr(rows)
+    o = np.empty((n, D), np.float64)
+    w = np.empty((n, D), np.float64)
+    lse = np.empty(n, np.float64)
+    tmax = np.empty(n, np.float64)
+    _check(_load().mxo_paged_attention(_ptr(q_codes), _ptr(q_scales), Hq * D, Hq * (D // BLOCK), _ptr(k_cache),
+                                       _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(page_table), pps,
+                                       _ptr(kv_lens), S, q_len, Hq, Hkv, D, page_size, float(sm_scale), int(causal),
+                                       rp, n, _ptr(o), _ptr(w), _ptr(lse), _ptr(tmax)))
+    return o, w, lse, tmax
 
 
 def num_threads() -> int:

@@ -352,6 +352,126 @@ int mxo_gemm_at(int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa, int
     return 0;
 }
 
+/* ---------------------------------------------------------------------------
+ * Paged attention over the MXFP8 KV cache [SM120 §0.2]. The KV cache holds K
+ * and V as E4M3 codes with one E8M0 scale per 32 values along the head
+ * dimension; the query arrives with its own scales. The consumer the page
+ * describes forms the scores Q K^T as a block-scaled FP8 product, restores V
+ * to BF16 and then forms P V. Written out for one query row (token t =
+ * seq * q_len + i, query head h), with L = kv_lens[seq]:
+ *   key j is allowed when j < L and, with `causal`, j <= L - q_len + i (the
+ *   query sits at absolute position L - q_len + i of its sequence);
+ *   S_j   = the block-scaled product of the query row and key row j over the
+ *           head dimension (the same sum as mxo_gemm);
+ *   z_j   = sm_scale * S_j;  P_j = exp(z_j - max z) / sum_k exp(z_k - max z);
+ *   Vb_jd = V code * scale, rounded to bf16 (the "restored to BF16" step);
+ *   O_d   = sum_j P_j * Vb_jd.
+ * Readings where the page is silent: the softmax runs over the allowed keys
+ * only; a row with no allowed key gives O = 0 and lse = -inf; the causal
+ * offset aligns the last query with the last key. Key j of the sequence is
+ * read from page page_table[seq * pages_per_seq + j / page_size], row
+ * j % page_size, kv head h / (hq / hkv); L is clamped to pages_per_seq *
+ * page_size. Also returned, for stating
+ * tolerances: W_d = sum_j P_j |Vb_jd|, lse = log sum_j exp(z_j), and
+ * tmax = max_j sum_d |q_hat_d k_hat_jd|. A NaN score makes the whole row NaN.
+ * ------------------------------------------------------------------------- */
+static double bf16_value(uint16_t bits) {
+    if ((bits & 0x7F80u) == 0x7F80u) {
+        if (bits & 0x7Fu) return NAN;
+        return (bits & 0x8000u) ? -INFINITY : INFINITY;
+    }
+    int e = (bits >> 7) & 0xFF;
+    double mant = (double)(bits & 0x7F);
+    double v = e == 0 ? ldexp(mant, -133) : ldexp(128.0 + mant, e - 134);
+    return (bits & 0x8000u) ? -v : v;
+}
+
+static void attention_one(const uint8_t* q, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                          const uint8_t* vc, const uint8_t* vs, const int32_t* ptab, int64_t n_allowed,
+                          int64_t hkv, int64_t hk, int64_t D, int64_t page_size, double sm_scale,
+                          const double* lut, double* z, double* o, double* w, double* lse, double* tmax) {
+    for (int64_t d = 0; d < D; ++d) o[d] = w[d] = 0.0;
+    if (n_allowed <= 0) {
+        *lse = -INFINITY;
+        *tmax = 0.0;
+        return;
+    }
+    const int64_t nb = D / MXO_BLOCK;
+    double m = -INFINITY, tm = 0.0;
+    int has_nan = 0;
+    for (int64_t j = 0; j < n_allowed; ++j) {
+        int64_t slot = (int64_t)ptab[j / page_size] * page_size + j % page_size;
+        int64_t row = slot * hkv + hk;
+        double sj, tj;
+        gemm_one(D, q, qs, lut, kc + row * D, ks + row * nb, lut, &sj, &tj);
+        z[j] = sm_scale * sj;
+        if (isnan(z[j])) has_nan = 1;
+        if (z[j] > m) m = z[j];
+        if (tj > tm) tm = tj;
+    }
+    *tmax = tm;
+    if (has_nan) {
+        for (int64_t d = 0; d < D; ++d) o[d] = w[d] = NAN;
+        *lse = NAN;
+        return;
+    }
+    double denom = 0.0;
+    for (int64_t j = 0; j < n_allowed; ++j) {
+        z[j] = exp(z[j] - m); /* now the unnormalised weight */
+        denom += z[j];
+    }
+    *lse = m + log(denom);
+    for (int64_t j = 0; j < n_allowed; ++j) {
+        double pj = z[j] / denom;
+        int64_t slot = (int64_t)ptab[j / page_size] * page_size + j % page_size;
+        int64_t row = slot * hkv + hk;
+        for (int64_t d = 0; d < D; ++d) {
+            double vb = bf16_value(mxo_double_to_bf16(mxo_dequant_value(MXO_E4M3, vc[row * D + d], vs[row * nb + d / MXO_BLOCK])));
+            o[d] += pj * vb;
+            w[d] += pj * fabs(vb);
+        }
+    }
+}
+
+int mxo_paged_attention(const uint8_t* q, const uint8_t* qs, int64_t ld_q, int64_t ld_qs, const uint8_t* kc,
+                        const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, const int32_t* page_table,
+                        int64_t pages_per_seq, const int32_t* kv_lens, int64_t num_seqs, int64_t q_len, int64_t hq,
+                        int64_t hkv, int64_t D, int64_t page_size, double sm_scale, int causal, const int64_t* rows,
+                        int64_t count, double* o, double* w, double* lse, double* tmax) {
+    if (D % MXO_BLOCK != 0 || D <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || page_size <= 0 || q_len < 0 ||
+        num_seqs < 0)
+        return -2;
+    const int64_t total = num_seqs * q_len * hq;
+    const int64_t n = rows ? count : total;
+    const int64_t max_keys = pages_per_seq * page_size;
+    double lut[256];
+    build_lut(MXO_E4M3, lut);
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)(max_keys > 0 ? max_keys : 1));
+        if (!z) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < n; ++r) {
+                const int64_t idx = rows ? rows[r] : r;
+                const int64_t t = idx / hq, h = idx % hq;
+                const int64_t seq = t / q_len, i = t % q_len;
+                const int64_t L = kv_lens[seq];
+                int64_t allowed = L < max_keys ? L : max_keys;
+                if (causal && L - q_len + i + 1 < allowed) allowed = L - q_len + i + 1;
+                attention_one(q + t * ld_q + h * D, qs + t * ld_qs + h * (D / MXO_BLOCK), kc, ks, vc, vs,
+                              page_table + seq * pages_per_seq, allowed, hkv, h / (hq / hkv), D, page_size,
+                              sm_scale, lut, z, o + r * D, w + r * D, lse + r, tmax + r);
+            }
+            free(z);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
 int mxo_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

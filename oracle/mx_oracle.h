@@ -38,6 +38,11 @@ int mxo_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, con
 int mxo_gemm_at(int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa, int64_t ldsa, int afmt, const uint8_t* b,
                 int64_t ldb, const uint8_t* sb, int64_t ldsb, int bfmt, const int64_t* mi, const int64_t* ni,
                 int64_t count, double* y, double* t);
+int mxo_paged_attention(const uint8_t* q, const uint8_t* qs, int64_t ld_q, int64_t ld_qs, const uint8_t* kc,
+                        const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, const int32_t* page_table,
+                        int64_t pages_per_seq, const int32_t* kv_lens, int64_t num_seqs, int64_t q_len, int64_t hq,
+                        int64_t hkv, int64_t D, int64_t page_size, double sm_scale, int causal, const int64_t* rows,
+                        int64_t count, double* o, double* w, double* lse, double* tmax);
 int mxo_num_threads(void);
 void mxo_set_num_threads(int n);
 

@@ -420,3 +420,171 @@ def test_gemm_at_equals_full_product(oracle):
     # y = A B^T: swapping the operands transposes the result
     y2, _ = oracle.gemm(b, sb, E4M3, a, sa, E4M3)
     assert np.array_equal(y2, y.T)
+
+
+# ---------------------------------------------------------------------------
+# Paged attention over the MXFP8 KV cache [MXFP8 SM120 software support,
+# section 0.2]. The reference here is torch's scaled_dot_product_attention in
+# float64 on the CPU, fed with values decoded by torch's own float8_e4m3fn
+# type and scaled with ldexp, V rounded by torch's bfloat16 cast: none of it
+# passes through the oracle's decode, softmax or sums.
+# ---------------------------------------------------------------------------
+from attn_util import quantized_case  # noqa: E402
+
+
+def _torch_decode(codes, scales):
+    import torch
+    v = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    e = torch.from_numpy(scales.astype(np.int64)).repeat_interleave(32, dim=-1)
+    return torch.where(e == 255, torch.tensor(float("nan"), dtype=torch.float64),
+                       torch.ldexp(v, (e - 127).to(torch.float64)))
+
+
+def _torch_attention(c, sm, causal):
+    """Per sequence: gather keys through the page table, build the mask, call
+    scaled_dot_product_attention; also logsumexp of the masked scores."""
+    import torch
+    import torch.nn.functional as F
+    Q = _torch_decode(c["qc"], c["qs"])
+    K = _torch_decode(c["kc"], c["ks"])
+    V = _torch_decode(c["vc"], c["vs"]).to(torch.bfloat16).to(torch.float64)
+    P, page, hkv, D = K.shape
+    T, hq, _ = Q.shape
+    ql = c["q_len"]
+    out = torch.full((T, hq, D), float("nan"), dtype=torch.float64)
+    lse = torch.full((T, hq), float("nan"), dtype=torch.float64)
+    for s, L in enumerate(c["kv_lens"]):
+        L = int(L)
+        if L == 0:
+            continue
+        j = np.arange(L)
+        slot = torch.from_numpy(c["table"][s, j // page].astype(np.int64) * page + j % page)
+        Ks = K.reshape(P * page, hkv, D)[slot].transpose(0, 1)[None]
+        Vs = V.reshape(P * page, hkv, D)[slot].transpose(0, 1)[None]
+        Qs = Q[s * ql:(s + 1) * ql].transpose(0, 1)[None]
+        i = torch.arange(ql)[:, None]
+        mask = torch.arange(L)[None, :] <= (L - ql + i) if causal else torch.ones(ql, L, dtype=torch.bool)
+        o = F.scaled_dot_product_attention(Qs, Ks, Vs, attn_mask=mask, scale=sm, enable_gqa=True)
+        rep = hq // hkv
+        sc = sm * torch.matmul(Qs, Ks.repeat_interleave(rep, dim=1).transpose(-1, -2).contiguous())
+        sc = sc.masked_fill(~mask, float("-inf"))
+        live = mask.any(dim=1)
+        out[s * ql:(s + 1) * ql][live] = o[0].transpose(0, 1)[live]
+        lse[s * ql:(s + 1) * ql][live] = torch.logsumexp(sc, dim=-1)[0].transpose(0, 1)[live]
+    return out.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv,page", [(2, 2, 16), (4, 2, 5), (3, 1, 64)])
+def test_attention_matches_torch_sdpa(oracle, causal, hq, hkv, page):
+    D, ql = 64, 6
+    lens = [13, 1, 40, 6]
+    c = quantized_case(oracle, 7100 + hq * 10 + page, len(lens), ql, lens, page, hq, hkv, D)
+    sm = 1.0 / math.sqrt(D)
+    o, w, lse, _ = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"],
+                                          c["kv_lens"], ql, sm, causal)
+    ref, ref_lse = _torch_attention(c, sm, causal)
+    o = o.reshape(ref.shape)
+    lse = lse.reshape(ref_lse.shape)
+    live = ~np.isnan(ref_lse)
+    assert live.sum() > 0
+    np.testing.assert_allclose(o[live], ref[live], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse[live], ref_lse[live], rtol=1e-12, atol=1e-12)
+    # rows without an allowed key (causal, L < q_len): zeros and lse = -inf
+    assert np.all(o[~live] == 0.0) and np.all(lse[~live] == -np.inf)
+    if causal:
+        assert (~live).sum() == (ql - 1) * hq  # L = 1 leaves 5 query rows empty per head; the others none
+    # W = sum_j P_j |Vb_j| bounds |O|
+    assert np.all(w.reshape(ref.shape) >= np.abs(o) - 1e-15)
+
+
+def test_attention_closed_forms(oracle):
+    D, ql, page = 32, 4, 8
+    lens = [4, 9, 0]
+    c = quantized_case(oracle, 7200, 3, ql, lens, page, 1, 1, D)
+    P = c["kc"].shape[0]
+    # sequence 0: all of its keys identical -> uniform weights -> O = mean of Vb
+    row0 = (c["table"][0, 0], 0)
+    for j in range(4):
+        pg, off = c["table"][0, j // page], j % page
+        c["kc"][pg, off] = c["kc"][row0]
+        c["ks"][pg, off] = c["ks"][row0]
+    sm = 0.125
+    o, w, lse, tmax = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"],
+                                             c["kv_lens"], ql, sm, False)
+    Vb = _torch_decode(c["vc"], c["vs"]).float().to(dtype=__import__("torch").bfloat16).double().numpy()
+    keys0 = np.stack([Vb[c["table"][0, j // page], j % page, 0] for j in range(4)])
+    for i in range(ql):
+        np.testing.assert_allclose(o[i], keys0.mean(axis=0), rtol=1e-13, atol=1e-15)
+        # lse = z + log(4) for four equal scores z
+        z = sm * oracle.gemm(c["qc"][i, 0][None], c["qs"][i, 0][None], E4M3, c["kc"][row0][0][None],
+                             c["ks"][row0][0][None], E4M3)[0][0, 0]
+        assert lse[i] == pytest.approx(z + math.log(4.0), rel=1e-13, abs=1e-13)
+    # sequence 2 is empty: zeros and -inf
+    assert np.all(o[2 * ql:] == 0.0) and np.all(np.isneginf(lse[2 * ql:]))
+    # causal prefill (q_len == L): row 0 sees key 0 only -> O = Vb[0] exactly, lse = z_00
+    c2 = quantized_case(oracle, 7201, 1, 9, [9], page, 1, 1, D)
+    o2, _, lse2, _ = oracle.paged_attention(c2["qc"], c2["qs"], c2["kc"], c2["ks"], c2["vc"], c2["vs"], c2["table"],
+                                           c2["kv_lens"], 9, sm, True)
+    Vb2 = _torch_decode(c2["vc"], c2["vs"]).to(__import__("torch").bfloat16).double().numpy()
+    k0 = (c2["table"][0, 0], 0)
+    assert np.array_equal(o2[0], Vb2[k0][0])
+    z00 = sm * oracle.gemm(c2["qc"][0, 0][None], c2["qs"][0, 0][None], E4M3, c2["kc"][k0][0][None],
+                           c2["ks"][k0][0][None], E4M3)[0][0, 0]
+    assert lse2[0] == pytest.approx(z00, rel=1e-14, abs=1e-14)
+    # one-hot limit: with a huge softmax scale the weight of the top key is 1
+    # and every other weight underflows to 0, so O equals that key's Vb
+    o3, _, _, _ = oracle.paged_attention(c2["qc"], c2["qs"], c2["kc"], c2["ks"], c2["vc"], c2["vs"], c2["table"],
+                                         c2["kv_lens"], 9, 1e6, False)
+    j = np.arange(9)
+    krows = c2["kc"][c2["table"][0, j // page], j % page, 0]
+    kscl = c2["ks"][c2["table"][0, j // page], j % page, 0]
+    for i in range(9):
+        s, _ = oracle.gemm(c2["qc"][i, 0][None], c2["qs"][i, 0][None], E4M3, krows, kscl, E4M3)
+        order = np.sort(s[0])
+        assert order[-1] - order[-2] > 1e-3  # the seeded scores have a clear top key
+        top = int(np.argmax(s[0]))
+        assert np.array_equal(o3[i], Vb2[c2["table"][0, top // page], top % page, 0])
+
+
+def test_attention_page_relocation_and_decode_offsets(oracle):
+    D, page = 64, 16
+    lens = [37, 16, 50]
+    c = quantized_case(oracle, 7300, 3, 5, lens, page, 2, 1, D)
+    args = lambda c: (c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"], c["kv_lens"], 5)
+    base = oracle.paged_attention(*args(c), 0.1, True)
+    # move every page to a new physical page and rewrite the table: same result, bit for bit
+    P = c["kc"].shape[0]
+    perm = inputs.rng(7301).permutation(P)
+    moved = dict(c)
+    for key in ("kc", "ks", "vc", "vs"):
+        arr = np.empty_like(c[key])
+        arr[perm] = c[key]
+        moved[key] = arr
+    moved["table"] = perm[c["table"]].astype(np.int32)
+    again = oracle.paged_attention(*args(moved), 0.1, True)
+    for a, b in zip(base, again):
+        assert np.array_equal(a, b)
+    # causal decode (q_len = 1): the single query sits at position L - 1 and sees every key
+    d1 = quantized_case(oracle, 7302, 3, 1, lens, page, 2, 1, D)
+    a1 = (d1["qc"], d1["qs"], d1["kc"], d1["ks"], d1["vc"], d1["vs"], d1["table"], d1["kv_lens"], 1)
+    for x, y in zip(oracle.paged_attention(*a1, 0.1, True), oracle.paged_attention(*a1, 0.1, False)):
+        assert np.array_equal(x, y)
+    # rows list = the same rows of the full evaluation
+    rows = np.array([0, 7, 9, 28, 29])
+    part = oracle.paged_attention(*args(c), 0.1, True, rows=rows)
+    for a, b in zip(base, part):
+        assert np.array_equal(a[rows], b)
+    # W equals O when every V value is non-negative (sign bits cleared)
+    pos = dict(c)
+    pos["vc"] = c["vc"] & 0x7F
+    o, w, _, _ = oracle.paged_attention(*args(pos), 0.1, False)
+    assert np.array_equal(o, w)
+    # tmax is the largest sum |q_hat k_hat| over the allowed keys
+    _, _, _, tmax = base
+    t, h = 2 * 5 + 3, 1  # sequence 2, query 3 (position 48): keys 0..48
+    j = np.arange(49)
+    krows = c["kc"][c["table"][2, j // page], j % page, 0]
+    kscl = c["ks"][c["table"][2, j // page], j % page, 0]
+    _, tt = oracle.gemm(c["qc"][t, h][None], c["qs"][t, h][None], E4M3, krows, kscl, E4M3)
+    assert tmax[t * 2 + h] == tt.max()
