@@ -191,6 +191,72 @@ typedef struct mx_gemm_desc {
 
 mx_status_t mx_gemm(const mx_gemm_desc_t* desc, hipStream_t stream);
 
+/*
+ * mx_paged_attention -- attention of MXFP8 queries over the paged MXFP8 KV
+ * cache that mx_kv_quant_write fills [SM120 §0.2]: the scores Q K^T are a
+ * block-scaled FP8 product (query and key scales applied per 32-element block
+ * of the head dimension), V is decoded to BF16 inside the kernel, and the
+ * softmax-weighted sum P V is formed from it. For query row i of sequence s
+ * (token t = s * q_len + i) and query head h, with L = kv_lens[s]:
+ *
+ *   key j is allowed  iff  j < L  and, when causal != 0, j <= L - q_len + i
+ *                          (the queries are the last q_len positions);
+ *   S_j  = sum_b sq[b] * sk_j[b] * sum_{e<32} q[32b+e] * k_j[32b+e]
+ *   P_j  = exp(sm_scale * S_j - max) / sum over allowed keys
+ *   O[d] = sum_j P_j * bf16(v_j[d] * sv_j[d/32])
+ *   lse  = log sum_j exp(sm_scale * S_j)        (natural log)
+ *
+ * A row with no allowed key gets O = 0 and lse = -inf. Key j of sequence s
+ * is read from cache slot page_table[s * pages_per_seq + j / page_size] *
+ * page_size + j % page_size, kv head h / (num_q_heads / num_kv_heads).
+ *
+ * Layouts (device memory, caller-owned):
+ *   q        [num_seqs * q_len][num_q_heads][head_dim] E4M3 codes, token pitch ld_q bytes
+ *   q_scale  [num_seqs * q_len][num_q_heads][head_dim / 32] E8M0, token pitch ld_qs bytes
+ *   k_cache, v_cache [pages][page_size][num_kv_heads][head_dim] E4M3 codes
+ *   k_scale, v_scale [pages][page_size][num_kv_heads][head_dim / 32] E8M0
+ *   page_table int32 [num_seqs][pages_per_seq]; kv_lens int32 [num_seqs]
+ *   out      [num_seqs * q_len][num_q_heads][head_dim] (out_dtype), token pitch ld_o elements
+ *   lse      f32 [num_seqs * q_len][num_q_heads], or NULL
+ * The caller guarantees that every page_table entry a sequence's first
+ * kv_lens[s] keys reach names a valid page; kv_lens values are clamped to
+ * [0, pages_per_seq * page_size].
+ *
+ * Arithmetic: S in FP32 from the scaled FP8 matrix instruction (each group
+ * of 8 products summed with about 14 significant bits, see mx_accum_t);
+ * the softmax in f32 with exp2; P rounded to bf16 for the bf16 matrix
+ * instruction, its normaliser summed in f32 from the unrounded values; O
+ * accumulated in FP32, then divided by the normaliser; bf16 output rounds
+ * to nearest even. A NaN score makes its row NaN; a NaN value in a V block
+ * (scale code 0xFF) makes NaN every output column it is multiplied into,
+ * including rows of the same query tile for which that key is masked.
+ *
+ * Requirements (MX_ERR_SHAPE / MX_ERR_ALIGN otherwise): head_dim == 128;
+ * num_kv_heads divides num_q_heads; page_size a multiple of 128;
+ * pages_per_seq >= 1 and pages_per_seq * page_size < 2^31; sm_scale finite
+ * and > 0; ld_q >= num_q_heads * 128 and a multiple of 16; ld_qs >=
+ * num_q_heads * 4 and a multiple of 4; ld_o >= num_q_heads * 128 and a
+ * multiple of 4; q, k_cache, v_cache 16-byte aligned; the three scale arrays
+ * and lse 4-byte aligned; out 16-byte (f32) or 8-byte (bf16) aligned.
+ * num_seqs == 0 or q_len == 0 launches nothing.
+ */
+typedef struct mx_attention_desc {
+    int64_t num_seqs, q_len, num_q_heads, num_kv_heads, head_dim;
+    const uint8_t* q;       int64_t ld_q;
+    const uint8_t* q_scale; int64_t ld_qs;
+    const uint8_t* k_cache; const uint8_t* k_scale;
+    const uint8_t* v_cache; const uint8_t* v_scale;
+    int64_t page_size;
+    const int32_t* page_table; int64_t pages_per_seq;
+    const int32_t* kv_lens;
+    float sm_scale;
+    int32_t causal;
+    void* out;              int64_t ld_o; mx_dtype_t out_dtype;
+    float* lse;
+} mx_attention_desc_t;
+
+mx_status_t mx_paged_attention(const mx_attention_desc_t* desc, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* mx_status_string(mx_status_t status);
 

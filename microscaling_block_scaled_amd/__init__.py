@@ -16,13 +16,13 @@ Layouts (row-major, unit stride along the last dimension):
 import ctypes
 
 from ._lib import (BLOCK, MX_ACCUM_AUTO, MX_ACCUM_FP8, MX_ACCUM_FP32, MX_BF16, MX_E4M3, MX_E5M2, MX_F32, MXError,
-                   check, lib, mx_gemm_desc_t)
+                   check, lib, mx_attention_desc_t, mx_gemm_desc_t)
 
 __all__ = [
     "MX_E4M3", "MX_E5M2", "MX_F32", "MX_BF16", "BLOCK", "MXError",
     "MX_ACCUM_AUTO", "MX_ACCUM_FP8", "MX_ACCUM_FP32",
     "mx_quantize", "mx_quantize_colwise", "mx_dequantize", "mx_kv_quant_write", "mx_gemm",
-    "mx_gemm_desc", "mx_paged_scores", "mx_status_string", "mx_query_support",
+    "mx_gemm_desc", "mx_paged_scores", "mx_paged_attention", "mx_status_string", "mx_query_support",
 ]
 
 
@@ -194,6 +194,51 @@ def mx_paged_scores(q_codes, q_scales, k_cache, k_scale, page_table, seq_len, ou
     d.b_page_stride_s = page_size * H * (D // BLOCK)
     d.accum = accum
     mx_gemm_desc(d, stream)
+    return out
+
+
+def mx_paged_attention(q_codes, q_scales, k_cache, k_scale, v_cache, v_scale, page_table, kv_lens, q_len,
+                       sm_scale=None, causal=False, out=None, out_dtype=None, lse=None, stream=None):
+    """Attention of MXFP8 queries over the paged MXFP8 KV cache.
+
+    q_codes [S*q_len, Hq, D] / q_scales [S*q_len, Hq, D/32] (rowwise E4M3
+    along D); k_cache, v_cache [pages, page_size, Hkv, D] and k_scale,
+    v_scale [pages, page_size, Hkv, D/32] as mx_kv_quant_write fills them;
+    page_table int32 [S, pages_per_seq]; kv_lens int32 [S] (device).
+    sm_scale defaults to 1/sqrt(D). Returns out [S*q_len, Hq, D] (bf16 unless
+    out / out_dtype say f32); `lse` (f32 [S*q_len, Hq]) is filled when given."""
+    torch = _torch()
+    T, Hq, D = q_codes.shape
+    S = page_table.shape[0]
+    Hkv = k_cache.shape[2]
+    if T != S * q_len or kv_lens.shape != (S,):
+        raise ValueError("inconsistent query / sequence sizes")
+    for name, t in (("q_codes", q_codes), ("q_scales", q_scales), ("k_cache", k_cache), ("k_scale", k_scale),
+                    ("v_cache", v_cache), ("v_scale", v_scale), ("page_table", page_table), ("kv_lens", kv_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if page_table.dtype != torch.int32 or kv_lens.dtype != torch.int32:
+        raise TypeError("page_table and kv_lens must be int32")
+    if out is None:
+        dt = torch.bfloat16 if out_dtype in (None, MX_BF16, torch.bfloat16) else torch.float32
+        out = torch.empty((T, Hq, D), dtype=dt, device=q_codes.device)
+    if out.shape != (T, Hq, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [S*q_len, Hq, D] tensor")
+    if lse is not None and (lse.shape != (T, Hq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [S*q_len, Hq] tensor")
+    d = mx_attention_desc_t()
+    d.num_seqs, d.q_len, d.num_q_heads, d.num_kv_heads, d.head_dim = S, q_len, Hq, Hkv, D
+    d.q, d.ld_q, d.q_scale, d.ld_qs = q_codes.data_ptr(), Hq * D, q_scales.data_ptr(), Hq * (D // BLOCK)
+    d.k_cache, d.k_scale, d.v_cache, d.v_scale = (k_cache.data_ptr(), k_scale.data_ptr(), v_cache.data_ptr(),
+                                                  v_scale.data_ptr())
+    d.page_size = k_cache.shape[1]
+    d.page_table, d.pages_per_seq = page_table.data_ptr(), page_table.shape[1]
+    d.kv_lens = kv_lens.data_ptr()
+    d.sm_scale = float(D ** -0.5 if sm_scale is None else sm_scale)
+    d.causal = 1 if causal else 0
+    d.out, d.ld_o, d.out_dtype = out.data_ptr(), Hq * D, _dtype_code(out)
+    d.lse = lse.data_ptr() if lse is not None else None
+    check("mx_paged_attention", lib().mx_paged_attention(ctypes.byref(d), _stream(stream)))
     return out
 
 

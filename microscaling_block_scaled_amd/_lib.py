@@ -47,6 +47,20 @@ class mx_gemm_desc_t(ctypes.Structure):
     ]
 
 
+class mx_attention_desc_t(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", _i64), ("q_len", _i64), ("num_q_heads", _i64), ("num_kv_heads", _i64), ("head_dim", _i64),
+        ("q", _p), ("ld_q", _i64), ("q_scale", _p), ("ld_qs", _i64),
+        ("k_cache", _p), ("k_scale", _p), ("v_cache", _p), ("v_scale", _p),
+        ("page_size", _i64),
+        ("page_table", _p), ("pages_per_seq", _i64),
+        ("kv_lens", _p),
+        ("sm_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("out", _p), ("ld_o", _i64), ("out_dtype", ctypes.c_int),
+        ("lse", _p),
+    ]
+
+
 _lib = None
 
 # name -> (restype, argtypes)
@@ -56,6 +70,7 @@ SIGNATURES = {
     "mx_dequantize": (_i32, [_p, _i64, _p, _i64, ctypes.c_int, _i64, _i64, _p, ctypes.c_int, _i64, _p]),
     "mx_kv_quant_write": (_i32, [_p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p]),
     "mx_gemm": (_i32, [ctypes.POINTER(mx_gemm_desc_t), _p]),
+    "mx_paged_attention": (_i32, [ctypes.POINTER(mx_attention_desc_t), _p]),
     "mx_status_string": (ctypes.c_char_p, [_i32]),
     "mx_query_support": (_i32, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p)]),
 }

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp8.so")
-SOURCES = ["abi.hip", "quantize.hip", "dequant.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "dequant.hip", "gemm.hip", "attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -32,9 +32,6 @@
 namespace {
 using namespace mx;
 
-typedef int v8i32 __attribute__((ext_vector_type(8)));
-typedef float v4f32 __attribute__((ext_vector_type(4)));
-typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 
 constexpr int kModeFP8 = 0;
 constexpr int kModeBF16 = 1;
@@ -54,29 +51,6 @@ struct GemmArgs {
   uint32_t scales_dword;  // 1: every row's 4 scale bytes of a K step can be read as one aligned dword
   uint32_t y_vec;         // 1: output rows allow 8/16-byte vector stores
 };
-
-// 2^(code - 127) as an f32 multiplier; code 0xFF (NaN scale) gives NaN.
-__device__ __forceinline__ float scale_value(uint32_t code) {
-  return code == 0xFFu ? __uint_as_float(0x7FC00000u) : __uint_as_float(code ? (code << 23) : 0x00400000u);
-}
-
-// Eight codes (two dwords) -> eight bf16 values times the block scale.
-template <int FMT>
-__device__ __forceinline__ v8bf16 decode8_bf16(uint2 w, float scale) {
-  v2bf16 r0, r1, r2, r3;
-  if constexpr (FMT == MX_E5M2) {
-    r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.x, scale, false);
-    r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.x, scale, true);
-    r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.y, scale, false);
-    r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.y, scale, true);
-  } else {
-    r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, scale, false);
-    r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, scale, true);
-    r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, scale, false);
-    r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, scale, true);
-  }
-  return v8bf16{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-}
 
 __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
   return row * kBK + (((chunk ^ row) & 7u) << 4);
@@ -469,45 +443,6 @@ constexpr int kFBM = 256, kFBN = 256, kFBK = 128;
 constexpr uint32_t kCodeStage = kFBM * kFBK;   // bytes per operand per stage
 constexpr uint32_t kScaleRow = 16;             // scale bytes per row per group of 4 stages
 constexpr uint32_t kScaleBuf = kFBM * kScaleRow;
-
-typedef float v16f32 __attribute__((ext_vector_type(16)));
-
-// 16-byte chunk permutation of a 128-byte LDS row: chunk ^ fperm(row) with
-// fperm = ((row >> 1) & 7) ^ ((row & 1) << 2). The 16 (or 8) lanes that a
-// ds_read_b128 serves together read 16 (8) consecutive rows at one logical
-// chunk; fperm gives them distinct bank groups whether the LDS serves 16
-// lanes over 64 banks or 8 lanes over 32 banks. It depends only on row bits
-// 0-3, so rows 32 apart share it.
-__device__ __forceinline__ uint32_t fperm(uint32_t row) { return ((row >> 1) & 7u) ^ ((row & 1u) << 2); }
-
-// LDS byte offset of a __shared__ object (the low half of its flat address).
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Direct global->LDS 16-byte loads: lane i's bytes land at M0 + 16i. The
-// address is a wave-uniform base (SGPR pair) plus a per-lane 32-bit offset.
-// They are issued as inline assembly so that the compiler does not add its
-// own drain of every outstanding load before each LDS read; completion is
-// tracked explicitly with wait_vmcnt before the barrier that publishes a
-// stage. Nothing else in this kernel uses M0.
-__device__ __forceinline__ void dma16(uint32_t lds, uint32_t off, const void* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
-}
-// A pointer that is the same in every lane, moved to SGPRs once, so that
-// the per-stage address arithmetic stays on the scalar unit.
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-  const uint64_t b = (uint64_t)p;
-  return (const uint8_t*)((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
-                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32));
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int AFMT, int BFMT, bool BF16OUT, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {

@@ -151,6 +151,74 @@ struct FastDiv {
   }
 };
 
+// ---------------------------------------------------------------- vectors
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef float v16f32 __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- decode
+// 2^(code - 127) as an f32 multiplier; code 0xFF (NaN scale) gives NaN.
+__device__ __forceinline__ float scale_value(uint32_t code) {
+  return code == 0xFFu ? __uint_as_float(0x7FC00000u) : __uint_as_float(code ? (code << 23) : 0x00400000u);
+}
+
+// Eight codes (two dwords) -> eight bf16 values times the block scale.
+template <int FMT>
+__device__ __forceinline__ v8bf16 decode8_bf16(uint2 w, float scale) {
+  v2bf16 r0, r1, r2, r3;
+  if constexpr (FMT == MX_E5M2) {
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.x, scale, false);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.x, scale, true);
+    r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.y, scale, false);
+    r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.y, scale, true);
+  } else {
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, scale, false);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, scale, true);
+    r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, scale, false);
+    r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, scale, true);
+  }
+  return v8bf16{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// ---------------------------------------------------------------- LDS staging
+// 16-byte chunk permutation of a 128-byte LDS row: chunk ^ fperm(row) with
+// fperm = ((row >> 1) & 7) ^ ((row & 1) << 2). The 16 (or 8) lanes that a
+// ds_read_b128 serves together read 16 (8) consecutive rows at one logical
+// chunk; fperm gives them distinct bank groups whether the LDS serves 16
+// lanes over 64 banks or 8 lanes over 32 banks. It depends only on row bits
+// 0-3, so rows 32 apart share it.
+__device__ __forceinline__ uint32_t fperm(uint32_t row) { return ((row >> 1) & 7u) ^ ((row & 1u) << 2); }
+
+// LDS byte offset of a __shared__ object (the low half of its flat address).
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct global->LDS 16-byte loads: lane i's bytes land at M0 + 16i. The
+// address is a wave-uniform base (SGPR pair) plus a per-lane 32-bit offset.
+// They are issued as inline assembly so that the compiler does not add its
+// own drain of every outstanding load before each LDS read; completion is
+// tracked explicitly with wait_vmcnt before the barrier that publishes the
+// data. Nothing else in the kernels that use them touches M0.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t off, const void* base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+}
+// A pointer that is the same in every lane, moved to SGPRs once, so that
+// the per-stage address arithmetic stays on the scalar unit.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t b = (uint64_t)p;
+  return (const uint8_t*)((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32));
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------- bf16 out
 // f32 -> bf16, round to nearest even; NaN inputs must already be canonical.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {

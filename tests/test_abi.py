@@ -29,7 +29,7 @@ def libmx():
 def test_header_declares_the_five_operations_and_status_api():
     names = declared_functions()
     for n in ("mx_quantize", "mx_quantize_colwise", "mx_dequantize", "mx_gemm", "mx_kv_quant_write",
-              "mx_status_string", "mx_query_support"):
+              "mx_paged_attention", "mx_status_string", "mx_query_support"):
         assert n in names, n
 
 
@@ -51,22 +51,59 @@ def test_status_strings_without_gpu(libmx):
     assert "unknown" in libmx.mx_status_string(12345).decode()
 
 
-def test_ctypes_descriptor_matches_c_layout(tmp_path):
+@pytest.mark.parametrize("name", ["mx_gemm_desc_t", "mx_attention_desc_t"])
+def test_ctypes_descriptor_matches_c_layout(tmp_path, name):
     """Compile a probe against the real header with gcc and compare field
     offsets and size with the ctypes mirror used by the binding."""
-    from microscaling_block_scaled_amd._lib import mx_gemm_desc_t
-    fields = [f for f, _ in mx_gemm_desc_t._fields_]
+    from microscaling_block_scaled_amd import _lib
+    desc = getattr(_lib, name)
+    fields = [f for f, _ in desc._fields_]
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "mxfp8.h"\nint main(void){\n'
-        + 'printf("size %zu\\n", sizeof(mx_gemm_desc_t));\n'
-        + "".join('printf("%s %%zu\\n", offsetof(mx_gemm_desc_t, %s));\n' % (f, f) for f in fields)
+        + 'printf("size %%zu\\n", sizeof(%s));\n' % name
+        + "".join('printf("%s %%zu\\n", offsetof(%s, %s));\n' % (f, name, f) for f in fields)
         + "return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
                     str(src), "-o", str(exe)], check=True)
     out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
                                                        check=True).stdout.splitlines())
-    assert int(out["size"]) == ctypes.sizeof(mx_gemm_desc_t)
+    assert int(out["size"]) == ctypes.sizeof(desc)
     for f in fields:
-        assert int(out[f]) == getattr(mx_gemm_desc_t, f).offset, f
+        assert int(out[f]) == getattr(desc, f).offset, f
+
+
+def test_attention_argument_errors_without_gpu(libmx):
+    """Host-side validation of mx_paged_attention runs before any device call;
+    the pointers below are never dereferenced."""
+    from microscaling_block_scaled_amd import _lib
+    f = libmx.mx_paged_attention
+    f.restype, f.argtypes = _lib.SIGNATURES["mx_paged_attention"]
+
+    def desc(**kw):
+        d = _lib.mx_attention_desc_t()
+        base = dict(num_seqs=2, q_len=64, num_q_heads=4, num_kv_heads=2, head_dim=128, q=0x10000, ld_q=512,
+                    q_scale=0x20000, ld_qs=16, k_cache=0x30000, k_scale=0x40000, v_cache=0x50000, v_scale=0x60000,
+                    page_size=128, page_table=0x70000, pages_per_seq=4, kv_lens=0x80000, sm_scale=0.088, causal=0,
+                    out=0x90000, ld_o=512, out_dtype=1, lse=None)
+        base.update(kw)
+        for k, v in base.items():
+            setattr(d, k, v)
+        return d
+
+    assert f(None, None) == -1
+    assert f(ctypes.byref(desc(q=None)), None) == -1
+    assert f(ctypes.byref(desc(head_dim=64, ld_q=256, ld_qs=8, ld_o=256)), None) == -2
+    assert f(ctypes.byref(desc(page_size=64)), None) == -2
+    assert f(ctypes.byref(desc(num_kv_heads=3)), None) == -2
+    assert f(ctypes.byref(desc(sm_scale=0.0)), None) == -2
+    assert f(ctypes.byref(desc(sm_scale=float("nan"))), None) == -2
+    assert f(ctypes.byref(desc(ld_q=256)), None) == -2
+    assert f(ctypes.byref(desc(q=0x10008)), None) == -3
+    assert f(ctypes.byref(desc(k_scale=0x40002)), None) == -3
+    assert f(ctypes.byref(desc(out=0x90004)), None) == -3
+    assert f(ctypes.byref(desc(out_dtype=7)), None) == -4
+    # empty problems launch nothing and succeed
+    assert f(ctypes.byref(desc(num_seqs=0)), None) == 0
+    assert f(ctypes.byref(desc(q_len=0, q=None)), None) == 0
