@@ -175,6 +175,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="only the metric's workload (quantize + 8192^3 GEMM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--kv-only", action="store_true",
+                    help="only the KV-cache rows (write, scores, attention), for profiling them alone")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each rank's work is the "
@@ -197,6 +199,10 @@ def main():
 
     def flush():
         flush_buf.sum()
+
+    if args.kv_only:
+        print(json.dumps({"kv_rows": other_rows(torch, mx, inputs, np, flush, stream, args.steps, kv_only=True)}))
+        return
 
     # ---- inputs (generated on the host, resident in HBM before timing)
     log("generating inputs")
@@ -274,7 +280,7 @@ def main():
     print(json.dumps(result))
 
 
-def other_rows(torch, mx, inputs, np, flush, stream, steps):
+def other_rows(torch, mx, inputs, np, flush, stream, steps, kv_only=False):
     """The remaining rows of the path, each timed like the metric's kernels."""
     out = {}
     tm = Timer(torch, stream)
@@ -315,7 +321,27 @@ def other_rows(torch, mx, inputs, np, flush, stream, steps):
                            "frac_of_hbm_peak": round(sc_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
                            "TFLOP/s": round(sc_flop / ms / 1e9, 1), "algorithmic_bytes": sc_bytes,
                            "accumulation": "AUTO -> bf16 MFMA (K = 128)"}
-    del S, Qc, Qs, Kd, Vd, kc, ks, vc, vs
+    del S
+    # paged attention over the same cache: every token's query attends over
+    # the 512 keys of its sequence (bf16 out); non-causal, and causal prefill
+    lens_d = torch.full((64,), 512, dtype=torch.int32, device="cuda")
+    O = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    at_bytes = 3 * T * H * (D + D // 32) + T * H * D * 2
+    for causal in (False, True):
+        name = "paged_attention_causal" if causal else "paged_attention"
+        ms = timed(name, lambda: mx.mx_paged_attention(Qc, Qs, kc, ks, vc, vs, table_d, lens_d, 512, causal=causal,
+                                                       out=O))
+        pairs = 64 * H * (512 * 513 // 2 if causal else 512 * 512)
+        flop = 4.0 * pairs * D  # QK^T (scaled FP8) and PV (bf16), 2 flops per multiply-add each
+        t_mfma = 2.0 * pairs * D / (MFMA_FP8_PEAK_TFLOPS * 1e12) + 2.0 * pairs * D / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        out[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(flop / ms / 1e9, 1),
+                     "frac_of_mfma_bound": round(t_mfma * 1e3 / ms, 4),
+                     "GB/s": round(at_bytes / ms / 1e6, 1), "frac_of_hbm_peak": round(at_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                     "algorithmic_bytes": at_bytes, "flop": flop,
+                     "shape": "64 seq x 512 queries x 8 heads x 128, 512 keys, pages of 128, bf16 out"}
+    del O, Qc, Qs, Kd, Vd, kc, ks, vc, vs
+    if kv_only:
+        return out
     # dequantize the 8192 x 4096 codes to bf16
     log("dequant row")
     xq, _ = inputs.quantize_input()

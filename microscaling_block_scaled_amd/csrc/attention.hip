@@ -24,8 +24,9 @@
 //
 // Per block of 128 keys: K codes (16 KB) and the K and V scales (512 B each)
 // arrive by direct global->LDS loads into one of two buffers; V codes come
-// into registers one block ahead, and every thread decodes 2 x 32 of them
-// into the shared bf16 V^T tile (32 KB). Each key block lies inside one page
+// into registers one block ahead, and every thread decodes 64 of them (8
+// keys x 8 head-dim columns of one scale block) into the shared bf16 V^T
+// tile (32 KB). Each key block lies inside one page
 // (page_size % 128 == 0), so the block's rows are consecutive cache slots.
 #include "mx_common.hpp"
 
@@ -49,16 +50,27 @@ struct AttnArgs {
 };
 
 // 16-byte chunk permutation of a 256-byte V^T row. The PV fragment reads
-// touch 16 consecutive rows at one logical chunk, and the decoder's writes
-// touch rows 4g + i for 16 consecutive g; (row ^ (row >> 4)) & 15 is
-// distinct across both sets, so neither conflicts on LDS banks.
-__device__ __forceinline__ uint32_t vt_perm(uint32_t row) { return (row ^ (row >> 4)) & 15u; }
+// touch rows 32t + r (r = 0..15 or 16..31) at one logical chunk; the
+// decoder's writes touch rows 32m + 4j + i (m, j = 0..3) at one chunk. With
+// chunk ^ ((row ^ (row >> 5)) & 15) both sets land on 16 distinct 16-byte
+// bank groups, so neither conflicts.
+__device__ __forceinline__ uint32_t vt_perm(uint32_t row) { return (row ^ (row >> 5)) & 15u; }
 
 __device__ __forceinline__ void dma4(uint32_t lds, uint32_t off, const void* base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
 }
 
-__device__ __forceinline__ float max2(float a, float b) { return a > b ? a : b; }
+// Buffer resource over [base, base + bytes): loads past the end return 0.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// The running softmax reference moves up only when a block's maximum
+// exceeds it by more than this (log2 units); weights relative to it then
+// stay below 2^8, far inside f32 and bf16 range, and most blocks skip the
+// rescaling of the accumulators.
+constexpr float kRescaleSlack = 8.f;
 
 template <bool BF16OUT>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
@@ -67,13 +79,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   __shared__ __attribute__((aligned(16))) uint32_t VSs[2][kKB];
   __shared__ __attribute__((aligned(1024))) uint8_t VT[kHD * kVTRow];
 
-  // ---- work item: (sequence, head, query tile); the query tiles of one
-  // (sequence, head) share its keys, so they are kept on one XCD.
-  uint32_t lid = blockIdx.x;
-  if (g.total_wg % 8 == 0) lid = (lid % 8) * (g.total_wg / 8) + lid / 8;
-  const uint32_t qt = lid % g.q_tiles;
-  const uint32_t h = (lid / g.q_tiles) % g.hq;
-  const uint32_t s = lid / (g.q_tiles * g.hq);
+  // ---- work item: (sequence, head, query tile). Without a mask the query
+  // tiles of one (sequence, head) share its keys, so they are kept on one XCD
+  // (the 8 XCDs take work-groups round-robin). Under a causal mask the work
+  // of a tile grows with its index, so all last tiles go first, then the
+  // tiles before them, in plain dispatch order, which spreads every class of
+  // tile evenly over the XCDs.
+  uint32_t qt, h, s;
+  {
+    const uint32_t lid = blockIdx.x;
+    if (g.causal) {
+      const uint32_t nsh = g.total_wg / g.q_tiles;  // (sequence, head) pairs
+      qt = g.q_tiles - 1 - lid / nsh;
+      h = (lid % nsh) % g.hq;
+      s = (lid % nsh) / g.hq;
+    } else {
+      const uint32_t l2 = g.total_wg % 8 == 0 ? (lid % 8) * (g.total_wg / 8) + lid / 8 : lid;
+      qt = l2 % g.q_tiles;
+      h = (l2 / g.q_tiles) % g.hq;
+      s = l2 / (g.q_tiles * g.hq);
+    }
+  }
   const uint32_t hk = h / g.group;
 
   const int tid = threadIdx.x;
@@ -81,25 +107,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
 
-  const int64_t max_keys = g.pages_per_seq * (int64_t)g.page_size;
-  int64_t L = g.lens[s];
+  // key counts fit in 31 bits (checked on the host)
+  const int max_keys = (int)(g.pages_per_seq * (int64_t)g.page_size);
+  int L = g.lens[s];
   L = L < 0 ? 0 : (L > max_keys ? max_keys : L);
-  const int64_t q_len = g.q_len;
-  const int64_t q0 = (int64_t)qt * kQT;
-  const int64_t q_last = min(q0 + kQT - 1, q_len - 1);
+  const int q_len = (int)g.q_len;
+  const int q0 = (int)qt * kQT;
+  const int q_last = min(q0 + kQT - 1, q_len - 1);
   // keys the tile needs, and the fewest any of its rows may use
-  int64_t kmax = L, kmin = L;
+  int kmax = L, kmin = L;
   if (g.causal) {
     kmax = min(L, L - q_len + q_last + 1);
     kmin = min(L, L - q_len + q0 + 1);
   }
-  const int nblk = kmax > 0 ? (int)((kmax + kKB - 1) / kKB) : 0;
+  const int nblk = kmax > 0 ? (kmax + kKB - 1) / kKB : 0;
 
   // ---- this lane's query row (rows past q_len load the last row and store nothing)
-  const int64_t qi = q0 + wave * 32 + lr;
+  const int qi = q0 + wave * 32 + lr;
   const bool q_ok = qi < q_len;
   const int64_t tok = (int64_t)s * q_len + (q_ok ? qi : q_len - 1);
-  const int64_t lim = g.causal ? min(L, L - q_len + qi + 1) : L;  // allowed keys: j < lim
+  const int lim = g.causal ? min(L, L - q_len + qi + 1) : L;  // allowed keys: j < lim
 
   const int64_t out_row = tok * g.ld_o + (int64_t)h * kHD;
   if (nblk == 0) {  // no allowed key anywhere in the tile
@@ -137,8 +164,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
 
   // ---- per-block sources. Key j of the sequence sits in cache slot
   // table[j / page_size] * page_size + j % page_size; within a block the
-  // slots are consecutive. Rows past the tile's last needed key are clamped
-  // to it (their scores are masked and their P is exactly 0).
+  // slots are consecutive.
   const uint32_t slot_bytes = g.hkv * kHD;        // code bytes per cache slot
   const uint32_t slot_sbytes = g.hkv * (kHD / 32); // scale bytes per cache slot
   const int32_t* tab = g.table + (int64_t)s * g.pages_per_seq;
@@ -147,28 +173,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
     return (int64_t)tab[j / g.page_size] * g.page_size + j % g.page_size;
   };
 
-  // K code rows handled by this lane's 4 DMA instructions, and its chunk
+  // K code rows of this lane's 4 direct-to-LDS loads and the chunk each
+  // fetches; rows past the last needed key are clamped to it (their scores
+  // are masked, so their P is exactly 0).
   uint32_t k_row[4], k_chunk[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     k_row[t] = 32 * wave + 8 * t + (lane >> 3);
     k_chunk[t] = (((uint32_t)lane & 7u) ^ fperm(k_row[t])) << 4;
   }
-  // V decode units: unit u covers V^T chunk pg (8 keys) x head-dim columns 4gd .. 4gd+3
-  const uint32_t gd = lr;
-  uint32_t v_key[2];  // first key of each unit; the unit's keys are v_key + {0,1,2,3,8,9,10,11}
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const uint32_t pg = 2 * wave + lg + 8 * u;
-    v_key[u] = 32 * (pg >> 2) + 16 * ((pg >> 1) & 1) + 4 * (pg & 1);
-  }
+  // V decode unit of this thread: V^T chunk pg (the 8 keys v_key + {0,1,2,3,
+  // 8,9,10,11}) x head-dim columns 4gd .. 4gd+3 for gd = gd0 and gd0 + 4,
+  // both in scale block db.
+  const uint32_t pg = (uint32_t)tid >> 4;
+  const uint32_t db = ((uint32_t)tid >> 2) & 3u;
+  const uint32_t gd0 = 8 * db + ((uint32_t)tid & 3u);
+  const uint32_t v_key = 32 * (pg >> 2) + 16 * ((pg >> 1) & 1) + 4 * (pg & 1);
+  const uint32_t v_off0 = v_key * slot_bytes + 4 * gd0;
 
   uint32_t vraw[2][8];
   auto issue_block = [&](int b, int buf) {
     const int64_t slot0 = slot0_of(b);
-    const uint32_t last = (uint32_t)min((int64_t)kKB, kmax - (int64_t)b * kKB) - 1;
+    const uint32_t last = (uint32_t)min(kKB, kmax - b * kKB) - 1;
     const uint8_t* kbase = uniform_ptr(g.kc + (slot0 * g.hkv + hk) * kHD);
-    const uint8_t* vbase = uniform_ptr(g.vc + (slot0 * g.hkv + hk) * kHD);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       dma16(lds_off(&Ks[buf][(32 * wave + 8 * t) * kHD]), min(k_row[t], last) * slot_bytes + k_chunk[t], kbase);
@@ -180,30 +207,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
       dma4(lds_off(is_k ? &KSs[buf][64 * (wave & 1)] : &VSs[buf][64 * (wave & 1)]), min(row, last) * slot_sbytes,
            sbase);
     }
+    // V codes: the buffer ends after the last needed key's row, so keys past
+    // it read as 0 (their P is 0 as well)
+    const __amdgpu_buffer_rsrc_t vr =
+        buffer_rsrc(uniform_ptr(g.vc + (slot0 * g.hkv + hk) * kHD), last * slot_bytes + kHD);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t key = v_key[u] + (e & 3) + 8 * (e >> 2);
-        vraw[u][e] = *(const uint32_t*)(vbase + min(key, last) * slot_bytes + 4 * gd);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t off = v_off0 + ((e & 3) + 8 * (e >> 2)) * slot_bytes;
+      vraw[0][e] = __builtin_amdgcn_raw_buffer_load_b32(vr, (int)off, 0, 0);
+      vraw[1][e] = __builtin_amdgcn_raw_buffer_load_b32(vr, (int)(off + 16), 0, 0);
+    }
   };
 
-  // decode this thread's two V units into V^T (rows 4gd .. 4gd+3)
+  // decode this thread's V unit into V^T rows 4gd .. 4gd+3 (gd = gd0, gd0 + 4)
   auto decode_v = [&](int buf) {
+    const uint4 sa = *(const uint4*)&VSs[buf][v_key];
+    const uint4 sb = *(const uint4*)&VSs[buf][v_key + 8];
+    const uint32_t sw[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+    float sc[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t pg = 2 * wave + lg + 8 * u;
-      const uint32_t sh = 8 * (gd >> 3);  // scale byte of head-dim block gd / 8
-      const uint4 sa = *(const uint4*)&VSs[buf][v_key[u]];
-      const uint4 sb = *(const uint4*)&VSs[buf][v_key[u] + 8];
-      const uint32_t sw[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+    for (int e = 0; e < 8; ++e) sc[e] = scale_value((sw[e] >> (8 * db)) & 0xFFu);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
       uint32_t lo[8], hi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float sc = scale_value((sw[e] >> sh) & 0xFFu);
-        lo[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)vraw[u][e], sc, false));
-        hi[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)vraw[u][e], sc, true));
+        lo[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)vraw[x][e], sc[e], false));
+        hi[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)vraw[x][e], sc[e], true));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -211,7 +241,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
         const uint4 w = make_uint4(__builtin_amdgcn_perm(src[1], src[0], sel), __builtin_amdgcn_perm(src[3], src[2], sel),
                                    __builtin_amdgcn_perm(src[5], src[4], sel), __builtin_amdgcn_perm(src[7], src[6], sel));
-        const uint32_t row = 4 * gd + i;
+        const uint32_t row = 4 * (gd0 + 4 * x) + i;
         *(uint4*)(VT + row * kVTRow + ((pg ^ vt_perm(row)) << 4)) = w;
       }
     }
@@ -222,8 +252,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o_acc[t][e] = 0.f;
-  float m_run = -__builtin_inff();  // running max of sm_scale * log2(e) * S
-  float l_run = 0.f;                 // running sum of exp2(x - m_run)
+  float m_ref = -__builtin_inff();  // softmax reference, in units of sm_scale * log2(e) * S
+  float l_run = 0.f;                 // sum of exp2(x - m_ref) over the keys so far
 
   const uint32_t fp = fperm(lr);
   issue_block(0, 0);
@@ -236,30 +266,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
     decode_v(buf);
     if (b + 1 < nblk) issue_block(b + 1, buf ^ 1);
 
-    // ---- S^T for this wave's 32 queries x 128 keys: 4 tiles of 32 keys
+    // ---- S^T for this wave's 32 queries x 128 keys: 4 tiles of 32 keys,
+    // accumulated over the two head-dim halves
     v16f32 sacc[4];
+    uint32_t kw[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
-      const uint8_t* krow = &Ks[buf][(32 * kt + lr) * kHD];
-      const uint32_t kw = KSs[buf][32 * kt + lr] >> (8 * lg);
+      kw[kt] = KSs[buf][32 * kt + lr] >> (8 * lg);
+    }
 #pragma unroll
-      for (int hd = 0; hd < 2; ++hd) {
+    for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint8_t* krow = &Ks[buf][(32 * kt + lr) * kHD];
         const uint4 lo = *(const uint4*)(krow + (((4 * hd + lg) ^ fp) << 4));
         const uint4 hi = *(const uint4*)(krow + (((4 * hd + 2 + lg) ^ fp) << 4));
         const v8i32 kf = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[hd], sacc[kt], MX_E4M3, MX_E4M3, 0,
-                                                                    (int)(kw >> (16 * hd)), 0, (int)qsc[hd]);
+                                                                    (int)(kw[kt] >> (16 * hd)), 0, (int)qsc[hd]);
       }
-    }
 
     // ---- online softmax. Element e of tile kt is key 32kt + 8(e/4) + 4lg + e%4.
-    if ((int64_t)(b + 1) * kKB > kmin) {
-      // allowed keys of this block for the row: local index < rel, i.e.
-      // (local index - 4lg) < rel - 4lg, a lane value against constants
-      const int64_t rel64 = lim - (int64_t)b * kKB - 4 * lg;
-      const int rel = (int)(rel64 < -1 ? -1 : (rel64 > kKB ? kKB : rel64));
+    if ((b + 1) * kKB > kmin) {
+      // allowed keys of this block for the row: local index < lim - 128b,
+      // i.e. (local index - 4lg) < rel, a lane value against constants
+      const int rel = lim - b * kKB - 4 * lg;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -270,19 +303,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = max2(mx, sacc[kt][e]);
+      for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, sacc[kt][e]);
     {
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = max2(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+      mx = __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
     }
-    const float m_new = max2(m_run, mx * g.c2);
-    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    const float x_max = mx * g.c2;
+    const bool lift = x_max > m_ref + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(lift)) {
+      // lanes that do not lift keep their reference (alpha = 1; computing it
+      // from m_ref - m_ref would give NaN for a reference still at -inf)
+      const float alpha = lift ? __builtin_amdgcn_exp2f(m_ref - x_max) : 1.f;
+      m_ref = lift ? x_max : m_ref;
+      l_run *= alpha;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o_acc[t][e] *= alpha;
+        for (int e = 0; e < 16; ++e) o_acc[t][e] *= alpha;
+    }
+    const float m_use = m_ref == -__builtin_inff() ? 0.f : m_ref;
 
     wait_lgkmcnt0();
     barrier();  // V^T of block b complete
@@ -318,7 +357,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
       ls = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
     }
-    l_run = l_run * alpha + ls;
+    l_run += ls;
   }
 
   // ---- epilogue: O = acc / l; element e of tile t is head-dim column
@@ -341,7 +380,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
       }
     }
   if (lg == 0 && g.lse)
-    g.lse[tok * g.hq + h] = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -__builtin_inff();
+    g.lse[tok * g.hq + h] = l_run > 0.f ? (m_ref + __log2f(l_run)) * 0.69314718055994531f : -__builtin_inff();
 }
 
 }  // namespace
