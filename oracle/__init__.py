@@ -10,7 +10,9 @@ Array conventions (host numpy arrays):
   * f32 inputs are ``np.float32``; bf16 inputs are their 16-bit patterns as
     ``np.uint16``;
   * codes and E8M0 scales are ``np.uint8``;
-  * formats: ``E4M3 = 0``, ``E5M2 = 1``.
+  * formats: ``E4M3 = 0``, ``E5M2 = 1``, ``E2M1 = 2`` (MXFP4). E2M1 codes are
+    packed two per byte, element 2i in the low nibble, so an E2M1 code array
+    of K elements per row is K/2 bytes wide.
 """
 import ctypes
 import os
@@ -19,6 +21,7 @@ import numpy as np
 
 E4M3 = 0
 E5M2 = 1
+E2M1 = 2
 F32 = 0
 BF16 = 1
 BLOCK = 32
@@ -111,17 +114,25 @@ def dequant_value(fmt: int, code: int, scale: int) -> float:
 
 
 def decode_table(fmt: int) -> np.ndarray:
-    return np.array([decode(fmt, c) for c in range(256)], dtype=np.float64)
+    n = 16 if fmt == E2M1 else 256
+    return np.array([decode(fmt, c) for c in range(n)], dtype=np.float64)
+
+
+def code_bytes(fmt: int, n: int) -> int:
+    """Bytes holding n codes of the format."""
+    return n // 2 if fmt == E2M1 else n
 
 
 # ---- array operations -----------------------------------------------------
 def quantize_rows(x: np.ndarray, fmt: int):
-    """Rowwise MXFP8: returns (codes [R, C] uint8, scales [R, C/32] uint8)."""
+    """Rowwise MX quantization: returns (codes [R, C] uint8 (E2M1: [R, C/2]
+    packed), scales [R, C/32] uint8)."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
-    q = np.empty((rows, cols), np.uint8)
+    cb = code_bytes(fmt, cols)
+    q = np.empty((rows, cb), np.uint8)
     s = np.empty((rows, cols // BLOCK), np.uint8)
-    _check(_load().mxo_quantize_rows(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, _ptr(q), cols, _ptr(s),
+    _check(_load().mxo_quantize_rows(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, _ptr(q), cb, _ptr(s),
                                      cols // BLOCK))
     return q, s
 
@@ -131,9 +142,10 @@ def quantize_cols(x: np.ndarray, fmt: int):
     returns (codes^T [C, R] uint8, scales^T [C, R/32] uint8)."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
-    qt = np.empty((cols, rows), np.uint8)
+    rb = code_bytes(fmt, rows)
+    qt = np.empty((cols, rb), np.uint8)
     st = np.empty((cols, rows // BLOCK), np.uint8)
-    _check(_load().mxo_quantize_cols(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, _ptr(qt), rows, _ptr(st),
+    _check(_load().mxo_quantize_cols(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, _ptr(qt), rb, _ptr(st),
                                      rows // BLOCK))
     return qt, st
 
@@ -165,32 +177,34 @@ def dequantize(q: np.ndarray, s: np.ndarray, fmt: int, out: str = "f32") -> np.n
     """x_hat = s * q rounded to f32 (np.float32) or bf16 (np.uint16 patterns)."""
     q = np.ascontiguousarray(q, dtype=np.uint8)
     s = np.ascontiguousarray(s, dtype=np.uint8)
-    rows, cols = q.shape
+    rows, cols = q.shape[0], s.shape[1] * BLOCK
+    assert q.shape[1] == code_bytes(fmt, cols)
     if out == "f32":
         y = np.empty((rows, cols), np.float32)
         ydt = F32
     else:
         y = np.empty((rows, cols), np.uint16)
         ydt = BF16
-    _check(_load().mxo_dequantize(_ptr(q), cols, _ptr(s), s.shape[1], fmt, rows, cols, _ptr(y), ydt, cols))
+    _check(_load().mxo_dequantize(_ptr(q), q.shape[1], _ptr(s), s.shape[1], fmt, rows, cols, _ptr(y), ydt, cols))
     return y
 
 
 def gemm(a: np.ndarray, sa: np.ndarray, afmt: int, b: np.ndarray, sb: np.ndarray, bfmt: int):
-    """Block-scaled product y = A * B^T with A [M, K], B [N, K] codes.
+    """Block-scaled product y = A * B^T with A [M, K], B [N, K] codes (E2M1
+    operands packed: [M, K/2] bytes); K is taken from the scales.
 
     Returns (y [M, N] float64, t [M, N] float64) with t = sum_k |a_k b_k|."""
     a = np.ascontiguousarray(a, dtype=np.uint8)
     b = np.ascontiguousarray(b, dtype=np.uint8)
     sa = np.ascontiguousarray(sa, dtype=np.uint8)
     sb = np.ascontiguousarray(sb, dtype=np.uint8)
-    M, K = a.shape
-    N = b.shape[0]
-    assert b.shape[1] == K and sa.shape == (M, K // BLOCK) and sb.shape == (N, K // BLOCK)
+    M, N = a.shape[0], b.shape[0]
+    K = sa.shape[1] * BLOCK
+    assert a.shape[1] == code_bytes(afmt, K) and b.shape[1] == code_bytes(bfmt, K) and sb.shape == (N, K // BLOCK)
     y = np.empty((M, N), np.float64)
     t = np.empty((M, N), np.float64)
-    _check(_load().mxo_gemm(M, N, K, _ptr(a), K, _ptr(sa), K // BLOCK, afmt, _ptr(b), K, _ptr(sb), K // BLOCK,
-                            bfmt, _ptr(y), N, _ptr(t), N))
+    _check(_load().mxo_gemm(M, N, K, _ptr(a), a.shape[1], _ptr(sa), K // BLOCK, afmt, _ptr(b), b.shape[1], _ptr(sb),
+                            K // BLOCK, bfmt, _ptr(y), N, _ptr(t), N))
     return y, t
 
 
@@ -201,7 +215,8 @@ def gemm_at(a: np.ndarray, sa: np.ndarray, afmt: int, b: np.ndarray, sb: np.ndar
     b = np.ascontiguousarray(b, dtype=np.uint8)
     sa = np.ascontiguousarray(sa, dtype=np.uint8)
     sb = np.ascontiguousarray(sb, dtype=np.uint8)
-    K = a.shape[1]
+    K = sa.shape[1] * BLOCK
+    assert a.shape[1] == code_bytes(afmt, K) and b.shape[1] == code_bytes(bfmt, K)
     mi = np.ascontiguousarray(mi, dtype=np.int64)
     ni = np.ascontiguousarray(ni, dtype=np.int64)
     assert mi.shape == ni.shape

@@ -27,6 +27,10 @@
  *   - amax == 0 gives scale code 0 and all-zero codes;
  *   - a block holding NaN or Inf gets scale code 0xFF and element codes 0x7F;
  *   - the sign of x is kept, so negative values that round to zero give 0x80.
+ *   - MXFP4 [NVFP4 §2.4, §5.5]: E2M1 elements with the same E8M0 scale per 32
+ *     and the same rule (emax_elem = 2, largest finite 6); codes packed two
+ *     per byte, element 2i in the low nibble; a NaN/Inf block gets scale
+ *     0xFF and element codes 0 (E2M1 has no NaN code).
  */
 #include <math.h>
 #include <stdint.h>
@@ -56,10 +60,18 @@ typedef struct {
 
 static const fp8_format FMT_E4M3 = {3, -6, 7, 448.0, 8};
 static const fp8_format FMT_E5M2 = {2, -14, 15, 57344.0, 15};
+/* E2M1 (the MXFP4 element) [NVFP4 §2.4]: 1 sign, 2 exponent and 1 mantissa
+ * bit, exponent bias 1, exponent field 0 subnormal (0.m); the 8 magnitudes are
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6, so the smallest normal is 2^0 and the largest
+ * finite 6 = 1.5 * 2^2. No Inf or NaN encodings. */
+static const fp8_format FMT_E2M1 = {1, 0, 1, 6.0, 2};
 
 static const fp8_format* fmt_of(int fmt) {
-    return fmt == MXO_E5M2 ? &FMT_E5M2 : &FMT_E4M3;
+    return fmt == MXO_E5M2 ? &FMT_E5M2 : fmt == MXO_E2M1 ? &FMT_E2M1 : &FMT_E4M3;
 }
+
+/* Code bits of an element and its sign bit. */
+static unsigned code_bits(int fmt) { return fmt == MXO_E2M1 ? 4u : 8u; }
 
 /* Value of an E4M3 code: exponent field 0 is subnormal (m * 2^-9); the one
  * pattern S.1111.111 is NaN and there is no infinity [FP8DS §三]. */
@@ -90,7 +102,16 @@ double mxo_decode_e5m2(unsigned code) {
     return s ? -v : v;
 }
 
+/* Value of an E2M1 code [NVFP4 §2.4]: sign bit 3, exponent bits 2-1 with
+ * bias 1, mantissa bit 0; exponent field 0 gives 0.m (0 or 0.5). */
+double mxo_decode_e2m1(unsigned code) {
+    unsigned s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + m / 2.0, (int)e - 1);
+    return s ? -v : v;
+}
+
 double mxo_decode(int fmt, unsigned code) {
+    if (fmt == MXO_E2M1) return mxo_decode_e2m1(code & 0xF);
     return fmt == MXO_E5M2 ? mxo_decode_e5m2(code & 0xFF) : mxo_decode_e4m3(code & 0xFF);
 }
 
@@ -134,12 +155,13 @@ static unsigned grid_bits(double r, int mbits, int emin, int bias) {
     return ((unsigned)(e + bias) << mbits) | m;
 }
 
-/* Code of the FP8 value nearest to y (ties to even), saturating at the largest
- * finite magnitude; the sign bit is taken from y. */
+/* Code of the element value nearest to y (ties to even), saturating at the
+ * largest finite magnitude; the sign bit is taken from y. E2M1 has no NaN
+ * code: a NaN gives code 0 (its block carries the NaN scale). */
 unsigned mxo_encode(int fmt, double y) {
     const fp8_format* f = fmt_of(fmt);
-    unsigned sign = signbit(y) ? 0x80u : 0u;
-    if (isnan(y)) return 0x7Fu;
+    unsigned sign = signbit(y) ? 1u << (code_bits(fmt) - 1) : 0u;
+    if (isnan(y)) return fmt == MXO_E2M1 ? 0u : 0x7Fu;
     double a = fabs(y);
     double r = a >= f->maxfinite ? f->maxfinite : round_to_grid(a, f->mbits, f->emin);
     if (r > f->maxfinite) r = f->maxfinite;
@@ -168,15 +190,30 @@ unsigned mxo_scale_code(int fmt, const double* x, int64_t n) {
     return (unsigned)k;
 }
 
-/* Quantize one block: scale code, then q_i = Q_FP8(x_i / s) [SM120 §0.1]. */
-static void quantize_block(int fmt, const double* x, int64_t n, uint8_t* codes, int64_t code_stride,
-                           uint8_t* scale) {
+/* Quantize one block: scale code, then q_i = Q_FP8(x_i / s) [SM120 §0.1].
+ * A block holding NaN or Inf gets element codes 0x7F (FP8) or 0 (E2M1).
+ * Codes are stored from codes[0] on: one byte each, or for E2M1 two per byte
+ * with element 2i in the low nibble [NVFP4 §5.5: 4 bits per element]. */
+static void quantize_block(int fmt, const double* x, int64_t n, uint8_t* codes, uint8_t* scale) {
     unsigned s = mxo_scale_code(fmt, x, n);
     *scale = (uint8_t)s;
     for (int64_t i = 0; i < n; ++i) {
-        unsigned c = (s == 0xFFu) ? 0x7Fu : mxo_encode(fmt, ldexp(x[i], -((int)s - 127)));
-        codes[i * code_stride] = (uint8_t)c;
+        unsigned c = (s == 0xFFu) ? (fmt == MXO_E2M1 ? 0u : 0x7Fu) : mxo_encode(fmt, ldexp(x[i], -((int)s - 127)));
+        if (fmt == MXO_E2M1) {
+            if (i % 2 == 0)
+                codes[i / 2] = (uint8_t)c;
+            else
+                codes[i / 2] |= (uint8_t)(c << 4);
+        } else {
+            codes[i] = (uint8_t)c;
+        }
     }
+}
+
+/* Bytes of codes per block, and the code of element k of a row. */
+static int64_t block_bytes(int fmt) { return fmt == MXO_E2M1 ? MXO_BLOCK / 2 : MXO_BLOCK; }
+static unsigned code_at(int fmt, const uint8_t* row, int64_t k) {
+    return fmt == MXO_E2M1 ? (row[k / 2] >> (4 * (k & 1))) & 0xFu : row[k];
 }
 
 /* ---------------------------------------------------------------------------
@@ -200,7 +237,7 @@ int mxo_quantize_rows(const void* x, int xdt, int64_t rows, int64_t cols, int64_
         double v[MXO_BLOCK];
         for (int64_t b = 0; b < cols / MXO_BLOCK; ++b) {
             for (int i = 0; i < MXO_BLOCK; ++i) v[i] = load_elem(x, xdt, r * ldx + b * MXO_BLOCK + i);
-            quantize_block(fmt, v, MXO_BLOCK, q + r * ldq + b * MXO_BLOCK, 1, s + r * lds + b);
+            quantize_block(fmt, v, MXO_BLOCK, q + r * ldq + b * block_bytes(fmt), s + r * lds + b);
         }
     }
     return 0;
@@ -218,7 +255,7 @@ int mxo_quantize_cols(const void* x, int xdt, int64_t rows, int64_t cols, int64_
         double v[MXO_BLOCK];
         for (int64_t b = 0; b < rows / MXO_BLOCK; ++b) {
             for (int i = 0; i < MXO_BLOCK; ++i) v[i] = load_elem(x, xdt, (b * MXO_BLOCK + i) * ldx + c);
-            quantize_block(fmt, v, MXO_BLOCK, qt + c * ldq + b * MXO_BLOCK, 1, st + c * lds + b);
+            quantize_block(fmt, v, MXO_BLOCK, qt + c * ldq + b * block_bytes(fmt), st + c * lds + b);
         }
     }
     return 0;
@@ -247,7 +284,7 @@ int mxo_kv_quant_write(const void* k, const void* v, int dt, int64_t T, int64_t 
             for (int64_t h = 0; h < H; ++h)
                 for (int64_t b = 0; b < D / MXO_BLOCK; ++b) {
                     for (int i = 0; i < MXO_BLOCK; ++i) buf[i] = load_elem(src, dt, t * ld_token + h * D + b * MXO_BLOCK + i);
-                    quantize_block(MXO_E4M3, buf, MXO_BLOCK, cache + (cache_row + h) * D + b * MXO_BLOCK, 1,
+                    quantize_block(MXO_E4M3, buf, MXO_BLOCK, cache + (cache_row + h) * D + b * MXO_BLOCK,
                                    scale + (cache_row + h) * (D / MXO_BLOCK) + b);
                 }
         }
@@ -282,7 +319,7 @@ int mxo_dequantize(const uint8_t* q, int64_t ldq, const uint8_t* s, int64_t lds,
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) {
-            double v = mxo_dequant_value(fmt, q[r * ldq + c], s[r * lds + c / MXO_BLOCK]);
+            double v = mxo_dequant_value(fmt, code_at(fmt, q + r * ldq, c), s[r * lds + c / MXO_BLOCK]);
             if (ydt == MXO_F32)
                 ((float*)y)[r * ldy + c] = (float)v;
             else
@@ -300,13 +337,14 @@ int mxo_dequantize(const uint8_t* q, int64_t ldq, const uint8_t* s, int64_t lds,
  * shape of the equation. t[m][n] = sum_k |a_hat_k * b_hat_k| is returned
  * beside it: the magnitude against which a tolerance is stated.
  * ------------------------------------------------------------------------- */
-static void gemm_one(int64_t K, const uint8_t* a, const uint8_t* sa, const double* lut_a, const uint8_t* b,
-                     const uint8_t* sb, const double* lut_b, double* y_out, double* t_out) {
+static void gemm_one(int64_t K, const uint8_t* a, const uint8_t* sa, int afmt, const double* lut_a, const uint8_t* b,
+                     const uint8_t* sb, int bfmt, const double* lut_b, double* y_out, double* t_out) {
     double y = 0.0, t = 0.0;
     for (int64_t blk = 0; blk < K / MXO_BLOCK; ++blk) {
         double inner = 0.0, inner_abs = 0.0;
         for (int i = 0; i < MXO_BLOCK; ++i) {
-            double p = lut_a[a[blk * MXO_BLOCK + i]] * lut_b[b[blk * MXO_BLOCK + i]];
+            const int64_t k = blk * MXO_BLOCK + i;
+            double p = lut_a[code_at(afmt, a, k)] * lut_b[code_at(bfmt, b, k)];
             inner += p;
             inner_abs += fabs(p);
         }
@@ -332,8 +370,8 @@ int mxo_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, con
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
-            gemm_one(K, a + m * lda, sa + m * ldsa, lut_a, b + n * ldb, sb + n * ldsb, lut_b, &y[m * ldy + n],
-                     &t[m * ldt + n]);
+            gemm_one(K, a + m * lda, sa + m * ldsa, afmt, lut_a, b + n * ldb, sb + n * ldsb, bfmt, lut_b,
+                     &y[m * ldy + n], &t[m * ldt + n]);
     return 0;
 }
 
@@ -347,8 +385,8 @@ int mxo_gemm_at(int64_t K, const uint8_t* a, int64_t lda, const uint8_t* sa, int
     build_lut(bfmt, lut_b);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < count; ++i)
-        gemm_one(K, a + mi[i] * lda, sa + mi[i] * ldsa, lut_a, b + ni[i] * ldb, sb + ni[i] * ldsb, lut_b, &y[i],
-                 &t[i]);
+        gemm_one(K, a + mi[i] * lda, sa + mi[i] * ldsa, afmt, lut_a, b + ni[i] * ldb, sb + ni[i] * ldsb, bfmt, lut_b,
+                 &y[i], &t[i]);
     return 0;
 }
 
@@ -403,7 +441,7 @@ static void attention_one(const uint8_t* q, const uint8_t* qs, const uint8_t* kc
         int64_t slot = (int64_t)ptab[j / page_size] * page_size + j % page_size;
         int64_t row = slot * hkv + hk;
         double sj, tj;
-        gemm_one(D, q, qs, lut, kc + row * D, ks + row * nb, lut, &sj, &tj);
+        gemm_one(D, q, qs, MXO_E4M3, lut, kc + row * D, ks + row * nb, MXO_E4M3, lut, &sj, &tj);
         z[j] = sm_scale * sj;
         if (isnan(z[j])) has_nan = 1;
         if (z[j] > m) m = z[j];

@@ -11,11 +11,12 @@
 
 #define MXO_BLOCK 32
 
-enum { MXO_E4M3 = 0, MXO_E5M2 = 1 };
+enum { MXO_E4M3 = 0, MXO_E5M2 = 1, MXO_E2M1 = 2 };
 enum { MXO_F32 = 0, MXO_BF16 = 1 };
 
 double mxo_decode_e4m3(unsigned code);
 double mxo_decode_e5m2(unsigned code);
+double mxo_decode_e2m1(unsigned code);
 double mxo_decode(int fmt, unsigned code);
 double mxo_decode_e8m0(unsigned e);
 unsigned mxo_encode(int fmt, double y);

@@ -588,3 +588,161 @@ def test_attention_page_relocation_and_decode_offsets(oracle):
     kscl = c["ks"][c["table"][2, j // page], j % page, 0]
     _, tt = oracle.gemm(c["qc"][t, h][None], c["qs"][t, h][None], E4M3, krows, kscl, E4M3)
     assert tmax[t * 2 + h] == tt.max()
+
+
+# ---------------------------------------------------------------------------
+# MXFP4: E2M1 elements with the E8M0 block scale [NVFP4 如何用 4 bit 实现高精度,
+# sections 2.4, 3.2, 5.1, 5.5]. Codes are packed two per byte, element 2i in
+# the low nibble.
+# ---------------------------------------------------------------------------
+E2M1 = 2
+
+
+def e2m1_grid():
+    f = load_golden("e2m1_page_facts.json")
+    return np.array(f["positive_values"]), f
+
+
+def unpack4(q):
+    """[R, C/2] packed bytes -> [R, C] codes (low nibble first)."""
+    out = np.empty((q.shape[0], q.shape[1] * 2), np.uint8)
+    out[:, 0::2] = q & 0xF
+    out[:, 1::2] = q >> 4
+    return out
+
+
+def test_e2m1_value_table_and_mxfp4_size(oracle):
+    grid, f = e2m1_grid()
+    vals = [oracle.decode(E2M1, c) for c in range(16)]
+    assert vals[:8] == list(grid)                      # codes 0..7: the page's magnitudes, in order
+    assert vals[8:] == [-v for v in grid]              # bit 3 is the sign (code 8 is -0)
+    assert math.copysign(1.0, vals[8]) == -1.0
+    assert max(vals) == f["max_finite"] and vals[1] == f["min_subnormal"] and vals[2] == f["min_normal"]
+    # exponent field 0 is subnormal (0.m); otherwise (1 + m/2) * 2^(e - bias)
+    for c in range(8):
+        e, m = c >> 1, c & 1
+        want = 0.5 * m if e == 0 else (1 + m / 2) * 2.0 ** (e - f["exponent_bias"])
+        assert vals[c] == want
+    for c in range(16):
+        assert oracle.encode(E2M1, vals[c]) == c     # round trip, -0 included
+    # 4.25 bits per element: 32 half-byte codes + one scale byte per block
+    q, s = oracle.quantize_rows(np.ones((1, 32), np.float32), E2M1)
+    assert (q.nbytes + s.nbytes) * 8 / 32 == f["mxfp4"]["bits_per_element"]
+
+
+def test_e2m1_page_examples(oracle):
+    _, f = e2m1_grid()
+    ex = f["rounding_example"]
+    c = oracle.encode(E2M1, ex["x"])
+    assert oracle.decode(E2M1, c) == ex["q"]
+    assert abs(ex["x"] - ex["q"]) == pytest.approx(ex["abs_error"])
+    assert round(100 * abs(ex["x"] - ex["q"]) / ex["x"], 1) == ex["relative_error_percent"]
+    # one shared scale s = 5 for the outlier and the small weights: 0.1 / 5 rounds to 0
+    sh = f["shared_scale_example"]
+    assert oracle.decode(E2M1, oracle.encode(E2M1, sh["small"] / sh["shared_scale"])) == sh["small_quantized"]
+    # MXFP4 blocks (scale 2^(floor(log2 amax) - 2)): sharing a block with the
+    # outlier the small weights still flush; in a block of their own they do not
+    blk = np.full((2, 32), sh["small"], np.float32)
+    blk[0, 0] = sh["outlier"]
+    q, s = oracle.quantize_rows(blk, E2M1)
+    codes = unpack4(q)
+    assert s[0, 0] == 127 + 4 - 2 and np.all(codes[0, 1:] == 0)
+    assert s[1, 0] == 127 - 4 - 2 and np.all(codes[1] != 0)
+    # the outlier 30 / 4 = 7.5 lies past 6: it saturates (the floor rule clips)
+    assert codes[0, 0] == 0x7
+
+
+def test_e2m1_packing_and_dequantize(oracle):
+    # amax 6 -> scale code 127 (s = 1); element 2i in the low nibble
+    x = np.array([[1.0, 6.0, -0.5, 3.0] + [0.0] * 28], np.float32)
+    q, s = oracle.quantize_rows(x, E2M1)
+    assert s[0, 0] == 127 and q.shape == (1, 16)
+    assert q[0, 0] == 0x72 and q[0, 1] == 0x59        # (1.0 -> 0x2, 6.0 -> 0x7), (-0.5 -> 0x9, 3.0 -> 0x5)
+    grid, _ = e2m1_grid()
+    table = np.concatenate([grid, -grid])
+    xs = inputs.normal_bf16(95, (8, 64))
+    q, s = oracle.quantize_rows(xs, E2M1)
+    want = table[unpack4(q)] * np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+    assert np.array_equal(oracle.dequantize(q, s, E2M1, "f32").astype(np.float64), want)
+    # colwise = rowwise of the transpose, packed along the (new) rows
+    qt, st = oracle.quantize_cols(xs.T.copy(), E2M1)
+    assert np.array_equal(qt, q) and np.array_equal(st, s)
+
+
+def test_e2m1_encode_matches_nearest_grid_value_for_all_bf16_and_scales(oracle):
+    """Every finite bf16 value under every scale code: the element code is the
+    nearest value of the page's grid (ties to the even code), clamped at 6."""
+    grid, _ = e2m1_grid()
+    bits = np.arange(0x7F80, dtype=np.uint16)  # the finite non-negative bf16 patterns
+    mag = inputs.bf16_bits_to_f32(bits).astype(np.float64)
+    keep = np.isfinite(mag)
+    bits, mag = bits[keep], mag[keep]
+    rows, expect, scales = [], [], []
+    for c in range(0, 127 + 127 - 2 + 1):
+        anchor = 2.0 ** (c - 127 + 2)
+        sel = bits[mag < 2 * anchor]
+        sel = np.concatenate([sel, sel | np.uint16(0x8000)])
+        pad = (-len(sel)) % 31
+        sel = np.concatenate([sel, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        anc = np.full((sel.shape[0], 1), inputs.f32_to_bf16_bits(np.float32([anchor]))[0], np.uint16)
+        blk = np.concatenate([anc, sel], axis=1)
+        rows.append(blk)
+        y = inputs.bf16_bits_to_f32(blk).astype(np.float64) / 2.0 ** (c - 127)
+        a = np.abs(y)
+        hi = np.clip(np.searchsorted(grid, a), 1, len(grid) - 1)
+        lo = hi - 1
+        take_hi = (grid[hi] - a < a - grid[lo]) | ((grid[hi] - a == a - grid[lo]) & (hi % 2 == 0))
+        idx = np.where(a >= grid[-1], len(grid) - 1, np.where(take_hi, hi, lo))
+        expect.append((idx | np.where(np.signbit(y), 8, 0)).astype(np.uint8))
+        scales.append(np.full(blk.shape[0], c, np.uint8))
+    x = np.concatenate(rows)
+    q, s = oracle.quantize_rows(x, E2M1)
+    assert np.array_equal(s[:, 0], np.concatenate(scales))
+    got, exp = unpack4(q), np.concatenate(expect)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, "first mismatch at %s: code %#x expected %#x" % (bad[0], got[tuple(bad[0])], exp[tuple(bad[0])])
+
+
+def test_e2m1_scale_rule_edges(oracle):
+    for bad in (np.nan, np.inf):
+        x = np.ones((1, 32), np.float32)
+        x[0, 3] = bad
+        q, s = oracle.quantize_rows(x, E2M1)
+        assert s[0, 0] == 0xFF and not q.any()          # no NaN code in E2M1: the scale carries it
+    big = np.full((1, 32), 2.0 ** 127, np.float32)
+    _, s = oracle.quantize_rows(big, E2M1)
+    assert s[0, 0] == 127 + 127 - 2
+    q, s = oracle.quantize_rows(np.full((1, 32), 7.0, np.float32), E2M1)
+    assert s[0, 0] == 127 and np.all(unpack4(q) == 0x7)   # 7 / 1 saturates to 6
+
+
+@pytest.mark.parametrize("afmt,bfmt", [(E2M1, E2M1), (E4M3, E2M1)])
+def test_e2m1_gemm_unit_scales_and_exact_sum(oracle, afmt, bfmt):
+    grid, _ = e2m1_grid()
+    t4 = np.concatenate([grid, -grid])
+    g = inputs.rng(97 + afmt)
+    M, N, K = 12, 20, 128
+    codes_b = g.integers(0, 16, (N, K), dtype=np.uint8)
+    b = (codes_b[:, 0::2] | (codes_b[:, 1::2] << 4)).astype(np.uint8)
+    if afmt == E2M1:
+        codes_a = g.integers(0, 16, (M, K), dtype=np.uint8)
+        a = (codes_a[:, 0::2] | (codes_a[:, 1::2] << 4)).astype(np.uint8)
+        A = t4[codes_a]
+    else:
+        a = g.integers(0, 0x7E, (M, K), dtype=np.uint8)
+        A = np.array([[value_of(int(c), E4M3) for c in row] for row in a], dtype=np.float64)
+    B = t4[codes_b]
+    ones_a = np.full((M, K // 32), 127, np.uint8)
+    ones_b = np.full((N, K // 32), 127, np.uint8)
+    y, t = oracle.gemm(a, ones_a, afmt, b, ones_b, bfmt)
+    assert np.array_equal(y, A @ B.T) and np.array_equal(t, np.abs(A) @ np.abs(B).T)
+    # per-block scales stay inside the sum over blocks
+    sa = g.integers(110, 140, (M, K // 32), dtype=np.uint8)
+    sb = g.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    y, _ = oracle.gemm(a, sa, afmt, b, sb, bfmt)
+    SA = np.repeat(np.exp2(sa.astype(np.float64) - 127), 32, axis=1)
+    SB = np.repeat(np.exp2(sb.astype(np.float64) - 127), 32, axis=1)
+    for m in range(M):
+        for n in range(N):
+            terms = [Fraction(A[m, k]) * Fraction(SA[m, k]) * Fraction(B[n, k]) * Fraction(SB[n, k]) for k in range(K)]
+            assert abs(Fraction(y[m, n]) - sum(terms)) <= Fraction(2) ** -50 * sum(abs(x) for x in terms)
