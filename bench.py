@@ -35,6 +35,7 @@ METRIC = "MXFP8 GEMM TFLOP/s @8192³ + quantize GB/s, each as % of MI355X peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 matrix peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 / MXFP4 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_8192_quantize_8192x4096.json")
 GEMM_SOURCE = os.path.join(ROOT, "microscaling_block_scaled_amd", "csrc", "gemm.hip")
 QUANT_SOURCE = os.path.join(ROOT, "microscaling_block_scaled_amd", "csrc", "quantize.hip")
@@ -352,6 +353,29 @@ def other_rows(torch, mx, inputs, np, flush, stream, steps, kv_only=False):
     out["dequantize_bf16"] = {"us": round(ms * 1e3, 2), "GB/s": round(dq_bytes / ms / 1e6, 1),
                               "frac_of_hbm_peak": round(dq_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
                               "algorithmic_bytes": dq_bytes}
+    # MXFP4: the quantize input to E2M1 rowwise, and the 8192^3 product of
+    # the GEMM workload's inputs quantized to E2M1 (bf16 out)
+    log("mxfp4 rows")
+    Xq = dev_bf16(torch, xq)
+    q4 = torch.empty((Xq.shape[0], Xq.shape[1] // 2), dtype=torch.uint8, device="cuda")
+    s4 = torch.empty((Xq.shape[0], Xq.shape[1] // 32), dtype=torch.uint8, device="cuda")
+    ms = timed("quantize_mxfp4", lambda: mx.mx_quantize(Xq, mx.MX_E2M1, q=q4, s=s4))
+    q4_bytes = 2 * Xq.numel() + Xq.numel() // 2 + Xq.numel() // 32
+    out["quantize_mxfp4_rowwise"] = {"us": round(ms * 1e3, 2), "GB/s": round(q4_bytes / ms / 1e6, 1),
+                                     "frac_of_hbm_peak": round(q4_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                     "algorithmic_bytes": q4_bytes}
+    del Xq, q4, s4
+    xa, xb = inputs.gemm_inputs()
+    A4, SA4 = mx.mx_quantize(dev_bf16(torch, xa), mx.MX_E2M1)
+    B4, SB4 = mx.mx_quantize(dev_bf16(torch, xb), mx.MX_E2M1)
+    del xa, xb
+    Y4 = torch.empty((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    ms = timed("gemm_mxfp4", lambda: mx.mx_gemm(A4, SA4, B4, SB4, a_fmt=mx.MX_E2M1, b_fmt=mx.MX_E2M1, y=Y4))
+    tf = 2.0 * 8192 ** 3 / ms / 1e9
+    out["gemm_mxfp4_8192"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                              "frac_of_fp4_peak": round(tf / MFMA_FP4_PEAK_TFLOPS, 4),
+                              "shape": [8192, 8192, 8192], "operands": "E2M1 x E2M1, bf16 out"}
+    del A4, SA4, B4, SB4, Y4
     del q, s, yd
     # training linear layer: fwd (E4M3 x E4M3, K = 4096) and dgrad (E5M2 x E4M3, K = 14336)
     log("training rows")

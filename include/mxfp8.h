@@ -61,8 +61,15 @@ typedef int32_t mx_status_t;
 #define MX_ERR_HIP    -6 /* the HIP runtime reported an error at launch */
 
 /* Element encodings [SM120 §0.1 table; GLOSS]: E4M3 (448 max, used for
- * activations and weights), E5M2 (57344 max, used for gradients). */
-typedef enum { MX_E4M3 = 0, MX_E5M2 = 1 } mx_fmt_t;
+ * activations and weights), E5M2 (57344 max, used for gradients).
+ * MX_E2M1 is the MXFP4 element [NVFP4 §2.4, §5.5]: values 0, +-0.5, +-1,
+ * +-1.5, +-2, +-3, +-4, +-6, the same E8M0 scale per 32 (rule with
+ * emax_elem = 2; a NaN/Inf block gets scale 0xFF and codes 0, E2M1 having no
+ * NaN). Its codes are packed two per byte, element 2i in the low nibble, so
+ * a row of `cols` elements holds cols/2 bytes and pitches stay in bytes.
+ * E2M1 is accepted by mx_quantize, mx_dequantize and mx_gemm (see there);
+ * the other entry points return MX_ERR_FORMAT for it. */
+typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2 } mx_fmt_t;
 /* High-precision data types of inputs and outputs. */
 typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype_t;
 
@@ -72,7 +79,7 @@ typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype_t;
  * find amax, choose a power-of-two E8M0 scale, round x / scale to FP8.
  *
  *   x    [rows x cols] input (xdt), pitch ldx >= cols
- *   q    [rows x cols] codes out, pitch ldq >= cols
+ *   q    [rows x cols] codes out, pitch ldq >= cols (E2M1: cols/2 bytes per row)
  *   s    [rows x cols/32] scales out, pitch lds >= cols/32
  * cols % 32 == 0.
  */
@@ -101,7 +108,8 @@ mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int
  * whole block NaN; NaN results are written as the canonical quiet NaN
  * (0x7FC00000 / 0x7FC0).
  *
- *   q    [rows x cols] codes, pitch ldq;  s [rows x cols/32] scales, pitch lds
+ *   q    [rows x cols] codes, pitch ldq (E2M1: cols/2 bytes per row);
+ *        s [rows x cols/32] scales, pitch lds
  *   y    [rows x cols] output (ydt), pitch ldy
  * cols % 32 == 0.
  */
@@ -172,6 +180,13 @@ mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_t dt, int64
  *   MX_ACCUM_AUTO -- MX_ACCUM_FP8 when both operands are E4M3 and K >= 2048,
  *                    where the grouped error stays far below 1e-5 * sum|a b|
  *                    for data of Gaussian-like spread; MX_ACCUM_FP32 otherwise.
+ *
+ * MXFP4 (a_fmt = b_fmt = MX_E2M1; codes packed two per byte, lda/ldb in bytes
+ * >= K/2): the scaled matrix instruction on the E2M1 codes (accum AUTO or
+ * FP8; FP32 is rejected with MX_ERR_FORMAT), on the large-tile kernel only:
+ * K % 1024 == 0, M >= 256, N >= 256, no page table, 16-byte aligned code and
+ * scale rows (MX_ERR_SHAPE / MX_ERR_ALIGN otherwise). E2M1 mixed with an FP8
+ * format returns MX_ERR_FORMAT.
  */
 typedef enum { MX_ACCUM_AUTO = 0, MX_ACCUM_FP8 = 1, MX_ACCUM_FP32 = 2 } mx_accum_t;
 

@@ -11,15 +11,17 @@ Layouts (row-major, unit stride along the last dimension):
   * codes  uint8 [rows, cols]; E8M0 scales uint8 [rows, cols/32];
   * mx_quantize_colwise returns the codes and scales of X^T (blocks down the
     columns of X), i.e. [cols, rows] and [cols, rows/32];
-  * mx_gemm(a, sa, b, sb) computes y = A * B^T for A [M, K], B [N, K].
+  * mx_gemm(a, sa, b, sb) computes y = A * B^T for A [M, K], B [N, K];
+  * MX_E2M1 (MXFP4) codes are packed two per byte, so their arrays are
+    [rows, cols/2]; K is then taken from the scales.
 """
 import ctypes
 
-from ._lib import (BLOCK, MX_ACCUM_AUTO, MX_ACCUM_FP8, MX_ACCUM_FP32, MX_BF16, MX_E4M3, MX_E5M2, MX_F32, MXError,
+from ._lib import (BLOCK, MX_ACCUM_AUTO, MX_ACCUM_FP8, MX_ACCUM_FP32, MX_BF16, MX_E2M1, MX_E4M3, MX_E5M2, MX_F32, MXError,
                    check, lib, mx_attention_desc_t, mx_gemm_desc_t)
 
 __all__ = [
-    "MX_E4M3", "MX_E5M2", "MX_F32", "MX_BF16", "BLOCK", "MXError",
+    "MX_E4M3", "MX_E5M2", "MX_E2M1", "MX_F32", "MX_BF16", "BLOCK", "MXError",
     "MX_ACCUM_AUTO", "MX_ACCUM_FP8", "MX_ACCUM_FP32",
     "mx_quantize", "mx_quantize_colwise", "mx_dequantize", "mx_kv_quant_write", "mx_gemm",
     "mx_gemm_desc", "mx_paged_scores", "mx_paged_attention", "mx_status_string", "mx_query_support",
@@ -66,11 +68,13 @@ def _ld(t):
 
 
 def mx_quantize(x, fmt=MX_E4M3, q=None, s=None, stream=None):
-    """Rowwise MXFP8 quantization of x [rows, cols] -> (codes, scales)."""
+    """Rowwise MX quantization of x [rows, cols] -> (codes, scales); E2M1
+    codes are [rows, cols/2] (two per byte)."""
     torch = _torch()
     _rowmajor(x, "x")
     rows, cols = x.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    cb = cols // 2 if fmt == MX_E2M1 else cols
+    q = torch.empty((rows, cb), dtype=torch.uint8, device=x.device) if q is None else q
     s = torch.empty((rows, cols // BLOCK), dtype=torch.uint8, device=x.device) if s is None else s
     check("mx_quantize", lib().mx_quantize(_p(x), _dtype_code(x), rows, cols, _ld(x), fmt, _p(q), _ld(q),
                                            _p(s), _ld(s), _stream(stream)))
@@ -95,7 +99,7 @@ def mx_dequantize(q, s, fmt=MX_E4M3, out_dtype=None, y=None, stream=None):
     """x_hat = scale * code -> y [rows, cols] in float32 or bfloat16."""
     torch = _torch()
     _rowmajor(q, "q")
-    rows, cols = q.shape
+    rows, cols = q.shape[0], s.shape[1] * BLOCK
     if y is None:
         y = torch.empty((rows, cols), dtype=out_dtype or torch.float32, device=q.device)
     check("mx_dequantize", lib().mx_dequantize(_p(q), _ld(q), _p(s), _ld(s), fmt, rows, cols, _p(y),
@@ -138,9 +142,11 @@ def mx_gemm(a, sa, b, sb, a_fmt=MX_E4M3, b_fmt=MX_E4M3, out_dtype=None, y=None, 
     torch = _torch()
     for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
         _rowmajor(t, n)
-    M, K = a.shape
-    N = b.shape[0]
-    if b.shape[1] != K or sa.shape != (M, K // BLOCK) or sb.shape != (N, K // BLOCK):
+    M, N = a.shape[0], b.shape[0]
+    K = sa.shape[1] * BLOCK
+    kb_a = K // 2 if a_fmt == MX_E2M1 else K
+    kb_b = K // 2 if b_fmt == MX_E2M1 else K
+    if a.shape[1] != kb_a or b.shape[1] != kb_b or sb.shape != (N, K // BLOCK):
         raise ValueError("shape mismatch: a %s sa %s b %s sb %s" % (tuple(a.shape), tuple(sa.shape), tuple(b.shape),
                                                                     tuple(sb.shape)))
     if y is None:

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(HERE, "libmxfp8.so")
 MX_OK = 0
 MX_E4M3 = 0
 MX_E5M2 = 1
+MX_E2M1 = 2  # MXFP4: codes packed two per byte, element 2i in the low nibble
 MX_F32 = 0
 MX_BF16 = 1
 MX_ACCUM_AUTO = 0

@@ -1,7 +1,8 @@
 // dequant.hip -- x_hat = s_b * q_i [MXFP8 SM120 software support, §0.1]:
-// FP8 codes times the block's E8M0 scale, exact in f32, written as f32 or as
-// bf16 rounded to nearest even. HBM-bound: each thread turns 16 codes (one
-// 16-byte load, half a block) into 64 bytes of f32 or 32 bytes of bf16.
+// FP8 (or packed E2M1) codes times the block's E8M0 scale, exact in f32,
+// written as f32 or as bf16 rounded to nearest even. HBM-bound: each thread
+// turns 16 codes (half a block: 16 bytes, or 8 for E2M1) into 64 bytes of f32
+// or 32 bytes of bf16.
 #include "mx_common.hpp"
 
 namespace {
@@ -28,16 +29,34 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
   if (g >= nchunks) return;
   const uint32_t row = per_row.div(g);
   const uint32_t c16 = g - row * per_row.d;
-  const uint4 codes = *(const uint4*)(q + (int64_t)row * ldq + (int64_t)c16 * 16);
   const uint32_t sc = s[(int64_t)row * lds + c16 / 2];
   // 2^(sc - 127) as an f32; code 0 is the subnormal 2^-127
   const float scale = __uint_as_float(sc ? (sc << 23) : 0x00400000u);
   float v[16];
-  const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
+  if constexpr (FMT == MX_E2M1) {
+    // 16 codes are 8 bytes; byte i holds elements 2i (low nibble) and 2i + 1
+    const uint2 codes = *(const uint2*)(q + (int64_t)row * ldq + (int64_t)c16 * 8);
+    const v2f32 d[8] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, scale, 0),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, scale, 1),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, scale, 2),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.x, scale, 3),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.y, scale, 0),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.y, scale, 1),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.y, scale, 2),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes.y, scale, 3)};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v2f32 lo = decode2<FMT>(w[i], scale, false), hi = decode2<FMT>(w[i], scale, true);
-    v[4 * i] = lo[0]; v[4 * i + 1] = lo[1]; v[4 * i + 2] = hi[0]; v[4 * i + 3] = hi[1];
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = d[i][0];
+      v[2 * i + 1] = d[i][1];
+    }
+  } else {
+    const uint4 codes = *(const uint4*)(q + (int64_t)row * ldq + (int64_t)c16 * 16);
+    const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v2f32 lo = decode2<FMT>(w[i], scale, false), hi = decode2<FMT>(w[i], scale, true);
+      v[4 * i] = lo[0]; v[4 * i + 1] = lo[1]; v[4 * i + 2] = hi[0]; v[4 * i + 3] = hi[1];
+    }
   }
   const bool nan_block = sc == 0xFFu;
 #pragma unroll
@@ -62,9 +81,10 @@ extern "C" mx_status_t mx_dequantize(const uint8_t* q, int64_t ldq, const uint8_
                                      int64_t rows, int64_t cols, void* y, mx_dtype_t ydt, int64_t ldy,
                                      hipStream_t stream) {
   if (!q || !s || !y) return MX_ERR_NULL;
-  if (fmt != MX_E4M3 && fmt != MX_E5M2) return MX_ERR_FORMAT;
+  if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1) return MX_ERR_FORMAT;
   if (ydt != MX_F32 && ydt != MX_BF16) return MX_ERR_FORMAT;
-  if (rows < 0 || cols < 0 || cols % kBlock != 0 || ldq < cols || lds < cols / kBlock || ldy < cols)
+  if (rows < 0 || cols < 0 || cols % kBlock != 0 || ldq < (fmt == MX_E2M1 ? cols / 2 : cols) ||
+      lds < cols / kBlock || ldy < cols)
     return MX_ERR_SHAPE;
   const int64_t esz = ydt == MX_F32 ? 4 : 2;
   if (!mx_host::aligned16(q) || ldq % 16 != 0 || !mx_host::aligned16(y) || (ldy * esz) % 16 != 0)
@@ -83,7 +103,12 @@ extern "C" mx_status_t mx_dequantize(const uint8_t* q, int64_t ldq, const uint8_
     const uint8_t* qq = q + r0 * ldq;
     const uint8_t* ss = s + r0 * lds;
     void* yy = (uint8_t*)y + r0 * ldy * esz;
-    if (fmt == MX_E5M2) {
+    if (fmt == MX_E2M1) {
+      if (ydt == MX_BF16)
+        hipLaunchKernelGGL((dequant_kernel<MX_E2M1, true>), grid, dim3(kThreads), 0, stream, qq, ldq, ss, lds, yy, ldy, n, per_row);
+      else
+        hipLaunchKernelGGL((dequant_kernel<MX_E2M1, false>), grid, dim3(kThreads), 0, stream, qq, ldq, ss, lds, yy, ldy, n, per_row);
+    } else if (fmt == MX_E5M2) {
       if (ydt == MX_BF16)
         hipLaunchKernelGGL((dequant_kernel<MX_E5M2, true>), grid, dim3(kThreads), 0, stream, qq, ldq, ss, lds, yy, ldy, n, per_row);
       else

@@ -35,6 +35,8 @@ using namespace mx;
 
 constexpr int kModeFP8 = 0;
 constexpr int kModeBF16 = 1;
+constexpr int kModeFP4 = 2;  // both operands E2M1 (MXFP4), large-tile kernel only
+constexpr int kMfmaFP4 = 4;  // the f8f6f4 instructions' format code for E2M1
 
 constexpr int kThreads = 256;
 constexpr int kBK = 128;  // K bytes per step = 4 MX blocks
@@ -438,6 +440,15 @@ __global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uin
 // dealt round-robin to the 8 XCDs, so tile ids are remapped to give each XCD
 // a contiguous band of tiles (shared panels stay in that XCD's L2).
 // Requires K % 512 == 0 and 16-byte aligned scale rows.
+//
+// FP4 mode (both operands MXFP4, codes two per byte): a 128-byte stage holds
+// 256 K. For E2M1 the instruction takes 16 bytes per lane, k = 32g .. 32g+31
+// of its 64 (checked on the device), so the two 16-byte chunks a lane reads
+// for a K half are the operands of two instructions (the upper half of each
+// 8-register operand is left undefined and the compiler narrows it to 4
+// registers). A stage has 8 scale blocks, so a group of 4 stages needs 32
+// scale bytes per row: the second 16 go to a second pair of buffers. Requires
+// K % 1024 == 0.
 // ---------------------------------------------------------------------------
 constexpr int kFBM = 256, kFBN = 256, kFBK = 128;
 constexpr uint32_t kCodeStage = kFBM * kFBK;   // bytes per operand per stage
@@ -450,6 +461,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t Bs[2][kCodeStage];
   __shared__ __attribute__((aligned(16))) uint8_t sAs[2][kScaleBuf];
   __shared__ __attribute__((aligned(16))) uint8_t sBs[2][kScaleBuf];
+  constexpr bool kFP4 = MODE == kModeFP4;
+  __shared__ __attribute__((aligned(16))) uint8_t sAs2[2][kFP4 ? kScaleBuf : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t sBs2[2][kFP4 ? kScaleBuf : 16];
 
   // ---- tile id: XCD-contiguous bands, then groups of 4 tile rows
   const uint32_t ntiles = g.tiles_m * g.tiles_n;
@@ -473,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int64_t nsteps = g.K / kFBK;  // a multiple of 4
+  const int64_t nsteps = (kFP4 ? g.K / 2 : g.K) / kFBK;  // a multiple of 4
 
   // ---- loads. Codes: per stage and operand, 8 instructions per wave, each
   // 8 rows x 128 bytes (lane i: row i / 8, LDS chunk i % 8, which holds the
@@ -499,6 +513,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   const uint32_t a_dst = lds_off(&As[0][0]) + wave * 64 * kFBK, b_dst = lds_off(&Bs[0][0]) + wave * 64 * kFBK;
   const uint32_t sa_dst = lds_off(&sAs[0][0]) + wave * 64 * kScaleRow;
   const uint32_t sb_dst = lds_off(&sBs[0][0]) + wave * 64 * kScaleRow;
+  const uint32_t sa2_dst = lds_off(&sAs2[0][0]) + (kFP4 ? wave * 64 * kScaleRow : 0);
+  const uint32_t sb2_dst = lds_off(&sBs2[0][0]) + (kFP4 ? wave * 64 * kScaleRow : 0);
   // codes of stage `src` into LDS buffer `buf`
   auto issue_codes = [&](int64_t src, uint32_t buf) {
     const uint8_t* ab = a_base + src * kFBK;
@@ -521,8 +537,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   };
   auto issue_scales = [&](int64_t grp) {
     const uint32_t buf = (uint32_t)(grp & 1);
-    dma16(sa_dst + buf * kScaleBuf, sa_off, sa_base + grp * kScaleRow);
-    dma16(sb_dst + buf * kScaleBuf, sb_off, sb_base + grp * kScaleRow);
+    constexpr uint32_t gbytes = kFP4 ? 2 * kScaleRow : kScaleRow;  // scale bytes per row per group
+    dma16(sa_dst + buf * kScaleBuf, sa_off, sa_base + grp * gbytes);
+    dma16(sb_dst + buf * kScaleBuf, sb_off, sb_base + grp * gbytes);
+    if constexpr (kFP4) {
+      dma16(sa2_dst + buf * kScaleBuf, sa_off, sa_base + grp * gbytes + kScaleRow);
+      dma16(sb2_dst + buf * kScaleBuf, sb_off, sb_base + grp * gbytes + kScaleRow);
+    }
   };
 
   // ---- fragment reads: lane (lr, lg) of fragment f reads row base + 32 f;
@@ -535,6 +556,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   const uint8_t* b_row = &Bs[0][0] + (wn * 128 + lr) * kFBK;
   const uint8_t* a_sc = &sAs[0][0] + (wm * 128 + lr) * kScaleRow;
   const uint8_t* b_sc = &sBs[0][0] + (wn * 128 + lr) * kScaleRow;
+  const uint8_t* a_sc2 = &sAs2[0][0] + (kFP4 ? (wm * 128 + lr) * kScaleRow : 0);
+  const uint8_t* b_sc2 = &sBs2[0][0] + (kFP4 ? (wn * 128 + lr) * kScaleRow : 0);
   // K half h of a stage: logical chunks 4h + lg and 4h + 2 + lg
   const uint32_t c_lo[2] = {((0 + lg) ^ fp) << 4, ((4 + lg) ^ fp) << 4};
   const uint32_t c_hi[2] = {((2 + lg) ^ fp) << 4, ((6 + lg) ^ fp) << 4};
@@ -547,28 +570,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   // instruction reads byte 0).
   // (FP32-accumulation mode: no shift; the lane needs both blocks 2h and
   // 2h + 1, found in bytes 0 and 1 of the word shifted right by 16 h.)
+  // (FP4 mode: the group's 32 bytes are words 0-3 here and 4-7 in the second
+  // buffer; stage w uses words 2w and 2w + 1, K half h word 2w + h, whose
+  // byte 0 (after the shift by 8 lg) is the scale of the half's first
+  // instruction and byte 2 that of its second.)
   uint4 sa4[4], sb4[4];
+  uint4 sa4h[kFP4 ? 4 : 1], sb4h[kFP4 ? 4 : 1];
   auto read_scales = [&](int sbuf) {
-    const uint32_t sh = MODE == kModeFP8 ? 8 * lg : 0;
+    const uint32_t sh = MODE != kModeBF16 ? 8 * lg : 0;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       uint4 va = *(const uint4*)(a_sc + sbuf * kScaleBuf + f * 32 * kScaleRow);
       uint4 vb = *(const uint4*)(b_sc + sbuf * kScaleBuf + f * 32 * kScaleRow);
       sa4[f] = make_uint4(va.x >> sh, va.y >> sh, va.z >> sh, va.w >> sh);
       sb4[f] = make_uint4(vb.x >> sh, vb.y >> sh, vb.z >> sh, vb.w >> sh);
+      if constexpr (kFP4) {
+        uint4 wa = *(const uint4*)(a_sc2 + sbuf * kScaleBuf + f * 32 * kScaleRow);
+        uint4 wb = *(const uint4*)(b_sc2 + sbuf * kScaleBuf + f * 32 * kScaleRow);
+        sa4h[f] = make_uint4(wa.x >> sh, wa.y >> sh, wa.z >> sh, wa.w >> sh);
+        sb4h[f] = make_uint4(wb.x >> sh, wb.y >> sh, wb.z >> sh, wb.w >> sh);
+      }
     }
   };
-  auto scale_of = [&](const uint4& w4, int sub, int h) -> int {
-    const uint32_t w = sub == 0 ? w4.x : sub == 1 ? w4.y : sub == 2 ? w4.z : w4.w;
-    return (int)(w >> (16 * h));
+  auto word_of = [&](const uint4& w4, int k) -> uint32_t {
+    return k == 0 ? w4.x : k == 1 ? w4.y : k == 2 ? w4.z : w4.w;
   };
-  auto read_frag = [&](const uint8_t* row_base, const uint4* s4, int buf, int sub, int h, int f, v8i32& fr,
-                       int& sc) {
+  auto scale_of = [&](const uint4* s4, const uint4* s4h, int f, int sub, int h) -> int {
+    if constexpr (kFP4) {
+      const int w = 2 * sub + h;
+      return (int)(w < 4 ? word_of(s4[f], w) : word_of(s4h[f], w - 4));
+    } else {
+      return (int)(word_of(s4[f], sub) >> (16 * h));
+    }
+  };
+  auto read_frag = [&](const uint8_t* row_base, const uint4* s4, const uint4* s4h, int buf, int sub, int h, int f,
+                       v8i32& fr, int& sc) {
     const uint8_t* r = row_base + buf * kCodeStage + f * 32 * kFBK;
     const uint4 lo = *(const uint4*)(r + c_lo[h]);
     const uint4 hi = *(const uint4*)(r + c_hi[h]);
     fr = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    sc = scale_of(s4[f], sub, h);
+    sc = scale_of(s4, s4h, f, sub, h);
   };
 
   v16f32 acc[4][4];
@@ -591,14 +632,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   // k positions in A and B), decoded exactly to bf16 with the block scale
   // folded in (blocks 2h for t < 2, 2h + 1 after), then 16
   // v_mfma_f32_32x32x16_bf16; each decoded B fragment feeds 4 of them.
+  // FP4 mode: the two instructions of a K half, on the lower and upper
+  // 16 bytes of each fragment
+  auto mfma_fp4 = [&](int set, int i, int j) {
+    const v8i32 a_lo = __builtin_shufflevector(fa[set][i], fa[set][i], 0, 1, 2, 3, -1, -1, -1, -1);
+    const v8i32 a_hi = __builtin_shufflevector(fa[set][i], fa[set][i], 4, 5, 6, 7, -1, -1, -1, -1);
+    const v8i32 b_lo = __builtin_shufflevector(fb[set][j], fb[set][j], 0, 1, 2, 3, -1, -1, -1, -1);
+    const v8i32 b_hi = __builtin_shufflevector(fb[set][j], fb[set][j], 4, 5, 6, 7, -1, -1, -1, -1);
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b_lo, a_lo, acc[i][j], kMfmaFP4, kMfmaFP4, 0,
+                                                                 sb[set][j], 0, sa[set][i]);
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b_hi, a_hi, acc[i][j], kMfmaFP4, kMfmaFP4, 0,
+                                                                 sb[set][j] >> 16, 0, sa[set][i] >> 16);
+  };
   auto mfma_pair = [&](int set, int i, int j0) {
 #pragma unroll
-    for (int j = j0; j < j0 + 2; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], BFMT, AFMT, 0,
-                                                                   sb[set][j], 0, sa[set][i]);
+    for (int j = j0; j < j0 + 2; ++j) {
+      if constexpr (kFP4)
+        mfma_fp4(set, i, j);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], BFMT, AFMT, 0,
+                                                                     sb[set][j], 0, sa[set][i]);
+    }
   };
   auto mfma_group = [&](int set, int i) {
-    if constexpr (MODE == kModeFP8) {
+    if constexpr (kFP4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mfma_fp4(set, i, j);
+    } else if constexpr (MODE == kModeFP8) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], BFMT, AFMT, 0,
@@ -637,8 +697,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   read_scales(0);
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
-    read_frag(a_row, sa4, 0, 0, 0, f, fa[0][f], sa[0][f]);
-    read_frag(b_row, sb4, 0, 0, 0, f, fb[0][f], sb[0][f]);
+    read_frag(a_row, sa4, sa4h, 0, 0, 0, f, fa[0][f], sa[0][f]);
+    read_frag(b_row, sb4, sb4h, 0, 0, 0, f, fb[0][f], sb[0][f]);
   }
 
   for (int64_t s0 = 0; s0 < nsteps; s0 += 4) {
@@ -649,8 +709,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
       // ---- first half: MFMAs on set 0; set 1 <- second half of stage s
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        read_frag(a_row, sa4, buf, u, 1, i, fa[1][i], sa[1][i]);
-        read_frag(b_row, sb4, buf, u, 1, i, fb[1][i], sb[1][i]);
+        read_frag(a_row, sa4, sa4h, buf, u, 1, i, fa[1][i], sa[1][i]);
+        read_frag(b_row, sb4, sb4h, buf, u, 1, i, fb[1][i], sb[1][i]);
         mfma_group(0, i);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -669,9 +729,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
       const int nbuf = buf ^ 1, nsub = (u + 1) & 3;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        read_frag(a_row, sa4, nbuf, nsub, 0, i, fa[0][i], sa[0][i]);
-        read_frag(b_row, sb4, nbuf, nsub, 0, i, fb[0][i], sb[0][i]);
-        if constexpr (MODE == kModeFP8) {
+        read_frag(a_row, sa4, sa4h, nbuf, nsub, 0, i, fa[0][i], sa[0][i]);
+        read_frag(b_row, sb4, sb4h, nbuf, nsub, 0, i, fb[0][i], sb[0][i]);
+        if constexpr (MODE != kModeBF16) {
           // the loads go out between two pairs of MFMAs, so the matrix unit
           // has queued work while the wave issues them
           mfma_pair(1, i, 0);
@@ -757,10 +817,14 @@ mx_status_t launch_big(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out
   hipLaunchKernelGGL((gemm_big_kernel<AF, BF, OUT, MODE>), grid, dim3(kThreads), 0, st, g)
 #define MX_BIG_OUT(AF, BF) \
   do { if (bf16out) MX_BIG_LAUNCH(AF, BF, true); else MX_BIG_LAUNCH(AF, BF, false); } while (0)
-  if (af == MX_E4M3 && bf == MX_E4M3) MX_BIG_OUT(MX_E4M3, MX_E4M3);
-  else if (af == MX_E5M2 && bf == MX_E4M3) MX_BIG_OUT(MX_E5M2, MX_E4M3);
-  else if (af == MX_E4M3 && bf == MX_E5M2) MX_BIG_OUT(MX_E4M3, MX_E5M2);
-  else MX_BIG_OUT(MX_E5M2, MX_E5M2);
+  if constexpr (MODE == kModeFP4) {
+    MX_BIG_OUT(MX_E2M1, MX_E2M1);
+  } else {
+    if (af == MX_E4M3 && bf == MX_E4M3) MX_BIG_OUT(MX_E4M3, MX_E4M3);
+    else if (af == MX_E5M2 && bf == MX_E4M3) MX_BIG_OUT(MX_E5M2, MX_E4M3);
+    else if (af == MX_E4M3 && bf == MX_E5M2) MX_BIG_OUT(MX_E4M3, MX_E5M2);
+    else MX_BIG_OUT(MX_E5M2, MX_E5M2);
+  }
 #undef MX_BIG_OUT
 #undef MX_BIG_LAUNCH
   return mx_host::launch_status();
@@ -805,8 +869,14 @@ mx_status_t launch(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, in
 
 extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   if (!d) return MX_ERR_NULL;
-  if (d->a_fmt != MX_E4M3 && d->a_fmt != MX_E5M2) return MX_ERR_FORMAT;
-  if (d->b_fmt != MX_E4M3 && d->b_fmt != MX_E5M2) return MX_ERR_FORMAT;
+  const bool fp4 = d->a_fmt == MX_E2M1 || d->b_fmt == MX_E2M1;
+  if (fp4) {
+    // MXFP4 x MXFP4 only, on the large-tile kernel
+    if (d->a_fmt != MX_E2M1 || d->b_fmt != MX_E2M1 || d->accum == MX_ACCUM_FP32) return MX_ERR_FORMAT;
+  } else {
+    if (d->a_fmt != MX_E4M3 && d->a_fmt != MX_E5M2) return MX_ERR_FORMAT;
+    if (d->b_fmt != MX_E4M3 && d->b_fmt != MX_E5M2) return MX_ERR_FORMAT;
+  }
   if (d->y_dtype != MX_F32 && d->y_dtype != MX_BF16) return MX_ERR_FORMAT;
   const int64_t M = d->M, N = d->N, K = d->K;
   if (M < 0 || N < 0 || K < 0 || K % kBlock != 0) return MX_ERR_SHAPE;
@@ -817,10 +887,14 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   if (M == 0 || N == 0) return mx_host::check_device();
   if (!d->y) return MX_ERR_NULL;
   if (K > 0 && (!d->a || !d->b || !d->sa || !d->sb)) return MX_ERR_NULL;
-  if (d->lda < K || d->ldb < K || d->ldsa < K / kBlock || d->ldsb < K / kBlock || d->ldy < N) return MX_ERR_SHAPE;
+  const int64_t krow = fp4 ? K / 2 : K;  // code bytes per operand row
+  if (d->lda < krow || d->ldb < krow || d->ldsa < K / kBlock || d->ldsb < K / kBlock || d->ldy < N)
+    return MX_ERR_SHAPE;
   if (paged && (d->b_page_rows <= 0 || d->b_pages_per_seq <= 0 || (N + d->b_page_rows - 1) / d->b_page_rows > d->b_pages_per_seq))
     return MX_ERR_SHAPE;
   if (d->accum != MX_ACCUM_AUTO && d->accum != MX_ACCUM_FP8 && d->accum != MX_ACCUM_FP32) return MX_ERR_FORMAT;
+  // MXFP4 runs on the large-tile kernel only: its shape limits
+  if (fp4 && (paged || K % 1024 != 0 || M < 256 || N < 256)) return MX_ERR_SHAPE;
   const int64_t ysz = d->y_dtype == MX_F32 ? 4 : 2;
   if (!mx_host::aligned16(d->a) || !mx_host::aligned16(d->b) || d->lda % 16 || d->ldb % 16 ||
       ((uintptr_t)d->y % ysz) != 0)
@@ -859,15 +933,17 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   if ((int64_t)g.tiles_m * g.tiles_n >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const bool bf16out = d->y_dtype == MX_BF16;
   // large aligned problems: the 256 x 256 pipelined kernel (either mode)
-  const bool big_ok = !paged && K % 512 == 0 && K > 0 && d->lda % 16 == 0 && d->ldb % 16 == 0 &&
+  const bool big_ok = !paged && K % (fp4 ? 1024 : 512) == 0 && K > 0 && d->lda % 16 == 0 && d->ldb % 16 == 0 &&
                       mx_host::aligned16(d->sa) && mx_host::aligned16(d->sb) && d->ldsa % 16 == 0 &&
                       d->ldsb % 16 == 0 && d->stride_sa_outer % 16 == 0 && d->stride_sa_inner % 16 == 0 &&
                       d->stride_sb_outer % 16 == 0 && d->stride_sb_inner % 16 == 0 && M >= 256 && N >= 256 &&
                       (M * d->lda) < ((int64_t)1 << 32) && (N * d->ldb) < ((int64_t)1 << 32);
+  if (fp4 && !big_ok) return MX_ERR_SHAPE;  // MXFP4 runs on the large-tile kernel only
   if (big_ok) {
     GemmArgs gb = g;
     gb.tiles_m = (uint32_t)((M + kFBM - 1) / kFBM);
     gb.tiles_n = (uint32_t)((N + kFBN - 1) / kFBN);
+    if (fp4) return launch_big<kModeFP4>(gb, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
     return fp8 ? launch_big<kModeFP8>(gb, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream)
                : launch_big<kModeBF16>(gb, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
   }

@@ -34,7 +34,7 @@ constexpr int kBlock = 32;  // elements per MX block
 // they clamp to code 0); E = 255 (Inf/NaN present) gives 0xFF.
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_code_from_exp(uint32_t E) {
-  constexpr uint32_t emax = FMT == MX_E5M2 ? 15u : 8u;
+  constexpr uint32_t emax = FMT == MX_E5M2 ? 15u : FMT == MX_E2M1 ? 2u : 8u;
   uint32_t c = E > emax ? E - emax : 0u;
   return E == 255u ? 0xFFu : c;
 }
@@ -87,6 +87,28 @@ __device__ __forceinline__ uint32_t encode4_f32(float a, float b, float c, float
     r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, div, true);
   }
   return fix_overflow<FMT>(__builtin_bit_cast(uint32_t, r));
+}
+
+// Eight bf16 / f32 values -> eight E2M1 codes in one dword, element 2i in
+// the low nibble of byte i. v_cvt_scalef32_pk_fp4_* round to nearest even and
+// saturate at +-6 (checked on the device over every bf16 input), so no fix-up
+// is needed; Inf becomes +-6 and NaN 6, which the callers override for NaN
+// blocks.
+__device__ __forceinline__ uint32_t encode8_fp4_bf16(uint4 w, float div) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf16, w.x), div, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf16, w.y), div, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf16, w.z), div, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf16, w.w), div, 3);
+  return r;
+}
+__device__ __forceinline__ uint32_t encode8_fp4_f32(uint4 a, uint4 b, float div) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(a.x), __uint_as_float(a.y), div, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(a.z), __uint_as_float(a.w), div, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(b.x), __uint_as_float(b.y), div, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __uint_as_float(b.z), __uint_as_float(b.w), div, 3);
+  return r;
 }
 
 // ---------------------------------------------------------------- reductions

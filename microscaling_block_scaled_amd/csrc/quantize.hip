@@ -1,6 +1,7 @@
 // quantize.hip -- MXFP8 quantization kernels for gfx950:
 //   rowwise (1 x 32 blocks), the fused paged KV-cache write, and colwise
-//   (32 x 1 blocks, stored transposed through an LDS tile).
+//   (32 x 1 blocks, stored transposed through an LDS tile). The rowwise
+//   kernel also writes MXFP4 (E2M1 codes, two per byte) [NVFP4 §2.4, §5.5].
 //
 // Method [MXFP8 SM120 software support, §0.1-§0.2; MXFP8 quantization
 // glossary]: each block of 32 consecutive values gets one E8M0 scale chosen
@@ -130,11 +131,20 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(RowArgs a) {
     if (!ok[u]) continue;
     const uint32_t amax = quad_max_u32(chunk_amax_bits<InT>(c[u]));
     const uint32_t code = scale_code_from_exp<FMT>(exp_field<InT>(amax));
-    uint2 out = encode_chunk<InT, FMT>(c[u], scale_divisor(code));
-    if (code == 0xFFu) out = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
     const int64_t ldq = KV ? a.head_dim : a.ldq;
     const int64_t lds = KV ? a.head_dim / kBlock : a.lds;
-    *(uint2*)(q + dst_row[u] * ldq + (int64_t)col8[u] * 8) = out;
+    if constexpr (FMT == MX_E2M1) {
+      // MXFP4: the 8 codes of the chunk are one dword (a NaN block gets 0s)
+      uint32_t out;
+      if constexpr (sizeof(InT) == 2) out = encode8_fp4_bf16(c[u].w, scale_divisor(code));
+      else out = encode8_fp4_f32(c[u].w0, c[u].w1, scale_divisor(code));
+      if (code == 0xFFu) out = 0u;
+      *(uint32_t*)(q + dst_row[u] * ldq + (int64_t)col8[u] * 4) = out;
+    } else {
+      uint2 out = encode_chunk<InT, FMT>(c[u], scale_divisor(code));
+      if (code == 0xFFu) out = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+      *(uint2*)(q + dst_row[u] * ldq + (int64_t)col8[u] * 8) = out;
+    }
     if ((threadIdx.x & 3) == 0) s[dst_row[u] * lds + col8[u] / 4] = (uint8_t)code;
   }
 }
@@ -313,6 +323,7 @@ mx_status_t launch_rows(RowArgs a, int64_t rows, int64_t cols, hipStream_t strea
 
 template <typename InT>
 mx_status_t dispatch_rows(mx_fmt_t fmt, RowArgs a, int64_t rows, int64_t cols, hipStream_t st) {
+  if (fmt == MX_E2M1) return launch_rows<InT, MX_E2M1, false>(a, rows, cols, st);
   return fmt == MX_E5M2 ? launch_rows<InT, MX_E5M2, false>(a, rows, cols, st)
                         : launch_rows<InT, MX_E4M3, false>(a, rows, cols, st);
 }
@@ -323,9 +334,10 @@ extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t xdt, int64_t rows, 
                                    mx_fmt_t fmt, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
                                    hipStream_t stream) {
   if (!x || !q || !s) return MX_ERR_NULL;
-  mx_status_t st = check_common(x, xdt, fmt, rows, cols, ldx);
+  const bool fp4 = fmt == MX_E2M1;
+  mx_status_t st = check_common(x, xdt, fp4 ? MX_E4M3 : fmt, rows, cols, ldx);
   if (st != MX_OK) return st;
-  if (cols % kBlock != 0 || ldq < cols || lds < cols / kBlock) return MX_ERR_SHAPE;
+  if (cols % kBlock != 0 || ldq < (fp4 ? cols / 2 : cols) || lds < cols / kBlock) return MX_ERR_SHAPE;
   if (!mx_host::aligned16(q) || ldq % 16 != 0) return MX_ERR_ALIGN;
   if ((st = mx_host::check_device()) != MX_OK) return st;
   if (rows == 0 || cols == 0) return MX_OK;

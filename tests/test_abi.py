@@ -107,3 +107,28 @@ def test_attention_argument_errors_without_gpu(libmx):
     # empty problems launch nothing and succeed
     assert f(ctypes.byref(desc(num_seqs=0)), None) == 0
     assert f(ctypes.byref(desc(q_len=0, q=None)), None) == 0
+
+
+def test_mxfp4_argument_errors_without_gpu(libmx):
+    """MXFP4 limits are checked on the host before any device call."""
+    from microscaling_block_scaled_amd import _lib
+    g = libmx.mx_gemm
+    g.restype, g.argtypes = _lib.SIGNATURES["mx_gemm"]
+
+    def desc(**kw):
+        d = _lib.mx_gemm_desc_t()
+        base = dict(M=512, N=512, K=2048, a=0x10000, lda=1024, sa=0x20000, ldsa=64, a_fmt=2, b=0x30000, ldb=1024,
+                    sb=0x40000, ldsb=64, b_fmt=2, y=0x50000, ldy=512, y_dtype=1, accum=0)
+        base.update(kw)
+        for k, v in base.items():
+            setattr(d, k, v)
+        return d
+
+    assert g(ctypes.byref(desc(b_fmt=0, ldb=2048)), None) == -4     # E2M1 x E4M3
+    assert g(ctypes.byref(desc(accum=2)), None) == -4               # FP32-accumulation mode has no FP4 path
+    assert g(ctypes.byref(desc(K=1536, lda=768, ldb=768, ldsa=48, ldsb=48)), None) == -2  # K % 1024
+    assert g(ctypes.byref(desc(M=128)), None) == -2
+    assert g(ctypes.byref(desc(lda=512)), None) == -2               # pitch below K/2 bytes
+    q = libmx.mx_quantize_colwise
+    q.restype, q.argtypes = _lib.SIGNATURES["mx_quantize_colwise"]
+    assert q(0x10000, 1, 64, 64, 64, 2, 0x20000, 64, 0x30000, 2, None) == -4  # colwise MXFP4 not offered
