@@ -376,6 +376,22 @@ def other_rows(torch, mx, inputs, np, flush, stream, steps, kv_only=False):
                               "frac_of_fp4_peak": round(tf / MFMA_FP4_PEAK_TFLOPS, 4),
                               "shape": [8192, 8192, 8192], "operands": "E2M1 x E2M1, bf16 out"}
     del A4, SA4, B4, SB4, Y4
+    # MoE grouped GEMM: 32768 routed rows (16384 tokens x top-2) over 8
+    # experts, hidden 4096 -> 4096, E4M3 x E4M3, bf16 out
+    log("moe grouped row")
+    sizes = inputs.moe_group_sizes(32768, 8)
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)).cuda()
+    Xm, SXm = mx.mx_quantize(dev_bf16(torch, inputs.normal_bf16(6002, (32768, 4096))), mx.MX_E4M3)
+    Wm, SWm = mx.mx_quantize(dev_bf16(torch, inputs.normal_bf16(6003, (8 * 4096, 4096), sigma=0.02)), mx.MX_E4M3)
+    Ym = torch.empty((32768, 4096), dtype=torch.bfloat16, device="cuda")
+    ms = timed("moe_grouped", lambda: mx.mx_grouped_gemm(Xm, SXm, Wm.view(8, 4096, 4096), SWm.view(8, 4096, 128), off,
+                                                         y=Ym))
+    tf = 2.0 * 32768 * 4096 * 4096 / ms / 1e9
+    out["moe_grouped_gemm"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                               "frac_of_fp8_peak": round(tf / MFMA_FP8_PEAK_TFLOPS, 4),
+                               "groups": [int(v) for v in sizes], "shape": "32768 rows x 4096 -> 4096, 8 experts",
+                               "accumulation": "AUTO -> scaled FP8 MFMA (E4M3 x E4M3, K = 4096)"}
+    del Xm, SXm, Wm, SWm, Ym, off
     del q, s, yd
     # training linear layer: fwd (E4M3 x E4M3, K = 4096) and dgrad (E5M2 x E4M3, K = 14336)
     log("training rows")

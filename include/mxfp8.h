@@ -272,6 +272,40 @@ typedef struct mx_attention_desc {
 
 mx_status_t mx_paged_attention(const mx_attention_desc_t* desc, hipStream_t stream);
 
+/*
+ * mx_grouped_gemm -- one block-scaled product per group over a shared K, for
+ * the many small GEMMs of a mixture-of-experts layer [SM120 §1.2: grouped
+ * GEMM is its own entry point, beside the single GEMM]. Group q owns rows
+ * [off[q], off[q+1]) of A and of y and its own B (the expert's weights):
+ *
+ *   y[r][n] = sum_b sa[r][b] * sb_q[n][b] * sum_{i<32} a[r][32b+i] * b_q[n][32b+i]
+ *
+ *   a, sa   [total_m x K] codes / [total_m x K/32] scales, pitches lda, ldsa
+ *   b, sb   group q's [N x K] codes at b + q*stride_b, scales at sb + q*stride_sb
+ *   group_offsets  DEVICE int64 [groups + 1] (typically a router's output, so
+ *           the host never reads it); off[0] <= off[1] <= ... are row indices.
+ *           Values are clamped to [0, total_m] and a decreasing step is an
+ *           empty group, so any contents keep every access in bounds; with
+ *           offsets that are not nondecreasing some rows may be left out.
+ *   y       [total_m x N] out (y_dtype), pitch ldy; rows outside every group
+ *           are left untouched.
+ * Formats and accumulation modes are those of mx_gemm (E2M1 x E2M1 included).
+ * Requirements (MX_ERR_SHAPE / MX_ERR_ALIGN otherwise): K % 512 == 0 (K %
+ * 1024 for E2M1), N >= 256, groups < 2^20, 16-byte aligned code and scale
+ * bases, pitches and group strides, 8-byte aligned group_offsets.
+ */
+typedef struct mx_grouped_gemm_desc {
+    int64_t groups, total_m, N, K;
+    const int64_t* group_offsets;
+    const uint8_t* a;  int64_t lda;  const uint8_t* sa; int64_t ldsa; mx_fmt_t a_fmt;
+    const uint8_t* b;  int64_t ldb;  const uint8_t* sb; int64_t ldsb; mx_fmt_t b_fmt;
+    int64_t stride_b, stride_sb;
+    void* y;           int64_t ldy;  mx_dtype_t y_dtype;
+    mx_accum_t accum;
+} mx_grouped_gemm_desc_t;
+
+mx_status_t mx_grouped_gemm(const mx_grouped_gemm_desc_t* desc, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* mx_status_string(mx_status_t status);
 

@@ -18,13 +18,14 @@ Layouts (row-major, unit stride along the last dimension):
 import ctypes
 
 from ._lib import (BLOCK, MX_ACCUM_AUTO, MX_ACCUM_FP8, MX_ACCUM_FP32, MX_BF16, MX_E2M1, MX_E4M3, MX_E5M2, MX_F32, MXError,
-                   check, lib, mx_attention_desc_t, mx_gemm_desc_t)
+                   check, lib, mx_attention_desc_t, mx_gemm_desc_t, mx_grouped_gemm_desc_t)
 
 __all__ = [
     "MX_E4M3", "MX_E5M2", "MX_E2M1", "MX_F32", "MX_BF16", "BLOCK", "MXError",
     "MX_ACCUM_AUTO", "MX_ACCUM_FP8", "MX_ACCUM_FP32",
     "mx_quantize", "mx_quantize_colwise", "mx_dequantize", "mx_kv_quant_write", "mx_gemm",
-    "mx_gemm_desc", "mx_paged_scores", "mx_paged_attention", "mx_status_string", "mx_query_support",
+    "mx_gemm_desc", "mx_grouped_gemm", "mx_paged_scores", "mx_paged_attention", "mx_status_string",
+    "mx_query_support",
 ]
 
 
@@ -158,6 +159,38 @@ def mx_gemm(a, sa, b, sb, a_fmt=MX_E4M3, b_fmt=MX_E4M3, out_dtype=None, y=None, 
     d.y, d.ldy, d.y_dtype = y.data_ptr(), _ld(y), _dtype_code(y)
     d.accum = accum
     mx_gemm_desc(d, stream)
+    return y
+
+
+def mx_grouped_gemm(a, sa, b, sb, group_offsets, a_fmt=MX_E4M3, b_fmt=MX_E4M3, out_dtype=None, y=None,
+                    stream=None, accum=MX_ACCUM_AUTO):
+    """Per-group block-scaled products: rows off[q] .. off[q+1]-1 of A [total_m,
+    K] times group q's B [N, K]^T. b [G, N, K] and sb [G, N, K/32] (E2M1: b is
+    [G, N, K/2]); group_offsets int64 [G+1] on the device. Rows of y outside
+    every group are left as they are (zeros when y is allocated here)."""
+    torch = _torch()
+    for t, n in ((a, "a"), (sa, "sa")):
+        _rowmajor(t, n)
+    if b.dim() != 3 or sb.dim() != 3 or not b.is_contiguous() or not sb.is_contiguous():
+        raise ValueError("b and sb must be contiguous [G, N, ...] tensors")
+    if group_offsets.dtype != torch.int64 or not group_offsets.is_cuda or group_offsets.shape != (b.shape[0] + 1,):
+        raise ValueError("group_offsets must be a device int64 tensor of groups + 1 entries")
+    G, N = b.shape[0], b.shape[1]
+    M = a.shape[0]
+    K = sa.shape[1] * BLOCK
+    if sb.shape != (G, N, K // BLOCK):
+        raise ValueError("sb must be [G, N, K/32]")
+    if y is None:
+        y = torch.zeros((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    d = mx_grouped_gemm_desc_t()
+    d.groups, d.total_m, d.N, d.K = G, M, N, K
+    d.group_offsets = group_offsets.data_ptr()
+    d.a, d.lda, d.sa, d.ldsa, d.a_fmt = a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), a_fmt
+    d.b, d.ldb, d.sb, d.ldsb, d.b_fmt = b.data_ptr(), b.shape[2], sb.data_ptr(), sb.shape[2], b_fmt
+    d.stride_b, d.stride_sb = N * b.shape[2], N * sb.shape[2]
+    d.y, d.ldy, d.y_dtype = y.data_ptr(), _ld(y), _dtype_code(y)
+    d.accum = accum
+    check("mx_grouped_gemm", lib().mx_grouped_gemm(ctypes.byref(d), _stream(stream)))
     return y
 
 

@@ -62,6 +62,18 @@ class mx_attention_desc_t(ctypes.Structure):
     ]
 
 
+class mx_grouped_gemm_desc_t(ctypes.Structure):
+    _fields_ = [
+        ("groups", _i64), ("total_m", _i64), ("N", _i64), ("K", _i64),
+        ("group_offsets", _p),
+        ("a", _p), ("lda", _i64), ("sa", _p), ("ldsa", _i64), ("a_fmt", ctypes.c_int),
+        ("b", _p), ("ldb", _i64), ("sb", _p), ("ldsb", _i64), ("b_fmt", ctypes.c_int),
+        ("stride_b", _i64), ("stride_sb", _i64),
+        ("y", _p), ("ldy", _i64), ("y_dtype", ctypes.c_int),
+        ("accum", ctypes.c_int),
+    ]
+
+
 _lib = None
 
 # name -> (restype, argtypes)
@@ -72,6 +84,7 @@ SIGNATURES = {
     "mx_kv_quant_write": (_i32, [_p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p]),
     "mx_gemm": (_i32, [ctypes.POINTER(mx_gemm_desc_t), _p]),
     "mx_paged_attention": (_i32, [ctypes.POINTER(mx_attention_desc_t), _p]),
+    "mx_grouped_gemm": (_i32, [ctypes.POINTER(mx_grouped_gemm_desc_t), _p]),
     "mx_status_string": (ctypes.c_char_p, [_i32]),
     "mx_query_support": (_i32, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p)]),
 }

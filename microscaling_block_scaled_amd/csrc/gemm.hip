@@ -52,6 +52,9 @@ struct GemmArgs {
   uint32_t tiles_m, tiles_n;
   uint32_t scales_dword;  // 1: every row's 4 scale bytes of a K step can be read as one aligned dword
   uint32_t y_vec;         // 1: output rows allow 8/16-byte vector stores
+  // grouped mode (large-tile kernel): group q owns rows [off[q], off[q+1])
+  // of A and y and uses B + q * sb_o; row tiles are dealt group by group
+  const int64_t* group_off; uint32_t groups;
 };
 
 __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
@@ -465,28 +468,75 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t sAs2[2][kFP4 ? kScaleBuf : 16];
   __shared__ __attribute__((aligned(16))) uint8_t sBs2[2][kFP4 ? kScaleBuf : 16];
 
-  // ---- tile id: XCD-contiguous bands, then groups of 4 tile rows
-  const uint32_t ntiles = g.tiles_m * g.tiles_n;
-  uint32_t lid = blockIdx.x;
-  if (ntiles % 8 == 0) lid = (lid % 8) * (ntiles / 8) + lid / 8;
-  const uint32_t group = 4;
-  const uint32_t per_group = group * g.tiles_n;
-  const uint32_t first_m = (lid / per_group) * group;
-  const uint32_t gm = min(g.tiles_m - first_m, group);
-  const uint32_t tile_m = first_m + (lid % per_group) % gm;
-  const uint32_t tile_n = (lid % per_group) / gm;
-  const int64_t m0 = (int64_t)tile_m * kFBM, n0 = (int64_t)tile_n * kFBN;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
 
-  const int64_t p = blockIdx.y;
-  const int64_t po = p / g.batch_inner, pi = p % g.batch_inner;
+  int64_t m0, n0, m_end, po, pi;
+  // ---- tile id: XCD-contiguous bands, then groups of 4 tile rows (in the
+  // grouped mode over the grid of ceil(M / 256) + groups row tiles)
+  uint32_t tile_m, tile_n;
+  {
+    const uint32_t ntiles = g.tiles_m * g.tiles_n;
+    uint32_t lid = blockIdx.x;
+    if (ntiles % 8 == 0) lid = (lid % 8) * (ntiles / 8) + lid / 8;
+    const uint32_t group = 4;
+    const uint32_t per_group = group * g.tiles_n;
+    const uint32_t first_m = (lid / per_group) * group;
+    const uint32_t gm = min(g.tiles_m - first_m, group);
+    tile_m = first_m + (lid % per_group) % gm;
+    tile_n = (lid % per_group) / gm;
+  }
+  n0 = (int64_t)tile_n * kFBN;
+  if (g.group_off == nullptr) {
+    m0 = (int64_t)tile_m * kFBM;
+    m_end = g.M;
+    const int64_t p = blockIdx.y;
+    po = p / g.batch_inner;
+    pi = p % g.batch_inner;
+  } else {
+    // ---- grouped: row tile t belongs to the group whose tiles
+    // (ceil(rows / 256) each, offsets clamped to [0, M]) cover it; every wave
+    // finds it with a prefix sum over the groups, 64 at a time. Tiles past
+    // the last group's return before any load or barrier.
+    const uint32_t t = tile_m;
+    int64_t found = -1, lo_f = 0, hi_f = 0, first_tile = 0, prefix = 0;
+    for (uint32_t q0 = 0; q0 < g.groups && found < 0; q0 += 64) {
+      const uint32_t q = q0 + lane;
+      int64_t lo = 0, hi = 0;
+      if (q < g.groups) {
+        lo = min(max(g.group_off[q], (int64_t)0), g.M);
+        hi = min(max(g.group_off[q + 1], lo), g.M);
+      }
+      const int64_t nt = (hi - lo + kFBM - 1) / kFBM;
+      int64_t incl = nt;  // inclusive prefix of the tile counts across the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int64_t v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+      }
+      const int64_t chunk = __shfl(incl, 63);
+      if ((int64_t)t < prefix + chunk) {
+        const bool mine = (int64_t)t >= prefix + incl - nt && (int64_t)t < prefix + incl;
+        const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+        found = q0 + src;
+        lo_f = __shfl(lo, src);
+        hi_f = __shfl(hi, src);
+        first_tile = prefix + __shfl(incl - nt, src);
+      }
+      prefix += chunk;
+    }
+    if (found < 0) return;
+    m0 = lo_f + ((int64_t)t - first_tile) * kFBM;
+    m_end = hi_f;
+    po = found;
+    pi = 0;
+  }
   const uint8_t* A = g.a + po * g.sa_o + pi * g.sa_i;
   const uint8_t* SA = g.sa + po * g.ssa_o + pi * g.ssa_i;
   const uint8_t* B = g.b + po * g.sb_o + pi * g.sb_i;
   const uint8_t* SB = g.sb + po * g.ssb_o + pi * g.ssb_i;
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
   const int64_t nsteps = (kFP4 ? g.K / 2 : g.K) / kFBK;  // a multiple of 4
 
   // ---- loads. Codes: per stage and operand, 8 instructions per wave, each
@@ -498,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   const uint8_t* b_base = uniform_ptr(B + n0 * g.ldb);
   const uint8_t* sa_base = uniform_ptr(SA + m0 * g.ldsa);
   const uint8_t* sb_base = uniform_ptr(SB + n0 * g.ldsb);
-  const int64_t a_last = g.M - 1 - m0, b_last = g.N - 1 - n0;
+  const int64_t a_last = m_end - 1 - m0, b_last = g.N - 1 - n0;
   uint32_t a_off[8], b_off[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -754,7 +804,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + wm * 128 + i * 32 + lr;
-    const bool mok = m < g.M;
+    const bool mok = m < m_end;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t nb = n0 + wn * 128 + j * 32;  // the lane's columns: nb + 8 q + 4 lg + 0..3
@@ -959,4 +1009,56 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
                  : launch<BM, BN, false, kModeFP8>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
   return paged ? launch<BM, BN, true, kModeBF16>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream)
                : launch<BM, BN, false, kModeBF16>(g, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
+}
+
+extern "C" mx_status_t mx_grouped_gemm(const mx_grouped_gemm_desc_t* d, hipStream_t stream) {
+  if (!d) return MX_ERR_NULL;
+  const bool fp4 = d->a_fmt == MX_E2M1 || d->b_fmt == MX_E2M1;
+  if (fp4) {
+    if (d->a_fmt != MX_E2M1 || d->b_fmt != MX_E2M1 || d->accum == MX_ACCUM_FP32) return MX_ERR_FORMAT;
+  } else {
+    if (d->a_fmt != MX_E4M3 && d->a_fmt != MX_E5M2) return MX_ERR_FORMAT;
+    if (d->b_fmt != MX_E4M3 && d->b_fmt != MX_E5M2) return MX_ERR_FORMAT;
+  }
+  if (d->y_dtype != MX_F32 && d->y_dtype != MX_BF16) return MX_ERR_FORMAT;
+  if (d->accum != MX_ACCUM_AUTO && d->accum != MX_ACCUM_FP8 && d->accum != MX_ACCUM_FP32) return MX_ERR_FORMAT;
+  const int64_t G = d->groups, M = d->total_m, N = d->N, K = d->K;
+  if (G < 0 || M < 0 || N < 0 || K <= 0 || G >= ((int64_t)1 << 20)) return MX_ERR_SHAPE;
+  if (G == 0 || M == 0 || N == 0) return mx_host::check_device();
+  if (!d->group_offsets || !d->a || !d->sa || !d->b || !d->sb || !d->y) return MX_ERR_NULL;
+  const int64_t krow = fp4 ? K / 2 : K;
+  if (K % (fp4 ? 1024 : 512) != 0 || N < 256 || d->lda < krow || d->ldb < krow || d->ldsa < K / kBlock ||
+      d->ldsb < K / kBlock || d->ldy < N || d->stride_b < N * d->ldb || d->stride_sb < N * d->ldsb ||
+      d->lda >= ((int64_t)1 << 24) || d->ldb >= ((int64_t)1 << 24))
+    return MX_ERR_SHAPE;
+  const int64_t ysz = d->y_dtype == MX_F32 ? 4 : 2;
+  if (!mx_host::aligned16(d->a) || !mx_host::aligned16(d->b) || d->lda % 16 || d->ldb % 16 || d->stride_b % 16 ||
+      !mx_host::aligned16(d->sa) || !mx_host::aligned16(d->sb) || d->ldsa % 16 || d->ldsb % 16 ||
+      d->stride_sb % 16 || ((uintptr_t)d->y % ysz) != 0 || ((uintptr_t)d->group_offsets % 8) != 0)
+    return MX_ERR_ALIGN;
+  mx_status_t st;
+  if ((st = mx_host::check_device()) != MX_OK) return st;
+
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.a = d->a; g.lda = d->lda; g.sa = d->sa; g.ldsa = d->ldsa;
+  g.b = d->b; g.ldb = d->ldb; g.sb = d->sb; g.ldsb = d->ldsb;
+  g.y = d->y; g.ldy = d->ldy;
+  g.batch_inner = 1;
+  g.sb_o = d->stride_b; g.ssb_o = d->stride_sb;  // per group; A and y rows are absolute
+  g.group_off = d->group_offsets;
+  g.groups = (uint32_t)G;
+  g.scales_dword = 1;
+  g.y_vec = (mx_host::aligned16(d->y) && (d->ldy * ysz) % 16 == 0) ? 1u : 0u;
+  g.tiles_n = (uint32_t)((N + kFBN - 1) / kFBN);
+  // every group adds at most one partial row tile
+  const int64_t tiles_m = (M + kFBM - 1) / kFBM + G;
+  if (tiles_m * g.tiles_n >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
+  g.tiles_m = (uint32_t)tiles_m;
+  const bool bf16out = d->y_dtype == MX_BF16;
+  if (fp4) return launch_big<kModeFP4>(g, d->a_fmt, d->b_fmt, bf16out, 1, stream);
+  const bool fp8 = d->accum == MX_ACCUM_FP8 ||
+                   (d->accum == MX_ACCUM_AUTO && d->a_fmt == MX_E4M3 && d->b_fmt == MX_E4M3 && K >= 2048);
+  return fp8 ? launch_big<kModeFP8>(g, d->a_fmt, d->b_fmt, bf16out, 1, stream)
+             : launch_big<kModeBF16>(g, d->a_fmt, d->b_fmt, bf16out, 1, stream);
 }

@@ -21,6 +21,9 @@ Workloads (sizes as given for the method's headline runs):
               5002 / 5003); 64 sequences of 512 tokens on pages of 128 tokens;
               sequence s owns logical pages 4s..4s+3, mapped to physical pages
               by a seeded permutation of 0..255 (5004).
+  * moe:      32768 rows (16384 tokens x top-2) split over 8 experts by
+              `moe_group_sizes` (seed 6001); X bf16 [32768, 4096] ~ N(0, 1)
+              (6002), expert weights bf16 [8 x 4096, 4096] ~ N(0, 0.02) (6003).
   * attention: the kv workload read back as paged attention: the query of
               every token (seed 5003) attends over its sequence's 512 cached
               keys. Smaller cases (`attention_case`) draw a ragged mix of
@@ -139,3 +142,12 @@ def attention_case(seed: int, n_seqs: int, q_len: int, kv_lens, page_size: int, 
     k = normal_bf16(seed + 2, (n_pages, page_size, kv_heads, head_dim))
     v = normal_bf16(seed + 3, (n_pages, page_size, kv_heads, head_dim))
     return q, k, v, table, kv_lens
+
+
+def moe_group_sizes(rows: int = 32768, groups: int = 8, seed: int = 6001):
+    """Rows per expert for a skewed routing: shares drawn from a Dirichlet(1)
+    (seeded), rounded to integers that sum to `rows`."""
+    share = rng(seed).dirichlet(np.ones(groups))
+    sizes = np.floor(share * rows).astype(np.int64)
+    sizes[np.argmax(sizes)] += rows - sizes.sum()
+    return sizes

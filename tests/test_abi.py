@@ -51,7 +51,7 @@ def test_status_strings_without_gpu(libmx):
     assert "unknown" in libmx.mx_status_string(12345).decode()
 
 
-@pytest.mark.parametrize("name", ["mx_gemm_desc_t", "mx_attention_desc_t"])
+@pytest.mark.parametrize("name", ["mx_gemm_desc_t", "mx_attention_desc_t", "mx_grouped_gemm_desc_t"])
 def test_ctypes_descriptor_matches_c_layout(tmp_path, name):
     """Compile a probe against the real header with gcc and compare field
     offsets and size with the ctypes mirror used by the binding."""
