@@ -22,6 +22,8 @@ import numpy as np
 E4M3 = 0
 E5M2 = 1
 E2M1 = 2
+RULE_FLOOR = 0  # X = 2^(floor(log2 amax) - emax_elem)
+RULE_CEIL = 1   # smallest power of two with amax / X <= largest finite element
 F32 = 0
 BF16 = 1
 BLOCK = 32
@@ -64,6 +66,15 @@ def _load():
                                 _i64, _p, _p]
     lib.mxo_paged_attention.argtypes = [_p, _p, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p, _i64, _i64, _i64, _i64,
                                         _i64, _i64, ctypes.c_double, ctypes.c_int, _p, _i64, _p, _p, _p, _p]
+    lib.mxo_scale_code_rule.restype = ctypes.c_uint
+    lib.mxo_scale_code_rule.argtypes = [ctypes.c_int, _p, _i64, ctypes.c_int]
+    lib.mxo_quantize_rows_rule.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _p, _i64, _p,
+                                           _i64]
+    lib.mxo_quantize_cols_rule.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _p, _i64, _p,
+                                           _i64]
+    lib.mxo_quantize_2d.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _p, _i64, _p, _i64,
+                                    _p, _i64, _p, _i64]
+    lib.mxo_scale_broadcast.argtypes = [_p, _i64, ctypes.c_int, _i64, _i64, _p, _i64]
     lib.mxo_num_threads.restype = ctypes.c_int
     lib.mxo_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
@@ -100,9 +111,9 @@ def encode(fmt: int, y: float) -> int:
     return _load().mxo_encode(fmt, float(y))
 
 
-def scale_code(fmt: int, block) -> int:
+def scale_code(fmt: int, block, rule: int = RULE_FLOOR) -> int:
     v = np.ascontiguousarray(block, dtype=np.float64)
-    return _load().mxo_scale_code(fmt, _ptr(v), v.size)
+    return _load().mxo_scale_code_rule(fmt, _ptr(v), v.size, rule)
 
 
 def double_to_bf16(v: float) -> int:
@@ -124,7 +135,7 @@ def code_bytes(fmt: int, n: int) -> int:
 
 
 # ---- array operations -----------------------------------------------------
-def quantize_rows(x: np.ndarray, fmt: int):
+def quantize_rows(x: np.ndarray, fmt: int, rule: int = RULE_FLOOR):
     """Rowwise MX quantization: returns (codes [R, C] uint8 (E2M1: [R, C/2]
     packed), scales [R, C/32] uint8)."""
     x = np.ascontiguousarray(x)
@@ -132,12 +143,12 @@ def quantize_rows(x: np.ndarray, fmt: int):
     cb = code_bytes(fmt, cols)
     q = np.empty((rows, cb), np.uint8)
     s = np.empty((rows, cols // BLOCK), np.uint8)
-    _check(_load().mxo_quantize_rows(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, _ptr(q), cb, _ptr(s),
-                                     cols // BLOCK))
+    _check(_load().mxo_quantize_rows_rule(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, rule, _ptr(q), cb, _ptr(s),
+                                          cols // BLOCK))
     return q, s
 
 
-def quantize_cols(x: np.ndarray, fmt: int):
+def quantize_cols(x: np.ndarray, fmt: int, rule: int = RULE_FLOOR):
     """Colwise MXFP8 (blocks down columns), stored transposed:
     returns (codes^T [C, R] uint8, scales^T [C, R/32] uint8)."""
     x = np.ascontiguousarray(x)
@@ -145,9 +156,33 @@ def quantize_cols(x: np.ndarray, fmt: int):
     rb = code_bytes(fmt, rows)
     qt = np.empty((cols, rb), np.uint8)
     st = np.empty((cols, rows // BLOCK), np.uint8)
-    _check(_load().mxo_quantize_cols(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, _ptr(qt), rb, _ptr(st),
-                                     rows // BLOCK))
+    _check(_load().mxo_quantize_cols_rule(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, rule, _ptr(qt), rb, _ptr(st),
+                                          rows // BLOCK))
     return qt, st
+
+
+def quantize_2d(x: np.ndarray, fmt: int, rule: int = RULE_FLOOR):
+    """One scale per 32 x 32 block: returns (q [R, C], s [R, C/32], qt [C, R],
+    st [C, R/32]) with s and st the block scales expanded to the MXFP8 layout."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // BLOCK), np.uint8)
+    qt = np.empty((cols, rows), np.uint8)
+    st = np.empty((cols, rows // BLOCK), np.uint8)
+    _check(_load().mxo_quantize_2d(_ptr(x), _in_dtype(x), rows, cols, cols, fmt, rule, _ptr(q), cols, _ptr(s),
+                                   cols // BLOCK, _ptr(qt), rows, _ptr(st), rows // BLOCK))
+    return q, s, qt, st
+
+
+def scale_broadcast(s_in: np.ndarray, layout: int, rows: int, cols: int) -> np.ndarray:
+    """Power-of-two FP32 block scales (layout 0: [rows, cols/128] for 1 x 128
+    blocks; layout 1: [ceil(rows/128), cols/128] for 128 x 128 blocks) ->
+    E8M0 scales [rows, cols/32]."""
+    s_in = np.ascontiguousarray(s_in, dtype=np.float32)
+    out = np.empty((rows, cols // BLOCK), np.uint8)
+    _check(_load().mxo_scale_broadcast(_ptr(s_in), s_in.shape[1], layout, rows, cols, _ptr(out), cols // BLOCK))
+    return out
 
 
 def kv_quant_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, page_size: int, num_pages: int,

@@ -175,7 +175,14 @@ unsigned mxo_encode(int fmt, double y) {
  * round x / scale to FP8. The rule itself is left to the implementation
  * [SM120 §0.1]; this file uses X = 2^(floor(log2 amax) - emax_elem).
  * ------------------------------------------------------------------------- */
-unsigned mxo_scale_code(int fmt, const double* x, int64_t n) {
+/* Scale rules. MXO_RULE_FLOOR (the default): X = 2^(floor(log2 amax) -
+ * emax_elem), which can leave amax / X up to just under 2 * 2^emax_elem, past
+ * the largest finite element, so the block maximum may saturate.
+ * MXO_RULE_CEIL: the smallest power of two X with amax / X <= the largest
+ * finite element, i.e. X = 2^ceil(log2(amax / maxfinite)), so nothing
+ * saturates. The pages note that how the E8M0 scale is chosen and rounded
+ * matters for accuracy [GLOSS]; the second rule is that alternative. */
+unsigned mxo_scale_code_rule(int fmt, const double* x, int64_t n, int rule) {
     const fp8_format* f = fmt_of(fmt);
     double amax = 0.0;
     for (int64_t i = 0; i < n; ++i) {
@@ -184,18 +191,24 @@ unsigned mxo_scale_code(int fmt, const double* x, int64_t n) {
         if (a > amax) amax = a;
     }
     if (amax == 0.0) return 0u;
-    int k = ilogb(amax) - f->emax_elem + 127; /* ilogb is floor(log2) exactly */
+    int k = ilogb(amax) - f->emax_elem; /* ilogb is floor(log2) exactly */
+    /* the ceiling rule's exponent is k or k + 1: amax / 2^k lies in
+     * [2^emax_elem, 2^(emax_elem + 1)) and maxfinite is in the same binade */
+    if (rule == MXO_RULE_CEIL && ldexp(f->maxfinite, k) < amax) k += 1;
+    k += 127;
     if (k < 0) k = 0;
     if (k > 254) k = 254;
     return (unsigned)k;
 }
 
+unsigned mxo_scale_code(int fmt, const double* x, int64_t n) { return mxo_scale_code_rule(fmt, x, n, MXO_RULE_FLOOR); }
+
 /* Quantize one block: scale code, then q_i = Q_FP8(x_i / s) [SM120 §0.1].
  * A block holding NaN or Inf gets element codes 0x7F (FP8) or 0 (E2M1).
  * Codes are stored from codes[0] on: one byte each, or for E2M1 two per byte
  * with element 2i in the low nibble [NVFP4 §5.5: 4 bits per element]. */
-static void quantize_block(int fmt, const double* x, int64_t n, uint8_t* codes, uint8_t* scale) {
-    unsigned s = mxo_scale_code(fmt, x, n);
+static void quantize_block_rule(int fmt, int rule, const double* x, int64_t n, uint8_t* codes, uint8_t* scale) {
+    unsigned s = mxo_scale_code_rule(fmt, x, n, rule);
     *scale = (uint8_t)s;
     for (int64_t i = 0; i < n; ++i) {
         unsigned c = (s == 0xFFu) ? (fmt == MXO_E2M1 ? 0u : 0x7Fu) : mxo_encode(fmt, ldexp(x[i], -((int)s - 127)));
@@ -208,6 +221,10 @@ static void quantize_block(int fmt, const double* x, int64_t n, uint8_t* codes, 
             codes[i] = (uint8_t)c;
         }
     }
+}
+
+static void quantize_block(int fmt, const double* x, int64_t n, uint8_t* codes, uint8_t* scale) {
+    quantize_block_rule(fmt, MXO_RULE_FLOOR, x, n, codes, scale);
 }
 
 /* Bytes of codes per block, and the code of element k of a row. */
@@ -231,13 +248,18 @@ static double load_elem(const void* x, int dt, int64_t idx) {
  * axis) [GLOSS]; codes and scales in separate arrays [SM120 §0.1]. */
 int mxo_quantize_rows(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
                       int64_t ldq, uint8_t* s, int64_t lds) {
+    return mxo_quantize_rows_rule(x, xdt, rows, cols, ldx, fmt, MXO_RULE_FLOOR, q, ldq, s, lds);
+}
+
+int mxo_quantize_rows_rule(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule,
+                           uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds) {
     if (cols % MXO_BLOCK != 0 || rows < 0 || cols < 0) return -2;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         double v[MXO_BLOCK];
         for (int64_t b = 0; b < cols / MXO_BLOCK; ++b) {
             for (int i = 0; i < MXO_BLOCK; ++i) v[i] = load_elem(x, xdt, r * ldx + b * MXO_BLOCK + i);
-            quantize_block(fmt, v, MXO_BLOCK, q + r * ldq + b * block_bytes(fmt), s + r * lds + b);
+            quantize_block_rule(fmt, rule, v, MXO_BLOCK, q + r * ldq + b * block_bytes(fmt), s + r * lds + b);
         }
     }
     return 0;
@@ -249,15 +271,84 @@ int mxo_quantize_rows(const void* x, int xdt, int64_t rows, int64_t cols, int64_
  * stored transposed: qt[c][r] (row pitch ldq), st[c][r/32] (row pitch lds). */
 int mxo_quantize_cols(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* qt,
                       int64_t ldq, uint8_t* st, int64_t lds) {
+    return mxo_quantize_cols_rule(x, xdt, rows, cols, ldx, fmt, MXO_RULE_FLOOR, qt, ldq, st, lds);
+}
+
+int mxo_quantize_cols_rule(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule,
+                           uint8_t* qt, int64_t ldq, uint8_t* st, int64_t lds) {
     if (rows % MXO_BLOCK != 0 || rows < 0 || cols < 0) return -2;
 #pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < cols; ++c) {
         double v[MXO_BLOCK];
         for (int64_t b = 0; b < rows / MXO_BLOCK; ++b) {
             for (int i = 0; i < MXO_BLOCK; ++i) v[i] = load_elem(x, xdt, (b * MXO_BLOCK + i) * ldx + c);
-            quantize_block(fmt, v, MXO_BLOCK, qt + c * ldq + b * block_bytes(fmt), st + c * lds + b);
+            quantize_block_rule(fmt, rule, v, MXO_BLOCK, qt + c * ldq + b * block_bytes(fmt), st + c * lds + b);
         }
     }
+    return 0;
+}
+
+/* Two-dimensional blocks [SM120 §1.3: weights may share one scale per 32 x 32
+ * block, expanded afterwards to the MXFP8 scale layout, with the FP8 element
+ * and E8M0 encodings unchanged]. Each 32 x 32 block of x gets one scale from
+ * its 1024 values (same rule as a 32-element block); every element is encoded
+ * with it. Outputs, either pair may be NULL:
+ *   q [rows x cols], s [rows x cols/32]: s[r][c/32] = the scale of block
+ *     (r/32, c/32), repeated on the block's 32 rows (the expanded layout);
+ *   qt [cols x rows], st [cols x rows/32]: the same codes and scales for x^T.
+ * Because a 32 x 32 block holds the same elements after a transpose, qt is
+ * exactly the transpose of q. rows % 32 == 0, cols % 32 == 0; E4M3 or E5M2. */
+int mxo_quantize_2d(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule, uint8_t* q,
+                    int64_t ldq, uint8_t* s, int64_t lds, uint8_t* qt, int64_t ldqt, uint8_t* st, int64_t ldst) {
+    if (rows % MXO_BLOCK != 0 || cols % MXO_BLOCK != 0 || rows < 0 || cols < 0 || fmt == MXO_E2M1) return -2;
+    const int64_t br = rows / MXO_BLOCK, bc = cols / MXO_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t blk = 0; blk < br * bc; ++blk) {
+        const int64_t r0 = (blk / bc) * MXO_BLOCK, c0 = (blk % bc) * MXO_BLOCK;
+        double v[MXO_BLOCK * MXO_BLOCK];
+        for (int i = 0; i < MXO_BLOCK; ++i)
+            for (int j = 0; j < MXO_BLOCK; ++j) v[i * MXO_BLOCK + j] = load_elem(x, xdt, (r0 + i) * ldx + c0 + j);
+        const unsigned sc = mxo_scale_code_rule(fmt, v, MXO_BLOCK * MXO_BLOCK, rule);
+        for (int i = 0; i < MXO_BLOCK; ++i) {
+            for (int j = 0; j < MXO_BLOCK; ++j) {
+                const unsigned c = sc == 0xFFu ? 0x7Fu : mxo_encode(fmt, ldexp(v[i * MXO_BLOCK + j], -((int)sc - 127)));
+                if (q) q[(r0 + i) * ldq + c0 + j] = (uint8_t)c;
+                if (qt) qt[(c0 + j) * ldqt + r0 + i] = (uint8_t)c;
+            }
+            if (s) s[(r0 + i) * lds + c0 / MXO_BLOCK] = (uint8_t)sc;
+            if (st) st[(c0 + i) * ldst + r0 / MXO_BLOCK] = (uint8_t)sc;
+        }
+    }
+    return 0;
+}
+
+/* Float8BlockScaling -> MXFP8 scales [SM120 §1.3]: a power-of-two scale of a
+ * 128-element block (layout 0: s_in[r][c/128]) or of a 128 x 128 block
+ * (layout 1: s_in[r/128][c/128]) becomes the E8M0 code of every 32-element
+ * block it covers; the FP8 codes are reused unchanged. s is the dequantizing
+ * factor (x_hat = q * s). A scale that is not a positive power of two 2^k with
+ * -127 <= k <= 127 cannot be held by E8M0 and gives 0xFF (NaN), so its blocks
+ * decode to NaN instead of to wrong values. cols % 128 == 0. */
+static unsigned e8m0_of_pow2(float v) {
+    const double d = (double)v;
+    if (!(d > 0.0) || isinf(d)) return 0xFFu;
+    int e;
+    const double m = frexp(d, &e); /* d = m * 2^e, m in [0.5, 1) */
+    if (m != 0.5) return 0xFFu;
+    const int k = e - 1;
+    if (k < -127 || k > 127) return 0xFFu;
+    return (unsigned)(k + 127);
+}
+
+int mxo_scale_broadcast(const float* s_in, int64_t ld_in, int layout, int64_t rows, int64_t cols, uint8_t* out,
+                        int64_t ld_out) {
+    if (cols % 128 != 0 || rows < 0 || cols < 0 || (layout != 0 && layout != 1)) return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < cols / MXO_BLOCK; ++b) {
+            const int64_t src_row = layout == 0 ? r : r / 128;
+            out[r * ld_out + b] = (uint8_t)e8m0_of_pow2(s_in[src_row * ld_in + (b * MXO_BLOCK) / 128]);
+        }
     return 0;
 }
 

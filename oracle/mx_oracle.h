@@ -13,6 +13,7 @@
 
 enum { MXO_E4M3 = 0, MXO_E5M2 = 1, MXO_E2M1 = 2 };
 enum { MXO_F32 = 0, MXO_BF16 = 1 };
+enum { MXO_RULE_FLOOR = 0, MXO_RULE_CEIL = 1 };
 
 double mxo_decode_e4m3(unsigned code);
 double mxo_decode_e5m2(unsigned code);
@@ -21,6 +22,7 @@ double mxo_decode(int fmt, unsigned code);
 double mxo_decode_e8m0(unsigned e);
 unsigned mxo_encode(int fmt, double y);
 unsigned mxo_scale_code(int fmt, const double* x, int64_t n);
+unsigned mxo_scale_code_rule(int fmt, const double* x, int64_t n, int rule);
 uint16_t mxo_double_to_bf16(double v);
 double mxo_dequant_value(int fmt, unsigned code, unsigned scale);
 
@@ -28,6 +30,14 @@ int mxo_quantize_rows(const void* x, int xdt, int64_t rows, int64_t cols, int64_
                       int64_t ldq, uint8_t* s, int64_t lds);
 int mxo_quantize_cols(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* qt,
                       int64_t ldq, uint8_t* st, int64_t lds);
+int mxo_quantize_rows_rule(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule,
+                           uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds);
+int mxo_quantize_cols_rule(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule,
+                           uint8_t* qt, int64_t ldq, uint8_t* st, int64_t lds);
+int mxo_quantize_2d(const void* x, int xdt, int64_t rows, int64_t cols, int64_t ldx, int fmt, int rule, uint8_t* q,
+                    int64_t ldq, uint8_t* s, int64_t lds, uint8_t* qt, int64_t ldqt, uint8_t* st, int64_t ldst);
+int mxo_scale_broadcast(const float* s_in, int64_t ld_in, int layout, int64_t rows, int64_t cols, uint8_t* out,
+                        int64_t ld_out);
 int mxo_kv_quant_write(const void* k, const void* v, int dt, int64_t T, int64_t H, int64_t D, int64_t ld_token,
                        const int64_t* slot_mapping, uint8_t* k_cache, uint8_t* k_scale, uint8_t* v_cache,
                        uint8_t* v_scale, int64_t page_size, int64_t num_pages);

@@ -746,3 +746,96 @@ def test_e2m1_gemm_unit_scales_and_exact_sum(oracle, afmt, bfmt):
         for n in range(N):
             terms = [Fraction(A[m, k]) * Fraction(SA[m, k]) * Fraction(B[n, k]) * Fraction(SB[n, k]) for k in range(K)]
             assert abs(Fraction(y[m, n]) - sum(terms)) <= Fraction(2) ** -50 * sum(abs(x) for x in terms)
+
+
+# ---------------------------------------------------------------------------
+# Scale variants [MXFP8 SM120 software support, section 1.3; MXFP8
+# quantization glossary: the choice and rounding of the E8M0 scale matter]
+# ---------------------------------------------------------------------------
+RULE_FLOOR, RULE_CEIL = 0, 1
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2, 2])
+def test_ceil_rule_is_the_smallest_power_of_two_that_avoids_clipping(oracle, fmt):
+    maxf = {E4M3: Fraction(448), E5M2: Fraction(57344), 2: Fraction(6)}[fmt]
+    g = inputs.rng(901 + fmt)
+    x = (g.standard_normal((200, 64)) * np.exp2(g.integers(-30, 30, (200, 1)))).astype(np.float32)
+    x[::7, 3] = np.float32(448.0 if fmt == E4M3 else 6.0)  # exact boundaries
+    _, s_floor = oracle.quantize_rows(x, fmt, RULE_FLOOR)
+    q, s = oracle.quantize_rows(x, fmt, RULE_CEIL)
+    for r in range(x.shape[0]):
+        for b in range(2):
+            amax = max(abs(Fraction(float(v))) for v in x[r, 32 * b:32 * b + 32])
+            k = int(s[r, b]) - 127
+            X = Fraction(2) ** k
+            assert amax / X <= maxf and amax / (X / 2) > maxf   # smallest such power of two
+            assert int(s[r, b]) - int(s_floor[r, b]) in (0, 1)   # at most one step above the floor rule
+    # nothing saturates: every element's error is within half a grid step
+    xhat = oracle.dequantize(q, s, fmt, "f32").astype(np.float64)
+    X = np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+    step_rel = {E4M3: 2.0 ** -3, E5M2: 2.0 ** -2, 2: 2.0 ** -1}[fmt]
+    sub = {E4M3: 2.0 ** -9, E5M2: 2.0 ** -16, 2: 0.5}[fmt]
+    half_step = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(x) / X, 1e-300)))) * step_rel, sub) / 2 * X
+    assert np.all(np.abs(xhat - x) <= half_step * (1 + 1e-12))
+
+
+def test_worked_example_has_the_same_scales_under_both_rules(oracle):
+    """[MXFP8 SM120 software support, section 0.1]: the two blocks of the
+    64-element vector get scales 2^2 and 2^-20; the round-up rule agrees
+    (2^10 / 448 and 2^-12 / 448 both round up to those powers)."""
+    ex = load_golden("worked_example_v64.json")
+    v = np.array([[ex["input"]["first_32"]] * 32 + [ex["input"]["last_32"]] * 32], np.float32)
+    for rule in (RULE_FLOOR, RULE_CEIL):
+        q, s = oracle.quantize_rows(v, E4M3, rule)
+        assert [int(c) - 127 for c in s[0]] == ex["per_block"]["scale_exponents"]
+        assert np.all(oracle.dequantize(q, s, E4M3, "f32") == v)
+
+
+def test_2d_blocks(oracle):
+    """One scale per 32 x 32 block [SM120 §1.3]: the block scale is the
+    largest of its 32 rows' 1 x 32 scales (the scale rule is monotone in
+    amax), a block whose every row holds the block maximum quantizes exactly
+    like the 1 x 32 rowwise path, the transposed output is the transpose, and
+    quantizing x^T swaps the two outputs."""
+    x = inputs.normal_bf16(910, (96, 128))
+    xf = inputs.bf16_bits_to_f32(x)
+    q, s, qt, st = oracle.quantize_2d(x, E4M3)
+    _, s_row = oracle.quantize_rows(x, E4M3)
+    for br in range(3):
+        for bc in range(4):
+            blk = s_row[32 * br:32 * br + 32, bc]
+            assert np.all(s[32 * br:32 * br + 32, bc] == blk.max())
+            assert np.all(st[32 * bc:32 * bc + 32, br] == blk.max())
+    assert np.array_equal(qt, q.T)
+    q2, s2, qt2, st2 = oracle.quantize_2d(np.ascontiguousarray(x.T), E4M3)
+    assert np.array_equal(q2, qt) and np.array_equal(s2, st) and np.array_equal(qt2, q) and np.array_equal(st2, s)
+    # every row of a block carries the block maximum: 2D == 1 x 32 rowwise
+    y = xf.copy()
+    y[:, ::32] = 3.0 * np.abs(xf).max()
+    qy, sy, _, _ = oracle.quantize_2d(y, E4M3)
+    qr, sr = oracle.quantize_rows(y, E4M3)
+    assert np.array_equal(qy, qr) and np.array_equal(sy, sr)
+
+
+def test_scale_broadcast(oracle):
+    """[SM120 §1.3]: a power-of-two scale s of a 128-element block becomes the
+    scale of its four 32-element blocks; the codes are reused, so the decoded
+    values are q * s exactly. 128 x 128 blocks broadcast down their rows too.
+    A scale E8M0 cannot hold gives the NaN code."""
+    g = inputs.rng(920)
+    R, C = 200, 512
+    codes = g.integers(0, 0x7E, (R, C), dtype=np.uint8)
+    k = g.integers(-30, 30, (R, C // 128))
+    s_in = np.exp2(k).astype(np.float32)
+    out = oracle.scale_broadcast(s_in, 0, R, C)
+    assert np.array_equal(out, np.repeat((k + 127).astype(np.uint8), 4, axis=1))
+    vals = np.array([float(value_of(c, E4M3)) if (c & 0x7F) != 0x7F else np.nan for c in range(256)])
+    want = vals[codes] * np.repeat(s_in.astype(np.float64), 128, axis=1)
+    assert np.array_equal(oracle.dequantize(codes, out, E4M3, "f32").astype(np.float64), want)
+    k2 = g.integers(-5, 5, ((R + 127) // 128, C // 128))
+    out2 = oracle.scale_broadcast(np.exp2(k2).astype(np.float32), 1, R, C)
+    assert np.array_equal(out2, np.repeat(np.repeat((k2 + 127).astype(np.uint8), 128, axis=0)[:R], 4, axis=1))
+    bad = np.array([[3.0, 0.0, -2.0, np.inf], [2.0 ** -128, 2.0 ** 127, np.nan, 0.5]], np.float32)
+    ob = oracle.scale_broadcast(bad, 0, 2, 512)
+    assert list(ob[0, ::4]) == [0xFF, 0xFF, 0xFF, 0xFF]
+    assert list(ob[1, ::4]) == [0xFF, 254, 0xFF, 126]
