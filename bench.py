@@ -414,6 +414,29 @@ def other_rows(torch, mx, inputs, np, flush, stream, steps, kv_only=False):
     out["quantize_W_colwise"] = {"us": round(ms * 1e3, 2), "GB/s": round(w_bytes / ms / 1e6, 1),
                                  "frac_of_hbm_peak": round(w_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                  "algorithmic_bytes": w_bytes}
+    # scale variants on the same weight: 32 x 32 blocks with the round-up
+    # rule, both orientations in one pass
+    qw2 = torch.empty(Wd.shape, dtype=torch.uint8, device="cuda")
+    sw2 = torch.empty((Wd.shape[0], Wd.shape[1] // 32), dtype=torch.uint8, device="cuda")
+    qwt2, swt2 = torch.empty_like(qwt), torch.empty_like(swt)
+    ms = timed("quantize_W_2d", lambda: mx.mx_quantize_ex(Wd, mx.MX_E4M3, rule=mx.MX_SCALE_CEIL,
+                                                          blocks=mx.MX_BLOCKS_2D, colwise=True, q=qw2, s=sw2,
+                                                          qt=qwt2, st=swt2))
+    w2_bytes = 4 * Wd.numel() + Wd.numel() // 16
+    out["quantize_W_2d_both"] = {"us": round(ms * 1e3, 2), "GB/s": round(w2_bytes / ms / 1e6, 1),
+                                 "frac_of_hbm_peak": round(w2_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                 "algorithmic_bytes": w2_bytes, "rule": "round-up, 32x32 blocks"}
+    del qw2, sw2, qwt2, swt2
+    # FP32 power-of-two scales of 1 x 128 blocks of G -> E8M0 per 32
+    sb_rows, sb_cols = Gd.shape
+    s128 = torch.ones((sb_rows, sb_cols // 128), dtype=torch.float32, device="cuda")
+    sg8 = torch.empty_like(sg)
+    ms = timed("scale_broadcast", lambda: mx.mx_scale_broadcast(s128, sb_rows, sb_cols, out=sg8))
+    sb_bytes = 4 * s128.numel() + sg8.numel()
+    out["scale_broadcast_1x128"] = {"us": round(ms * 1e3, 2), "GB/s": round(sb_bytes / ms / 1e6, 1),
+                                    "frac_of_hbm_peak": round(sb_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                    "algorithmic_bytes": sb_bytes}
+    del s128, sg8
     qx, sx = mx.mx_quantize(Xd, mx.MX_E4M3)
     qw, sw = mx.mx_quantize(Wd, mx.MX_E4M3)
     Yf = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")

@@ -103,6 +103,62 @@ mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int
                                 hipStream_t stream);
 
 /*
+ * mx_quantize_ex -- quantization with a choice of scale rule and block shape
+ * [SM120 §1.3; GLOSS: how the E8M0 scale is chosen and rounded affects
+ * accuracy].
+ *
+ *   rule    MX_SCALE_FLOOR: the rule of mx_quantize (X = 2^(floor(log2 amax)
+ *           - emax_elem); the block maximum may saturate).
+ *           MX_SCALE_CEIL: the smallest power of two X with amax / X <= the
+ *           largest finite element, so no element saturates (one E8M0 step
+ *           above the floor rule when amax's significand exceeds 1.75 (FP8)
+ *           or 1.5 (E2M1), the same otherwise).
+ *   blocks  MX_BLOCKS_1D: 1 x 32 blocks for the rowwise output and 32 x 1
+ *           blocks for the colwise output, as mx_quantize / _colwise.
+ *           MX_BLOCKS_2D: one scale per 32 x 32 block (the 2-D weight
+ *           quantization of [SM120 §1.3]), written in the MXFP8 layout: s
+ *           repeats a block's scale on its 32 rows, st on its 32 columns, and
+ *           the colwise codes are exactly the transpose of the rowwise codes.
+ *           E4M3 / E5M2 only; rows % 32 == 0 and rows / 32 <= 65535.
+ *   q, s    rowwise output [rows x cols] / [rows x cols/32] (pitches ldq,
+ *           lds), or both NULL;
+ *   qt, st  colwise output stored transposed [cols x rows] / [cols x rows/32]
+ *           (pitches ldqt, ldst), or both NULL. At least one pair is given.
+ * Shapes, alignment and E2M1 packing follow mx_quantize / mx_quantize_colwise
+ * (E2M1: rowwise 1-D only).
+ */
+typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_CEIL = 1 } mx_scale_rule_t;
+typedef enum { MX_BLOCKS_1D = 0, MX_BLOCKS_2D = 1 } mx_blocks_t;
+typedef struct mx_quantize_desc {
+    const void* x;  mx_dtype_t xdt;  int64_t rows, cols, ldx;
+    mx_fmt_t fmt;   mx_scale_rule_t rule;  mx_blocks_t blocks;
+    uint8_t* q;  int64_t ldq;  uint8_t* s;  int64_t lds;
+    uint8_t* qt; int64_t ldqt; uint8_t* st; int64_t ldst;
+} mx_quantize_desc_t;
+
+mx_status_t mx_quantize_ex(const mx_quantize_desc_t* desc, hipStream_t stream);
+
+/*
+ * mx_scale_broadcast -- Float8BlockScaling scales to MXFP8 [SM120 §1.3]: a
+ * power-of-two FP32 scale of a 128-element block becomes the E8M0 scale of
+ * each of its four 32-element blocks, so the block's FP8 codes are used by
+ * mx_gemm / mx_dequantize unchanged (nothing is re-quantized).
+ *
+ *   s_in    MX_BCAST_1X128: [rows x cols/128], s_in[r][c/128] scales row r's
+ *           elements c; MX_BCAST_128X128: [ceil(rows/128) x cols/128], one
+ *           scale per 128 x 128 block. Pitch ld_in (elements). s is the
+ *           dequantizing factor: x_hat = q * s.
+ *   out     E8M0 [rows x cols/32], pitch ld_out (bytes, a multiple of 4).
+ * cols % 128 == 0; s_in and out 4-byte aligned. A scale that is not a positive
+ * power of two 2^k with -127 <= k <= 127 gives code 0xFF, so its blocks
+ * decode to NaN rather than to wrong values.
+ */
+typedef enum { MX_BCAST_1X128 = 0, MX_BCAST_128X128 = 1 } mx_bcast_layout_t;
+
+mx_status_t mx_scale_broadcast(const float* s_in, int64_t ld_in, mx_bcast_layout_t layout, int64_t rows,
+                               int64_t cols, uint8_t* out, int64_t ld_out, hipStream_t stream);
+
+/*
  * mx_dequantize -- x_hat = s_b * q_i [SM120 §0.1], exact in f32, then
  * rounded to nearest-even for bf16 output. A scale code 0xFF (NaN) makes its
  * whole block NaN; NaN results are written as the canonical quiet NaN

@@ -17,13 +17,16 @@ Layouts (row-major, unit stride along the last dimension):
 """
 import ctypes
 
-from ._lib import (BLOCK, MX_ACCUM_AUTO, MX_ACCUM_FP8, MX_ACCUM_FP32, MX_BF16, MX_E2M1, MX_E4M3, MX_E5M2, MX_F32, MXError,
-                   check, lib, mx_attention_desc_t, mx_gemm_desc_t, mx_grouped_gemm_desc_t)
+from ._lib import (BLOCK, MX_ACCUM_AUTO, MX_ACCUM_FP8, MX_ACCUM_FP32, MX_BCAST_1X128, MX_BCAST_128X128, MX_BF16,
+                   MX_BLOCKS_1D, MX_BLOCKS_2D, MX_E2M1, MX_E4M3, MX_E5M2, MX_F32, MX_SCALE_CEIL, MX_SCALE_FLOOR,
+                   MXError, check, lib, mx_attention_desc_t, mx_gemm_desc_t, mx_grouped_gemm_desc_t,
+                   mx_quantize_desc_t)
 
 __all__ = [
     "MX_E4M3", "MX_E5M2", "MX_E2M1", "MX_F32", "MX_BF16", "BLOCK", "MXError",
-    "MX_ACCUM_AUTO", "MX_ACCUM_FP8", "MX_ACCUM_FP32",
-    "mx_quantize", "mx_quantize_colwise", "mx_dequantize", "mx_kv_quant_write", "mx_gemm",
+    "MX_ACCUM_AUTO", "MX_ACCUM_FP8", "MX_ACCUM_FP32", "MX_SCALE_FLOOR", "MX_SCALE_CEIL",
+    "MX_BLOCKS_1D", "MX_BLOCKS_2D", "MX_BCAST_1X128", "MX_BCAST_128X128",
+    "mx_quantize", "mx_quantize_colwise", "mx_quantize_ex", "mx_scale_broadcast", "mx_dequantize", "mx_kv_quant_write", "mx_gemm",
     "mx_gemm_desc", "mx_grouped_gemm", "mx_paged_scores", "mx_paged_attention", "mx_status_string",
     "mx_query_support",
 ]
@@ -94,6 +97,48 @@ def mx_quantize_colwise(x, fmt=MX_E4M3, qt=None, st=None, stream=None):
                                                            _p(qt), _ld(qt), _p(st), _ld(st),
                                                            _stream(stream)))
     return qt, st
+
+
+def mx_quantize_ex(x, fmt=MX_E4M3, rule=MX_SCALE_FLOOR, blocks=MX_BLOCKS_1D, rowwise=True, colwise=False,
+                   q=None, s=None, qt=None, st=None, stream=None):
+    """Quantization with a scale rule (MX_SCALE_FLOOR / MX_SCALE_CEIL) and a
+    block shape (MX_BLOCKS_1D: 1x32 rowwise and 32x1 colwise blocks;
+    MX_BLOCKS_2D: one scale per 32x32 block, repeated in the MXFP8 scale
+    layout). Returns (q, s, qt, st); the outputs not asked for are None."""
+    torch = _torch()
+    _rowmajor(x, "x")
+    rows, cols = x.shape
+    u8 = dict(dtype=torch.uint8, device=x.device)
+    d = mx_quantize_desc_t(x=_p(x).value, xdt=_dtype_code(x), rows=rows, cols=cols, ldx=_ld(x), fmt=fmt, rule=rule,
+                           blocks=blocks)
+    if rowwise:
+        q = torch.empty((rows, cols // 2 if fmt == MX_E2M1 else cols), **u8) if q is None else q
+        s = torch.empty((rows, cols // BLOCK), **u8) if s is None else s
+        d.q, d.ldq, d.s, d.lds = _p(q).value, _ld(q), _p(s).value, _ld(s)
+    else:
+        q = s = None
+    if colwise:
+        qt = torch.empty((cols, rows), **u8) if qt is None else qt
+        st = torch.empty((cols, rows // BLOCK), **u8) if st is None else st
+        d.qt, d.ldqt, d.st, d.ldst = _p(qt).value, _ld(qt), _p(st).value, _ld(st)
+    else:
+        qt = st = None
+    check("mx_quantize_ex", lib().mx_quantize_ex(ctypes.byref(d), _stream(stream)))
+    return q, s, qt, st
+
+
+def mx_scale_broadcast(s_in, rows, cols, layout=MX_BCAST_1X128, out=None, stream=None):
+    """Power-of-two FP32 scales of 128-element blocks (layout MX_BCAST_1X128:
+    s_in [rows, cols/128]; MX_BCAST_128X128: [ceil(rows/128), cols/128]) ->
+    E8M0 scales [rows, cols/32] for the same FP8 codes."""
+    torch = _torch()
+    _rowmajor(s_in, "s_in")
+    if s_in.dtype != torch.float32:
+        raise TypeError("s_in must be float32")
+    out = torch.empty((rows, cols // BLOCK), dtype=torch.uint8, device=s_in.device) if out is None else out
+    check("mx_scale_broadcast", lib().mx_scale_broadcast(_p(s_in), _ld(s_in), layout, rows, cols, _p(out), _ld(out),
+                                                         _stream(stream)))
+    return out
 
 
 def mx_dequantize(q, s, fmt=MX_E4M3, out_dtype=None, y=None, stream=None):

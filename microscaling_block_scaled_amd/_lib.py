@@ -19,6 +19,12 @@ MX_BF16 = 1
 MX_ACCUM_AUTO = 0
 MX_ACCUM_FP8 = 1
 MX_ACCUM_FP32 = 2
+MX_SCALE_FLOOR = 0
+MX_SCALE_CEIL = 1
+MX_BLOCKS_1D = 0
+MX_BLOCKS_2D = 1
+MX_BCAST_1X128 = 0
+MX_BCAST_128X128 = 1
 BLOCK = 32
 
 _i64 = ctypes.c_int64
@@ -74,12 +80,23 @@ class mx_grouped_gemm_desc_t(ctypes.Structure):
     ]
 
 
+class mx_quantize_desc_t(ctypes.Structure):
+    _fields_ = [
+        ("x", _p), ("xdt", ctypes.c_int), ("rows", _i64), ("cols", _i64), ("ldx", _i64),
+        ("fmt", ctypes.c_int), ("rule", ctypes.c_int), ("blocks", ctypes.c_int),
+        ("q", _p), ("ldq", _i64), ("s", _p), ("lds", _i64),
+        ("qt", _p), ("ldqt", _i64), ("st", _p), ("ldst", _i64),
+    ]
+
+
 _lib = None
 
 # name -> (restype, argtypes)
 SIGNATURES = {
     "mx_quantize": (_i32, [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _p, _i64, _p, _i64, _p]),
     "mx_quantize_colwise": (_i32, [_p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _p, _i64, _p, _i64, _p]),
+    "mx_quantize_ex": (_i32, [ctypes.POINTER(mx_quantize_desc_t), _p]),
+    "mx_scale_broadcast": (_i32, [_p, _i64, ctypes.c_int, _i64, _i64, _p, _i64, _p]),
     "mx_dequantize": (_i32, [_p, _i64, _p, _i64, ctypes.c_int, _i64, _i64, _p, ctypes.c_int, _i64, _p]),
     "mx_kv_quant_write": (_i32, [_p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p]),
     "mx_gemm": (_i32, [ctypes.POINTER(mx_gemm_desc_t), _p]),

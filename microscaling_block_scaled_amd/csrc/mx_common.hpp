@@ -39,6 +39,22 @@ __device__ __forceinline__ uint32_t scale_code_from_exp(uint32_t E) {
   return E == 255u ? 0xFFu : c;
 }
 
+// Scale code from the largest |x| bit pattern (MBITS significand bits: 7 for
+// bf16, 23 for f32) under either rule. The floor rule is scale_code_from_exp.
+// The round-up rule (the smallest power of two X with amax / X <= the largest
+// finite element) is one step higher exactly when amax's significand exceeds
+// the largest element's: 1.75 for E4M3 and E5M2 (448 = 1.75 * 2^8, 57344 =
+// 1.75 * 2^15), 1.5 for E2M1 (6 = 1.5 * 2^2).
+template <int FMT, int MBITS>
+__device__ __forceinline__ uint32_t scale_code_bits(uint32_t amax_bits, uint32_t round_up) {
+  constexpr uint32_t emax = FMT == MX_E5M2 ? 15u : FMT == MX_E2M1 ? 2u : 8u;
+  constexpr uint32_t thr = (FMT == MX_E2M1 ? 2u : 3u) << (MBITS - 2);
+  const uint32_t E = amax_bits >> MBITS;
+  uint32_t code = scale_code_from_exp<FMT>(E);
+  if (round_up && E != 255u && (amax_bits & ((1u << MBITS) - 1u)) > thr && E + 1u > emax) code = E + 1u - emax;
+  return code;
+}
+
 // The divisor 2^(code - 127) as an f32 (code 0 -> the subnormal 2^-127).
 __device__ __forceinline__ float scale_divisor(uint32_t code) {
   return __uint_as_float(code ? (code << 23) : 0x00400000u);

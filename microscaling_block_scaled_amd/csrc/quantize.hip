@@ -40,6 +40,7 @@ struct RowArgs {
   const void* x2;     // second tensor (V) for the fused KV write
   uint8_t* q2;
   uint8_t* s2;
+  uint32_t round_up;  // 1: the round-up scale rule (see scale_code_bits)
 };
 
 template <typename InT>
@@ -71,11 +72,6 @@ __device__ __forceinline__ uint32_t chunk_amax_bits(const Chunk<InT>& c) {
     uint32_t b = umax(umax(c.w1.x & 0x7FFFFFFFu, c.w1.y & 0x7FFFFFFFu), umax(c.w1.z & 0x7FFFFFFFu, c.w1.w & 0x7FFFFFFFu));
     return umax(a, b);
   }
-}
-
-template <typename InT>
-__device__ __forceinline__ uint32_t exp_field(uint32_t amax_bits) {
-  return sizeof(InT) == 2 ? (amax_bits >> 7) : (amax_bits >> 23);
 }
 
 template <typename InT, int FMT>
@@ -130,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(RowArgs a) {
     // whole quads share `ok` (cols % 32 == 0 and the chunk base is quad aligned)
     if (!ok[u]) continue;
     const uint32_t amax = quad_max_u32(chunk_amax_bits<InT>(c[u]));
-    const uint32_t code = scale_code_from_exp<FMT>(exp_field<InT>(amax));
+    const uint32_t code = scale_code_bits<FMT, sizeof(InT) == 2 ? 7 : 23>(amax, a.round_up);
     const int64_t ldq = KV ? a.head_dim : a.ldq;
     const int64_t lds = KV ? a.head_dim / kBlock : a.lds;
     if constexpr (FMT == MX_E2M1) {
@@ -176,7 +172,7 @@ template <typename InT, int FMT>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restrict__ x, int64_t rows, int64_t cols,
                                                               int64_t ldx, uint8_t* __restrict__ qt, int64_t ldq,
                                                               uint8_t* __restrict__ st, int64_t lds,
-                                                              uint32_t col_tiles) {
+                                                              uint32_t col_tiles, uint32_t round_up) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kColTileCols * kColTileRows];
   __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 4];
   const uint32_t tile_r = blockIdx.x / col_tiles, tile_c = blockIdx.x % col_tiles;
@@ -224,8 +220,8 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
 #pragma unroll
         for (int i = 1; i < 8; ++i) m = pk_max_u16(m, v[i][p] & 0x7FFF7FFFu);
         m = quad_max_pk_u16(m);
-        codes[2 * p] = scale_code_from_exp<FMT>((m & 0xFFFFu) >> 7);
-        codes[2 * p + 1] = scale_code_from_exp<FMT>(m >> 23);
+        codes[2 * p] = scale_code_bits<FMT, 7>(m & 0xFFFFu, round_up);
+        codes[2 * p + 1] = scale_code_bits<FMT, 7>(m >> 16, round_up);
       }
     } else {
 #pragma unroll
@@ -234,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
 #pragma unroll
         for (int i = 1; i < 8; ++i) m = umax(m, v[i][p] & 0x7FFFFFFFu);
         m = quad_max_u32(m);
-        codes[p] = scale_code_from_exp<FMT>(m >> 23);
+        codes[p] = scale_code_bits<FMT, 23>(m, round_up);
       }
     }
     // encode: column c gets two dwords = rows 8b .. 8b+3 and 8b+4 .. 8b+7
@@ -289,6 +285,99 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
 }
 
 // ---------------------------------------------------------------- host side
+// ---------------------------------------------------------------------------
+// Two-dimensional blocks: one scale per 32 x 32 block [SM120 §1.3]. A
+// work-group covers 32 rows x 256 columns (8 blocks); thread t takes row
+// t % 32 of block t / 32, i.e. 32 consecutive elements, so the 32 threads of
+// a block are one half of a wave and reduce its amax with lane exchanges
+// inside the half. Codes go to the rowwise output as two 16-byte stores per
+// row and to the transposed output as 32 byte stores, each instruction
+// writing 32 consecutive bytes of one transposed row. Weights are quantized
+// once per step, so this kernel favours simplicity over the last bit of
+// bandwidth.
+// ---------------------------------------------------------------------------
+template <typename InT, int FMT>
+__global__ __launch_bounds__(kThreads) void quant_2d_kernel(const InT* __restrict__ x, int64_t cols, int64_t ldx,
+                                                            uint8_t* __restrict__ q, int64_t ldq,
+                                                            uint8_t* __restrict__ s, int64_t lds,
+                                                            uint8_t* __restrict__ qt, int64_t ldqt,
+                                                            uint8_t* __restrict__ st, int64_t ldst,
+                                                            uint32_t round_up) {
+  const int64_t r0 = (int64_t)blockIdx.y * kBlock;
+  const int64_t c0 = (int64_t)blockIdx.x * 256 + kBlock * (threadIdx.x >> 5);
+  const uint32_t r = threadIdx.x & 31u;
+  if (c0 >= cols) return;  // cols % 32 == 0: whole blocks, whole half-waves
+  constexpr int W = sizeof(InT) == 2 ? 16 : 32;  // words holding the row's 32 values
+  uint32_t v[W];
+  const InT* src = x + (r0 + r) * ldx + c0;
+#pragma unroll
+  for (int i = 0; i < W / 4; ++i) {
+    const uint4 t = *(const uint4*)((const uint8_t*)src + 16 * i);
+    v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+  }
+  uint32_t amax = 0;
+  if constexpr (W == 16) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) m = pk_max_u16(m, v[i] & 0x7FFF7FFFu);
+    amax = umax(m & 0xFFFFu, m >> 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) amax = umax(amax, v[i] & 0x7FFFFFFFu);
+  }
+#pragma unroll
+  for (int d = 1; d < 32; d <<= 1) amax = umax(amax, (uint32_t)__shfl_xor((int)amax, d));  // stays in the half-wave
+  const uint32_t code = scale_code_bits<FMT, W == 16 ? 7 : 23>(amax, round_up);
+  const float div = scale_divisor(code);
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (W == 16)
+      out[i] = encode4_bf16<FMT>(v[2 * i], v[2 * i + 1], div);
+    else
+      out[i] = encode4_f32<FMT>(__uint_as_float(v[4 * i]), __uint_as_float(v[4 * i + 1]), __uint_as_float(v[4 * i + 2]),
+                                __uint_as_float(v[4 * i + 3]), div);
+    if (code == 0xFFu) out[i] = 0x7F7F7F7Fu;
+  }
+  if (q) {
+    uint4* dst = (uint4*)(q + (r0 + r) * ldq + c0);
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  }
+  if (s) s[(r0 + r) * lds + c0 / kBlock] = (uint8_t)code;
+  if (qt) {
+#pragma unroll
+    for (int j = 0; j < kBlock; ++j) qt[(c0 + j) * ldqt + r0 + r] = (uint8_t)(out[j >> 2] >> (8 * (j & 3)));
+  }
+  if (st) st[(c0 + r) * ldst + r0 / kBlock] = (uint8_t)code;
+}
+
+// ---------------------------------------------------------------------------
+// Scale broadcast [SM120 §1.3]: a power-of-two FP32 scale of a 128-element
+// (or 128 x 128) block becomes the E8M0 code of its four 32-element blocks.
+// A positive normal power of two 2^(E - 127) has code E (its exponent field);
+// 2^-127 is the f32 subnormal 0x00400000 and has code 0; anything else
+// (another subnormal, a significand other than 1, zero, negative, Inf, NaN)
+// gets 0xFF. One thread writes the 4 codes of one source scale.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e8m0_of_pow2_bits(uint32_t b) {
+  const uint32_t E = (b >> 23) & 0xFFu, m = b & 0x7FFFFFu;
+  if ((b >> 31) != 0u || E == 255u) return 0xFFu;
+  if (E >= 1u) return m == 0u ? E : 0xFFu;
+  return m == 0x400000u ? 0u : 0xFFu;
+}
+
+__global__ __launch_bounds__(kThreads) void scale_bcast_kernel(const float* __restrict__ s_in, int64_t ld_in,
+                                                               uint32_t layout, uint32_t n, FastDiv per_row,
+                                                               uint8_t* __restrict__ out, int64_t ld_out) {
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t r = per_row.div(i), cb = i - r * per_row.d;
+  const int64_t src_row = layout ? r / 128 : r;
+  const uint32_t code = e8m0_of_pow2_bits(__float_as_uint(s_in[src_row * ld_in + cb]));
+  *(uint32_t*)(out + (int64_t)r * ld_out + 4 * (int64_t)cb) = code * 0x01010101u;
+}
+
 mx_status_t check_common(const void* x, mx_dtype_t xdt, mx_fmt_t fmt, int64_t rows, int64_t cols, int64_t ldx) {
   if (xdt != MX_F32 && xdt != MX_BF16) return MX_ERR_FORMAT;
   if (fmt != MX_E4M3 && fmt != MX_E5M2) return MX_ERR_FORMAT;
@@ -330,9 +419,10 @@ mx_status_t dispatch_rows(mx_fmt_t fmt, RowArgs a, int64_t rows, int64_t cols, h
 
 }  // namespace
 
-extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
-                                   mx_fmt_t fmt, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
-                                   hipStream_t stream) {
+namespace {
+mx_status_t quantize_rows_host(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx, mx_fmt_t fmt,
+                               uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, uint32_t round_up,
+                               hipStream_t stream) {
   if (!x || !q || !s) return MX_ERR_NULL;
   const bool fp4 = fmt == MX_E2M1;
   mx_status_t st = check_common(x, xdt, fp4 ? MX_E4M3 : fmt, rows, cols, ldx);
@@ -343,10 +433,18 @@ extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t xdt, int64_t rows, 
   if (rows == 0 || cols == 0) return MX_OK;
   RowArgs a{};
   a.x = x; a.q = q; a.s = s; a.ldx = ldx; a.ldq = ldq; a.lds = lds;
+  a.round_up = round_up;
   a.per_row = FastDiv::make((uint32_t)(cols / 8));
   if (cols / 8 >= ((int64_t)1 << 30)) return MX_ERR_SHAPE;
   return xdt == MX_BF16 ? dispatch_rows<uint16_t>(fmt, a, rows, cols, stream)
                         : dispatch_rows<float>(fmt, a, rows, cols, stream);
+}
+}  // namespace
+
+extern "C" mx_status_t mx_quantize(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                                   mx_fmt_t fmt, uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds,
+                                   hipStream_t stream) {
+  return quantize_rows_host(x, xdt, rows, cols, ldx, fmt, q, ldq, s, lds, 0u, stream);
 }
 
 extern "C" mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_t dt, int64_t T, int64_t H, int64_t D,
@@ -393,9 +491,10 @@ extern "C" mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_
   return MX_OK;
 }
 
-extern "C" mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
-                                           mx_fmt_t fmt, uint8_t* qt, int64_t ldq, uint8_t* st, int64_t lds,
-                                           hipStream_t stream) {
+namespace {
+mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx, mx_fmt_t fmt,
+                               uint8_t* qt, int64_t ldq, uint8_t* st, int64_t lds, uint32_t round_up,
+                               hipStream_t stream) {
   if (!x || !qt || !st) return MX_ERR_NULL;
   mx_status_t rc = check_common(x, xdt, fmt, rows, cols, ldx);
   if (rc != MX_OK) return rc;
@@ -409,12 +508,79 @@ extern "C" mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_
   const dim3 grid((uint32_t)(row_tiles * col_tiles));
 #define MX_COLS_LAUNCH(T, F)                                                                                        \
   hipLaunchKernelGGL((quant_cols_kernel<T, F>), grid, dim3(kThreads), 0, stream, (const T*)x, rows, cols, ldx, qt, \
-                     ldq, st, lds, (uint32_t)col_tiles)
+                     ldq, st, lds, (uint32_t)col_tiles, round_up)
   if (xdt == MX_BF16) {
     if (fmt == MX_E5M2) MX_COLS_LAUNCH(uint16_t, MX_E5M2); else MX_COLS_LAUNCH(uint16_t, MX_E4M3);
   } else {
     if (fmt == MX_E5M2) MX_COLS_LAUNCH(float, MX_E5M2); else MX_COLS_LAUNCH(float, MX_E4M3);
   }
 #undef MX_COLS_LAUNCH
+  return mx_host::launch_status();
+}
+
+mx_status_t quantize_2d_host(const mx_quantize_desc_t* d, uint32_t round_up, hipStream_t stream) {
+  const bool rowout = d->q != nullptr, colout = d->qt != nullptr;
+  if (d->fmt != MX_E4M3 && d->fmt != MX_E5M2) return MX_ERR_FORMAT;
+  mx_status_t rc = check_common(d->x, d->xdt, d->fmt, d->rows, d->cols, d->ldx);
+  if (rc != MX_OK) return rc;
+  if (d->rows % kBlock != 0 || d->cols % kBlock != 0 || d->rows / kBlock > 65535) return MX_ERR_SHAPE;
+  if (rowout && (d->ldq < d->cols || d->lds < d->cols / kBlock)) return MX_ERR_SHAPE;
+  if (colout && (d->ldqt < d->rows || d->ldst < d->rows / kBlock)) return MX_ERR_SHAPE;
+  if (rowout && (!mx_host::aligned16(d->q) || d->ldq % 16 != 0)) return MX_ERR_ALIGN;
+  if ((rc = mx_host::check_device()) != MX_OK) return rc;
+  if (d->rows == 0 || d->cols == 0) return MX_OK;
+  const dim3 grid((uint32_t)((d->cols + 255) / 256), (uint32_t)(d->rows / kBlock));
+#define MX_2D_LAUNCH(T, F)                                                                                         \
+  hipLaunchKernelGGL((quant_2d_kernel<T, F>), grid, dim3(kThreads), 0, stream, (const T*)d->x, d->cols, d->ldx,  \
+                     d->q, d->ldq, d->s, d->lds, d->qt, d->ldqt, d->st, d->ldst, round_up)
+  if (d->xdt == MX_BF16) {
+    if (d->fmt == MX_E5M2) MX_2D_LAUNCH(uint16_t, MX_E5M2); else MX_2D_LAUNCH(uint16_t, MX_E4M3);
+  } else {
+    if (d->fmt == MX_E5M2) MX_2D_LAUNCH(float, MX_E5M2); else MX_2D_LAUNCH(float, MX_E4M3);
+  }
+#undef MX_2D_LAUNCH
+  return mx_host::launch_status();
+}
+}  // namespace
+
+extern "C" mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                                           mx_fmt_t fmt, uint8_t* qt, int64_t ldq, uint8_t* st, int64_t lds,
+                                           hipStream_t stream) {
+  return quantize_cols_host(x, xdt, rows, cols, ldx, fmt, qt, ldq, st, lds, 0u, stream);
+}
+
+extern "C" mx_status_t mx_quantize_ex(const mx_quantize_desc_t* d, hipStream_t stream) {
+  if (!d) return MX_ERR_NULL;
+  if (d->rule != MX_SCALE_FLOOR && d->rule != MX_SCALE_CEIL) return MX_ERR_FORMAT;
+  if (d->blocks != MX_BLOCKS_1D && d->blocks != MX_BLOCKS_2D) return MX_ERR_FORMAT;
+  const bool rowout = d->q != nullptr || d->s != nullptr, colout = d->qt != nullptr || d->st != nullptr;
+  if (!d->x || (!rowout && !colout)) return MX_ERR_NULL;
+  if ((rowout && (!d->q || !d->s)) || (colout && (!d->qt || !d->st))) return MX_ERR_NULL;
+  const uint32_t round_up = d->rule == MX_SCALE_CEIL ? 1u : 0u;
+  if (d->blocks == MX_BLOCKS_2D) return quantize_2d_host(d, round_up, stream);
+  if (colout && d->fmt == MX_E2M1) return MX_ERR_FORMAT;
+  mx_status_t rc = MX_OK;
+  if (rowout)
+    rc = quantize_rows_host(d->x, d->xdt, d->rows, d->cols, d->ldx, d->fmt, d->q, d->ldq, d->s, d->lds, round_up, stream);
+  if (rc == MX_OK && colout)
+    rc = quantize_cols_host(d->x, d->xdt, d->rows, d->cols, d->ldx, d->fmt, d->qt, d->ldqt, d->st, d->ldst, round_up,
+                            stream);
+  return rc;
+}
+
+extern "C" mx_status_t mx_scale_broadcast(const float* s_in, int64_t ld_in, mx_bcast_layout_t layout, int64_t rows,
+                                          int64_t cols, uint8_t* out, int64_t ld_out, hipStream_t stream) {
+  if (!s_in || !out) return MX_ERR_NULL;
+  if (layout != MX_BCAST_1X128 && layout != MX_BCAST_128X128) return MX_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || cols % 128 != 0 || ld_in < cols / 128 || ld_out < cols / kBlock) return MX_ERR_SHAPE;
+  if (((uintptr_t)s_in & 3u) != 0 || ((uintptr_t)out & 3u) != 0 || ld_out % 4 != 0) return MX_ERR_ALIGN;
+  mx_status_t rc;
+  if ((rc = mx_host::check_device()) != MX_OK) return rc;
+  if (rows == 0 || cols == 0) return MX_OK;
+  const int64_t n = rows * (cols / 128);
+  if (n >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
+  hipLaunchKernelGGL(scale_bcast_kernel, dim3((uint32_t)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                     s_in, ld_in, layout == MX_BCAST_128X128 ? 1u : 0u, (uint32_t)n,
+                     FastDiv::make((uint32_t)(cols / 128)), out, ld_out);
   return mx_host::launch_status();
 }

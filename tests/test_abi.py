@@ -51,7 +51,8 @@ def test_status_strings_without_gpu(libmx):
     assert "unknown" in libmx.mx_status_string(12345).decode()
 
 
-@pytest.mark.parametrize("name", ["mx_gemm_desc_t", "mx_attention_desc_t", "mx_grouped_gemm_desc_t"])
+@pytest.mark.parametrize("name", ["mx_gemm_desc_t", "mx_attention_desc_t", "mx_grouped_gemm_desc_t",
+                                  "mx_quantize_desc_t"])
 def test_ctypes_descriptor_matches_c_layout(tmp_path, name):
     """Compile a probe against the real header with gcc and compare field
     offsets and size with the ctypes mirror used by the binding."""
@@ -132,3 +133,44 @@ def test_mxfp4_argument_errors_without_gpu(libmx):
     q = libmx.mx_quantize_colwise
     q.restype, q.argtypes = _lib.SIGNATURES["mx_quantize_colwise"]
     assert q(0x10000, 1, 64, 64, 64, 2, 0x20000, 64, 0x30000, 2, None) == -4  # colwise MXFP4 not offered
+
+
+def test_scale_variant_argument_errors_without_gpu(libmx):
+    """mx_quantize_ex and mx_scale_broadcast check rule, block shape, shapes
+    and alignment on the host before any device call."""
+    from microscaling_block_scaled_amd import _lib
+    f = libmx.mx_quantize_ex
+    f.restype, f.argtypes = _lib.SIGNATURES["mx_quantize_ex"]
+
+    def desc(**kw):
+        d = _lib.mx_quantize_desc_t()
+        base = dict(x=0x10000, xdt=1, rows=64, cols=64, ldx=64, fmt=0, rule=1, blocks=1, q=0x20000, ldq=64,
+                    s=0x30000, lds=2, qt=0x40000, ldqt=64, st=0x50000, ldst=2)
+        base.update(kw)
+        for k, v in base.items():
+            setattr(d, k, v)
+        return d
+
+    assert f(None, None) == -1
+    assert f(ctypes.byref(desc(x=None)), None) == -1
+    assert f(ctypes.byref(desc(q=None, s=None, qt=None, st=None)), None) == -1  # no output asked for
+    assert f(ctypes.byref(desc(s=None)), None) == -1                          # half an output pair
+    assert f(ctypes.byref(desc(rule=2)), None) == -4
+    assert f(ctypes.byref(desc(blocks=3)), None) == -4
+    assert f(ctypes.byref(desc(fmt=2)), None) == -4                           # 2-D MXFP4 not offered
+    assert f(ctypes.byref(desc(blocks=0, fmt=2, q=None, s=None)), None) == -4  # colwise MXFP4 not offered
+    assert f(ctypes.byref(desc(rows=48, ldqt=48)), None) == -2                # rows % 32
+    assert f(ctypes.byref(desc(rows=32 * 65536, ldqt=32 * 65536, ldst=65536)), None) == -2  # grid rows
+    assert f(ctypes.byref(desc(ldq=32)), None) == -2
+    assert f(ctypes.byref(desc(ldst=1)), None) == -2
+    assert f(ctypes.byref(desc(q=0x20008)), None) == -3
+    assert f(ctypes.byref(desc(x=0x10004)), None) == -3
+    b = libmx.mx_scale_broadcast
+    b.restype, b.argtypes = _lib.SIGNATURES["mx_scale_broadcast"]
+    assert b(None, 2, 0, 64, 256, 0x20000, 8, None) == -1
+    assert b(0x10000, 2, 2, 64, 256, 0x20000, 8, None) == -4                  # layout
+    assert b(0x10000, 2, 0, 64, 224, 0x20000, 8, None) == -2                  # cols % 128
+    assert b(0x10000, 1, 0, 64, 256, 0x20000, 8, None) == -2                  # ld_in below cols / 128
+    assert b(0x10000, 2, 0, 64, 256, 0x20000, 4, None) == -2                  # ld_out below cols / 32
+    assert b(0x10002, 2, 0, 64, 256, 0x20000, 8, None) == -3
+    assert b(0x10000, 2, 0, 64, 256, 0x20000, 10, None) == -3                 # ld_out % 4
