@@ -119,7 +119,7 @@ mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int
  *           quantization of [SM120 §1.3]), written in the MXFP8 layout: s
  *           repeats a block's scale on its 32 rows, st on its 32 columns, and
  *           the colwise codes are exactly the transpose of the rowwise codes.
- *           E4M3 / E5M2 only; rows % 32 == 0 and rows / 32 <= 65535.
+ *           E4M3 / E5M2 only; rows % 32 == 0.
  *   q, s    rowwise output [rows x cols] / [rows x cols/32] (pitches ldq,
  *           lds), or both NULL;
  *   qt, st  colwise output stored transposed [cols x rows] / [cols x rows/32]

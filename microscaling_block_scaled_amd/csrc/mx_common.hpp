@@ -139,6 +139,7 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b 
 #define MX_DPP_QUAD_XOR1 0xB1   // quad_perm [1,0,3,2]
 #define MX_DPP_QUAD_XOR2 0x4E   // quad_perm [2,3,0,1]
 #define MX_DPP_HALF_MIRROR 0x141  // reverse within each group of 8 lanes
+#define MX_DPP_ROW_MIRROR 0x140   // reverse within each group of 16 lanes
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
@@ -163,6 +164,11 @@ __device__ __forceinline__ uint32_t oct_max_u32(uint32_t v) {
   v = umax(v, dpp<MX_DPP_QUAD_XOR1>(v));
   v = umax(v, dpp<MX_DPP_QUAD_XOR2>(v));
   return umax(v, dpp<MX_DPP_HALF_MIRROR>(v));
+}
+// max over the 16 lanes of a DPP row
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = oct_max_u32(v);
+  return umax(v, dpp<MX_DPP_ROW_MIRROR>(v));
 }
 
 // ---------------------------------------------------------------- division

@@ -156,6 +156,14 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(RowArgs a) {
 // block row) are gathered in LDS and leave as one 4-byte store. Tiles are
 // ordered along the rows of x, so the work-groups in flight read whole rows
 // (grouping a column tile's row tiles on one XCD was measured 9 % slower).
+//
+// B2D: two-dimensional blocks, one scale per 32 x 32 block [SM120 §1.3]. The
+// 16 lanes of a DPP row hold one whole block (4 column groups x 4 row
+// groups), so the block's amax is a 16-lane reduction and every column of the
+// block takes that code. The tile's transposed codes leave as above (qt may be
+// NULL), and the rowwise codes are encoded a second time along the rows and
+// stored straight from registers: each store instruction writes 4 rows x 128
+// contiguous bytes. The rowwise scales are 4 bytes per row (q may be NULL).
 // ---------------------------------------------------------------------------
 constexpr int kColTileRows = 128;
 constexpr int kColTileCols = 128;
@@ -168,11 +176,13 @@ __device__ __forceinline__ uint32_t col_lds_offset(uint32_t c, uint32_t rbyte) {
   return c * 128u + ((((rbyte >> 4) ^ (2u * (c >> 3))) & 7u) << 4) + (rbyte & 15u);
 }
 
-template <typename InT, int FMT>
+template <typename InT, int FMT, bool B2D>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restrict__ x, int64_t rows, int64_t cols,
                                                               int64_t ldx, uint8_t* __restrict__ qt, int64_t ldq,
                                                               uint8_t* __restrict__ st, int64_t lds,
-                                                              uint32_t col_tiles, uint32_t round_up) {
+                                                              uint32_t col_tiles, uint32_t round_up,
+                                                              uint8_t* __restrict__ q2, int64_t ldq2,
+                                                              uint8_t* __restrict__ s2, int64_t lds2) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kColTileCols * kColTileRows];
   __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 4];
   const uint32_t tile_r = blockIdx.x / col_tiles, tile_c = blockIdx.x % col_tiles;
@@ -213,7 +223,50 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
     }
     // per-column amax over the lane's 8 rows, then over the 4 lanes of the quad
     uint32_t codes[8];
-    if constexpr (W == 4) {
+    if constexpr (B2D) {
+      // block amax: the lane's 64 values, then the 16 lanes of the block
+      uint32_t m = 0;
+      if constexpr (W == 4) {
+        uint32_t pm = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) pm = pk_max_u16(pm, v[i][p] & 0x7FFF7FFFu);
+        m = umax(pm & 0xFFFFu, pm >> 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int p = 0; p < 8; ++p) m = umax(m, v[i][p] & 0x7FFFFFFFu);
+      }
+      const uint32_t code = scale_code_bits<FMT, W == 4 ? 7 : 23>(row16_max_u32(m), round_up);
+#pragma unroll
+      for (int ci = 0; ci < 8; ++ci) codes[ci] = code;
+      if (q2 && ncol == 8) {  // cols % 32 == 0: a lane's 8 columns are all in or all out
+        // rowwise codes: row 8b + i, columns cc .. cc + 7
+        const float div = scale_divisor(code);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint2 o;
+          if constexpr (W == 4) {
+            o.x = encode4_bf16<FMT>(v[i][0], v[i][1], div);
+            o.y = encode4_bf16<FMT>(v[i][2], v[i][3], div);
+          } else {
+            o.x = encode4_f32<FMT>(__uint_as_float(v[i][0]), __uint_as_float(v[i][1]), __uint_as_float(v[i][2]),
+                                   __uint_as_float(v[i][3]), div);
+            o.y = encode4_f32<FMT>(__uint_as_float(v[i][4]), __uint_as_float(v[i][5]), __uint_as_float(v[i][6]),
+                                   __uint_as_float(v[i][7]), div);
+          }
+          if (code == 0xFFu) o = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+          *(uint2*)(q2 + (rblk + 8 * b + i) * ldq2 + cc) = o;
+        }
+        // rowwise scales: the first column group of each block writes its 8 rows
+        if ((k & 3u) == 0u) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s2[(rblk + 8 * b + i) * lds2 + cc / kBlock] = (uint8_t)code;
+        }
+      }
+    } else if constexpr (W == 4) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         uint32_t m = v[0][p] & 0x7FFF7FFFu;
@@ -236,6 +289,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
     // encode: column c gets two dwords = rows 8b .. 8b+3 and 8b+4 .. 8b+7
 #pragma unroll
     for (int ci = 0; ci < 8; ++ci) {
+      if (B2D && !qt) break;
       const float div = scale_divisor(codes[ci]);
       uint32_t d[2];
 #pragma unroll
@@ -258,6 +312,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
       if (b == 0) stile[c * 4 + wave] = (uint8_t)codes[ci];
     }
   }
+  if (B2D && !qt) return;  // uniform over the grid: rowwise output only
   __syncthreads();
   // codes: 128 columns x 128 bytes = 1024 chunks of 16 bytes
 #pragma unroll
@@ -285,73 +340,6 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
 }
 
 // ---------------------------------------------------------------- host side
-// ---------------------------------------------------------------------------
-// Two-dimensional blocks: one scale per 32 x 32 block [SM120 §1.3]. A
-// work-group covers 32 rows x 256 columns (8 blocks); thread t takes row
-// t % 32 of block t / 32, i.e. 32 consecutive elements, so the 32 threads of
-// a block are one half of a wave and reduce its amax with lane exchanges
-// inside the half. Codes go to the rowwise output as two 16-byte stores per
-// row and to the transposed output as 32 byte stores, each instruction
-// writing 32 consecutive bytes of one transposed row. Weights are quantized
-// once per step, so this kernel favours simplicity over the last bit of
-// bandwidth.
-// ---------------------------------------------------------------------------
-template <typename InT, int FMT>
-__global__ __launch_bounds__(kThreads) void quant_2d_kernel(const InT* __restrict__ x, int64_t cols, int64_t ldx,
-                                                            uint8_t* __restrict__ q, int64_t ldq,
-                                                            uint8_t* __restrict__ s, int64_t lds,
-                                                            uint8_t* __restrict__ qt, int64_t ldqt,
-                                                            uint8_t* __restrict__ st, int64_t ldst,
-                                                            uint32_t round_up) {
-  const int64_t r0 = (int64_t)blockIdx.y * kBlock;
-  const int64_t c0 = (int64_t)blockIdx.x * 256 + kBlock * (threadIdx.x >> 5);
-  const uint32_t r = threadIdx.x & 31u;
-  if (c0 >= cols) return;  // cols % 32 == 0: whole blocks, whole half-waves
-  constexpr int W = sizeof(InT) == 2 ? 16 : 32;  // words holding the row's 32 values
-  uint32_t v[W];
-  const InT* src = x + (r0 + r) * ldx + c0;
-#pragma unroll
-  for (int i = 0; i < W / 4; ++i) {
-    const uint4 t = *(const uint4*)((const uint8_t*)src + 16 * i);
-    v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-  }
-  uint32_t amax = 0;
-  if constexpr (W == 16) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < W; ++i) m = pk_max_u16(m, v[i] & 0x7FFF7FFFu);
-    amax = umax(m & 0xFFFFu, m >> 16);
-  } else {
-#pragma unroll
-    for (int i = 0; i < W; ++i) amax = umax(amax, v[i] & 0x7FFFFFFFu);
-  }
-#pragma unroll
-  for (int d = 1; d < 32; d <<= 1) amax = umax(amax, (uint32_t)__shfl_xor((int)amax, d));  // stays in the half-wave
-  const uint32_t code = scale_code_bits<FMT, W == 16 ? 7 : 23>(amax, round_up);
-  const float div = scale_divisor(code);
-  uint32_t out[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if constexpr (W == 16)
-      out[i] = encode4_bf16<FMT>(v[2 * i], v[2 * i + 1], div);
-    else
-      out[i] = encode4_f32<FMT>(__uint_as_float(v[4 * i]), __uint_as_float(v[4 * i + 1]), __uint_as_float(v[4 * i + 2]),
-                                __uint_as_float(v[4 * i + 3]), div);
-    if (code == 0xFFu) out[i] = 0x7F7F7F7Fu;
-  }
-  if (q) {
-    uint4* dst = (uint4*)(q + (r0 + r) * ldq + c0);
-    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-  }
-  if (s) s[(r0 + r) * lds + c0 / kBlock] = (uint8_t)code;
-  if (qt) {
-#pragma unroll
-    for (int j = 0; j < kBlock; ++j) qt[(c0 + j) * ldqt + r0 + r] = (uint8_t)(out[j >> 2] >> (8 * (j & 3)));
-  }
-  if (st) st[(c0 + r) * ldst + r0 / kBlock] = (uint8_t)code;
-}
-
 // ---------------------------------------------------------------------------
 // Scale broadcast [SM120 §1.3]: a power-of-two FP32 scale of a 128-element
 // (or 128 x 128) block becomes the E8M0 code of its four 32-element blocks.
@@ -507,8 +495,8 @@ mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int6
   if (row_tiles * col_tiles >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const dim3 grid((uint32_t)(row_tiles * col_tiles));
 #define MX_COLS_LAUNCH(T, F)                                                                                        \
-  hipLaunchKernelGGL((quant_cols_kernel<T, F>), grid, dim3(kThreads), 0, stream, (const T*)x, rows, cols, ldx, qt, \
-                     ldq, st, lds, (uint32_t)col_tiles, round_up)
+  hipLaunchKernelGGL((quant_cols_kernel<T, F, false>), grid, dim3(kThreads), 0, stream, (const T*)x, rows, cols, ldx, \
+                     qt, ldq, st, lds, (uint32_t)col_tiles, round_up, nullptr, 0, nullptr, 0)
   if (xdt == MX_BF16) {
     if (fmt == MX_E5M2) MX_COLS_LAUNCH(uint16_t, MX_E5M2); else MX_COLS_LAUNCH(uint16_t, MX_E4M3);
   } else {
@@ -523,16 +511,21 @@ mx_status_t quantize_2d_host(const mx_quantize_desc_t* d, uint32_t round_up, hip
   if (d->fmt != MX_E4M3 && d->fmt != MX_E5M2) return MX_ERR_FORMAT;
   mx_status_t rc = check_common(d->x, d->xdt, d->fmt, d->rows, d->cols, d->ldx);
   if (rc != MX_OK) return rc;
-  if (d->rows % kBlock != 0 || d->cols % kBlock != 0 || d->rows / kBlock > 65535) return MX_ERR_SHAPE;
+  if (d->rows % kBlock != 0 || d->cols % kBlock != 0) return MX_ERR_SHAPE;
   if (rowout && (d->ldq < d->cols || d->lds < d->cols / kBlock)) return MX_ERR_SHAPE;
   if (colout && (d->ldqt < d->rows || d->ldst < d->rows / kBlock)) return MX_ERR_SHAPE;
   if (rowout && (!mx_host::aligned16(d->q) || d->ldq % 16 != 0)) return MX_ERR_ALIGN;
+  if (colout && (!mx_host::aligned16(d->qt) || d->ldqt % 16 != 0)) return MX_ERR_ALIGN;
   if ((rc = mx_host::check_device()) != MX_OK) return rc;
   if (d->rows == 0 || d->cols == 0) return MX_OK;
-  const dim3 grid((uint32_t)((d->cols + 255) / 256), (uint32_t)(d->rows / kBlock));
-#define MX_2D_LAUNCH(T, F)                                                                                         \
-  hipLaunchKernelGGL((quant_2d_kernel<T, F>), grid, dim3(kThreads), 0, stream, (const T*)d->x, d->cols, d->ldx,  \
-                     d->q, d->ldq, d->s, d->lds, d->qt, d->ldqt, d->st, d->ldst, round_up)
+  const int64_t row_tiles = (d->rows + kColTileRows - 1) / kColTileRows;
+  const int64_t col_tiles = (d->cols + kColTileCols - 1) / kColTileCols;
+  if (row_tiles * col_tiles >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
+  const dim3 grid((uint32_t)(row_tiles * col_tiles));
+#define MX_2D_LAUNCH(T, F)                                                                                          \
+  hipLaunchKernelGGL((quant_cols_kernel<T, F, true>), grid, dim3(kThreads), 0, stream, (const T*)d->x, d->rows,   \
+                     d->cols, d->ldx, d->qt, d->ldqt, d->st, d->ldst, (uint32_t)col_tiles, round_up, d->q, d->ldq, \
+                     d->s, d->lds)
   if (d->xdt == MX_BF16) {
     if (d->fmt == MX_E5M2) MX_2D_LAUNCH(uint16_t, MX_E5M2); else MX_2D_LAUNCH(uint16_t, MX_E4M3);
   } else {

@@ -160,7 +160,7 @@ def test_scale_variant_argument_errors_without_gpu(libmx):
     assert f(ctypes.byref(desc(fmt=2)), None) == -4                           # 2-D MXFP4 not offered
     assert f(ctypes.byref(desc(blocks=0, fmt=2, q=None, s=None)), None) == -4  # colwise MXFP4 not offered
     assert f(ctypes.byref(desc(rows=48, ldqt=48)), None) == -2                # rows % 32
-    assert f(ctypes.byref(desc(rows=32 * 65536, ldqt=32 * 65536, ldst=65536)), None) == -2  # grid rows
+    assert f(ctypes.byref(desc(qt=0x40008)), None) == -3                      # transposed codes 16-aligned
     assert f(ctypes.byref(desc(ldq=32)), None) == -2
     assert f(ctypes.byref(desc(ldst=1)), None) == -2
     assert f(ctypes.byref(desc(q=0x20008)), None) == -3
