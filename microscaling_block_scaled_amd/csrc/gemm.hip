@@ -49,6 +49,7 @@ struct GemmArgs {
   int64_t batch_inner;
   int64_t sa_o, sa_i, ssa_o, ssa_i, sb_o, sb_i, ssb_o, ssb_i, sy_o, sy_i;
   const int32_t* page_table; int64_t pages_per_seq, page_rows, page_stride, page_stride_s;
+  FastDiv page_div;  // row -> (page, offset) for row indices below 2^30 (the row-panel kernel's)
   uint32_t tiles_m, tiles_n;
   uint32_t scales_dword;  // 1: every row's 4 scale bytes of a K step can be read as one aligned dword
   uint32_t y_vec;         // 1: output rows allow 8/16-byte vector stores
@@ -287,6 +288,7 @@ template <int AFMT, int BFMT, bool BF16OUT, bool PAGED>
 __global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uint32_t row_blocks, uint32_t nprob) {
   __shared__ __attribute__((aligned(16))) uint8_t Bs[kRPMaxN * kBK];
   __shared__ uint32_t sBs[kRPMaxN];
+  __shared__ int32_t sPage[PAGED ? kRPMaxN : 1];
 
   // work-group -> (problem, row block); with 8 or more problems and a
   // problem count divisible by 8, the row blocks of problem p run on XCD p % 8
@@ -308,14 +310,23 @@ __global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uin
     B += po * g.sb_o;
     SB += po * g.ssb_o;
   }
+  const int tid = threadIdx.x;
+  // Paged B: the problem's page-table entries (at most N <= 512) go to LDS
+  // first, so every row address below is one LDS read and a multiply-high
+  // split instead of a dependent global load and a 64-bit division each
+  // (that chain made the loads of a thread go out one round trip at a time).
+  if (PAGED) {
+    const uint32_t npages = g.page_div.div((uint32_t)g.N - 1u) + 1u;  // host: <= pages_per_seq
+    for (uint32_t i = tid; i < npages; i += kThreads) sPage[i] = g.page_table[po * g.pages_per_seq + i];
+    __syncthreads();
+  }
   auto b_row_ptr = [&](int64_t n, const uint8_t* base, int64_t ld, int64_t pstride) -> const uint8_t* {
     if (PAGED) {
-      const int32_t page = g.page_table[po * g.pages_per_seq + n / g.page_rows];
-      return base + (int64_t)page * pstride + (n % g.page_rows) * ld;
+      const uint32_t pg = g.page_div.div((uint32_t)n);
+      return base + (int64_t)sPage[pg] * pstride + (int64_t)((uint32_t)n - pg * g.page_div.d) * ld;
     }
     return base + n * ld;
   };
-  const int tid = threadIdx.x;
   const int64_t kblocks = g.K / kBlock;  // 1 .. 4
   const bool dword_ok = g.scales_dword != 0;
 
@@ -1006,6 +1017,9 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   g.sb_o = d->stride_b_outer; g.sb_i = d->stride_b_inner; g.ssb_o = d->stride_sb_outer; g.ssb_i = d->stride_sb_inner;
   g.sy_o = d->stride_y_outer; g.sy_i = d->stride_y_inner;
   g.page_table = d->b_page_table; g.pages_per_seq = d->b_pages_per_seq; g.page_rows = d->b_page_rows;
+  // the divider serves row indices below 2^30, for which a page of 2^30 rows
+  // or more splits the same way as the real page size
+  if (paged) g.page_div = FastDiv::make((uint32_t)std::min<int64_t>(d->b_page_rows, (int64_t)1 << 30));
   g.page_stride = d->b_page_stride; g.page_stride_s = d->b_page_stride_s;
   // dword scale reads need 4-byte aligned scale rows in every problem and page
   const bool sa4 = ((uintptr_t)d->sa % 4 == 0) && d->ldsa % 4 == 0 && d->stride_sa_outer % 4 == 0 && d->stride_sa_inner % 4 == 0;
