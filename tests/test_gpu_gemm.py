@@ -220,12 +220,15 @@ def test_padded_pitches_and_unaligned_scale_rows(mx, oracle):
     assert np.all(Yh[:, N:] == -7.0)
 
 
-def test_batched_paged_scores_small(mx, oracle):
-    """Paged QK^T: 3 sequences x 2 heads, seq_len 96 on pages of 32 rows."""
+@pytest.mark.parametrize("L,page", [(96, 32), (96, 24), (100, 24), (90, 48), (90, 128)])
+def test_batched_paged_scores_small(mx, oracle, L, page):
+    """Paged QK^T: 3 sequences x 2 heads on pages of `page` rows, including
+    page sizes that are not powers of two and a last page left partly empty
+    (the kernel splits row indices into (page, offset) by multiply-high)."""
     torch = _torch()
-    S, L, H, D, page = 3, 96, 2, 64, 32
-    n_pages = 12
-    pages_per_seq = L // page
+    S, H, D = 3, 2, 64
+    pages_per_seq = -(-L // page)
+    n_pages = S * pages_per_seq + 3
     k = inputs.normal_bf16(71, (S * L, H, D))
     q = inputs.normal_bf16(72, (S * L, H, D))
     perm = inputs.rng(73).permutation(n_pages)
