@@ -123,8 +123,10 @@ def test_every_bf16_input_under_every_scale(mx, oracle, fmt):
 
 
 # --------------------------------------------------------------------------- colwise
+# (96, 8200) and (288, 8192) have 64 or more column tiles, where the tiles
+# are ordered down the columns
 COL_SHAPES = [(32, 1, 8), (64, 7, 1), (96, 65, 7), (160, 100, 4), (128, 64, 0), (256, 1000, 8), (4096, 96, 0),
-              (160, 1024, 0), (96, 2043, 5), (384, 1032, 0)]
+              (160, 1024, 0), (96, 2043, 5), (384, 1032, 0), (96, 8200, 3), (288, 8192, 0)]
 
 
 @pytest.mark.parametrize("rows,cols,pad", COL_SHAPES)

@@ -107,7 +107,7 @@ def test_floor_rule_matches_mx_quantize(mx):
 @pytest.mark.parametrize("fmt", [E4M3, E5M2])
 @pytest.mark.parametrize("rule", [FLOOR, CEIL])
 @pytest.mark.parametrize("f32", [False, True])
-@pytest.mark.parametrize("rows,cols,seed", [(32, 32, 1), (96, 320, 2), (256, 1056, 3)])
+@pytest.mark.parametrize("rows,cols,seed", [(32, 32, 1), (96, 320, 2), (256, 1056, 3), (160, 8224, 4)])
 def test_2d_blocks(mx, oracle, fmt, rule, f32, rows, cols, seed):
     x = planted(730 + seed, (rows, cols), f32)
     q, s, qt, st = mx.mx_quantize_ex(to_dev(x), fmt, rule=rule, blocks=mx.MX_BLOCKS_2D, colwise=True)
