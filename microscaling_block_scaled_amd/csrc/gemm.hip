@@ -460,9 +460,8 @@ __global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uin
 // of its 64 (checked on the device), so the two 16-byte chunks a lane reads
 // for a K half are the operands of two instructions (the upper half of each
 // 8-register operand is left undefined and the compiler narrows it to 4
-// registers). A stage has 8 scale blocks, so a group of 4 stages needs 32
-// scale bytes per row: the second 16 go to a second pair of buffers. Requires
-// K % 1024 == 0.
+// registers). A stage has 8 scale blocks, so its scale groups hold 2 stages
+// (16 bytes per row) instead of 4. Requires K % 1024 == 0.
 // ---------------------------------------------------------------------------
 // Two f32 -> two bf16 in one v_cvt_pk_bf16_f32 (round to nearest even; checked
 // on the device against the integer rounding for every non-NaN f32 pattern).
@@ -473,7 +472,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float a, float b) {
 }
 constexpr int kFBM = 256, kFBN = 256, kFBK = 128;
 constexpr uint32_t kCodeStage = kFBM * kFBK;   // bytes per operand per stage
-constexpr uint32_t kScaleRow = 16;             // scale bytes per row per group of 4 stages
+constexpr uint32_t kScaleRow = 16;             // scale bytes per row per scale group (4 FP8 / 2 FP4 stages)
 constexpr uint32_t kScaleBuf = kFBM * kScaleRow;
 
 // Direct global -> LDS load of one dword per lane.
@@ -487,8 +486,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t sAs[2][kScaleBuf];
   __shared__ __attribute__((aligned(16))) uint8_t sBs[2][kScaleBuf];
   constexpr bool kFP4 = MODE == kModeFP4;
-  __shared__ __attribute__((aligned(16))) uint8_t sAs2[2][kFP4 ? kScaleBuf : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t sBs2[2][kFP4 ? kScaleBuf : 16];
+  // stages per scale group: 16 scale bytes per row hold 4 FP8 stages (4 blocks
+  // each) or 2 FP4 stages (8 blocks each)
+  constexpr int kG = kFP4 ? 2 : 4;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -585,8 +585,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   const uint32_t a_dst = lds_off(&As[0][0]) + wave * 64 * kFBK, b_dst = lds_off(&Bs[0][0]) + wave * 64 * kFBK;
   const uint32_t sa_dst = lds_off(&sAs[0][0]) + wave * 64 * kScaleRow;
   const uint32_t sb_dst = lds_off(&sBs[0][0]) + wave * 64 * kScaleRow;
-  const uint32_t sa2_dst = lds_off(&sAs2[0][0]) + (kFP4 ? wave * 64 * kScaleRow : 0);
-  const uint32_t sb2_dst = lds_off(&sBs2[0][0]) + (kFP4 ? wave * 64 * kScaleRow : 0);
   // L2 prefetch. The 32 work-groups that an XCD runs at once (4 tile rows x
   // 8 tile columns) walk K together, so without it every stage's lines are
   // new to that XCD's L2 and each stage's loads wait for HBM. Four stages
@@ -600,10 +598,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   // kernel's cycles (load waits 12.2k -> 3.0k, slow second halves 99.7k ->
   // 82.8k per wave). With N(0,1) operands the part is at its power limit and
   // the clock drops from 1.85 to 1.70 GHz, so the time gains ~1-8 %; with
-  // less toggling operands it gains 9 %. Only the FP8 mode uses it: the FP4
-  // mode fills the LDS, and the FP32-accumulation mode measured 1 % slower.
-  constexpr int kPF = MODE == kModeFP8 ? 1 : 0;
-  __shared__ __attribute__((aligned(16))) uint8_t pf_sink[kFP4 ? 16 : 256];
+  // less toggling operands it gains 9 %. The FP8 and FP4 modes use it; the
+  // FP32-accumulation mode measured no gain (its slow second halves are not
+  // load waits).
+  constexpr int kPF = MODE != kModeBF16 ? 1 : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t pf_sink[kPF ? 256 : 16];  // 64 lanes x 4 bytes
   const uint32_t pf_dst = lds_off(&pf_sink[0]);
   const uint8_t* pf_base = wave < 2 ? a_base : b_base;
   uint32_t pf_off;
@@ -638,13 +637,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   };
   auto issue_scales = [&](int64_t grp) {
     const uint32_t buf = (uint32_t)(grp & 1);
-    constexpr uint32_t gbytes = kFP4 ? 2 * kScaleRow : kScaleRow;  // scale bytes per row per group
-    dma16(sa_dst + buf * kScaleBuf, sa_off, sa_base + grp * gbytes);
-    dma16(sb_dst + buf * kScaleBuf, sb_off, sb_base + grp * gbytes);
-    if constexpr (kFP4) {
-      dma16(sa2_dst + buf * kScaleBuf, sa_off, sa_base + grp * gbytes + kScaleRow);
-      dma16(sb2_dst + buf * kScaleBuf, sb_off, sb_base + grp * gbytes + kScaleRow);
-    }
+    dma16(sa_dst + buf * kScaleBuf, sa_off, sa_base + grp * kScaleRow);
+    dma16(sb_dst + buf * kScaleBuf, sb_off, sb_base + grp * kScaleRow);
   };
 
   // ---- fragment reads: lane (lr, lg) of fragment f reads row base + 32 f;
@@ -657,8 +651,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   const uint8_t* b_row = &Bs[0][0] + (wn * 128 + lr) * kFBK;
   const uint8_t* a_sc = &sAs[0][0] + (wm * 128 + lr) * kScaleRow;
   const uint8_t* b_sc = &sBs[0][0] + (wn * 128 + lr) * kScaleRow;
-  const uint8_t* a_sc2 = &sAs2[0][0] + (kFP4 ? (wm * 128 + lr) * kScaleRow : 0);
-  const uint8_t* b_sc2 = &sBs2[0][0] + (kFP4 ? (wn * 128 + lr) * kScaleRow : 0);
   // K half h of a stage: logical chunks 4h + lg and 4h + 2 + lg
   const uint32_t c_lo[2] = {((0 + lg) ^ fp) << 4, ((4 + lg) ^ fp) << 4};
   const uint32_t c_hi[2] = {((2 + lg) ^ fp) << 4, ((6 + lg) ^ fp) << 4};
@@ -676,7 +668,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   // byte 0 (after the shift by 8 lg) is the scale of the half's first
   // instruction and byte 2 that of its second.)
   uint4 sa4[4], sb4[4];
-  uint4 sa4h[kFP4 ? 4 : 1], sb4h[kFP4 ? 4 : 1];
   auto read_scales = [&](int sbuf) {
     const uint32_t sh = MODE != kModeBF16 ? 8 * lg : 0;
 #pragma unroll
@@ -685,32 +676,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
       uint4 vb = *(const uint4*)(b_sc + sbuf * kScaleBuf + f * 32 * kScaleRow);
       sa4[f] = make_uint4(va.x >> sh, va.y >> sh, va.z >> sh, va.w >> sh);
       sb4[f] = make_uint4(vb.x >> sh, vb.y >> sh, vb.z >> sh, vb.w >> sh);
-      if constexpr (kFP4) {
-        uint4 wa = *(const uint4*)(a_sc2 + sbuf * kScaleBuf + f * 32 * kScaleRow);
-        uint4 wb = *(const uint4*)(b_sc2 + sbuf * kScaleBuf + f * 32 * kScaleRow);
-        sa4h[f] = make_uint4(wa.x >> sh, wa.y >> sh, wa.z >> sh, wa.w >> sh);
-        sb4h[f] = make_uint4(wb.x >> sh, wb.y >> sh, wb.z >> sh, wb.w >> sh);
-      }
     }
   };
   auto word_of = [&](const uint4& w4, int k) -> uint32_t {
     return k == 0 ? w4.x : k == 1 ? w4.y : k == 2 ? w4.z : w4.w;
   };
-  auto scale_of = [&](const uint4* s4, const uint4* s4h, int f, int sub, int h) -> int {
+  auto scale_of = [&](const uint4* s4, int f, int sub, int h) -> int {
     if constexpr (kFP4) {
-      const int w = 2 * sub + h;
-      return (int)(w < 4 ? word_of(s4[f], w) : word_of(s4h[f], w - 4));
+      return (int)word_of(s4[f], 2 * sub + h);
     } else {
       return (int)(word_of(s4[f], sub) >> (16 * h));
     }
   };
-  auto read_frag = [&](const uint8_t* row_base, const uint4* s4, const uint4* s4h, int buf, int sub, int h, int f,
+  auto read_frag = [&](const uint8_t* row_base, const uint4* s4, int buf, int sub, int h, int f,
                        v8i32& fr, int& sc) {
     const uint8_t* r = row_base + buf * kCodeStage + f * 32 * kFBK;
     const uint4 lo = *(const uint4*)(r + c_lo[h]);
     const uint4 hi = *(const uint4*)(r + c_hi[h]);
     fr = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    sc = scale_of(s4, s4h, f, sub, h);
+    sc = scale_of(s4, f, sub, h);
   };
 
   v16f32 acc[4][4];
@@ -799,20 +783,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   read_scales(0);
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
-    read_frag(a_row, sa4, sa4h, 0, 0, 0, f, fa[0][f], sa[0][f]);
-    read_frag(b_row, sb4, sb4h, 0, 0, 0, f, fb[0][f], sb[0][f]);
+    read_frag(a_row, sa4, 0, 0, 0, f, fa[0][f], sa[0][f]);
+    read_frag(b_row, sb4, 0, 0, 0, f, fb[0][f], sb[0][f]);
   }
 
   for (int64_t s0 = 0; s0 < nsteps; s0 += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t s = s0 + u;
-      const int buf = u & 1, sbuf = (int)((s0 / 4) & 1);
+      const int buf = u & 1, sbuf = (int)((s / kG) & 1), sub = (int)(s % kG);
       // ---- first half: MFMAs on set 0; set 1 <- second half of stage s
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        read_frag(a_row, sa4, sa4h, buf, u, 1, i, fa[1][i], sa[1][i]);
-        read_frag(b_row, sb4, sb4h, buf, u, 1, i, fb[1][i], sb[1][i]);
+        read_frag(a_row, sa4, buf, sub, 1, i, fa[1][i], sa[1][i]);
+        read_frag(b_row, sb4, buf, sub, 1, i, fb[1][i], sb[1][i]);
         mfma_group(0, i);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -821,18 +805,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
       wait_vmcnt<kPF>();
       wait_lgkmcnt0();
       barrier();
-      if (((u + 2) & 3) == 0) issue_scales(min((s + 2) >> 2, nsteps / 4 - 1));
+      if ((u + 2) % kG == 0) issue_scales(min((s + 2) / kG, nsteps / kG - 1));
       // the next scale group was published by this barrier
-      if (u == 3) read_scales(sbuf ^ 1);
+      if (u % kG == kG - 1) read_scales(sbuf ^ 1);
       __builtin_amdgcn_sched_barrier(0);
       // ---- second half: MFMAs on set 1; set 0 <- first half of stage s+1.
       // The loads of stage s+2 are issued a quarter per MFMA group: a wave
       // issues in order, and 18 loads in a row would hold back its MFMAs.
-      const int nbuf = buf ^ 1, nsub = (u + 1) & 3;
+      const int nbuf = buf ^ 1, nsub = (sub + 1) % kG;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        read_frag(a_row, sa4, sa4h, nbuf, nsub, 0, i, fa[0][i], sa[0][i]);
-        read_frag(b_row, sb4, sb4h, nbuf, nsub, 0, i, fb[0][i], sb[0][i]);
+        read_frag(a_row, sa4, nbuf, nsub, 0, i, fa[0][i], sa[0][i]);
+        read_frag(b_row, sb4, nbuf, nsub, 0, i, fb[0][i], sb[0][i]);
         if constexpr (MODE != kModeBF16) {
           // the loads go out between two pairs of MFMAs, so the matrix unit
           // has queued work while the wave issues them
