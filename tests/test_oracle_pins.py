@@ -798,6 +798,11 @@ def test_2d_blocks(oracle):
     like the 1 x 32 rowwise path, the transposed output is the transpose, and
     quantizing x^T swaps the two outputs."""
     x = inputs.normal_bf16(910, (96, 128))
+    # each block's largest element in its last row and column, 2^(8 + br + bc):
+    # a scale taken from only part of the block would miss it
+    for br in range(3):
+        for bc in range(4):
+            x[32 * br + 31, 32 * bc + 31] = inputs.f32_to_bf16_bits(np.float32([2.0 ** (8 + br + bc)]))[0]
     xf = inputs.bf16_bits_to_f32(x)
     q, s, qt, st = oracle.quantize_2d(x, E4M3)
     _, s_row = oracle.quantize_rows(x, E4M3)
@@ -806,6 +811,7 @@ def test_2d_blocks(oracle):
             blk = s_row[32 * br:32 * br + 32, bc]
             assert np.all(s[32 * br:32 * br + 32, bc] == blk.max())
             assert np.all(st[32 * bc:32 * bc + 32, br] == blk.max())
+            assert blk.max() == 127 + 8 + br + bc - 8  # floor rule: exponent of the planted maximum - emax
     assert np.array_equal(qt, q.T)
     q2, s2, qt2, st2 = oracle.quantize_2d(np.ascontiguousarray(x.T), E4M3)
     assert np.array_equal(q2, qt) and np.array_equal(s2, st) and np.array_equal(qt2, q) and np.array_equal(st2, s)
