@@ -33,6 +33,10 @@
  *   - Sizes and leading dimensions ("ld", row pitches) are in elements of the
  *     array they describe (bytes for codes and scales). Matrices are
  *     row-major: element (r, c) of an array with pitch ld is at r * ld + c.
+ *   - An empty problem (a zero row, column, token or group count) writes
+ *     nothing and returns MX_OK (MX_ERR_DEVICE off gfx950); its buffers,
+ *     pitches and alignment are then not checked (NULL is accepted). Formats
+ *     and negative sizes still are.
  *   - A blocked dimension must be a multiple of 32 (MX_ERR_SHAPE otherwise).
  *   - Alignment (MX_ERR_ALIGN otherwise): the base address and the byte pitch
  *     of every high-precision input, of the dequantize output and of every

@@ -80,9 +80,10 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 extern "C" mx_status_t mx_dequantize(const uint8_t* q, int64_t ldq, const uint8_t* s, int64_t lds, mx_fmt_t fmt,
                                      int64_t rows, int64_t cols, void* y, mx_dtype_t ydt, int64_t ldy,
                                      hipStream_t stream) {
-  if (!q || !s || !y) return MX_ERR_NULL;
   if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1) return MX_ERR_FORMAT;
   if (ydt != MX_F32 && ydt != MX_BF16) return MX_ERR_FORMAT;
+  if (rows == 0 || cols == 0) return rows < 0 || cols < 0 ? MX_ERR_SHAPE : mx_host::check_device();  // empty
+  if (!q || !s || !y) return MX_ERR_NULL;
   if (rows < 0 || cols < 0 || cols % kBlock != 0 || ldq < (fmt == MX_E2M1 ? cols / 2 : cols) ||
       lds < cols / kBlock || ldy < cols)
     return MX_ERR_SHAPE;

@@ -416,6 +416,12 @@ namespace {
 mx_status_t quantize_rows_host(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx, mx_fmt_t fmt,
                                uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, uint32_t round_up,
                                hipStream_t stream) {
+  if (rows == 0 || cols == 0) {  // empty: no buffer, pitch or alignment matters
+    if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
+    if (xdt != MX_F32 && xdt != MX_BF16) return MX_ERR_FORMAT;
+    if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1) return MX_ERR_FORMAT;
+    return mx_host::check_device();
+  }
   if (!x || !q || !s) return MX_ERR_NULL;
   const bool fp4 = fmt == MX_E2M1;
   mx_status_t st = check_common(x, xdt, fp4 ? MX_E4M3 : fmt, rows, cols, ldx);
@@ -444,6 +450,11 @@ extern "C" mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_
                                          int64_t ld_token, const int64_t* slot_mapping, uint8_t* k_cache,
                                          uint8_t* k_scale, uint8_t* v_cache, uint8_t* v_scale, int64_t page_size,
                                          int64_t num_pages, hipStream_t stream) {
+  if (T == 0 || H == 0 || D == 0) {  // empty: no buffer, pitch or alignment matters
+    if (T < 0 || H < 0 || D < 0) return MX_ERR_SHAPE;
+    if (dt != MX_F32 && dt != MX_BF16) return MX_ERR_FORMAT;
+    return mx_host::check_device();
+  }
   if (!k || !v || !slot_mapping || !k_cache || !k_scale || !v_cache || !v_scale) return MX_ERR_NULL;
   if (dt != MX_F32 && dt != MX_BF16) return MX_ERR_FORMAT;
   if (T < 0 || H < 0 || D < 0 || page_size <= 0 || num_pages < 0 || D % kBlock != 0 || ld_token < H * D)
@@ -488,6 +499,12 @@ namespace {
 mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int64_t cols, int64_t ldx, mx_fmt_t fmt,
                                uint8_t* qt, int64_t ldq, uint8_t* st, int64_t lds, uint32_t round_up,
                                hipStream_t stream) {
+  if (rows == 0 || cols == 0) {  // empty: no buffer, pitch or alignment matters
+    if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
+    if (xdt != MX_F32 && xdt != MX_BF16) return MX_ERR_FORMAT;
+    if (fmt != MX_E4M3 && fmt != MX_E5M2) return MX_ERR_FORMAT;
+    return mx_host::check_device();
+  }
   if (!x || !qt || !st) return MX_ERR_NULL;
   mx_status_t rc = check_common(x, xdt, fmt, rows, cols, ldx);
   if (rc != MX_OK) return rc;
@@ -553,6 +570,12 @@ extern "C" mx_status_t mx_quantize_ex(const mx_quantize_desc_t* d, hipStream_t s
   if (!d) return MX_ERR_NULL;
   if (d->rule != MX_SCALE_FLOOR && d->rule != MX_SCALE_CEIL) return MX_ERR_FORMAT;
   if (d->blocks != MX_BLOCKS_1D && d->blocks != MX_BLOCKS_2D) return MX_ERR_FORMAT;
+  if (d->rows < 0 || d->cols < 0) return MX_ERR_SHAPE;
+  if (d->rows == 0 || d->cols == 0) {  // nothing to read or write: buffers may be NULL
+    if (d->xdt != MX_F32 && d->xdt != MX_BF16) return MX_ERR_FORMAT;
+    if (d->fmt != MX_E4M3 && d->fmt != MX_E5M2 && (d->fmt != MX_E2M1 || d->blocks == MX_BLOCKS_2D)) return MX_ERR_FORMAT;
+    return mx_host::check_device();
+  }
   const bool rowout = d->q != nullptr || d->s != nullptr, colout = d->qt != nullptr || d->st != nullptr;
   if (!d->x || (!rowout && !colout)) return MX_ERR_NULL;
   if ((rowout && (!d->q || !d->s)) || (colout && (!d->qt || !d->st))) return MX_ERR_NULL;
@@ -570,8 +593,9 @@ extern "C" mx_status_t mx_quantize_ex(const mx_quantize_desc_t* d, hipStream_t s
 
 extern "C" mx_status_t mx_scale_broadcast(const float* s_in, int64_t ld_in, mx_bcast_layout_t layout, int64_t rows,
                                           int64_t cols, uint8_t* out, int64_t ld_out, hipStream_t stream) {
-  if (!s_in || !out) return MX_ERR_NULL;
   if (layout != MX_BCAST_1X128 && layout != MX_BCAST_128X128) return MX_ERR_FORMAT;
+  if (rows == 0 || cols == 0) return rows < 0 || cols < 0 ? MX_ERR_SHAPE : mx_host::check_device();  // empty
+  if (!s_in || !out) return MX_ERR_NULL;
   if (rows < 0 || cols < 0 || cols % 128 != 0 || ld_in < cols / 128 || ld_out < cols / kBlock) return MX_ERR_SHAPE;
   if (((uintptr_t)s_in & 3u) != 0 || ((uintptr_t)out & 3u) != 0 || ld_out % 4 != 0) return MX_ERR_ALIGN;
   mx_status_t rc;

@@ -262,3 +262,38 @@ def test_argument_errors_are_returned_not_launched(mx):
         mx.mx_quantize_colwise(x[:48], E4M3)            # rows % 32 != 0
     assert e.value.status == -2
     torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------- empty problems
+def test_empty_problems_are_no_ops(mx):
+    """A zero dimension writes nothing and succeeds, although torch hands
+    over NULL for the empty buffers."""
+    import torch
+    for shape in ((0, 64), (64, 0)):
+        x = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        q, s = mx.mx_quantize(x, E4M3)
+        assert q.numel() == 0 and s.numel() == 0
+        qt, st = mx.mx_quantize_colwise(x, E5M2)
+        assert qt.numel() == 0 and st.numel() == 0
+        q, s, qt, st = mx.mx_quantize_ex(x, E4M3, rule=mx.MX_SCALE_CEIL, blocks=mx.MX_BLOCKS_2D, colwise=True)
+        assert q.numel() == 0 and qt.numel() == 0
+        y = mx.mx_dequantize(torch.empty((shape[0], shape[1]), dtype=torch.uint8, device="cuda"),
+                             torch.empty((shape[0], shape[1] // 32), dtype=torch.uint8, device="cuda"), E4M3)
+        assert y.numel() == 0
+    assert mx.mx_quantize(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), mx.MX_E2M1)[0].shape == (0, 32)
+    e8 = mx.mx_scale_broadcast(torch.empty((0, 2), dtype=torch.float32, device="cuda"), 0, 256)
+    assert e8.shape == (0, 8)
+    # KV write of zero tokens leaves the cache untouched
+    kc = torch.full((2, 128, 2, 64), 0xA5, dtype=torch.uint8, device="cuda")
+    ks = torch.full((2, 128, 2, 2), 0x5A, dtype=torch.uint8, device="cuda")
+    vc, vs = kc.clone(), ks.clone()
+    kv = torch.empty((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    mx.mx_kv_quant_write(kv, kv, torch.empty((0,), dtype=torch.int64, device="cuda"), kc, ks, vc, vs)
+    assert bool((kc == 0xA5).all()) and bool((ks == 0x5A).all()) and bool((vc == 0xA5).all())
+    # products with no rows or no columns
+    a = torch.empty((0, 512), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((0, 16), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((64, 512), dtype=torch.uint8, device="cuda")
+    sb = torch.full((64, 16), 127, dtype=torch.uint8, device="cuda")
+    assert mx.mx_gemm(a, sa, b, sb).shape == (0, 64)
+    assert mx.mx_gemm(b, sb, a, sa).shape == (64, 0)
