@@ -297,3 +297,63 @@ def test_empty_problems_are_no_ops(mx):
     sb = torch.full((64, 16), 127, dtype=torch.uint8, device="cuda")
     assert mx.mx_gemm(a, sa, b, sb).shape == (0, 64)
     assert mx.mx_gemm(b, sb, a, sa).shape == (64, 0)
+
+
+@pytest.mark.slow
+def test_launch_split_at_two_to_the_30_chunks(mx, oracle):
+    """Rowwise quantize and dequantize split a problem into launches of at
+    most 2^30 work items (chunks of 8, resp. 16, elements). A 2^27 + 96 row x
+    128 column bf16 input (32 GiB) is quantized in three launches (rows 0,
+    2^26, 2^27) and dequantized in two (rows 0, 2^27); rows on both sides of
+    every boundary, and the first and last rows, are compared with the oracle
+    bit for bit."""
+    import torch
+    rows, cols = (1 << 27) + 96, 128
+    g = torch.Generator(device="cuda").manual_seed(21)
+    x = torch.randn((rows, cols), device="cuda", dtype=torch.bfloat16, generator=g)
+    q, s = mx.mx_quantize(x, E4M3)
+    y = mx.mx_dequantize(q, s, E4M3, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    pick = np.concatenate([np.arange(0, 8), np.arange((1 << 26) - 40, (1 << 26) + 40),
+                           np.arange((1 << 27) - 40, (1 << 27) + 40), np.arange(rows - 40, rows)])
+    pick = np.unique(pick[pick < rows])
+    idx = torch.from_numpy(pick).cuda()
+    xs = x[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    qo, so = oracle.quantize_rows(xs, E4M3)
+    assert_bitexact(host(q[idx]), qo, "codes around the launch splits")
+    assert_bitexact(host(s[idx]), so, "scales around the launch splits")
+    assert_bitexact(host(y[idx]), oracle.dequantize(qo, so, E4M3, "bf16"), "dequantized rows around the splits")
+    del x, q, s, y
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+def test_kv_write_launch_split(mx, oracle):
+    """The fused KV write splits at 2^30 work items too: with 8 heads of 128,
+    every 2^23 tokens. 2^23 + 64 tokens (K and V 17 GiB each) are written
+    through a shuffled slot mapping; the cache slots of tokens on both sides
+    of the split, and the last ones, are compared with the oracle."""
+    import torch
+    T, H, D, page = (1 << 23) + 64, 8, 128, 128
+    pages = -(-T // page)
+    g = torch.Generator(device="cuda").manual_seed(22)
+    k = torch.randn((T, H, D), device="cuda", dtype=torch.bfloat16, generator=g)
+    v = torch.randn((T, H, D), device="cuda", dtype=torch.bfloat16, generator=g)
+    slots = torch.randperm(pages * page, device="cuda", generator=g)[:T].contiguous()
+    kc = torch.empty((pages, page, H, D), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((pages, page, H, D // 32), dtype=torch.uint8, device="cuda")
+    vc, vs = torch.empty_like(kc), torch.empty_like(ks)
+    mx.mx_kv_quant_write(k, v, slots, kc, ks, vc, vs)
+    torch.cuda.synchronize()
+    pick = np.unique(np.concatenate([np.arange(0, 4), np.arange((1 << 23) - 32, (1 << 23) + 32), np.arange(T - 16, T)]))
+    idx = torch.from_numpy(pick).cuda()
+    sl = slots[idx]
+    for src, cache, scale, name in ((k, kc, ks, "K"), (v, vc, vs, "V")):
+        xs = src[idx].reshape(-1, D).view(torch.int16).cpu().numpy().view(np.uint16)
+        qo, so = oracle.quantize_rows(xs, E4M3)
+        got_q = cache.view(-1, H, D)[sl].reshape(-1, D)
+        got_s = scale.view(-1, H, D // 32)[sl].reshape(-1, D // 32)
+        assert_bitexact(host(got_q), qo, name + " cache codes around the launch split")
+        assert_bitexact(host(got_s), so, name + " cache scales around the launch split")
+    del k, v, kc, ks, vc, vs
+    torch.cuda.empty_cache()
