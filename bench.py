@@ -437,6 +437,21 @@ def other_rows(torch, mx, inputs, np, flush, stream, steps, kv_only=False):
                                     "frac_of_hbm_peak": round(sb_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
                                     "algorithmic_bytes": sb_bytes}
     del s128, sg8
+    # X [16384 x 4096] quantized in both 1-D orientations from one read
+    # (forward operand and wgrad operand of the same activation)
+    qxr = torch.empty(Xd.shape, dtype=torch.uint8, device="cuda")
+    sxr = torch.empty((Xd.shape[0], Xd.shape[1] // 32), dtype=torch.uint8, device="cuda")
+    qxc = torch.empty((Xd.shape[1], Xd.shape[0]), dtype=torch.uint8, device="cuda")
+    sxc = torch.empty((Xd.shape[1], Xd.shape[0] // 32), dtype=torch.uint8, device="cuda")
+    ms = timed("quantize_X_both", lambda: mx.mx_quantize_ex(Xd, mx.MX_E4M3, colwise=True, q=qxr, s=sxr, qt=qxc, st=sxc))
+    xb_bytes = 2 * Xd.numel() + 2 * (Xd.numel() + Xd.numel() // 32)
+    ms_r = timed("quantize_X_rows", lambda: mx.mx_quantize(Xd, mx.MX_E4M3, q=qxr, s=sxr))
+    ms_c = timed("quantize_X_cols", lambda: mx.mx_quantize_colwise(Xd, mx.MX_E4M3, qt=qxc, st=sxc))
+    out["quantize_X_rows_and_cols_one_pass"] = {"us": round(ms * 1e3, 2), "GB/s": round(xb_bytes / ms / 1e6, 1),
+                                                "frac_of_hbm_peak": round(xb_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                                "algorithmic_bytes": xb_bytes,
+                                                "two_calls_us": round((ms_r + ms_c) * 1e3, 2)}
+    del qxr, sxr, qxc, sxc
     qx, sx = mx.mx_quantize(Xd, mx.MX_E4M3)
     qw, sw = mx.mx_quantize(Wd, mx.MX_E4M3)
     Yf = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")

@@ -118,7 +118,9 @@ mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int
  *           above the floor rule when amax's significand exceeds 1.75 (FP8)
  *           or 1.5 (E2M1), the same otherwise).
  *   blocks  MX_BLOCKS_1D: 1 x 32 blocks for the rowwise output and 32 x 1
- *           blocks for the colwise output, as mx_quantize / _colwise.
+ *           blocks for the colwise output, as mx_quantize / _colwise. With
+ *           both outputs asked for, x is read once (rows % 32 == 0 and
+ *           cols % 32 == 0; E4M3 / E5M2).
  *           MX_BLOCKS_2D: one scale per 32 x 32 block (the 2-D weight
  *           quantization of [SM120 §1.3]), written in the MXFP8 layout: s
  *           repeats a block's scale on its 32 rows, st on its 32 columns, and

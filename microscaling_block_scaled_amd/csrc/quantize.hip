@@ -167,6 +167,12 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(RowArgs a) {
 // NULL), and the rowwise codes are encoded a second time along the rows and
 // stored straight from registers: each store instruction writes 4 rows x 128
 // contiguous bytes. The rowwise scales are 4 bytes per row (q may be NULL).
+//
+// ROWS: 1-D blocks in both orientations from one read of x. The colwise
+// output is as above; a row's 32-column block lies in the 4 lanes j, j ^ 4,
+// j ^ 8, j ^ 12 of a DPP row (the same row group, 4 column groups), so each
+// of a lane's 8 rows gets its block amax from two lane exchanges, and its 8
+// codes are encoded along the row and stored from registers as with B2D.
 // ---------------------------------------------------------------------------
 constexpr int kColTileRows = 128;
 constexpr int kColTileCols = 128;
@@ -179,7 +185,7 @@ __device__ __forceinline__ uint32_t col_lds_offset(uint32_t c, uint32_t rbyte) {
   return c * 128u + ((((rbyte >> 4) ^ (2u * (c >> 3))) & 7u) << 4) + (rbyte & 15u);
 }
 
-template <typename InT, int FMT, bool B2D>
+template <typename InT, int FMT, bool B2D, bool ROWS>
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restrict__ x, int64_t rows, int64_t cols,
                                                               int64_t ldx, uint8_t* __restrict__ qt, int64_t ldq,
                                                               uint8_t* __restrict__ st, int64_t lds,
@@ -289,6 +295,61 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
         for (int i = 1; i < 8; ++i) m = umax(m, v[i][p] & 0x7FFFFFFFu);
         m = quad_max_u32(m);
         codes[p] = scale_code_bits<FMT, 23>(m, round_up);
+      }
+    }
+    if constexpr (ROWS) {
+      // rowwise 1-D blocks: amax of row 8b + i over the lane's 8 columns, then
+      // over the 4 column groups of its 32-column block (lanes j ^ 4, j ^ 8)
+      uint32_t ram[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (W == 4) {
+          uint32_t pm = pk_max_u16(pk_max_u16(v[i][0] & 0x7FFF7FFFu, v[i][1] & 0x7FFF7FFFu),
+                                   pk_max_u16(v[i][2] & 0x7FFF7FFFu, v[i][3] & 0x7FFF7FFFu));
+          ram[i] = umax(pm & 0xFFFFu, pm >> 16);
+        } else {
+          uint32_t m = 0;
+#pragma unroll
+          for (int p = 0; p < 8; ++p) m = umax(m, v[i][p] & 0x7FFFFFFFu);
+          ram[i] = m;
+        }
+      }
+      if constexpr (W == 4) {
+        // two rows per dword for the exchanges
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          uint32_t pk = ram[i] | (ram[i + 1] << 16);
+          pk = pk_max_u16(pk, (uint32_t)__shfl_xor((int)pk, 4));
+          pk = pk_max_u16(pk, (uint32_t)__shfl_xor((int)pk, 8));
+          ram[i] = pk & 0xFFFFu;
+          ram[i + 1] = pk >> 16;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ram[i] = umax(ram[i], (uint32_t)__shfl_xor((int)ram[i], 4));
+          ram[i] = umax(ram[i], (uint32_t)__shfl_xor((int)ram[i], 8));
+        }
+      }
+      if (ncol == 8) {  // cols % 32 == 0: a lane's 8 columns are all in or all out
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t rc = scale_code_bits<FMT, W == 4 ? 7 : 23>(ram[i], round_up);
+          const float div = scale_divisor(rc);
+          uint2 o;
+          if constexpr (W == 4) {
+            o.x = encode4_bf16<FMT>(v[i][0], v[i][1], div);
+            o.y = encode4_bf16<FMT>(v[i][2], v[i][3], div);
+          } else {
+            o.x = encode4_f32<FMT>(__uint_as_float(v[i][0]), __uint_as_float(v[i][1]), __uint_as_float(v[i][2]),
+                                   __uint_as_float(v[i][3]), div);
+            o.y = encode4_f32<FMT>(__uint_as_float(v[i][4]), __uint_as_float(v[i][5]), __uint_as_float(v[i][6]),
+                                   __uint_as_float(v[i][7]), div);
+          }
+          if (rc == 0xFFu) o = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+          *(uint2*)(q2 + (rblk + 8 * b + i) * ldq2 + cc) = o;
+          if ((k & 3u) == 0u) s2[(rblk + 8 * b + i) * lds2 + cc / kBlock] = (uint8_t)rc;
+        }
       }
     }
     // encode: column c gets two dwords = rows 8b .. 8b+3 and 8b+4 .. 8b+7
@@ -518,7 +579,7 @@ mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int6
   const dim3 grid((uint32_t)(row_tiles * col_tiles));
   const uint32_t col_major = col_tiles >= 64 ? 1u : 0u;
 #define MX_COLS_LAUNCH(T, F)                                                                                        \
-  hipLaunchKernelGGL((quant_cols_kernel<T, F, false>), grid, dim3(kThreads), 0, stream, (const T*)x, rows, cols, ldx, \
+  hipLaunchKernelGGL((quant_cols_kernel<T, F, false, false>), grid, dim3(kThreads), 0, stream, (const T*)x, rows, cols, ldx, \
                      qt, ldq, st, lds, (uint32_t)col_tiles, col_major, round_up, nullptr, 0, nullptr, 0)
   if (xdt == MX_BF16) {
     if (fmt == MX_E5M2) MX_COLS_LAUNCH(uint16_t, MX_E5M2); else MX_COLS_LAUNCH(uint16_t, MX_E4M3);
@@ -529,7 +590,9 @@ mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int6
   return mx_host::launch_status();
 }
 
-mx_status_t quantize_2d_host(const mx_quantize_desc_t* d, uint32_t round_up, hipStream_t stream) {
+// One pass of the tile kernel over x: 32 x 32 blocks (B2D), or 1-D blocks in
+// both orientations (rows1d; both outputs given).
+mx_status_t quantize_tile_host(const mx_quantize_desc_t* d, uint32_t round_up, bool rows1d, hipStream_t stream) {
   const bool rowout = d->q != nullptr, colout = d->qt != nullptr;
   if (d->fmt != MX_E4M3 && d->fmt != MX_E5M2) return MX_ERR_FORMAT;
   mx_status_t rc = check_common(d->x, d->xdt, d->fmt, d->rows, d->cols, d->ldx);
@@ -546,16 +609,19 @@ mx_status_t quantize_2d_host(const mx_quantize_desc_t* d, uint32_t round_up, hip
   if (row_tiles * col_tiles >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const dim3 grid((uint32_t)(row_tiles * col_tiles));
   const uint32_t col_major = col_tiles >= 64 ? 1u : 0u;
-#define MX_2D_LAUNCH(T, F)                                                                                          \
-  hipLaunchKernelGGL((quant_cols_kernel<T, F, true>), grid, dim3(kThreads), 0, stream, (const T*)d->x, d->rows,   \
+#define MX_TILE_LAUNCH(T, F, B2D, ROWS)                                                                            \
+  hipLaunchKernelGGL((quant_cols_kernel<T, F, B2D, ROWS>), grid, dim3(kThreads), 0, stream, (const T*)d->x, d->rows, \
                      d->cols, d->ldx, d->qt, d->ldqt, d->st, d->ldst, (uint32_t)col_tiles, col_major, round_up,  \
                      d->q, d->ldq, d->s, d->lds)
+#define MX_TILE_MODE(T, F) \
+  do { if (rows1d) MX_TILE_LAUNCH(T, F, false, true); else MX_TILE_LAUNCH(T, F, true, false); } while (0)
   if (d->xdt == MX_BF16) {
-    if (d->fmt == MX_E5M2) MX_2D_LAUNCH(uint16_t, MX_E5M2); else MX_2D_LAUNCH(uint16_t, MX_E4M3);
+    if (d->fmt == MX_E5M2) MX_TILE_MODE(uint16_t, MX_E5M2); else MX_TILE_MODE(uint16_t, MX_E4M3);
   } else {
-    if (d->fmt == MX_E5M2) MX_2D_LAUNCH(float, MX_E5M2); else MX_2D_LAUNCH(float, MX_E4M3);
+    if (d->fmt == MX_E5M2) MX_TILE_MODE(float, MX_E5M2); else MX_TILE_MODE(float, MX_E4M3);
   }
-#undef MX_2D_LAUNCH
+#undef MX_TILE_MODE
+#undef MX_TILE_LAUNCH
   return mx_host::launch_status();
 }
 }  // namespace
@@ -580,8 +646,12 @@ extern "C" mx_status_t mx_quantize_ex(const mx_quantize_desc_t* d, hipStream_t s
   if (!d->x || (!rowout && !colout)) return MX_ERR_NULL;
   if ((rowout && (!d->q || !d->s)) || (colout && (!d->qt || !d->st))) return MX_ERR_NULL;
   const uint32_t round_up = d->rule == MX_SCALE_CEIL ? 1u : 0u;
-  if (d->blocks == MX_BLOCKS_2D) return quantize_2d_host(d, round_up, stream);
+  if (d->blocks == MX_BLOCKS_2D) return quantize_tile_host(d, round_up, false, stream);
   if (colout && d->fmt == MX_E2M1) return MX_ERR_FORMAT;
+  // both 1-D orientations: one pass over x (~134 MB instead of ~203 MB of
+  // traffic for an 8192 x 4096 bf16 input); x needs rows % 32 == 0 as for
+  // the colwise output alone, and cols % 32 == 0 as for the rowwise one
+  if (rowout && colout) return quantize_tile_host(d, round_up, true, stream);
   mx_status_t rc = MX_OK;
   if (rowout)
     rc = quantize_rows_host(d->x, d->xdt, d->rows, d->cols, d->ldx, d->fmt, d->q, d->ldq, d->s, d->lds, round_up, stream);

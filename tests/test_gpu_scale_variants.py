@@ -82,15 +82,34 @@ def test_round_up_rule_colwise(mx, oracle, fmt, f32, rows, cols, seed):
 
 
 @pytest.mark.parametrize("rule", [FLOOR, CEIL])
-def test_1d_both_orientations_in_one_call(mx, oracle, rule):
-    x = planted(720, (256, 640))
-    q, s, qt, st = mx.mx_quantize_ex(to_dev(x), E4M3, rule=rule, rowwise=True, colwise=True)
-    qo, so = oracle.quantize_rows(x, E4M3, rule)
-    qto, sto = oracle.quantize_cols(x, E4M3, rule)
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("rows,cols,seed", [(256, 640, 0), (96, 224, 1), (160, 8224, 2)])
+def test_1d_both_orientations_in_one_call(mx, oracle, rule, fmt, f32, rows, cols, seed):
+    """Both 1-D orientations from one pass over x (the tile kernel's rowwise
+    mode), against the oracle's rowwise and colwise quantizations; (160, 8224)
+    has more than 64 column tiles, so its tiles run down the columns."""
+    x = planted(720 + seed, (rows, cols), f32)
+    q, s, qt, st = mx.mx_quantize_ex(to_dev(x), fmt, rule=rule, rowwise=True, colwise=True)
+    qo, so = oracle.quantize_rows(x, fmt, rule)
+    qto, sto = oracle.quantize_cols(x, fmt, rule)
     assert_bitexact(host(q), qo, "rowwise codes")
     assert_bitexact(host(s), so, "rowwise scales")
     assert_bitexact(host(qt), qto, "colwise codes")
     assert_bitexact(host(st), sto, "colwise scales")
+
+
+def test_1d_both_orientations_special_blocks(mx, oracle):
+    """NaN, Inf and all-zero blocks in the one-pass rowwise + colwise mode."""
+    x = inputs.normal_bf16(722, (128, 256))
+    x[5, 40] = 0x7FC0      # NaN
+    x[70, 200] = 0xFF80    # -Inf
+    x[96:128, 0:64] = 0    # zero blocks in both orientations
+    q, s, qt, st = mx.mx_quantize_ex(dev(x, bf16=True), E4M3, rowwise=True, colwise=True)
+    qo, so = oracle.quantize_rows(x, E4M3)
+    qto, sto = oracle.quantize_cols(x, E4M3)
+    for g, w, n in ((q, qo, "q"), (s, so, "s"), (qt, qto, "qt"), (st, sto, "st")):
+        assert_bitexact(host(g), w, n)
 
 
 def test_floor_rule_matches_mx_quantize(mx):
