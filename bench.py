@@ -353,6 +353,18 @@ def other_rows(torch, mx, inputs, np, flush, stream, steps, kv_only=False):
     out["dequantize_bf16"] = {"us": round(ms * 1e3, 2), "GB/s": round(dq_bytes / ms / 1e6, 1),
                               "frac_of_hbm_peak": round(dq_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
                               "algorithmic_bytes": dq_bytes}
+    # the quantize input in both 1-D orientations from one read of x
+    Xq2 = dev_bf16(torch, xq)
+    q1, s1 = torch.empty_like(q), torch.empty_like(s)
+    qt1 = torch.empty((Xq2.shape[1], Xq2.shape[0]), dtype=torch.uint8, device="cuda")
+    st1 = torch.empty((Xq2.shape[1], Xq2.shape[0] // 32), dtype=torch.uint8, device="cuda")
+    ms = timed("quantize_both", lambda: mx.mx_quantize_ex(Xq2, mx.MX_E4M3, colwise=True, q=q1, s=s1, qt=qt1, st=st1))
+    b_bytes = 2 * Xq2.numel() + 2 * (Xq2.numel() + Xq2.numel() // 32)
+    out["quantize_rows_and_cols_one_pass"] = {"us": round(ms * 1e3, 2), "GB/s": round(b_bytes / ms / 1e6, 1),
+                                              "frac_of_hbm_peak": round(b_bytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                              "algorithmic_bytes": b_bytes,
+                                              "shape": "the quantize input [8192 x 4096] bf16, E4M3"}
+    del Xq2, q1, s1, qt1, st1
     # MXFP4: the quantize input to E2M1 rowwise, and the 8192^3 product of
     # the GEMM workload's inputs quantized to E2M1 (bf16 out)
     log("mxfp4 rows")
