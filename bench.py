@@ -180,7 +180,7 @@ def main():
                     help="only the KV-cache rows (write, scores, attention), for profiling them alone")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each rank's work is the "
+        print("bench.py measures one GPU: the library has no multi-GPU path (each rank's work would be the "
               "single-GPU kernel at its full shape); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
