@@ -62,7 +62,10 @@ typedef int32_t mx_status_t;
 #define MX_ERR_ALIGN  -3 /* base address or pitch breaks the 16-byte rule above */
 #define MX_ERR_FORMAT -4 /* unknown element format or data type */
 #define MX_ERR_DEVICE -5 /* current device is not gfx950 */
-#define MX_ERR_HIP    -6 /* the HIP runtime reported an error at launch */
+#define MX_ERR_HIP    -6 /* the HIP runtime reported an error at launch: read with
+                             hipGetLastError() after the launch, so an error
+                             left pending by an earlier HIP call on the same
+                             thread is reported (and cleared) the same way */
 
 /* Element encodings [SM120 §0.1 table; GLOSS]: E4M3 (448 max, used for
  * activations and weights), E5M2 (57344 max, used for gradients).
