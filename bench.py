@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kv-only", action="store_true",
                     help="only the KV-cache rows (write, scores, attention), for profiling them alone")
+    ap.add_argument("--quantize-only", action="store_true",
+                    help="only the quantize-family kernels on the 8192 x 4096 input, for profiling them alone")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (each rank's work would be the "
@@ -203,6 +205,9 @@ def main():
 
     if args.kv_only:
         print(json.dumps({"kv_rows": other_rows(torch, mx, inputs, np, flush, stream, args.steps, kv_only=True)}))
+        return
+    if args.quantize_only:
+        print(json.dumps({"quantize_rows": quantize_rows_only(torch, mx, inputs, flush, stream, args.steps)}))
         return
 
     # ---- inputs (generated on the host, resident in HBM before timing)
@@ -279,6 +284,45 @@ def main():
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(xa, xb, xq)
     print(json.dumps(result))
+
+
+def quantize_rows_only(torch, mx, inputs, flush, stream, steps):
+    """The quantize-family kernels on the quantize input [8192 x 4096] bf16,
+    each after a cache-evicting read: rowwise, colwise, both in one pass,
+    32 x 32 blocks (both outputs), MXFP4 rowwise, dequantize to bf16."""
+    tm = Timer(torch, stream)
+    xq, _ = inputs.quantize_input()
+    X = dev_bf16(torch, xq)
+    R, C = X.shape
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    q, s = torch.empty((R, C), **u8), torch.empty((R, C // 32), **u8)
+    qt, st = torch.empty((C, R), **u8), torch.empty((C, R // 32), **u8)
+    q4 = torch.empty((R, C // 2), **u8)
+    y = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    calls = {
+        "rowwise": (lambda: mx.mx_quantize(X, mx.MX_E4M3, q=q, s=s), 3 * R * C + R * C // 32),
+        "colwise": (lambda: mx.mx_quantize_colwise(X, mx.MX_E4M3, qt=qt, st=st), 3 * R * C + R * C // 32),
+        "rows_and_cols_one_pass": (lambda: mx.mx_quantize_ex(X, mx.MX_E4M3, colwise=True, q=q, s=s, qt=qt, st=st),
+                                   4 * R * C + R * C // 16),
+        "blocks_32x32_both": (lambda: mx.mx_quantize_ex(X, mx.MX_E4M3, blocks=mx.MX_BLOCKS_2D, colwise=True, q=q, s=s,
+                                                        qt=qt, st=st), 4 * R * C + R * C // 16),
+        "mxfp4_rowwise": (lambda: mx.mx_quantize(X, mx.MX_E2M1, q=q4, s=s), 2 * R * C + R * C // 2 + R * C // 32),
+        "dequantize_bf16": (lambda: mx.mx_dequantize(q, s, mx.MX_E4M3, y=y), 3 * R * C + R * C // 32),
+    }
+    out = {}
+    for _ in range(3):  # every kernel once, three times over, before any is timed (clocks ramp up)
+        for fn, _ in calls.values():
+            fn()
+    torch.cuda.synchronize()
+    for name, (fn, nbytes) in calls.items():
+        for _ in range(max(3, steps)):
+            flush()
+            tm.run(name, fn)
+        torch.cuda.synchronize()
+        ms = tm.mean_ms(name)
+        out[name] = {"us": round(ms * 1e3, 2), "GB/s": round(nbytes / ms / 1e6, 1),
+                     "frac_of_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nbytes}
+    return out
 
 
 def other_rows(torch, mx, inputs, np, flush, stream, steps, kv_only=False):

@@ -194,6 +194,11 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
                                                               uint8_t* __restrict__ s2, int64_t lds2) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kColTileCols * kColTileRows];
   __shared__ __attribute__((aligned(16))) uint8_t stile[kColTileCols * 4];
+  // rowwise scales of the tile's 128 rows x 4 blocks (B2D / ROWS with the
+  // transposed output, whose barrier publishes them): one 4-byte store per row
+  __shared__ __attribute__((aligned(16))) uint8_t rstile[(B2D || ROWS) ? kColTileRows * 4 : 4];
+  // (only when the rowwise output is asked for: a colwise-only call has s2 == NULL)
+  const bool rs_lds = (B2D || ROWS) && qt != nullptr && s2 != nullptr;
   const uint32_t row_tiles = gridDim.x / col_tiles;  // the grid is row_tiles x col_tiles
   const uint32_t tile_r = col_major ? blockIdx.x % row_tiles : blockIdx.x / col_tiles;
   const uint32_t tile_c = col_major ? blockIdx.x / row_tiles : blockIdx.x % col_tiles;
@@ -271,10 +276,13 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
           if (code == 0xFFu) o = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
           *(uint2*)(q2 + (rblk + 8 * b + i) * ldq2 + cc) = o;
         }
-        // rowwise scales: the first column group of each block writes its 8 rows
+        // rowwise scales: the first column group of each block takes its 8 rows
         if ((k & 3u) == 0u) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) s2[(rblk + 8 * b + i) * lds2 + cc / kBlock] = (uint8_t)code;
+          for (int i = 0; i < 8; ++i) {
+            if (rs_lds) rstile[(32 * wave + 8 * b + i) * 4 + (k >> 2)] = (uint8_t)code;
+            else s2[(rblk + 8 * b + i) * lds2 + cc / kBlock] = (uint8_t)code;
+          }
         }
       }
     } else if constexpr (W == 4) {
@@ -348,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
           }
           if (rc == 0xFFu) o = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
           *(uint2*)(q2 + (rblk + 8 * b + i) * ldq2 + cc) = o;
-          if ((k & 3u) == 0u) s2[(rblk + 8 * b + i) * lds2 + cc / kBlock] = (uint8_t)rc;
+          if ((k & 3u) == 0u) rstile[(32 * wave + 8 * b + i) * 4 + (k >> 2)] = (uint8_t)rc;  // ROWS: qt given
         }
       }
     }
@@ -389,6 +397,18 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
     if (c0 + c < cols && r < rows) {
       uint4 val = *(const uint4*)(tile + col_lds_offset(c, 16 * m));
       *(uint4*)(qt + (c0 + c) * ldq + r) = val;
+    }
+  }
+  // rowwise scales (B2D / ROWS): row r's 4 blocks are 4 consecutive bytes of s2 row r0 + r
+  if (rs_lds && threadIdx.x >= kColTileCols && r0 + (threadIdx.x - kColTileCols) < rows) {
+    const uint32_t r = threadIdx.x - kColTileCols;
+    const int64_t nb = min((cols - c0) / kBlock, (int64_t)4);
+    uint8_t* dst = s2 + (r0 + r) * lds2 + c0 / kBlock;
+    const uint32_t sv = *(const uint32_t*)(rstile + 4 * r);
+    if (nb == 4 && ((uintptr_t)dst & 3u) == 0) {
+      *(uint32_t*)dst = sv;
+    } else {
+      for (int64_t j = 0; j < nb; ++j) dst[j] = (uint8_t)(sv >> (8 * j));
     }
   }
   // scales: column c's 4 block rows are 4 consecutive bytes of st row c0 + c
