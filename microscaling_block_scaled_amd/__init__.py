@@ -61,6 +61,27 @@ def _rowmajor(t, name, ndim=2):
         raise ValueError("%s must be a GPU tensor" % name)
 
 
+def _buf(t, name, shape, dtype, like=None):
+    """Checks a buffer the kernels read or write through a bare pointer: its
+    exact shape and dtype, unit stride along the last dimension, rows that do
+    not overlap, and (with `like`) the same GPU as `like`. A smaller tensor
+    would otherwise let a kernel run past its end."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.numel() > 0:
+        if t.stride(-1) != 1:
+            raise ValueError("%s must have unit stride along its last dimension" % name)
+        for i in range(t.dim() - 1):
+            if t.shape[i] > 1 and t.stride(i) < t.shape[i + 1] * t.stride(i + 1):
+                raise ValueError("%s has overlapping rows" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if like is not None and t.device != like.device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, like.device))
+
+
 def _p(t):
     return ctypes.c_void_p(t.data_ptr())
 
@@ -80,6 +101,8 @@ def mx_quantize(x, fmt=MX_E4M3, q=None, s=None, stream=None):
     cb = cols // 2 if fmt == MX_E2M1 else cols
     q = torch.empty((rows, cb), dtype=torch.uint8, device=x.device) if q is None else q
     s = torch.empty((rows, cols // BLOCK), dtype=torch.uint8, device=x.device) if s is None else s
+    _buf(q, "q", (rows, cb), torch.uint8, x)
+    _buf(s, "s", (rows, cols // BLOCK), torch.uint8, x)
     check("mx_quantize", lib().mx_quantize(_p(x), _dtype_code(x), rows, cols, _ld(x), fmt, _p(q), _ld(q),
                                            _p(s), _ld(s), _stream(stream)))
     return q, s
@@ -93,6 +116,8 @@ def mx_quantize_colwise(x, fmt=MX_E4M3, qt=None, st=None, stream=None):
     rows, cols = x.shape
     qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if qt is None else qt
     st = torch.empty((cols, rows // BLOCK), dtype=torch.uint8, device=x.device) if st is None else st
+    _buf(qt, "qt", (cols, rows), torch.uint8, x)
+    _buf(st, "st", (cols, rows // BLOCK), torch.uint8, x)
     check("mx_quantize_colwise", lib().mx_quantize_colwise(_p(x), _dtype_code(x), rows, cols, _ld(x), fmt,
                                                            _p(qt), _ld(qt), _p(st), _ld(st),
                                                            _stream(stream)))
@@ -114,12 +139,16 @@ def mx_quantize_ex(x, fmt=MX_E4M3, rule=MX_SCALE_FLOOR, blocks=MX_BLOCKS_1D, row
     if rowwise:
         q = torch.empty((rows, cols // 2 if fmt == MX_E2M1 else cols), **u8) if q is None else q
         s = torch.empty((rows, cols // BLOCK), **u8) if s is None else s
+        _buf(q, "q", (rows, cols // 2 if fmt == MX_E2M1 else cols), torch.uint8, x)
+        _buf(s, "s", (rows, cols // BLOCK), torch.uint8, x)
         d.q, d.ldq, d.s, d.lds = _p(q).value, _ld(q), _p(s).value, _ld(s)
     else:
         q = s = None
     if colwise:
         qt = torch.empty((cols, rows), **u8) if qt is None else qt
         st = torch.empty((cols, rows // BLOCK), **u8) if st is None else st
+        _buf(qt, "qt", (cols, rows), torch.uint8, x)
+        _buf(st, "st", (cols, rows // BLOCK), torch.uint8, x)
         d.qt, d.ldqt, d.st, d.ldst = _p(qt).value, _ld(qt), _p(st).value, _ld(st)
     else:
         qt = st = None
@@ -136,6 +165,9 @@ def mx_scale_broadcast(s_in, rows, cols, layout=MX_BCAST_1X128, out=None, stream
     if s_in.dtype != torch.float32:
         raise TypeError("s_in must be float32")
     out = torch.empty((rows, cols // BLOCK), dtype=torch.uint8, device=s_in.device) if out is None else out
+    src_rows = rows if layout == MX_BCAST_1X128 else (rows + 127) // 128
+    _buf(s_in, "s_in", (src_rows, cols // 128), torch.float32)
+    _buf(out, "out", (rows, cols // BLOCK), torch.uint8, s_in)
     check("mx_scale_broadcast", lib().mx_scale_broadcast(_p(s_in), _ld(s_in), layout, rows, cols, _p(out), _ld(out),
                                                          _stream(stream)))
     return out
@@ -146,8 +178,11 @@ def mx_dequantize(q, s, fmt=MX_E4M3, out_dtype=None, y=None, stream=None):
     torch = _torch()
     _rowmajor(q, "q")
     rows, cols = q.shape[0], s.shape[1] * BLOCK
+    _buf(q, "q", (rows, cols // 2 if fmt == MX_E2M1 else cols), torch.uint8)
+    _buf(s, "s", (rows, cols // BLOCK), torch.uint8, q)
     if y is None:
         y = torch.empty((rows, cols), dtype=out_dtype or torch.float32, device=q.device)
+    _buf(y, "y", (rows, cols), y.dtype, q)
     check("mx_dequantize", lib().mx_dequantize(_p(q), _ld(q), _p(s), _ld(s), fmt, rows, cols, _p(y),
                                                _dtype_code(y), _ld(y), _stream(stream)))
     return y
@@ -163,15 +198,18 @@ def mx_kv_quant_write(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale, st
     T, H, D = k.shape
     if k.stride(2) != 1 or k.stride(1) != D:
         raise ValueError("k/v must be contiguous within a token")
-    if slot_mapping.dtype != torch.int64:
-        raise TypeError("slot_mapping must be int64")
+    if not k.is_cuda or v.device != k.device:
+        raise ValueError("k and v must be on one GPU")
+    _buf(slot_mapping, "slot_mapping", (T,), torch.int64, k)
     pages, page_size = k_cache.shape[0], k_cache.shape[1]
     for c, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
         if tuple(c.shape) != (pages, page_size, H, D) or not c.is_contiguous():
             raise ValueError("%s must be contiguous [pages, page_size, H, D]" % n)
+        _buf(c, n, (pages, page_size, H, D), torch.uint8, k)
     for c, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
         if tuple(c.shape) != (pages, page_size, H, D // BLOCK) or not c.is_contiguous():
             raise ValueError("%s must be contiguous [pages, page_size, H, D/32]" % n)
+        _buf(c, n, (pages, page_size, H, D // BLOCK), torch.uint8, k)
     check("mx_kv_quant_write", lib().mx_kv_quant_write(_p(k), _p(v), _dtype_code(k), T, H, D, k.stride(0),
                                                        _p(slot_mapping), _p(k_cache), _p(k_scale), _p(v_cache),
                                                        _p(v_scale), page_size, pages, _stream(stream)))
@@ -192,11 +230,15 @@ def mx_gemm(a, sa, b, sb, a_fmt=MX_E4M3, b_fmt=MX_E4M3, out_dtype=None, y=None, 
     K = sa.shape[1] * BLOCK
     kb_a = K // 2 if a_fmt == MX_E2M1 else K
     kb_b = K // 2 if b_fmt == MX_E2M1 else K
-    if a.shape[1] != kb_a or b.shape[1] != kb_b or sb.shape != (N, K // BLOCK):
+    if a.shape[1] != kb_a or b.shape[1] != kb_b or sb.shape != (N, K // BLOCK) or sa.shape[0] != M:
         raise ValueError("shape mismatch: a %s sa %s b %s sb %s" % (tuple(a.shape), tuple(sa.shape), tuple(b.shape),
                                                                     tuple(sb.shape)))
+    for t, n, shp in ((a, "a", (M, kb_a)), (sa, "sa", (M, K // BLOCK)), (b, "b", (N, kb_b)),
+                      (sb, "sb", (N, K // BLOCK))):
+        _buf(t, n, shp, torch.uint8, a)
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    _buf(y, "y", (M, N), y.dtype, a)
     d = mx_gemm_desc_t()
     d.M, d.N, d.K = M, N, K
     d.a, d.lda, d.sa, d.ldsa, d.a_fmt = a.data_ptr(), _ld(a), sa.data_ptr(), _ld(sa), a_fmt
@@ -225,8 +267,15 @@ def mx_grouped_gemm(a, sa, b, sb, group_offsets, a_fmt=MX_E4M3, b_fmt=MX_E4M3, o
     K = sa.shape[1] * BLOCK
     if sb.shape != (G, N, K // BLOCK):
         raise ValueError("sb must be [G, N, K/32]")
+    kb_a = K // 2 if a_fmt == MX_E2M1 else K
+    kb_b = K // 2 if b_fmt == MX_E2M1 else K
+    for t, n, shp in ((a, "a", (M, kb_a)), (sa, "sa", (M, K // BLOCK)), (b, "b", (G, N, kb_b)),
+                      (sb, "sb", (G, N, K // BLOCK))):
+        _buf(t, n, shp, torch.uint8, a)
+    _buf(group_offsets, "group_offsets", (G + 1,), torch.int64, a)
     if y is None:
         y = torch.zeros((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    _buf(y, "y", (M, N), y.dtype, a)
     d = mx_grouped_gemm_desc_t()
     d.groups, d.total_m, d.N, d.K = G, M, N, K
     d.group_offsets = group_offsets.data_ptr()
@@ -259,8 +308,17 @@ def mx_paged_scores(q_codes, q_scales, k_cache, k_scale, page_table, seq_len, ou
         raise ValueError("inputs must be contiguous")
     if page_table.dtype != torch.int32:
         raise TypeError("page_table must be int32")
+    pages = k_cache.shape[0]
+    for t, n, shp in ((q_codes, "q_codes", (tokens, H, D)), (q_scales, "q_scales", (tokens, H, D // BLOCK)),
+                      (k_cache, "k_cache", (pages, page_size, H, D)),
+                      (k_scale, "k_scale", (pages, page_size, H, D // BLOCK))):
+        _buf(t, n, shp, torch.uint8, q_codes)
+    _buf(page_table, "page_table", (S, page_table.shape[1]), torch.int32, q_codes)
     if out is None:
         out = torch.empty((S, H, seq_len, seq_len), dtype=torch.float32, device=q_codes.device)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    _buf(out, "out", (S, H, seq_len, seq_len), torch.float32, q_codes)
     d = mx_gemm_desc_t()
     d.M, d.N, d.K = seq_len, seq_len, D
     d.a, d.lda, d.sa, d.ldsa, d.a_fmt = q_codes.data_ptr(), H * D, q_scales.data_ptr(), H * (D // BLOCK), MX_E4M3
@@ -303,13 +361,25 @@ def mx_paged_attention(q_codes, q_scales, k_cache, k_scale, v_cache, v_scale, pa
             raise ValueError("%s must be a contiguous GPU tensor" % name)
     if page_table.dtype != torch.int32 or kv_lens.dtype != torch.int32:
         raise TypeError("page_table and kv_lens must be int32")
+    pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    for t, n, shp in ((q_codes, "q_codes", (T, Hq, D)), (q_scales, "q_scales", (T, Hq, D // BLOCK)),
+                      (k_cache, "k_cache", (pages, page_size, Hkv, D)),
+                      (k_scale, "k_scale", (pages, page_size, Hkv, D // BLOCK)),
+                      (v_cache, "v_cache", (pages, page_size, Hkv, D)),
+                      (v_scale, "v_scale", (pages, page_size, Hkv, D // BLOCK))):
+        _buf(t, n, shp, torch.uint8, q_codes)
+    _buf(page_table, "page_table", (S, page_table.shape[1]), torch.int32, q_codes)
+    _buf(kv_lens, "kv_lens", (S,), torch.int32, q_codes)
     if out is None:
         dt = torch.bfloat16 if out_dtype in (None, MX_BF16, torch.bfloat16) else torch.float32
         out = torch.empty((T, Hq, D), dtype=dt, device=q_codes.device)
     if out.shape != (T, Hq, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [S*q_len, Hq, D] tensor")
+    _buf(out, "out", (T, Hq, D), out.dtype, q_codes)
     if lse is not None and (lse.shape != (T, Hq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [S*q_len, Hq] tensor")
+    if lse is not None:
+        _buf(lse, "lse", (T, Hq), torch.float32, q_codes)
     d = mx_attention_desc_t()
     d.num_seqs, d.q_len, d.num_q_heads, d.num_kv_heads, d.head_dim = S, q_len, Hq, Hkv, D
     d.q, d.ld_q, d.q_scale, d.ld_qs = q_codes.data_ptr(), Hq * D, q_scales.data_ptr(), Hq * (D // BLOCK)

@@ -174,3 +174,26 @@ def test_scale_variant_argument_errors_without_gpu(libmx):
     assert b(0x10000, 2, 0, 64, 256, 0x20000, 4, None) == -2                  # ld_out below cols / 32
     assert b(0x10002, 2, 0, 64, 256, 0x20000, 8, None) == -3
     assert b(0x10000, 2, 0, 64, 256, 0x20000, 10, None) == -3                 # ld_out % 4
+
+
+def test_binding_checks_buffers_before_any_call():
+    """The binding knows each tensor's size, the C ABI only its pointer: a
+    buffer of the wrong shape, dtype or layout is refused in Python."""
+    import torch
+    from microscaling_block_scaled_amd import _buf
+    u8 = torch.uint8
+    with pytest.raises(ValueError, match="shape"):
+        _buf(torch.empty((63, 96), dtype=u8), "q", (64, 96), u8)
+    with pytest.raises(TypeError, match="uint8"):
+        _buf(torch.empty((64, 96), dtype=torch.int8), "q", (64, 96), u8)
+    with pytest.raises(ValueError, match="unit stride"):
+        _buf(torch.empty((96, 64), dtype=u8).t(), "q", (64, 96), u8)
+    with pytest.raises(ValueError, match="overlapping"):
+        _buf(torch.empty((1, 96), dtype=u8).expand(64, 96), "q", (64, 96), u8)
+    with pytest.raises(ValueError, match="GPU"):
+        _buf(torch.empty((64, 96), dtype=u8), "q", (64, 96), u8)
+    # a padded pitch and an empty buffer pass the layout checks
+    with pytest.raises(ValueError, match="GPU"):
+        _buf(torch.empty((64, 128), dtype=u8)[:, :96], "q", (64, 96), u8)
+    with pytest.raises(ValueError, match="GPU"):
+        _buf(torch.empty((0, 96), dtype=u8), "q", (0, 96), u8)

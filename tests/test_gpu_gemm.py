@@ -365,3 +365,17 @@ def test_gemm_repeat_runs_identical(mx):
     y1 = mx.mx_gemm(a, sa, b, sb, out_dtype=torch.float32)
     y2 = mx.mx_gemm(a, sa, b, sb, out_dtype=torch.float32)
     assert torch.equal(y1, y2)
+
+
+def test_binding_refuses_short_buffers(mx):
+    """Buffers the kernels would run past are refused before any launch."""
+    import torch
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    a, sa = torch.zeros((256, 512), **u8), torch.zeros((256, 16), **u8)
+    with pytest.raises(ValueError, match="shape"):
+        mx.mx_gemm(a, sa[:200], a, sa)
+    with pytest.raises(ValueError, match="shape"):
+        mx.mx_gemm(a, sa, a, sa, y=torch.empty((256, 200), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError, match="shape"):
+        mx.mx_dequantize(a[:100], sa, y=None)
+    torch.cuda.synchronize()

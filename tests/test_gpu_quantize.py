@@ -261,6 +261,13 @@ def test_argument_errors_are_returned_not_launched(mx):
     with pytest.raises(mx.MXError) as e:
         mx.mx_quantize_colwise(x[:48], E4M3)            # rows % 32 != 0
     assert e.value.status == -2
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="shape"):     # an output one row short
+        mx.mx_quantize(x, E4M3, q=torch.empty((63, 96), **u8))
+    with pytest.raises(ValueError, match="shape"):
+        mx.mx_quantize_colwise(x, E4M3, st=torch.empty((96, 1), **u8))
+    with pytest.raises(TypeError):
+        mx.mx_quantize_ex(x, E4M3, colwise=True, qt=torch.empty((96, 64), dtype=torch.int16, device="cuda"))
     torch.cuda.synchronize()
 
 
