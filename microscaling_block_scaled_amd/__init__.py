@@ -16,6 +16,7 @@ Layouts (row-major, unit stride along the last dimension):
     [rows, cols/2]; K is then taken from the scales.
 """
 import ctypes
+import functools
 
 from ._lib import (BLOCK, MX_ACCUM_AUTO, MX_ACCUM_FP8, MX_ACCUM_FP32, MX_BCAST_1X128, MX_BCAST_128X128, MX_BF16,
                    MX_BLOCKS_1D, MX_BLOCKS_2D, MX_E2M1, MX_E4M3, MX_E5M2, MX_F32, MX_SCALE_CEIL, MX_SCALE_FLOOR,
@@ -35,6 +36,19 @@ __all__ = [
 def _torch():
     import torch
     return torch
+
+
+def _on_device_of_first_tensor(fn):
+    """Runs an entry point with its first tensor's GPU as the current device,
+    so that the library's device checks and the default stream
+    (torch.cuda.current_stream()) refer to the GPU that holds the data."""
+    @functools.wraps(fn)
+    def wrapper(t, *args, **kwargs):
+        if getattr(t, "is_cuda", False):
+            with _torch().cuda.device(t.device):
+                return fn(t, *args, **kwargs)
+        return fn(t, *args, **kwargs)
+    return wrapper
 
 
 def _stream(stream):
@@ -92,6 +106,7 @@ def _ld(t):
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
+@_on_device_of_first_tensor
 def mx_quantize(x, fmt=MX_E4M3, q=None, s=None, stream=None):
     """Rowwise MX quantization of x [rows, cols] -> (codes, scales); E2M1
     codes are [rows, cols/2] (two per byte)."""
@@ -108,6 +123,7 @@ def mx_quantize(x, fmt=MX_E4M3, q=None, s=None, stream=None):
     return q, s
 
 
+@_on_device_of_first_tensor
 def mx_quantize_colwise(x, fmt=MX_E4M3, qt=None, st=None, stream=None):
     """Colwise MXFP8 quantization of x [rows, cols] (blocks of 32 down each
     column), stored transposed -> (codes [cols, rows], scales [cols, rows/32])."""
@@ -124,6 +140,7 @@ def mx_quantize_colwise(x, fmt=MX_E4M3, qt=None, st=None, stream=None):
     return qt, st
 
 
+@_on_device_of_first_tensor
 def mx_quantize_ex(x, fmt=MX_E4M3, rule=MX_SCALE_FLOOR, blocks=MX_BLOCKS_1D, rowwise=True, colwise=False,
                    q=None, s=None, qt=None, st=None, stream=None):
     """Quantization with a scale rule (MX_SCALE_FLOOR / MX_SCALE_CEIL) and a
@@ -156,6 +173,7 @@ def mx_quantize_ex(x, fmt=MX_E4M3, rule=MX_SCALE_FLOOR, blocks=MX_BLOCKS_1D, row
     return q, s, qt, st
 
 
+@_on_device_of_first_tensor
 def mx_scale_broadcast(s_in, rows, cols, layout=MX_BCAST_1X128, out=None, stream=None):
     """Power-of-two FP32 scales of 128-element blocks (layout MX_BCAST_1X128:
     s_in [rows, cols/128]; MX_BCAST_128X128: [ceil(rows/128), cols/128]) ->
@@ -173,6 +191,7 @@ def mx_scale_broadcast(s_in, rows, cols, layout=MX_BCAST_1X128, out=None, stream
     return out
 
 
+@_on_device_of_first_tensor
 def mx_dequantize(q, s, fmt=MX_E4M3, out_dtype=None, y=None, stream=None):
     """x_hat = scale * code -> y [rows, cols] in float32 or bfloat16."""
     torch = _torch()
@@ -188,6 +207,7 @@ def mx_dequantize(q, s, fmt=MX_E4M3, out_dtype=None, y=None, stream=None):
     return y
 
 
+@_on_device_of_first_tensor
 def mx_kv_quant_write(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale, stream=None):
     """Fused E4M3 quantize + paged write of k, v [T, H, D] into
     k_cache / v_cache [pages, page_size, H, D] and k_scale / v_scale
@@ -220,6 +240,7 @@ def mx_gemm_desc(desc, stream=None):
     check("mx_gemm", lib().mx_gemm(ctypes.byref(desc), _stream(stream)))
 
 
+@_on_device_of_first_tensor
 def mx_gemm(a, sa, b, sb, a_fmt=MX_E4M3, b_fmt=MX_E4M3, out_dtype=None, y=None, stream=None, accum=MX_ACCUM_AUTO):
     """y [M, N] = block-scaled A [M, K] * B [N, K]^T with FP32 accumulation
     (accum selects the matrix-instruction path; see include/mxfp8.h)."""
@@ -249,6 +270,7 @@ def mx_gemm(a, sa, b, sb, a_fmt=MX_E4M3, b_fmt=MX_E4M3, out_dtype=None, y=None, 
     return y
 
 
+@_on_device_of_first_tensor
 def mx_grouped_gemm(a, sa, b, sb, group_offsets, a_fmt=MX_E4M3, b_fmt=MX_E4M3, out_dtype=None, y=None,
                     stream=None, accum=MX_ACCUM_AUTO):
     """Per-group block-scaled products: rows off[q] .. off[q+1]-1 of A [total_m,
@@ -288,6 +310,7 @@ def mx_grouped_gemm(a, sa, b, sb, group_offsets, a_fmt=MX_E4M3, b_fmt=MX_E4M3, o
     return y
 
 
+@_on_device_of_first_tensor
 def mx_paged_scores(q_codes, q_scales, k_cache, k_scale, page_table, seq_len, out=None, stream=None,
                     accum=MX_ACCUM_AUTO):
     """QK^T scores per (sequence, head) with K read through a page table.
@@ -339,6 +362,7 @@ def mx_paged_scores(q_codes, q_scales, k_cache, k_scale, page_table, seq_len, ou
     return out
 
 
+@_on_device_of_first_tensor
 def mx_paged_attention(q_codes, q_scales, k_cache, k_scale, v_cache, v_scale, page_table, kv_lens, q_len,
                        sm_scale=None, causal=False, out=None, out_dtype=None, lse=None, stream=None):
     """Attention of MXFP8 queries over the paged MXFP8 KV cache.
