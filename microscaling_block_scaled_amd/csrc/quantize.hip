@@ -16,7 +16,7 @@ namespace {
 using namespace mx;
 
 constexpr int kThreads = 256;
-constexpr int kRowUnroll = 4;  // 8-element chunks per thread in the rowwise kernel
+constexpr int kRowUnroll = 2;  // 8-element chunks per thread in the rowwise kernel
 
 // ---------------------------------------------------------------------------
 // Rowwise. One thread handles chunks of 8 consecutive elements; the 4 lanes
