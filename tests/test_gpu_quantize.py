@@ -309,11 +309,11 @@ def test_empty_problems_are_no_ops(mx):
 @pytest.mark.slow
 def test_launch_split_at_two_to_the_30_chunks(mx, oracle):
     """Rowwise quantize and dequantize split a problem into launches of at
-    most 2^30 work items (chunks of 8, resp. 16, elements). A 2^27 + 96 row x
-    128 column bf16 input (32 GiB) is quantized in three launches (rows 0,
-    2^26, 2^27) and dequantized in two (rows 0, 2^27); rows on both sides of
-    every boundary, and the first and last rows, are compared with the oracle
-    bit for bit."""
+    most 2^30 work items (chunks of 8 elements; for a bf16 dequantize, pieces
+    of 8). A 2^27 + 96 row x 128 column bf16 input (32 GiB) is quantized and
+    dequantized in three launches each (rows 0, 2^26, 2^27); rows on both
+    sides of every boundary, and the first and last rows, are compared with
+    the oracle bit for bit."""
     import torch
     rows, cols = (1 << 27) + 96, 128
     g = torch.Generator(device="cuda").manual_seed(21)
