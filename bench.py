@@ -12,7 +12,8 @@ of unrelated data lands in the kernel's time. Kernel durations come from HIP eve
 stream the kernels run on; ms_per_step is wall time per step including the
 fills.
 
-`value` is the GEMM's TFLOP/s (2*M*N*K per launch / mean launch time); the
+`value` is the GEMM's TFLOP/s (2*M*N*K per launch / mean launch time; the
+median is printed beside it as gemm_us_median, and us_median per quantizer); the
 quantizers' GB/s (algorithmic bytes: read 2RC, write RC + RC/32) are reported
 beside it, and the other rows of the path (paged KV write, paged QK^T scores,
 dequantize, training linear fwd / dgrad / wgrad) unless --quick. cpu_baseline times
@@ -84,7 +85,7 @@ class Timer:
             raise RuntimeError("hipEventRecord failed")
         self.pairs.setdefault(name, []).append((e0, e1))
 
-    def mean_ms(self, name):
+    def times_ms(self, name):
         self.torch.cuda.synchronize()
         ts = []
         for e0, e1 in self.pairs[name]:
@@ -92,7 +93,16 @@ class Timer:
             if self.hip.hipEventElapsedTime(self.ct.byref(ms), e0, e1) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
             ts.append(ms.value)
+        return ts
+
+    def mean_ms(self, name):
+        ts = self.times_ms(name)
         return sum(ts) / len(ts)
+
+    def median_ms(self, name):
+        ts = sorted(self.times_ms(name))
+        n = len(ts)
+        return ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
 
     def release(self):
         for pairs in self.pairs.values():
@@ -152,10 +162,15 @@ def cpu_baseline(xa, xb, xq, budget_s=10.0):
         oracle.gemm(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3)
         return time.perf_counter() - t0
 
+    # size the square sample for ~budget_s: a first guess from a tiny run
+    # (dominated by start-up), then one correction from a run of that size
     n = 32
     t = run(n)
-    n = int(min(4096, max(32, n * (budget_s / max(t, 1e-3)) ** 0.5)))
+    n = int(min(8192, max(32, n * (budget_s / 4 / max(t, 1e-3)) ** 0.5)))
     t = run(n)
+    if t < budget_s / 2 and n < 8192:
+        n = int(min(8192, n * (budget_s / max(t, 1e-3)) ** 0.5))
+        t = run(n)
     flop = 2.0 * n * n * K
     t0 = time.perf_counter()
     oracle.quantize_rows(xq, oracle.E4M3)
@@ -255,8 +270,8 @@ def main():
     for name in ("quantize_rowwise", "quantize_colwise"):
         ms = tm.mean_ms(name)
         gbps = qbytes / (ms * 1e-3) / 1e9
-        quant[name] = {"us": round(ms * 1e3, 2), "GB/s": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                       "algorithmic_bytes": qbytes}
+        quant[name] = {"us": round(ms * 1e3, 2), "us_median": round(tm.median_ms(name) * 1e3, 2), "GB/s": round(gbps, 1),
+                       "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": qbytes}
 
     result = {
         "metric": METRIC, "value": round(gemm_tflops, 1), "unit": "TFLOP/s", "n_gpus": 1,
@@ -274,6 +289,7 @@ def main():
                               "traffic": committed_traffic("quant_rows_kernel 8192x4096 bf16 E4M3", QUANT_SOURCE,
                                                            "quantize_source_sha256")},
         "gemm_us": round(gemm_ms * 1e3, 2),
+        "gemm_us_median": round(tm.median_ms("gemm_8192") * 1e3, 2),
         "quantize": quant,
     }
 
