@@ -1,0 +1,126 @@
+"""Seeded sweep of random shapes, formats, input types and padded pitches
+through the quantizers, dequantize and the GEMM, each against the oracle:
+codes, scales and dequantized values bit for bit, products within
+1e-5 * sum_k |a_k b_k| (f32 output). The GEMM's operands are the oracle's
+own codes, so no expected value depends on the GPU path."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_bitexact, assert_gemm_bound, dev, host
+from microscaling_block_scaled_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2, E2M1 = 0, 1, 2
+N_CASES = 64
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import torch
+    import microscaling_block_scaled_amd as m
+    assert torch.cuda.is_available()
+    ok, reason = m.mx_query_support(0)
+    assert ok, reason
+    return m
+
+
+def case(i):
+    """Shape, formats, input type and pitch paddings of sweep case i."""
+    g = inputs.rng(7000 + i)
+    return dict(
+        rows=32 * int(g.integers(1, 41)), cols=32 * int(g.integers(1, 81)),
+        fmt=int(g.choice([E4M3, E5M2])), f32_in=bool(g.integers(0, 2)),
+        pad_x=8 * int(g.integers(0, 5)), pad_q=16 * int(g.integers(0, 4)), pad_s=int(g.integers(0, 9)),
+        n=32 * int(g.integers(1, 13)), m=32 * int(g.integers(1, 17)), seed=7100 + i)
+
+
+def data(c):
+    """N(0,1) values with a random power-of-two magnitude per 32-block and
+    some zero blocks, as bf16 bits (or f32 with random low bits)."""
+    g = inputs.rng(c["seed"])
+    rows, cols = c["rows"], c["cols"]
+    x = g.standard_normal((rows, cols)) * np.exp2(g.integers(-40, 40, (rows, cols // 32))).repeat(32, 1)
+    x = np.where(g.random((rows, cols // 32)).repeat(32, 1) < 0.05, 0.0, x).astype(np.float32)
+    if c["f32_in"]:
+        return x
+    return inputs.f32_to_bf16_bits(x)
+
+
+def padded(torch, rows, cols, dtype, pad):
+    """A [rows, cols] view whose row pitch is cols + pad."""
+    return torch.empty((rows, cols + pad), dtype=dtype, device="cuda")[:, :cols]
+
+
+def to_dev(torch, x, pad):
+    t = padded(torch, x.shape[0], x.shape[1], torch.float32 if x.dtype == np.float32 else torch.bfloat16, pad)
+    t.copy_(dev(x) if x.dtype == np.float32 else dev(x, bf16=True))
+    return t
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_quantize_dequantize_sweep(mx, oracle, i):
+    import torch
+    c = case(i)
+    x = data(c)
+    rows, cols, fmt = c["rows"], c["cols"], c["fmt"]
+    u8 = torch.uint8
+    xd = to_dev(torch, x, c["pad_x"])
+    qo, so = oracle.quantize_rows(x, fmt)
+    qto, sto = oracle.quantize_cols(x, fmt)
+    what = "case %d %s" % (i, c)
+
+    q, s = mx.mx_quantize(xd, fmt, q=padded(torch, rows, cols, u8, c["pad_q"]), s=padded(torch, rows, cols // 32, u8, c["pad_s"]))
+    assert_bitexact(host(q), qo, "rowwise codes, " + what)
+    assert_bitexact(host(s), so, "rowwise scales, " + what)
+    qt, st = mx.mx_quantize_colwise(xd, fmt, qt=padded(torch, cols, rows, u8, c["pad_q"]),
+                                    st=padded(torch, cols, rows // 32, u8, c["pad_s"]))
+    assert_bitexact(host(qt), qto, "colwise codes, " + what)
+    assert_bitexact(host(st), sto, "colwise scales, " + what)
+    q2, s2, qt2, st2 = mx.mx_quantize_ex(xd, fmt, rowwise=True, colwise=True)
+    for got, want, name in ((q2, qo, "codes"), (s2, so, "scales"), (qt2, qto, "transposed codes"), (st2, sto, "transposed scales")):
+        assert_bitexact(host(got), want, "one-pass %s, %s" % (name, what))
+
+    for out, dt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        y = mx.mx_dequantize(q, s, fmt, y=padded(torch, rows, cols, dt, c["pad_x"]))
+        assert_bitexact(host(y).view(np.uint16 if out == "bf16" else np.uint32),
+                        oracle.dequantize(qo, so, fmt, out).view(np.uint16 if out == "bf16" else np.uint32),
+                        "dequantize to %s, %s" % (out, what))
+
+    # MXFP4 of the same data (rowwise and back)
+    q4, s4 = mx.mx_quantize(xd, E2M1, q=padded(torch, rows, cols // 2, u8, c["pad_q"]))
+    q4o, s4o = oracle.quantize_rows(x, E2M1)
+    assert_bitexact(host(q4), q4o, "E2M1 codes, " + what)
+    assert_bitexact(host(s4), s4o, "E2M1 scales, " + what)
+    y4 = mx.mx_dequantize(q4, s4, E2M1, out_dtype=torch.float32)
+    assert_bitexact(host(y4).view(np.uint32), oracle.dequantize(q4o, s4o, E2M1, "f32").view(np.uint32),
+                    "E2M1 dequantize, " + what)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_gemm_sweep(mx, oracle, i):
+    """y = A B^T for A = the case's first m rows (K = its columns) and B = n
+    rows of other data, both quantized by the oracle, in the case's format
+    for A and the other FP8 format for B, f32 out with padded pitches."""
+    import torch
+    c = case(i)
+    K = c["cols"]
+    m = min(c["m"], c["rows"])
+    x = data(c)[:m]
+    other = dict(c, rows=c["n"], seed=c["seed"] + 50)
+    w = data(other)
+    afmt, bfmt = c["fmt"], E5M2 if c["fmt"] == E4M3 else E4M3
+    qa, sa = oracle.quantize_rows(x, afmt)
+    qb, sb = oracle.quantize_rows(w, bfmt)
+    y_ref, t_ref = oracle.gemm(qa, sa, afmt, qb, sb, bfmt)
+    u8 = torch.uint8
+
+    def put(a, pad):
+        t = padded(torch, a.shape[0], a.shape[1], u8, pad)
+        t.copy_(dev(a))
+        return t
+
+    y = padded(torch, m, c["n"], torch.float32, c["pad_x"] // 2 * 4)
+    mx.mx_gemm(put(qa, c["pad_q"]), put(sa, c["pad_s"]), put(qb, c["pad_q"]), put(sb, c["pad_s"]), afmt, bfmt, y=y)
+    assert_gemm_bound(host(y), y_ref, t_ref, "gemm case %d %s (m=%d)" % (i, c, m))
