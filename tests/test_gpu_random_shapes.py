@@ -87,6 +87,21 @@ def test_quantize_dequantize_sweep(mx, oracle, i):
                         oracle.dequantize(qo, so, fmt, out).view(np.uint16 if out == "bf16" else np.uint32),
                         "dequantize to %s, %s" % (out, what))
 
+    # scale variants: the round-up rule in both orientations (one pass), and
+    # 32 x 32 blocks under the case's rule choice, both outputs padded
+    qo_c, so_c = oracle.quantize_rows(x, fmt, oracle.RULE_CEIL)
+    qto_c, sto_c = oracle.quantize_cols(x, fmt, oracle.RULE_CEIL)
+    got = mx.mx_quantize_ex(xd, fmt, rule=mx.MX_SCALE_CEIL, rowwise=True, colwise=True)
+    for t, want, name in zip(got, (qo_c, so_c, qto_c, sto_c), ("codes", "scales", "transposed codes", "transposed scales")):
+        assert_bitexact(host(t), want, "round-up rule %s, %s" % (name, what))
+    rule2d = oracle.RULE_CEIL if c["seed"] % 2 else oracle.RULE_FLOOR
+    want2d = oracle.quantize_2d(x, fmt, rule2d)
+    got2d = mx.mx_quantize_ex(xd, fmt, rule=rule2d, blocks=mx.MX_BLOCKS_2D, rowwise=True, colwise=True,
+                              q=padded(torch, rows, cols, u8, c["pad_q"]), s=padded(torch, rows, cols // 32, u8, c["pad_s"]),
+                              qt=padded(torch, cols, rows, u8, c["pad_q"]), st=padded(torch, cols, rows // 32, u8, c["pad_s"]))
+    for t, want, name in zip(got2d, want2d, ("codes", "scales", "transposed codes", "transposed scales")):
+        assert_bitexact(host(t), want, "32x32 blocks (rule %d) %s, %s" % (rule2d, name, what))
+
     # MXFP4 of the same data (rowwise and back)
     q4, s4 = mx.mx_quantize(xd, E2M1, q=padded(torch, rows, cols // 2, u8, c["pad_q"]))
     q4o, s4o = oracle.quantize_rows(x, E2M1)
