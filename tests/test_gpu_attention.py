@@ -187,3 +187,26 @@ def test_attention_repeat_runs_identical(mx, oracle):
     a, la = _run(mx, c, 0.1, True, True)
     b, lb = _run(mx, c, 0.1, True, True)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def random_case(i):
+    """Seeded random configuration i: sequences, queries, ragged kv_lens
+    (zero allowed), page size, query/KV heads and the causal flag."""
+    g = inputs.rng(8500 + i)
+    S = int(g.integers(1, 4))
+    ql = int(g.integers(1, 261))
+    lens = [int(v) for v in g.integers(0, 901, S)]
+    page = int(g.choice([128, 256, 384]))
+    hq, hkv = [(1, 1), (2, 1), (4, 2), (8, 8), (8, 2), (6, 3)][int(g.integers(0, 6))]
+    return S, ql, lens, page, hq, hkv, bool(g.integers(0, 2))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_attention_random_configurations(mx, oracle, i):
+    S, ql, lens, page, hq, hkv, causal = random_case(i)
+    c = quantized_case(oracle, 8600 + i, S, ql, lens, page, hq, hkv, 128)
+    sm = 1.0 / math.sqrt(128)
+    ref = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"], c["kv_lens"], ql,
+                                 sm, causal)
+    o, lse = _run(mx, c, sm, causal, True)
+    assert_attention_bound(o, lse, ref, sm, "random case %d %s" % (i, (S, ql, lens, page, hq, hkv, causal)))
