@@ -112,3 +112,38 @@ def test_grouped_gemm_moe_workload_sampled(mx, oracle):
     got = host(y[dev(mi), dev(ni)]).astype(np.float64)
     worst = assert_gemm_bound(got, y_ref, t_ref, "moe workload")
     print("moe workload: worst |err|/T = %.3g" % worst)
+
+
+def random_grouped_case(i):
+    """Seeded random grouped product i: 1-12 groups of 0-600 rows (about a
+    fifth empty), N, K and the operand formats."""
+    g = inputs.rng(760 + i)
+    G = int(g.integers(1, 13))
+    sizes = [int(v) if g.random() > 0.2 else 0 for v in g.integers(0, 601, G)]
+    N = int(g.choice([256, 384, 512]))
+    K = int(g.choice([512, 1024, 2048]))
+    af, bf = [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2)][int(g.integers(0, 3))]
+    return sizes, N, K, af, bf
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_grouped_gemm_random(mx, oracle, i):
+    """The operands are the oracle's codes, uploaded; f32 output."""
+    import torch
+    sizes, N, K, af, bf = random_grouped_case(i)
+    G = len(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    M = int(off[-1]) + 5
+    qa, sa = oracle.quantize_rows(inputs.normal_bf16(780 + i, (M, K)), af)
+    qb, sb = oracle.quantize_rows(inputs.normal_bf16(800 + i, (G * N, K), sigma=0.05), bf)
+    sentinel = -7.0
+    y = torch.full((M, N), sentinel, dtype=torch.float32, device="cuda")
+    mx.mx_grouped_gemm(dev(qa), dev(sa), dev(qb).view(G, N, K), dev(sb).view(G, N, K // 32), dev(off), a_fmt=af,
+                       b_fmt=bf, y=y)
+    yh = host(y).astype(np.float64)
+    for q in range(G):
+        r0, r1 = int(off[q]), int(off[q + 1])
+        if r1 > r0:
+            y_ref, t_ref = oracle.gemm(qa[r0:r1], sa[r0:r1], af, qb[q * N:(q + 1) * N], sb[q * N:(q + 1) * N], bf)
+            assert_gemm_bound(yh[r0:r1], y_ref, t_ref, "random case %d %s group %d" % (i, (sizes, N, K, af, bf), q))
+    assert np.all(yh[int(off[-1]):] == sentinel), "rows outside every group were written"
