@@ -139,3 +139,46 @@ def test_gemm_sweep(mx, oracle, i):
     y = padded(torch, m, c["n"], torch.float32, c["pad_x"] // 2 * 4)
     mx.mx_gemm(put(qa, c["pad_q"]), put(sa, c["pad_s"]), put(qb, c["pad_q"]), put(sb, c["pad_s"]), afmt, bfmt, y=y)
     assert_gemm_bound(host(y), y_ref, t_ref, "gemm case %d %s (m=%d)" % (i, c, m))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_kv_write_sweep(mx, oracle, i):
+    """Fused KV quantize + paged write with random tokens, heads, head_dim,
+    page size, input type and token pitch; slot maps with padding tokens
+    (-1) and slots past the cache, which must be skipped. Untouched slots
+    keep their contents."""
+    import torch
+    g = inputs.rng(7500 + i)
+    T, H = int(g.integers(1, 601)), int(g.integers(1, 9))
+    D = int(g.choice([32, 64, 96, 128, 256]))
+    page_size = int(g.choice([16, 64, 128]))
+    pages = -(-T // page_size) + int(g.integers(0, 4))
+    f32_in = bool(g.integers(0, 2))
+    slots = g.permutation(pages * page_size)[:T].astype(np.int64)
+    slots[g.random(T) < 0.1] = -1
+    slots[g.random(T) < 0.02] = pages * page_size + int(g.integers(0, 100))
+    raw = g.standard_normal((2, T, H, D)) * np.exp2(g.integers(-20, 20, (2, T, H, D // 32))).repeat(32, -1)
+    raw = raw.astype(np.float32)
+    k, v = (raw[0], raw[1]) if f32_in else (inputs.f32_to_bf16_bits(raw[0]), inputs.f32_to_bf16_bits(raw[1]))
+    dt = torch.float32 if f32_in else torch.bfloat16
+    pad = (4 if f32_in else 8) * int(g.integers(0, 3))
+
+    def put(a):
+        buf = torch.empty((T, H * D + pad), dtype=dt, device="cuda")
+        t = buf.as_strided((T, H, D), (H * D + pad, D, 1))
+        t.copy_(dev(a) if f32_in else dev(a, bf16=True))
+        return t
+
+    kc = torch.full((pages, page_size, H, D), 0x33, dtype=torch.uint8, device="cuda")
+    vc = torch.full_like(kc, 0x33)
+    ks = torch.full((pages, page_size, H, D // 32), 0x44, dtype=torch.uint8, device="cuda")
+    vs = torch.full_like(ks, 0x44)
+    mx.mx_kv_quant_write(put(k), put(v), dev(slots), kc, ks, vc, vs)
+    ok_slots = np.where((slots >= 0) & (slots < pages * page_size), slots, -1)
+    init_c = np.full((pages, page_size, H, D), 0x33, np.uint8)
+    init_s = np.full((pages, page_size, H, D // 32), 0x44, np.uint8)
+    want = oracle.kv_quant_write(k, v, ok_slots, page_size, pages, k_cache=init_c.copy(), k_scale=init_s.copy(),
+                                 v_cache=init_c.copy(), v_scale=init_s.copy())
+    what = "case %d: T=%d H=%d D=%d page=%d pages=%d f32=%d pad=%d" % (i, T, H, D, page_size, pages, f32_in, pad)
+    for got, w, name in zip((kc, ks, vc, vs), want, ("k_cache", "k_scale", "v_cache", "v_scale")):
+        assert_bitexact(host(got), w, "%s, %s" % (name, what))
