@@ -598,8 +598,14 @@ mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int6
   if (row_tiles * col_tiles >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const dim3 grid((uint32_t)(row_tiles * col_tiles));
   const uint32_t col_major = col_tiles >= 64 ? 1u : 0u;
+  // Up to 4096 tiles the whole grid is resident at once (8 work-groups per
+  // CU), so every work-group reads, then writes, in step with the others.
+  // 20000 bytes of unused dynamic LDS leave 4 per CU and stagger them:
+  // 8192 x 4096 25.1 -> 24.2 us, 14336 x 4096 37.7 -> 37.3 us, 16384 x 4096
+  // 42.5 -> 42.3 us; on 16384 x 14336 (14336 tiles) it measured 1.2 % slower.
+  const uint32_t lds_pad = row_tiles * col_tiles <= 4096 ? 20000u : 0u;
 #define MX_COLS_LAUNCH(T, F)                                                                                        \
-  hipLaunchKernelGGL((quant_cols_kernel<T, F, false, false>), grid, dim3(kThreads), 0, stream, (const T*)x, rows, cols, ldx, \
+  hipLaunchKernelGGL((quant_cols_kernel<T, F, false, false>), grid, dim3(kThreads), lds_pad, stream, (const T*)x, rows, cols, ldx, \
                      qt, ldq, st, lds, (uint32_t)col_tiles, col_major, round_up, nullptr, 0, nullptr, 0)
   if (xdt == MX_BF16) {
     if (fmt == MX_E5M2) MX_COLS_LAUNCH(uint16_t, MX_E5M2); else MX_COLS_LAUNCH(uint16_t, MX_E4M3);
