@@ -635,8 +635,9 @@ mx_status_t quantize_tile_host(const mx_quantize_desc_t* d, uint32_t round_up, b
   if (row_tiles * col_tiles >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const dim3 grid((uint32_t)(row_tiles * col_tiles));
   const uint32_t col_major = col_tiles >= 64 ? 1u : 0u;
+  const uint32_t lds_pad = row_tiles * col_tiles <= 4096 ? 20000u : 0u;  // as in the colwise call
 #define MX_TILE_LAUNCH(T, F, B2D, ROWS)                                                                            \
-  hipLaunchKernelGGL((quant_cols_kernel<T, F, B2D, ROWS>), grid, dim3(kThreads), 0, stream, (const T*)d->x, d->rows, \
+  hipLaunchKernelGGL((quant_cols_kernel<T, F, B2D, ROWS>), grid, dim3(kThreads), lds_pad, stream, (const T*)d->x, d->rows, \
                      d->cols, d->ldx, d->qt, d->ldqt, d->st, d->ldst, (uint32_t)col_tiles, col_major, round_up,  \
                      d->q, d->ldq, d->s, d->lds)
 #define MX_TILE_MODE(T, F) \
