@@ -23,8 +23,11 @@
  *
  * Conventions shared by every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller. The library
- *     allocates no memory, keeps no pointer after returning, and holds no
- *     mutable global state; calls on different streams may run concurrently.
+ *     allocates no memory and keeps no pointer after returning. Its only
+ *     global state is a per-device cache of the architecture check (filled
+ *     atomically on the first call on each device, never changed after), so
+ *     calls from several threads and on different streams may run
+ *     concurrently.
  *   - Work is enqueued on `stream` (asynchronous; no implicit sync). Argument
  *     errors are detected on the host before anything is launched and are
  *     returned synchronously; then nothing is written. A launch failure
@@ -230,25 +233,42 @@ mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_t dt, int64
  *
  * Accumulation (field `accum`). The sum over blocks is FP32 in every mode;
  * the modes differ inside one matrix instruction:
+ *   MX_ACCUM_FP32 -- codes decoded exactly to bf16 with the block scale
+ *                    folded in, then bf16 MFMA with FP32-level accumulation;
+ *                    half the peak rate of MX_ACCUM_FP8. Every output meets
+ *                    |y - y_ref| <= 1e-5 * sum_k |a_k b_k| over the whole
+ *                    E8M0 range, wherever that sum lies between 2^-100 and
+ *                    2^120 (smaller sums fall under the f32 grid, larger ones
+ *                    may overflow a partial sum). The fold is exact for scale
+ *                    codes 10..246 (E4M3) / 17..239 (E5M2); a block with a
+ *                    scale outside that window and a non-zero code is added
+ *                    afterwards by an exact pass on the same kernel (slower;
+ *                    all-zero blocks, e.g. code-0 padding, never start it).
+ *                    E5M2 Inf codes under such a scale give NaN.
+ *   MX_ACCUM_AUTO -- the same as MX_ACCUM_FP32 (E4M3 / E5M2 operands; for
+ *                    MXFP4 see below).
  *   MX_ACCUM_FP8  -- the scaled FP8 matrix instructions on the codes
  *                    (v_mfma_scale_f32_16x16x128_f8f6f4 / _32x32x64_), peak
- *                    rate. On gfx950 these instructions add the products of
- *                    each group of 8 consecutive k with only about 14
- *                    significant bits, aligned to the group's largest product
- *                    (measured), i.e. a per-group error up to ~2^-13 of that
- *                    product. [FP8DS §6.1-§6.3] discusses the same kind of
- *                    limited-precision accumulation in FP8 tensor cores.
- *   MX_ACCUM_FP32 -- codes decoded exactly to bf16 with the block scale
- *                    folded in (exact for scale codes 3..246 with E4M3 and
- *                    10..239 with E5M2), then bf16 MFMA with FP32-level
- *                    accumulation; half the peak rate of MX_ACCUM_FP8.
- *   MX_ACCUM_AUTO -- MX_ACCUM_FP8 when both operands are E4M3 and K >= 2048,
- *                    where the grouped error stays far below 1e-5 * sum|a b|
- *                    for data of Gaussian-like spread; MX_ACCUM_FP32 otherwise.
+ *                    rate, E8M0 scales applied by the instruction over the
+ *                    whole range. On gfx950 these instructions add the
+ *                    products of each group of 8 consecutive k with only about
+ *                    14 significant bits, aligned to the group's largest
+ *                    product (measured), so each group may lose up to ~2^-13
+ *                    of that product: |err| <= ~2^-13 * sum|a b| in the worst
+ *                    case, reached when a few products dominate an output.
+ *                    Measured worst |err| / sum|a b| on every output: N(0,1)
+ *                    E4M3 at 8192^3 1.6e-6, |N(0,1)| (same sign) at K = 2048
+ *                    5.5e-6, Student-t (nu = 3) at K = 8192 8.4e-5 -- so the
+ *                    1e-5 bound holds on data whose per-group errors cancel,
+ *                    not on heavy-tailed data. [FP8DS §6.1-§6.3] discusses the
+ *                    same kind of limited-precision accumulation in FP8 tensor
+ *                    cores.
  *
  * MXFP4 (a_fmt = b_fmt = MX_E2M1; codes packed two per byte, lda/ldb in bytes
  * >= K/2): the scaled matrix instruction on the E2M1 codes (accum AUTO or
- * FP8; FP32 is rejected with MX_ERR_FORMAT), on the large-tile kernel only:
+ * FP8, both exact here: a product of two E2M1 values has at most 4
+ * significant bits, so a group of 8 fits the instruction's accumulator; FP32
+ * is rejected with MX_ERR_FORMAT), on the large-tile kernel only:
  * K % 1024 == 0, M >= 256, N >= 256, no page table, 16-byte aligned code and
  * scale rows (MX_ERR_SHAPE / MX_ERR_ALIGN otherwise). E2M1 mixed with an FP8
  * format returns MX_ERR_FORMAT.
@@ -307,7 +327,16 @@ mx_status_t mx_gemm(const mx_gemm_desc_t* desc, hipStream_t stream);
  * the softmax in f32 with exp2; P rounded to bf16 for the bf16 matrix
  * instruction, its normaliser summed in f32 from the unrounded values; O
  * accumulated in FP32, then divided by the normaliser; bf16 output rounds
- * to nearest even. A NaN score makes its row NaN; a NaN value in a V block
+ * to nearest even. Scales cover the whole E8M0 range: Q and K scales go to
+ * the instruction; V is decoded with its scale clamped into 10..246 (exact
+ * normal bf16) and a key whose scales leave that window has the rest of its
+ * scale moved onto its weight P_j, which is exact unless one key's four V
+ * scales span more than 236 codes (then its blocks 2^236 and more below its
+ * largest are clamped). O is formed as the f32 sum of P_j * V_jd with the
+ * weights taken relative to a running reference that lags the row maximum
+ * by up to 2^8, before the division by the normaliser: an output whose
+ * sum_j |V_jd| times 2^8 leaves the f32 range overflows even if O itself
+ * would fit. A NaN score makes its row NaN; a NaN value in a V block
  * (scale code 0xFF) makes NaN every output column it is multiplied into,
  * including rows of the same query tile for which that key is masked.
  *

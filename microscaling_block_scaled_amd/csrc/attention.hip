@@ -11,8 +11,10 @@
 //   P   = softmax(sm_scale * S) over the allowed keys, online over blocks of
 //         128 keys (running max and sum in f32), rounded to bf16;
 //   O   = P V           v_mfma_f32_32x32x16_bf16, V decoded to bf16 with its
-//                       block scale (v_cvt_scalef32_pk_bf16_fp8, exact for
-//                       scale codes 3..246) into LDS once per work-group.
+//                       block scale (v_cvt_scalef32_pk_bf16_fp8) into LDS once
+//                       per work-group; a key whose scales leave the range
+//                       where that is exact moves part of its scale to P
+//                       (v_key_shift).
 //
 // Work-group: 4 waves, 128 queries (32 per wave) of one (sequence, query
 // head). Each wave computes S^T for its queries (keys on the instruction's
@@ -66,18 +68,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
+// V over the whole E8M0 range. code * 2^(s - 127) is an exact normal bf16
+// for every finite E4M3 code when the scale code s lies in [10, 246]. A key
+// whose four head-dim scales leave that window gets a shift r (v_key_shift):
+// its V^T entries hold code * 2^(clamp(s - r, 10, 246) - 127) and its weight
+// P_j is multiplied by 2^r, so P_j * V_jd is unchanged. r = 0 whenever the
+// scales are inside the window (the usual case: a block whose scales all
+// are skips the shift computation and multiplies its weights by 1);
+// otherwise r is the smallest move that brings them in. Only a key whose own
+// scales span more than 236 codes cannot be brought in whole: its largest
+// block is kept exact and its blocks more than 2^236 below that one are
+// clamped up to the window's floor.
+// The NaN code 0xFF is kept, so its blocks decode to NaN.
+constexpr int kVFoldLo = 10, kVFoldHi = 246;
+__device__ __forceinline__ int v_key_shift(uint32_t w) {
+  int lo = 255, hi = -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = (int)((w >> (8 * i)) & 0xFFu);
+    if (s != 0xFF) {
+      lo = min(lo, s);
+      hi = max(hi, s);
+    }
+  }
+  // the largest block must stay exact: r >= hi - 246; within that, lift the
+  // key as far as its smallest block needs (never past 0 from above)
+  return max(hi - kVFoldHi, min(lo - kVFoldLo, 0));
+}
+__device__ __forceinline__ uint32_t v_fold_code(uint32_t s, int r) {
+  return s == 0xFFu ? s : (uint32_t)min(max((int)s - r, kVFoldLo), kVFoldHi);
+}
+
 // The running softmax reference moves up only when a block's maximum
 // exceeds it by more than this (log2 units); weights relative to it then
 // stay below 2^8, far inside f32 and bf16 range, and most blocks skip the
 // rescaling of the accumulators.
 constexpr float kRescaleSlack = 8.f;
 
-template <bool BF16OUT>
+template <bool BF16OUT, bool SHIFTED>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t Ks[2][kKB * kHD];
   __shared__ __attribute__((aligned(16))) uint32_t KSs[2][kKB];
   __shared__ __attribute__((aligned(16))) uint32_t VSs[2][kKB];
   __shared__ __attribute__((aligned(1024))) uint8_t VT[kHD * kVTRow];
+  __shared__ __attribute__((aligned(16))) float VShift[SHIFTED ? kKB : 4];  // 2^r of each key (v_key_shift)
 
   // ---- work item: (sequence, head, query tile). Without a mask the query
   // tiles of one (sequence, head) share its keys, so they are kept on one XCD
@@ -129,6 +163,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   const int lim = g.causal ? min(L, L - q_len + qi + 1) : L;  // allowed keys: j < lim
 
   const int64_t out_row = tok * g.ld_o + (int64_t)h * kHD;
+  const int32_t* tab = g.table + (int64_t)s * g.pages_per_seq;
+
+  // Does some V scale of the keys this tile reads lie outside the fold
+  // window? Such tiles are left to the SHIFTED instantiation of this kernel
+  // (launched after this one on the same stream), which moves part of those
+  // keys' scales onto P (v_key_shift); the plain one stays free of it.
+  bool v_out = false;
+  for (int j = tid; j < kmax; j += kAttnThreads) {
+    const int64_t slot = (int64_t)tab[j / g.page_size] * g.page_size + j % g.page_size;
+    const uint32_t w = *(const uint32_t*)(g.vs + (slot * g.hkv + hk) * (kHD / 32));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t c = (w >> (8 * i)) & 0xFFu;
+      v_out |= c != 0xFFu && (c < (uint32_t)kVFoldLo || c > (uint32_t)kVFoldHi);
+    }
+  }
+  if ((__syncthreads_or(v_out) != 0) != SHIFTED) return;
+
   if (nblk == 0) {  // no allowed key anywhere in the tile
     if (q_ok) {
 #pragma unroll
@@ -167,7 +219,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   // slots are consecutive.
   const uint32_t slot_bytes = g.hkv * kHD;        // code bytes per cache slot
   const uint32_t slot_sbytes = g.hkv * (kHD / 32); // scale bytes per cache slot
-  const int32_t* tab = g.table + (int64_t)s * g.pages_per_seq;
   auto slot0_of = [&](int b) -> int64_t {
     const uint32_t j = (uint32_t)b * kKB;
     return (int64_t)tab[j / g.page_size] * g.page_size + j % g.page_size;
@@ -220,13 +271,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   };
 
   // decode this thread's V unit into V^T rows 4gd .. 4gd+3 (gd = gd0, gd0 + 4)
-  auto decode_v = [&](int buf) {
+  auto decode_v = [&](int buf, bool shifted) {
     const uint4 sa = *(const uint4*)&VSs[buf][v_key];
     const uint4 sb = *(const uint4*)&VSs[buf][v_key + 8];
     const uint32_t sw[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
     float sc[8];
+    if (!shifted) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sc[e] = scale_value((sw[e] >> (8 * db)) & 0xFFu);
+      for (int e = 0; e < 8; ++e) sc[e] = scale_value((sw[e] >> (8 * db)) & 0xFFu);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = v_key_shift(sw[e]);
+        sc[e] = scale_value(v_fold_code((sw[e] >> (8 * db)) & 0xFFu, r));
+        // the threads of head-dim block 0 publish the key's 2^r
+        if (db == 0) VShift[v_key + (e & 3) + 8 * (e >> 2)] = __uint_as_float((uint32_t)(127 + r) << 23);
+      }
+    }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       uint32_t lo[8], hi[8];
@@ -256,6 +317,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   float l_run = 0.f;                 // sum of exp2(x - m_ref) over the keys so far
 
   const uint32_t fp = fperm(lr);
+
   issue_block(0, 0);
 
   for (int b = 0; b < nblk; ++b) {
@@ -263,7 +325,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     barrier();  // block b staged; V^T and buffer buf ^ 1 are free
-    decode_v(buf);
+    decode_v(buf, SHIFTED);
     if (b + 1 < nblk) issue_block(b + 1, buf ^ 1);
 
     // ---- S^T for this wave's 32 queries x 128 keys: 4 tiles of 32 keys,
@@ -339,6 +401,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
         for (int e = 0; e < 8; ++e) {
           p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][8 * c + e], g.c2, -m_use));
           ls += p[e];
+        }
+        if constexpr (SHIFTED) {
+          // 2^r of each key; element e is key 32 kt + 16 c + 8 (e / 4) + 4 lg + e % 4
+          const float4 s0 = *(const float4*)&VShift[32 * kt + 16 * c + 4 * lg];
+          const float4 s1 = *(const float4*)&VShift[32 * kt + 16 * c + 8 + 4 * lg];
+          p[0] *= s0.x; p[1] *= s0.y; p[2] *= s0.z; p[3] *= s0.w;
+          p[4] *= s1.x; p[5] *= s1.y; p[6] *= s1.z; p[7] *= s1.w;
         }
         pb[c] = v8bf16{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
                        (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
@@ -424,9 +493,14 @@ extern "C" mx_status_t mx_paged_attention(const mx_attention_desc_t* d, hipStrea
   g.hq = (uint32_t)hq; g.hkv = (uint32_t)hkv; g.group = (uint32_t)(hq / hkv);
   g.causal = d->causal ? 1u : 0u; g.q_tiles = (uint32_t)q_tiles; g.total_wg = (uint32_t)total;
   g.c2 = d->sm_scale * 1.4426950408889634f;
-  if (d->out_dtype == MX_BF16)
-    hipLaunchKernelGGL(attn_kernel<true>, dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
-  else
-    hipLaunchKernelGGL(attn_kernel<false>, dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
+  // the plain kernel takes every tile whose V scales lie inside the fold
+  // window, the shifted one the rest (each tile decides the same way in both)
+  if (d->out_dtype == MX_BF16) {
+    hipLaunchKernelGGL((attn_kernel<true, false>), dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
+    hipLaunchKernelGGL((attn_kernel<true, true>), dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<false, false>), dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
+    hipLaunchKernelGGL((attn_kernel<false, true>), dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
+  }
   return mx_host::launch_status();
 }

@@ -73,6 +73,101 @@ __device__ __forceinline__ uint32_t load_scales4(const uint8_t* p, int64_t kt, i
   return v;
 }
 
+// FP32-accumulation mode: the per-lane record of a block whose scale lies
+// outside the fold window while it holds a non-zero code; the terms of such
+// blocks are replaced afterwards by an exact pass (exact_block16 / the
+// large-tile kernel's).
+template <int FMT>
+__device__ __forceinline__ uint32_t unfolded_codes(uint32_t scale, uint2 w) {
+  return fold_excluded<FMT>(scale) ? ((w.x | w.y) & 0x7F7F7F7Fu) : 0u;
+}
+
+// fold_decode8 when `take`, else zeros (zero codes and a neutral scale: a
+// NaN scale would still give NaN)
+template <int FMT>
+__device__ __forceinline__ v8bf16 fold_decode8_or_zero(uint2 w, uint32_t s, bool take) {
+  return decode8_bf16<FMT>(take ? w : make_uint2(0u, 0u), take ? fold_scale<FMT>(s) : 1.f);
+}
+// -v, elementwise (sign bits flipped; exact)
+__device__ __forceinline__ v8bf16 neg_bf16x8(v8bf16 v) {
+  uint4 u = __builtin_bit_cast(uint4, v);
+  u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
+  return __builtin_bit_cast(v8bf16, u);
+}
+
+// The exact pass for one 32-K block of a wave's 4 x 4 tiles of 16 x 16
+// outputs (v_mfma_f32_16x16x32_bf16: lane (r, g) supplies row r of a fragment
+// and k = 8 g .. 8 g + 7 of the block; its outputs lie on its A row and on B
+// rows 4 g .. 4 g + 3 of a tile). qa / ca: the lane's codes and scale of A
+// row tile i; qb / cb: those of B row tile j. The terms of pairs with an A
+// or B scale outside the fold window are replaced: the main loop's folded
+// terms are taken back and the exact ones added cell by cell (ExactCells).
+template <int AF, int BF>
+__device__ __forceinline__ void exact_block16(const uint2 (&qa)[4], const uint32_t (&ca)[4], const uint2 (&qb)[4],
+                                              const uint32_t (&cb)[4], v4f32 (&acc)[4][4]) {
+  constexpr ExactCells<AF, BF> cells{};
+  static_assert(cells.feasible(), "a cell of the exact pass has no common shift");
+  uint32_t nz = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nz |= unfolded_codes<AF>(ca[i], qa[i]) | unfolded_codes<BF>(cb[i], qb[i]);
+  if (__builtin_amdgcn_ballot_w64(nz != 0u) == 0) return;
+  // take back the main loop's (folded) terms of the pairs the fold does not
+  // cover: R1 = left-out A rows x every B row, R2 = the other A rows x
+  // left-out B rows
+  bool exa[4], exb[4];
+  v8bf16 b_all[4], b_ex[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    exa[i] = fold_excluded<AF>(ca[i]);
+    exb[i] = fold_excluded<BF>(cb[i]);
+    b_all[i] = fold_decode8<BF>(qb[i], cb[i]);
+    b_ex[i] = fold_decode8_or_zero<BF>(qb[i], cb[i], exb[i]);
+  }
+  const bool any_exb = __builtin_amdgcn_ballot_w64(exb[0] || exb[1] || exb[2] || exb[3]) != 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (__builtin_amdgcn_ballot_w64(exa[i]) != 0) {
+      const v8bf16 a1 = neg_bf16x8(fold_decode8_or_zero<AF>(qa[i], ca[i], exa[i]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_all[j], a1, acc[i][j], 0, 0, 0);
+    }
+    if (any_exb) {
+      const v8bf16 a2 = neg_bf16x8(fold_decode8_or_zero<AF>(qa[i], ca[i], !exa[i]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_ex[j], a2, acc[i][j], 0, 0, 0);
+    }
+  }
+  // and add their exact values, cell by cell
+  uint32_t xa[4], xb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xa[i] = exact_class<AF>(ca[i]);
+    xb[i] = exact_class<BF>(cb[i]);
+  }
+  for (int c = 0; c < cells.n; ++c) {
+    const int cx = cells.cell[c].x, cy = cells.cell[c].y, w = cells.cell[c].w;
+    v8bf16 bf[4];
+    bool bon[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = xb[j] == (uint32_t)cy && cb[j] != 0xFFu;
+      bon[j] = __builtin_amdgcn_ballot_w64(in) != 0;
+      // rows outside the cell: zero codes and a neutral scale (their shifted
+      // code could reach the NaN exponent)
+      bf[j] = decode8_bf16<BF>(in ? qb[j] : make_uint2(0u, 0u), in ? __uint_as_float((uint32_t)((int)cb[j] + w) << 23) : 1.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = xa[i] == (uint32_t)cx && ca[i] != 0xFFu;
+      if (__builtin_amdgcn_ballot_w64(in) == 0) continue;
+      const v8bf16 af = decode8_bf16<AF>(in ? qa[i] : make_uint2(0u, 0u), in ? __uint_as_float((uint32_t)((int)ca[i] - w) << 23) : 1.f);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (bon[j]) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af, acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
 template <int BM, int BN, int AFMT, int BFMT, bool BF16OUT, bool PAGED, int MODE>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-tile
@@ -177,6 +272,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v4f32{0.f, 0.f, 0.f, 0.f};
 
+  // FP32-accumulation mode: nonzero once a decoded block with a scale
+  // outside the fold window held a non-zero code (exact pass below)
+  uint32_t unfolded = 0;
+
   load_global(0);
   store_lds(0);
   __syncthreads();
@@ -218,13 +317,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j) {
           const uint32_t row = wn * WN + j * 16 + lr;
           const uint2 w = *(const uint2*)(&Bs[buf][swz(row, chunk) + off]);
-          bf[j] = decode8_bf16<BFMT>(w, scale_value((sBs[buf][row] >> (8 * kb)) & 0xFFu));
+          const uint32_t sc = (sBs[buf][row] >> (8 * kb)) & 0xFFu;
+          unfolded |= unfolded_codes<BFMT>(sc, w);
+          bf[j] = fold_decode8<BFMT>(w, sc);
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const uint32_t row = wm * WM + i * 16 + lr;
           const uint2 w = *(const uint2*)(&As[buf][swz(row, chunk) + off]);
-          const v8bf16 af = decode8_bf16<AFMT>(w, scale_value((sAs[buf][row] >> (8 * kb)) & 0xFFu));
+          const uint32_t sc = (sAs[buf][row] >> (8 * kb)) & 0xFFu;
+          unfolded |= unfolded_codes<AFMT>(sc, w);
+          const v8bf16 af = fold_decode8<AFMT>(w, sc);
 #pragma unroll
           for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af, acc[i][j], 0, 0, 0);
         }
@@ -232,6 +335,38 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     }
     if (kt + 1 < ksteps) store_lds(buf ^ 1);
     __syncthreads();
+  }
+
+  // ---- FP32-accumulation mode, exact pass over the blocks with a scale
+  // outside the fold window, one 32-K block at a time (codes and scales read
+  // again from global memory; rows past M or N read as zero codes)
+  if constexpr (MODE == kModeBF16 && FM == 4 && FN == 4) {
+    if (__builtin_amdgcn_ballot_w64(unfolded != 0u) != 0) {
+      const uint8_t* ar[4];
+      const uint8_t* br[4];
+      const uint8_t* sar[4];
+      const uint8_t* sbr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + wm * WM + i * 16 + lr, n = n0 + wn * WN + i * 16 + lr;
+        ar[i] = m < g.M ? A + m * g.lda + 8 * lg : nullptr;
+        sar[i] = m < g.M ? SA + m * g.ldsa : nullptr;
+        br[i] = n < g.N ? b_row_ptr(n, B, g.ldb, g.page_stride) + 8 * lg : nullptr;
+        sbr[i] = n < g.N ? b_row_ptr(n, SB, g.ldsb, g.page_stride_s) : nullptr;
+      }
+      for (int64_t b = 0; b < kblocks; ++b) {
+        uint2 qa[4], qb[4];
+        uint32_t ca[4], cb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qa[i] = ar[i] ? *(const uint2*)(ar[i] + 32 * b) : make_uint2(0, 0);
+          ca[i] = sar[i] ? sar[i][b] : 127u;
+          qb[i] = br[i] ? *(const uint2*)(br[i] + 32 * b) : make_uint2(0, 0);
+          cb[i] = sbr[i] ? sbr[i][b] : 127u;
+        }
+        exact_block16<AFMT, BFMT>(qa, ca, qb, cb, acc);
+      }
+    }
   }
 
   // ---- epilogue: lane owns y[m][n .. n+3]
@@ -365,17 +500,23 @@ __global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uin
   const uint32_t lr = lane & 15, lg = lane >> 4;
   const int64_t mw = (int64_t)rb * kRPRows + wave * 16 * kRPTiles + lr;  // + 16 t
   v8bf16 af[kRPTiles][4];
+  uint32_t sa4s[kRPTiles];
+  // nonzero once a block with a scale outside the fold window holds a
+  // non-zero code: that chunk then takes the exact pass before its store
+  uint32_t unfolded_a = 0;
 #pragma unroll
   for (int t = 0; t < kRPTiles; ++t) {
     const int64_t m = mw + 16 * t;
     const bool mok = m < g.M;
     const uint8_t* arow = A + (mok ? m : 0) * g.lda;
-    const uint32_t sa4 = mok ? load_scales4(SA + m * g.ldsa, 0, kblocks, dword_ok) : 0x7F7F7F7Fu;
+    sa4s[t] = mok ? load_scales4(SA + m * g.ldsa, 0, kblocks, dword_ok) : 0x7F7F7F7Fu;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       uint2 w = make_uint2(0, 0);
       if (mok && kb < kblocks) w = *(const uint2*)(arow + 32 * kb + 8 * lg);
-      af[t][kb] = decode8_bf16<AFMT>(w, scale_value((sa4 >> (8 * kb)) & 0xFFu));
+      const uint32_t sc = (sa4s[t] >> (8 * kb)) & 0xFFu;
+      unfolded_a |= unfolded_codes<AFMT>(sc, w);
+      af[t][kb] = fold_decode8<AFMT>(w, sc);
     }
   }
   __syncthreads();
@@ -388,6 +529,7 @@ __global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uin
     for (int t = 0; t < kRPTiles; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[t][j] = v4f32{0.f, 0.f, 0.f, 0.f};
+    uint32_t unfolded = unfolded_a;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       if (kb < kblocks) {
@@ -396,11 +538,32 @@ __global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uin
         for (int j = 0; j < 4; ++j) {
           const uint32_t row = (uint32_t)min(n0 + j * 16 + lr, (int64_t)kRPMaxN - 1);
           const uint2 w = *(const uint2*)(&Bs[swz(row, chunk) + off]);
-          const v8bf16 bf = decode8_bf16<BFMT>(w, scale_value((sBs[row] >> (8 * kb)) & 0xFFu));
+          const uint32_t sc = (sBs[row] >> (8 * kb)) & 0xFFu;
+          if (n0 + j * 16 + lr < nrows) unfolded |= unfolded_codes<BFMT>(sc, w);
+          const v8bf16 bf = fold_decode8<BFMT>(w, sc);
 #pragma unroll
           for (int t = 0; t < kRPTiles; ++t)
             acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[t][kb], acc[t][j], 0, 0, 0);
         }
+      }
+    }
+    // exact pass over the blocks outside the fold window (A codes read again from
+    // global memory, B codes and scales from LDS)
+    if (__builtin_amdgcn_ballot_w64(unfolded != 0u) != 0) {
+      for (int kb = 0; kb < kblocks; ++kb) {
+        const uint32_t chunk = 2 * kb + (lg >> 1), off = 8 * (lg & 1);
+        uint2 qa[4], qb[4];
+        uint32_t ca[4], cb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t m = mw + 16 * t;
+          qa[t] = m < g.M ? *(const uint2*)(A + m * g.lda + 32 * kb + 8 * lg) : make_uint2(0, 0);
+          ca[t] = (sa4s[t] >> (8 * kb)) & 0xFFu;
+          const uint32_t row = (uint32_t)min(n0 + t * 16 + lr, (int64_t)kRPMaxN - 1);
+          qb[t] = *(const uint2*)(&Bs[swz(row, chunk) + off]);
+          cb[t] = (sBs[row] >> (8 * kb)) & 0xFFu;
+        }
+        exact_block16<AFMT, BFMT>(qa, ca, qb, cb, acc);
       }
     }
 #pragma unroll
@@ -711,6 +874,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   // are spread evenly over the stage.
   v8i32 fa[2][4], fb[2][4];
   int sa[2][4], sb[2][4];
+
+  // FP32-accumulation mode over the whole E8M0 range. A block whose scale
+  // lies outside its fold window is folded inexactly (fold_decode8); it
+  // matters only if it holds a non-zero code, and then the wave replaces its
+  // terms in the exact pass after the main loop. Per K half, lanes of the
+  // lower half test the two scale bytes of the wave's A rows, lanes of the
+  // upper half those of its B rows (both halves hold the same rows); only
+  // when some scale is outside do the lanes look at their codes. All-zero
+  // blocks (scale code 0) therefore never start the exact pass.
+  bool needs_exact = false;
+  auto check_half = [&](int set) {
+    if constexpr (MODE == kModeBF16) {
+      const uint32_t lo = lg ? fold_lo<BFMT>() : fold_lo<AFMT>(), hi = lg ? fold_hi<BFMT>() : fold_hi<AFMT>();
+      const uint32_t s0 = (uint32_t)(lg ? sb[set][0] : sa[set][0]), s1 = (uint32_t)(lg ? sb[set][1] : sa[set][1]);
+      const uint32_t s2 = (uint32_t)(lg ? sb[set][2] : sa[set][2]), s3 = (uint32_t)(lg ? sb[set][3] : sa[set][3]);
+      // bytes 0-1 of each word are the scales of the half's two blocks
+      const uint32_t out = any_byte_outside(__builtin_amdgcn_perm(s1, s0, 0x05040100u), lo, hi) |
+                           any_byte_outside(__builtin_amdgcn_perm(s3, s2, 0x05040100u), lo, hi);
+      if (__builtin_amdgcn_ballot_w64(out != 0u) != 0) {
+        // branch-free (no short-circuit): divergent branches in the main
+        // loop make the compiler move the accumulators out of registers
+        uint32_t bad = 0;
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            const v8i32 x = fa[set][f], y = fb[set][f];
+            const uint32_t nza = ((uint32_t)(x[4 * blk] | x[4 * blk + 1] | x[4 * blk + 2] | x[4 * blk + 3])) & 0x7F7F7F7Fu;
+            const uint32_t nzb = ((uint32_t)(y[4 * blk] | y[4 * blk + 1] | y[4 * blk + 2] | y[4 * blk + 3])) & 0x7F7F7F7Fu;
+            bad |= (fold_excluded<AFMT>(((uint32_t)sa[set][f] >> (8 * blk)) & 0xFFu) ? nza : 0u) |
+                   (fold_excluded<BFMT>(((uint32_t)sb[set][f] >> (8 * blk)) & 0xFFu) ? nzb : 0u);
+          }
+        needs_exact |= bad != 0u;
+      }
+    }
+  };
+
   // One of the 4 MFMA groups of a K half. FP8 mode: group i is the 4
   // scaled MFMAs of A fragment i. FP32-accumulation mode: group t is K step
   // t of the half (8 of each lane's 32 codes, bytes 8t .. 8t+7, the same
@@ -750,15 +950,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
                                                                      sb[set][j], 0, sa[set][i]);
     } else {
       const int t = i;
+      if (t == 0) check_half(set);
       v8bf16 bb[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bb[j] = decode8_bf16<BFMT>(make_uint2((uint32_t)fb[set][j][2 * t], (uint32_t)fb[set][j][2 * t + 1]),
-                                   scale_value(((uint32_t)sb[set][j] >> (8 * (t >> 1))) & 0xFFu));
+        bb[j] = fold_decode8<BFMT>(make_uint2((uint32_t)fb[set][j][2 * t], (uint32_t)fb[set][j][2 * t + 1]),
+                                   ((uint32_t)sb[set][j] >> (8 * (t >> 1))) & 0xFFu);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const v8bf16 aa = decode8_bf16<AFMT>(make_uint2((uint32_t)fa[set][a][2 * t], (uint32_t)fa[set][a][2 * t + 1]),
-                                             scale_value(((uint32_t)sa[set][a] >> (8 * (t >> 1))) & 0xFFu));
+        const v8bf16 aa = fold_decode8<AFMT>(make_uint2((uint32_t)fa[set][a][2 * t], (uint32_t)fa[set][a][2 * t + 1]),
+                                             ((uint32_t)sa[set][a] >> (8 * (t >> 1))) & 0xFFu);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[a][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bb[j], aa, acc[a][j], 0, 0, 0);
       }
@@ -835,6 +1036,136 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
     }
   }
   wait_vmcnt<0>();  // no load may still be writing LDS when the group ends
+
+  // ---- FP32-accumulation mode, exact pass. The main loop folded every
+  // block, exactly only where the scale lies inside its window; a wave that
+  // met a block outside it holding a non-zero code replaces those terms
+  // here, reading the blocks' scales and codes again (from L2): the folded
+  // terms are taken back (two passes of the negated folded operands), and
+  // the exact ones added over the cells of ExactCells, where the A rows of
+  // class x and the B rows of class y are folded with scales shifted by -w
+  // and +w (every other row's codes zeroed), which keeps both exact, normal
+  // bf16. Every pass accumulates the block's two K steps straight into the
+  // output tiles, as the main loop does. Lane (lr, lg) holds k = 16 lg .. 16 lg + 15 of a block,
+  // as in the main loop, so the two steps take its dwords 0-1 and 2-3.
+  if constexpr (MODE == kModeBF16) {
+    if (__builtin_amdgcn_ballot_w64(needs_exact) != 0) {
+      constexpr ExactCells<AFMT, BFMT> cells{};
+      static_assert(cells.feasible(), "a cell of the exact pass has no common shift");
+      // row offsets from the tile's (wave-uniform) bases; they fit in 32
+      // bits, as the main loop's do
+      uint32_t ao[4], bo[4], sao[4], sbo[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const uint32_t ra = (uint32_t)min((int64_t)(wm * 128 + f * 32 + lr), a_last);
+        const uint32_t rb = (uint32_t)min((int64_t)(wn * 128 + f * 32 + lr), b_last);
+        ao[f] = ra * (uint32_t)g.lda + 16 * lg;
+        bo[f] = rb * (uint32_t)g.ldb + 16 * lg;
+        sao[f] = ra * (uint32_t)g.ldsa;
+        sbo[f] = rb * (uint32_t)g.ldsb;
+      }
+      const uint32_t kblocks = (uint32_t)(g.K / kBlock);
+      for (uint32_t b = 0; b < kblocks; ++b) {
+        uint32_t ca[4], cb[4];
+        bool any = false;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          ca[f] = sa_base[sao[f] + b];
+          cb[f] = sb_base[sbo[f] + b];
+          any |= fold_excluded<AFMT>(ca[f]) | fold_excluded<BFMT>(cb[f]);
+        }
+        if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
+        uint4 qa[4], qb[4];
+        uint32_t nz = 0;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          qa[f] = *(const uint4*)(a_base + ao[f] + 32 * b);
+          qb[f] = *(const uint4*)(b_base + bo[f] + 32 * b);
+          nz |= fold_excluded<AFMT>(ca[f]) ? (qa[f].x | qa[f].y | qa[f].z | qa[f].w) : 0u;
+          nz |= fold_excluded<BFMT>(cb[f]) ? (qb[f].x | qb[f].y | qb[f].z | qb[f].w) : 0u;
+        }
+        if (__builtin_amdgcn_ballot_w64((nz & 0x7F7F7F7Fu) != 0u) == 0) continue;
+        // take back the main loop's (folded) terms of the pairs the fold
+        // does not cover: R1 = left-out A rows x every B row, R2 = the other
+        // A rows x left-out B rows
+        bool exa[4], exb[4];
+        v8bf16 b0[4], b1[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          exa[f] = fold_excluded<AFMT>(ca[f]);
+          exb[f] = fold_excluded<BFMT>(cb[f]);
+          b0[f] = fold_decode8<BFMT>(make_uint2(qb[f].x, qb[f].y), cb[f]);
+          b1[f] = fold_decode8<BFMT>(make_uint2(qb[f].z, qb[f].w), cb[f]);
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          if (__builtin_amdgcn_ballot_w64(exa[f]) == 0) continue;
+          const v8bf16 a0 = neg_bf16x8(fold_decode8_or_zero<AFMT>(make_uint2(qa[f].x, qa[f].y), ca[f], exa[f]));
+          const v8bf16 a1 = neg_bf16x8(fold_decode8_or_zero<AFMT>(make_uint2(qa[f].z, qa[f].w), ca[f], exa[f]));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[f][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0[j], a0, acc[f][j], 0, 0, 0);
+            acc[f][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[j], a1, acc[f][j], 0, 0, 0);
+          }
+        }
+        if (__builtin_amdgcn_ballot_w64(exb[0] || exb[1] || exb[2] || exb[3]) != 0) {
+          bool bon[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bon[j] = __builtin_amdgcn_ballot_w64(exb[j]) != 0;
+            b0[j] = fold_decode8_or_zero<BFMT>(make_uint2(qb[j].x, qb[j].y), cb[j], exb[j]);
+            b1[j] = fold_decode8_or_zero<BFMT>(make_uint2(qb[j].z, qb[j].w), cb[j], exb[j]);
+          }
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const v8bf16 a0 = neg_bf16x8(fold_decode8_or_zero<AFMT>(make_uint2(qa[f].x, qa[f].y), ca[f], !exa[f]));
+            const v8bf16 a1 = neg_bf16x8(fold_decode8_or_zero<AFMT>(make_uint2(qa[f].z, qa[f].w), ca[f], !exa[f]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (bon[j]) {
+                acc[f][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0[j], a0, acc[f][j], 0, 0, 0);
+                acc[f][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[j], a1, acc[f][j], 0, 0, 0);
+              }
+          }
+        }
+        // and add their exact values, cell by cell
+        uint32_t xa[4], xb[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          xa[f] = exact_class<AFMT>(ca[f]);
+          xb[f] = exact_class<BFMT>(cb[f]);
+        }
+        for (int c = 0; c < cells.n; ++c) {
+          const int cx = cells.cell[c].x, cy = cells.cell[c].y, w = cells.cell[c].w;
+          bool bon[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool in = xb[j] == (uint32_t)cy && cb[j] != 0xFFu;
+            bon[j] = __builtin_amdgcn_ballot_w64(in) != 0;
+            // rows outside the cell: zero codes and a neutral scale (their
+            // shifted code could reach the NaN exponent)
+            const float fs = in ? __uint_as_float((uint32_t)((int)cb[j] + w) << 23) : 1.f;
+            b0[j] = decode8_bf16<BFMT>(in ? make_uint2(qb[j].x, qb[j].y) : make_uint2(0u, 0u), fs);
+            b1[j] = decode8_bf16<BFMT>(in ? make_uint2(qb[j].z, qb[j].w) : make_uint2(0u, 0u), fs);
+          }
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const bool in = xa[f] == (uint32_t)cx && ca[f] != 0xFFu;
+            if (__builtin_amdgcn_ballot_w64(in) == 0) continue;
+            const float fs = in ? __uint_as_float((uint32_t)((int)ca[f] - w) << 23) : 1.f;
+            const v8bf16 a0 = decode8_bf16<AFMT>(in ? make_uint2(qa[f].x, qa[f].y) : make_uint2(0u, 0u), fs);
+            const v8bf16 a1 = decode8_bf16<AFMT>(in ? make_uint2(qa[f].z, qa[f].w) : make_uint2(0u, 0u), fs);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (bon[j]) {
+                acc[f][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0[j], a0, acc[f][j], 0, 0, 0);
+                acc[f][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[j], a1, acc[f][j], 0, 0, 0);
+              }
+          }
+        }
+      }
+    }
+  }
 
   // ---- epilogue: lane owns y[m][n .. n+3] for 4 groups of n
   uint8_t* Y = (uint8_t*)g.y + (po * g.sy_o + pi * g.sy_i) * (BF16OUT ? 2 : 4);
@@ -1012,8 +1343,9 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   g.scales_dword = (sa4 && sb4) ? 1u : 0u;
   g.y_vec = (mx_host::aligned16(d->y) && (d->ldy * ysz) % 16 == 0 && (d->stride_y_outer * ysz) % 16 == 0 &&
              (d->stride_y_inner * ysz) % 16 == 0) ? 1u : 0u;
-  const bool fp8 = d->accum == MX_ACCUM_FP8 ||
-                   (d->accum == MX_ACCUM_AUTO && d->a_fmt == MX_E4M3 && d->b_fmt == MX_E4M3 && K >= 2048);
+  // MX_ACCUM_AUTO is the FP32-accumulation mode: the scaled FP8 instruction
+  // meets 1e-5 * sum|a b| only on data whose errors cancel (see mx_accum_t)
+  const bool fp8 = d->accum == MX_ACCUM_FP8;
 
   constexpr int BM = 128, BN = 128;
   g.tiles_m = (uint32_t)((M + BM - 1) / BM);
@@ -1095,8 +1427,7 @@ extern "C" mx_status_t mx_grouped_gemm(const mx_grouped_gemm_desc_t* d, hipStrea
   g.tiles_m = (uint32_t)tiles_m;
   const bool bf16out = d->y_dtype == MX_BF16;
   if (fp4) return launch_big<kModeFP4>(g, d->a_fmt, d->b_fmt, bf16out, 1, stream);
-  const bool fp8 = d->accum == MX_ACCUM_FP8 ||
-                   (d->accum == MX_ACCUM_AUTO && d->a_fmt == MX_E4M3 && d->b_fmt == MX_E4M3 && K >= 2048);
+  const bool fp8 = d->accum == MX_ACCUM_FP8;
   return fp8 ? launch_big<kModeFP8>(g, d->a_fmt, d->b_fmt, bf16out, 1, stream)
              : launch_big<kModeBF16>(g, d->a_fmt, d->b_fmt, bf16out, 1, stream);
 }

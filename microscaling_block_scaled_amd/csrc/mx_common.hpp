@@ -225,6 +225,125 @@ __device__ __forceinline__ v8bf16 decode8_bf16(uint2 w, float scale) {
   return v8bf16{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
 }
 
+// ---------------------------------------------------------------- exact scaling
+// The FP32-accumulation paths fold a block's E8M0 scale into its bf16
+// operands. q * 2^(s - 127) is an exact *normal* bf16 for every finite code q
+// exactly when s lies in [fold_lo, fold_hi]: E4M3 values run from 2^-9 to
+// 448 = 1.75 * 2^8, so 2^-9 * 2^(s - 127) >= 2^-126 needs s >= 10 and
+// 448 * 2^(s - 127) < 2^128 needs s <= 246; E5M2 values run from 2^-16 to
+// 1.75 * 2^15, giving [17, 239]. Blocks outside the window (and holding a
+// non-zero code) take an exact path instead: the codes alone, decoded
+// without a scale, go through the matrix instruction, and the block's
+// partial sum is scaled by 2^(sa + sb - 254) with ldexp, which is exact
+// until the f32 result itself under- or overflows.
+template <int FMT>
+constexpr uint32_t fold_lo() { return FMT == MX_E5M2 ? 17u : 10u; }
+template <int FMT>
+constexpr uint32_t fold_hi() { return FMT == MX_E5M2 ? 239u : 246u; }
+
+// A scale outside the fold window (the NaN code aside): its block's terms
+// are replaced by the exact pass. (Rows are left out of a pass by zeroing
+// their codes: the scaled conversions read only the exponent field of their
+// f32 scale operand, so a scale of 0.0 would act as 2^-127, not as 0.)
+template <int FMT>
+__device__ __forceinline__ bool fold_excluded(uint32_t s) {
+  return s != 0xFFu && s - fold_lo<FMT>() > fold_hi<FMT>() - fold_lo<FMT>();
+}
+
+// ---- the exact pass over blocks the fold leaves out.
+// Scale codes fall in 7 classes: 0 below the fold window, 1 its first codes
+// [lo, 33], 2-5 four near-equal parts of [34, hi], 6 above it (0xFF, the NaN
+// code, is folded and never reaches the pass). A term of a block pairs an A
+// row of class x with a B row of class y; the main loop's fold is exact for
+// the pairs with x and y in 1..5. The pass takes back the main loop's terms
+// of every other pair (two passes of the folded operands, negated) and adds
+// their exact values cell by cell: A rows of class x folded with
+// 2^(sa - w - 127), B rows of class y with 2^(sb + w - 127), every other
+// row's codes zeroed, so each pair lands in exactly one cell and its product
+// is unchanged. For every cell some shift w keeps both
+// folds inside their windows (checked at compile time below), except cells
+// whose terms cannot matter: all of them below 2^-160 (far under any f32
+// result they could change), or all of them beyond the f32 range.
+template <int FMT>
+constexpr int exact_class_start(int c) {  // first code of class c (0..6); 7 -> 255
+  return c == 0 ? 0 : c == 1 ? (int)fold_lo<FMT>() : c == 6 ? (int)fold_hi<FMT>() + 1 : c == 7 ? 255
+       : 34 + ((c - 2) * ((int)fold_hi<FMT>() + 1 - 34) + 2) / 4;
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t exact_class(uint32_t s) {
+  return (uint32_t)(s >= (uint32_t)exact_class_start<FMT>(1)) + (s >= (uint32_t)exact_class_start<FMT>(2)) +
+         (s >= (uint32_t)exact_class_start<FMT>(3)) + (s >= (uint32_t)exact_class_start<FMT>(4)) +
+         (s >= (uint32_t)exact_class_start<FMT>(5)) + (s >= (uint32_t)exact_class_start<FMT>(6));
+}
+// log2 bounds of the largest and smallest non-zero element magnitude
+template <int FMT>
+constexpr int elem_log2_max() { return FMT == MX_E5M2 ? 16 : 9; }
+template <int FMT>
+constexpr int elem_log2_min() { return FMT == MX_E5M2 ? -16 : -9; }
+
+struct ExactCell { int x, y, w; };
+template <int AF, int BF>
+struct ExactCells {
+  ExactCell cell[49];
+  int n;
+  constexpr ExactCells() : cell(), n(0) {
+    for (int x = 0; x < 7; ++x)
+      for (int y = 0; y < 7; ++y) {
+        if (x != 0 && x != 6 && y != 0 && y != 6) continue;  // folded by the main loop
+        const int a1 = exact_class_start<AF>(x), a2 = exact_class_start<AF>(x + 1) - 1;
+        const int b1 = exact_class_start<BF>(y), b2 = exact_class_start<BF>(y + 1) - 1;
+        // every term of the cell: |sum of 32 products| * 2^(sa + sb - 254)
+        if (5 + elem_log2_max<AF>() + elem_log2_max<BF>() + a2 + b2 - 254 < -160) continue;
+        if (elem_log2_min<AF>() + elem_log2_min<BF>() + a1 + b1 - 254 > 128) continue;
+        const int wlo = max_i(a2 - (int)fold_hi<AF>(), (int)fold_lo<BF>() - b1);
+        const int whi = min_i(a1 - (int)fold_lo<AF>(), (int)fold_hi<BF>() - b2);
+        cell[n++] = ExactCell{x, y, wlo <= whi ? (wlo + whi) / 2 : -1000};
+      }
+  }
+  static constexpr int max_i(int a, int b) { return a > b ? a : b; }
+  static constexpr int min_i(int a, int b) { return a < b ? a : b; }
+  constexpr bool feasible() const {
+    for (int i = 0; i < n; ++i)
+      if (cell[i].w == -1000) return false;
+    return true;
+  }
+};
+
+// The scale the main loops fold a block with: 2^(s - 127), NaN for 0xFF, and
+// above the window the window's top (so the fold stays finite). Inside the
+// window the fold is exact; outside it the block is folded inexactly but
+// never enlarged, and the exact pass replaces its terms (exact ones added,
+// these subtracted).
+template <int FMT>
+__device__ __forceinline__ float fold_scale(uint32_t s) {
+  return s == 0xFFu ? __uint_as_float(0x7FC00000u) : scale_value(min(s, fold_hi<FMT>()));
+}
+// Eight codes of one block decoded with fold_scale.
+template <int FMT>
+__device__ __forceinline__ v8bf16 fold_decode8(uint2 w, uint32_t s) {
+  return decode8_bf16<FMT>(w, fold_scale<FMT>(s));
+}
+
+// Nonzero when some byte of w is below lo (lo <= 128): the borrow of a byte
+// that underflows sets its top bit where the byte's own top bit was clear.
+__device__ __forceinline__ uint32_t any_byte_below(uint32_t w, uint32_t lo) {
+  return (w - lo * 0x01010101u) & ~w & 0x80808080u;
+}
+// Nonzero when some byte of w lies outside [lo, hi] (lo <= 128, hi >= 127).
+__device__ __forceinline__ uint32_t any_byte_outside(uint32_t w, uint32_t lo, uint32_t hi) {
+  return any_byte_below(w, lo) | any_byte_below(~w, 255u - hi);
+}
+// Some of the element codes in the given dwords encode a non-zero value
+// (0x00 and 0x80 are the two zeros of E4M3 and E5M2).
+__device__ __forceinline__ bool codes_nonzero(uint32_t a, uint32_t b) { return ((a | b) & 0x7F7F7F7Fu) != 0u; }
+
+// One block's exact contribution: the unscaled partial sum times
+// 2^(sa + sb - 254); a NaN scale (0xFF) on either side makes it NaN.
+__device__ __forceinline__ float scaled_partial(float part, uint32_t sa, uint32_t sb) {
+  return (sa == 0xFFu || sb == 0xFFu) ? __uint_as_float(0x7FC00000u)
+                                       : __builtin_amdgcn_ldexpf(part, (int)(sa + sb) - 254);
+}
+
 // ---------------------------------------------------------------- LDS staging
 // 16-byte chunk permutation of a 128-byte LDS row: chunk ^ fperm(row) with
 // fperm = ((row >> 1) & 7) ^ ((row & 1) << 2). The 16 (or 8) lanes that a

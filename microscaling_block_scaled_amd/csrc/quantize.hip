@@ -598,10 +598,11 @@ mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int6
   if (row_tiles * col_tiles >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const dim3 grid((uint32_t)(row_tiles * col_tiles));
   const uint32_t col_major = col_tiles >= 64 ? 1u : 0u;
-  // Up to 4096 tiles the whole grid is resident at once (8 work-groups per
-  // CU), so every work-group reads, then writes, in step with the others.
-  // 20000 bytes of unused dynamic LDS leave 4 per CU and stagger them:
-  // 8192 x 4096 25.1 -> 24.2 us, 14336 x 4096 37.7 -> 37.3 us, 16384 x 4096
+  // With 8 work-groups per CU, grids of up to 2048 tiles are resident all at
+  // once, so every work-group reads, then writes, in step with the others.
+  // 20000 bytes of unused dynamic LDS leave 4 per CU and stagger them. The
+  // 4096-tile threshold is measured, not derived: 8192 x 4096 (2048 tiles)
+  // 25.1 -> 24.2 us, 14336 x 4096 (3584) 37.7 -> 37.3 us, 16384 x 4096 (4096)
   // 42.5 -> 42.3 us; on 16384 x 14336 (14336 tiles) it measured 1.2 % slower.
   const uint32_t lds_pad = row_tiles * col_tiles <= 4096 ? 20000u : 0u;
 #define MX_COLS_LAUNCH(T, F)                                                                                        \

@@ -76,6 +76,13 @@ def student_t_bf16(seed: int, shape, df: float = 3.0, scale: float = 1e-3, chunk
     return out
 
 
+def abs_normal_bf16(seed: int, shape, chunk_rows: int = 1024) -> np.ndarray:
+    """bf16 patterns of |N(0, 1)| float32 draws: same-sign data, for which the
+    rounding errors of a sum cannot cancel between terms."""
+    out = normal_bf16(seed, shape, chunk_rows=chunk_rows)
+    return out & np.uint16(0x7FFF)
+
+
 # ---------------------------------------------------------------- workloads
 def tiny():
     v64 = np.concatenate([np.full(32, 2.0 ** 10, np.float32), np.full(32, 2.0 ** -12, np.float32)])[None, :]

@@ -63,3 +63,24 @@ def assert_gemm_bound(y: np.ndarray, y_ref: np.ndarray, t_ref: np.ndarray, what:
                              "(err/T %g)" % (what, int((~ok).sum()), ok.size, i, y[i], y_ref[i], err[i], bound[i],
                                              err[i] / max(t_ref[i], 1e-300)))
     return float(np.max(err / np.maximum(t_ref, 1e-300)))
+
+
+def check_every_output(oracle, outputs, qa, sa, afmt, qb, sb, bfmt, what, chunk_rows=1024):
+    """Compare every element of each GPU product in `outputs` -- a list of
+    (name, device tensor [M, N] of f32 or bf16, rel) -- with the oracle's
+    y = A * B^T, computed row chunk by row chunk so that y_ref and sum|a b|
+    never have to be held for the whole output at once. Returns the worst
+    |err| / sum|a b| of each output."""
+    import torch
+    M = qa.shape[0]
+    worst = {name: 0.0 for name, _, _ in outputs}
+    for r0 in range(0, M, chunk_rows):
+        r1 = min(M, r0 + chunk_rows)
+        y_ref, t_ref = oracle.gemm(qa[r0:r1], sa[r0:r1], afmt, qb, sb, bfmt)
+        for name, y, rel in outputs:
+            bf = y.dtype == torch.bfloat16
+            yc = host(y[r0:r1])
+            yc = bf16_to_f64(yc) if bf else yc.astype(np.float64)
+            w = assert_gemm_bound(yc, y_ref, t_ref, "%s %s rows %d-%d" % (what, name, r0, r1), bf16_out=bf, rel=rel)
+            worst[name] = max(worst[name], w)
+    return worst

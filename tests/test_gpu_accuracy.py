@@ -1,0 +1,229 @@
+"""GPU accuracy of the block-scaled product on data that stresses it.
+
+Two things are checked here, each against the oracle on every output:
+
+1. The accumulation modes on data whose rounding errors cannot cancel:
+   same-sign operands (|N(0,1)|) and heavy tails (Student-t, nu = 3), at
+   K = 2048 and K = 8192 with E4M3 operands, where MX_ACCUM_AUTO may pick the
+   scaled FP8 instruction. AUTO and FP32 must meet the product bound
+   |y - y_ref| <= 1e-5 * sum_k |a_k b_k| on every output; forced FP8 is held
+   to its own grouped bound (2^-10).
+
+2. The full E8M0 range [MXFP8 SM120 software support, §0.1: a finite scale
+   is 2^k with -127 <= k <= 127]. Blocks with scale codes at both ends
+   (E4M3: 0, 1, 2, 3, 246, 247, 254; E5M2: 0..10 and 239..254) are mixed with
+   ordinary ones across the A and B operands (high scales of one operand
+   meet low ones of the other, so the products stay in f32 range), in all
+   three accumulation modes and on every kernel (row-panel, general,
+   large-tile). The bound
+   applies wherever the f32 result is representable at the bound's
+   resolution: 2^-100 <= sum |a b| <= 2^120 (smaller sums fall below the f32
+   grid, larger ones may overflow a partial sum).
+"""
+import numpy as np
+import pytest
+
+from gpu_util import FP8_GROUPED_REL, REL_T, assert_gemm_bound, bf16_to_f64, dev, host
+from microscaling_block_scaled_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E5M2 = 0, 1
+AUTO, FP8, FP32 = 0, 1, 2
+MODE_NAME = {AUTO: "AUTO", FP8: "FP8", FP32: "FP32"}
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import torch
+    import microscaling_block_scaled_amd as m
+    assert torch.cuda.is_available()
+    ok, reason = m.mx_query_support(0)
+    assert ok, reason
+    return m
+
+
+def _gemm(mx, qa, sa, qb, sb, afmt, bfmt, accum, f32=True):
+    import torch
+    y = mx.mx_gemm(dev(qa), dev(sa), dev(qb), dev(sb), afmt, bfmt,
+                   out_dtype=torch.float32 if f32 else torch.bfloat16, accum=accum)
+    y = host(y)
+    return y.astype(np.float64) if f32 else bf16_to_f64(y)
+
+
+# --------------------------------------------------------------------------- 1. data that does not cancel
+def _dist(name, seed, shape):
+    if name == "normal":
+        return inputs.normal_bf16(seed, shape)
+    if name == "same_sign":
+        return inputs.abs_normal_bf16(seed, shape)
+    if name == "student_t":
+        return inputs.student_t_bf16(seed, shape, scale=1.0)
+    raise ValueError(name)
+
+
+@pytest.mark.parametrize("K", [2048, 8192])
+@pytest.mark.parametrize("dist", ["normal", "same_sign", "student_t"])
+def test_accumulation_modes_on_hard_data(mx, oracle, dist, K):
+    M = N = 512
+    xa = _dist(dist, 7100 + K, (M, K))
+    xb = _dist(dist, 7200 + K, (N, K))
+    qa, sa = oracle.quantize_rows(xa, E4M3)
+    qb, sb = oracle.quantize_rows(xb, E4M3)
+    y_ref, t_ref = oracle.gemm(qa, sa, E4M3, qb, sb, E4M3)
+    worst = {}
+    for accum in (AUTO, FP32, FP8):
+        rel = FP8_GROUPED_REL if accum == FP8 else REL_T
+        what = "%s K=%d %s" % (dist, K, MODE_NAME[accum])
+        y = _gemm(mx, qa, sa, qb, sb, E4M3, E4M3, accum)
+        worst[MODE_NAME[accum]] = assert_gemm_bound(y, y_ref, t_ref, what + " f32", rel=rel)
+        yb = _gemm(mx, qa, sa, qb, sb, E4M3, E4M3, accum, f32=False)
+        assert_gemm_bound(yb, y_ref, t_ref, what + " bf16", bf16_out=True, rel=rel)
+    print("%s K=%d worst |err|/T: %s" % (dist, K, " ".join("%s %.3g" % kv for kv in worst.items())))
+
+
+# --------------------------------------------------------------------------- 2. the whole E8M0 range
+EXTREME = {E4M3: [0, 1, 2, 3, 246, 247, 254], E5M2: list(range(0, 11)) + list(range(239, 255))}
+
+
+def _finite_codes(g, fmt, shape, small=False):
+    """Random element codes of finite values (no NaN / Inf codes); `small`
+    keeps magnitudes <= 0.25 so that blocks under the largest scales stay in
+    f32 range."""
+    if fmt == E4M3:
+        pool = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+        lim = 0x28  # 0.25
+    else:
+        pool = np.array([c for c in range(256) if (c & 0x7F) < 0x7C], np.uint8)
+        lim = 0x34  # 0.25
+    if small:
+        pool = pool[(pool & 0x7F) <= lim]
+    return pool[g.integers(0, pool.size, shape)]
+
+
+LOW = {E4M3: [0, 1, 2, 3], E5M2: list(range(0, 11))}
+HIGH = {E4M3: [246, 247, 254], E5M2: list(range(239, 255))}
+
+
+def _extreme_scales(g, fmt, shape):
+    """Half the blocks at the ends of the E8M0 range, half ordinary."""
+    ext = np.array(EXTREME[fmt], np.uint8)
+    s = g.integers(100, 155, shape).astype(np.uint8)
+    pick = g.random(shape) < 0.5
+    s[pick] = ext[g.integers(0, ext.size, int(pick.sum()))]
+    return s
+
+
+def _pick(g, shape, choices):
+    """Per element, a code drawn from one of the (probability, code list) choices."""
+    out = np.empty(shape, np.uint8)
+    u = g.random(shape)
+    acc = 0.0
+    for p, codes in choices:
+        sel = (u >= acc) & (u < acc + p)
+        codes = np.asarray(codes, np.uint8)
+        out[sel] = codes[g.integers(0, codes.size, int(sel.sum()))]
+        acc += p
+    return out
+
+
+def _extreme_pair(g, afmt, bfmt, M, N, K):
+    """Codes and scales of A [M, K] and B [N, K] whose blocks use both ends of
+    the E8M0 range. Each 32-wide block column is one of three kinds: ordinary
+    (both operands ordinary or low), A-high (A's rows high, low or ordinary,
+    every B row low) or B-high (the mirror), so that high scales only ever
+    meet low ones and the products of the blocks stay inside f32 range. Within
+    one block column an operand's codes can span nearly the whole range."""
+    kb = K // 32
+    kind = g.choice(3, size=kb, p=[0.4, 0.3, 0.3])
+    norm = list(range(100, 155))
+    sa = np.empty((M, kb), np.uint8)
+    sb = np.empty((N, kb), np.uint8)
+    for b in range(kb):
+        if kind[b] == 0:
+            sa[:, b] = _pick(g, M, [(0.7, norm), (0.3, LOW[afmt])])
+            sb[:, b] = _pick(g, N, [(0.7, norm), (0.3, LOW[bfmt])])
+        elif kind[b] == 1:
+            sa[:, b] = _pick(g, M, [(0.4, HIGH[afmt]), (0.2, LOW[afmt]), (0.4, norm)])
+            sb[:, b] = _pick(g, N, [(1.0, LOW[bfmt])])
+        else:
+            sa[:, b] = _pick(g, M, [(1.0, LOW[afmt])])
+            sb[:, b] = _pick(g, N, [(0.4, HIGH[bfmt]), (0.2, LOW[bfmt]), (0.4, norm)])
+
+    def codes(fmt, s, rows):
+        q = _finite_codes(g, fmt, (rows, K))
+        # blocks under scales whose 2^(s - 127) * 448 (57344) would overflow f32 get small codes
+        big = np.repeat(s >= (240 if fmt == E4M3 else 232), 32, axis=1)
+        q[big] = _finite_codes(g, fmt, (int(big.sum()),), small=True)
+        return q
+
+    return codes(afmt, sa, M), sa, codes(bfmt, sb, N), sb
+
+
+def _representable(y_ref, t_ref):
+    return (t_ref >= 2.0 ** -100) & (t_ref <= 2.0 ** 120)
+
+
+# one shape per kernel: row-panel (K <= 128, N <= 512, FP32-accumulation
+# mode), the general kernel, the large-tile kernel (K % 512 == 0, M, N >= 256)
+EXTREME_SHAPES = [(300, 200, 96), (130, 129, 160), (256, 512, 512), (512, 256, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", EXTREME_SHAPES)
+@pytest.mark.parametrize("afmt,bfmt", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)])
+@pytest.mark.parametrize("accum", [AUTO, FP8, FP32])
+def test_extreme_scale_codes(mx, oracle, M, N, K, afmt, bfmt, accum):
+    g = inputs.rng(7300 + M + N + K + 10 * afmt + 20 * bfmt)
+    qa, sa, qb, sb = _extreme_pair(g, afmt, bfmt, M, N, K)
+    y_ref, t_ref = oracle.gemm(qa, sa, afmt, qb, sb, bfmt)
+    keep = _representable(y_ref, t_ref)
+    assert keep.mean() > 0.5, "too few representable outputs: %.2f" % keep.mean()
+    rel = FP8_GROUPED_REL if accum == FP8 else REL_T
+    what = "%s x %s %s %s" % (afmt, bfmt, MODE_NAME[accum], (M, N, K))
+    y = _gemm(mx, qa, sa, qb, sb, afmt, bfmt, accum)
+    worst = assert_gemm_bound(y[keep], y_ref[keep], t_ref[keep], what + " f32", rel=rel)
+    yb = _gemm(mx, qa, sa, qb, sb, afmt, bfmt, accum, f32=False)
+    ok_b = keep & (np.abs(y_ref) < 2.0 ** 126)
+    assert_gemm_bound(yb[ok_b], y_ref[ok_b], t_ref[ok_b], what + " bf16", bf16_out=True, rel=rel)
+    print("%s: worst |err|/T %.3g over %d representable outputs" % (what, worst, int(keep.sum())))
+
+
+# --------------------------------------------------------------------------- attention over the whole E8M0 range
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_extreme_scale_codes(mx, oracle, causal):
+    """V blocks with scale codes from both ends of the E8M0 range mixed with
+    ordinary ones, within every key and across keys; Q and K blocks at the
+    ends of the range in pairs whose products stay moderate (query block b at
+    code c_b, key block b near 242 - c_b), so the scores are ordinary numbers
+    computed from extreme operands. Checked on every output element whose
+    W = sum_j P_j |Vb_jd| is representable: 2^-100 <= W <= 2^100 (the
+    kernel forms the unnormalised sum of P_j * V_jd, with weights up to 2^8
+    over hundreds of keys, in f32 before dividing)."""
+    import math
+    from attn_util import assert_attention_bound, quantized_case, run_attention
+    S, ql, lens, page, hq, hkv = 2, 200, [333, 256], 128, 2, 1
+    c = quantized_case(oracle, 7400, S, ql, lens, page, hq, hkv, 128)
+    g = inputs.rng(7401)
+    vs = _extreme_scales(g, E4M3, c["vs"].shape)
+    vc = _finite_codes(g, E4M3, c["vc"].shape)
+    big = np.repeat(vs >= 240, 32, axis=-1)
+    vc[big] = _finite_codes(g, E4M3, (int(big.sum()),), small=True)
+    c["vs"], c["vc"] = vs, vc
+    qbase = np.array([0, 2, 240, 242], np.int64)[g.integers(0, 4, 4)]
+    jq = g.integers(0, 3, c["qs"].shape)
+    jk = g.integers(0, 3, c["ks"].shape)
+    c["qs"] = np.where(qbase < 128, qbase + jq, qbase - jq).astype(np.uint8)
+    kbase = 242 - qbase
+    c["ks"] = np.where(kbase < 128, kbase + jk, kbase - jk).astype(np.uint8)
+    sm = 1.0 / math.sqrt(128)
+    ref = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"], c["kv_lens"], ql,
+                                 sm, causal)
+    o_ref, w_ref = ref[0], ref[1]
+    keep = (w_ref >= 2.0 ** -100) & (w_ref <= 2.0 ** 100)
+    assert keep.mean() > 0.5, "too few representable outputs: %.2f" % keep.mean()
+    for out_f32 in (True, False):
+        o, lse = run_attention(mx, c, sm, causal, out_f32)
+        k = keep if out_f32 else keep & (np.abs(o_ref) < 2.0 ** 126)
+        worst = assert_attention_bound(o, lse, ref, sm, "extreme scales causal %d f32 %d" % (causal, out_f32),
+                                       out_f32=out_f32, keep=k)
+        print("extreme scales causal %d f32 %d: worst |err|/W = %.3g" % (causal, out_f32, worst))

@@ -21,16 +21,13 @@ import math
 import numpy as np
 import pytest
 
-from attn_util import quantized_case
+from attn_util import assert_attention_bound, quantized_case, run_attention
 from gpu_util import assert_bitexact, bf16_to_f64, dev, host
 from microscaling_block_scaled_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
 E4M3 = 0
-SCORE_REL = 2.0 ** -10
-P_REL = 2.0 ** -7
-BF16_OUT_REL = 2.0 ** -8
 
 
 @pytest.fixture(scope="module")
@@ -41,39 +38,6 @@ def mx():
     ok, reason = m.mx_query_support(0)
     assert ok, reason
     return m
-
-
-def _run(mx, c, sm, causal, out_f32):
-    import torch
-    T, Hq, D = c["qc"].shape
-    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
-    out = mx.mx_paged_attention(dev(c["qc"]), dev(c["qs"]), dev(c["kc"]), dev(c["ks"]), dev(c["vc"]), dev(c["vs"]),
-                                dev(c["table"]), dev(c["kv_lens"]), c["q_len"], sm_scale=sm, causal=causal,
-                                out_dtype=torch.float32 if out_f32 else torch.bfloat16, lse=lse)
-    torch.cuda.synchronize()
-    o = host(out)
-    o = o.astype(np.float64) if out_f32 else bf16_to_f64(o)
-    return o.reshape(T * Hq, D), host(lse).astype(np.float64).reshape(-1)
-
-
-def assert_attention_bound(o, lse, ref, sm, what, out_f32=True, score_rel=SCORE_REL):
-    o_ref, w_ref, lse_ref, tmax = ref
-    eps = sm * score_rel * tmax
-    rel = P_REL + np.expm1(2.0 * eps) + (0.0 if out_f32 else BF16_OUT_REL)
-    bound = rel[:, None] * w_ref
-    err = np.abs(o - o_ref)
-    bad = ~(err <= bound)
-    assert not bad.any(), "%s: %d elements out of bound; first at %s: got %r want %r bound %r" % (
-        what, bad.sum(), tuple(np.argwhere(bad)[0]), o[bad][0], o_ref[bad][0], bound[bad][0])
-    live = np.isfinite(lse_ref)
-    assert np.all(np.isneginf(lse[~live])), what + ": rows without keys must have lse = -inf"
-    assert np.all(o[~live] == 0.0), what + ": rows without keys must be zero"
-    lerr = np.abs(lse[live] - lse_ref[live])
-    lb = eps[live] + 1e-5 * (1 + np.abs(lse_ref[live]))
-    assert np.all(lerr <= lb), "%s: lse error %g > %g" % (what, lerr.max(), lb[np.argmax(lerr - lb)])
-    with np.errstate(invalid="ignore", divide="ignore"):
-        r = np.where(w_ref > 0, err / w_ref, 0.0)
-    return float(r.max(initial=0.0))
 
 
 CASES = [
@@ -95,7 +59,7 @@ def test_attention_matches_oracle(mx, oracle, case, causal):
     ref = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"], c["kv_lens"], ql,
                                  sm, causal)
     for out_f32 in (True, False):
-        o, lse = _run(mx, c, sm, causal, out_f32)
+        o, lse = run_attention(mx, c, sm, causal, out_f32)
         worst = assert_attention_bound(o, lse, ref, sm, "case %d causal %d f32 %d" % (case, causal, out_f32),
                                        out_f32=out_f32)
         print("case %d causal %d f32 %d: worst |err|/W = %.3g" % (case, causal, out_f32, worst))
@@ -122,7 +86,7 @@ def test_attention_exact_scores_and_one_hot(mx, oracle, causal):
     sm = 1.0 / math.sqrt(128)
     ref = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"], c["kv_lens"], ql,
                                  sm, causal)
-    o, lse = _run(mx, c, sm, causal, True)
+    o, lse = run_attention(mx, c, sm, causal, True)
     worst = assert_attention_bound(o, lse, ref, sm, "exact scores", score_rel=0.0)
     print("exact scores: worst |err|/W = %.3g" % worst)
     # one-hot: a softmax scale so large that every weight but the top key's
@@ -132,7 +96,7 @@ def test_attention_exact_scores_and_one_hot(mx, oracle, causal):
     big = 2000.0
     ref1 = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"], c["kv_lens"], ql,
                                   big, causal)
-    o1, l1 = _run(mx, c, big, causal, True)
+    o1, l1 = run_attention(mx, c, big, causal, True)
     # rows whose reference is a single key's value lie on the bf16 grid (an
     # f32 value whose low 16 bits are zero); rows mixing nearly tied keys do not
     f32 = ref1[0].astype(np.float32)
@@ -184,8 +148,8 @@ def test_attention_kv_workload(mx, oracle):
 
 def test_attention_repeat_runs_identical(mx, oracle):
     c = quantized_case(oracle, 8400, 2, 256, [256, 200], 128, 2, 2, 128)
-    a, la = _run(mx, c, 0.1, True, True)
-    b, lb = _run(mx, c, 0.1, True, True)
+    a, la = run_attention(mx, c, 0.1, True, True)
+    b, lb = run_attention(mx, c, 0.1, True, True)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
@@ -208,5 +172,5 @@ def test_attention_random_configurations(mx, oracle, i):
     sm = 1.0 / math.sqrt(128)
     ref = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"], c["kv_lens"], ql,
                                  sm, causal)
-    o, lse = _run(mx, c, sm, causal, True)
+    o, lse = run_attention(mx, c, sm, causal, True)
     assert_attention_bound(o, lse, ref, sm, "random case %d %s" % (i, (S, ql, lens, page, hq, hkv, causal)))
