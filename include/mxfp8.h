@@ -245,6 +245,10 @@ mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_t dt, int64
  *                    afterwards by an exact pass on the same kernel (slower;
  *                    all-zero blocks, e.g. code-0 padding, never start it).
  *                    E5M2 Inf codes under such a scale give NaN.
+ * In every mode a block under the NaN scale code 0xFF is NaN, so every output
+ * it enters is NaN, also when its element codes are all zero (the FP32 mode
+ * routes such blocks through the exact pass; the FP8 instruction does so by
+ * itself).
  *   MX_ACCUM_AUTO -- the same as MX_ACCUM_FP32 (E4M3 / E5M2 operands; for
  *                    MXFP4 see below).
  *   MX_ACCUM_FP8  -- the scaled FP8 matrix instructions on the codes
@@ -336,9 +340,15 @@ mx_status_t mx_gemm(const mx_gemm_desc_t* desc, hipStream_t stream);
  * weights taken relative to a running reference that lags the row maximum
  * by up to 2^8, before the division by the normaliser: an output whose
  * sum_j |V_jd| times 2^8 leaves the f32 range overflows even if O itself
- * would fit. A NaN score makes its row NaN; a NaN value in a V block
- * (scale code 0xFF) makes NaN every output column it is multiplied into,
- * including rows of the same query tile for which that key is masked.
+ * would fit. Weights below bf16's normal range after that move (in the
+ * worst case those under about 2^-116 of the row's normaliser) are flushed
+ * or rounded coarsely: an output may then differ by up to the sum of
+ * P_j |V_jd| over such keys beyond the relative bound, which matters only
+ * where a tiny weight meets a huge V value. A NaN score (e.g. under a Q or K
+ * scale code 0xFF) makes its row and its lse NaN; a V block under scale code
+ * 0xFF makes NaN its 32 output columns in every row that sees the key, and
+ * may do so in the rows of the same 128-query tile that the causal mask
+ * hides it from.
  *
  * Requirements (MX_ERR_SHAPE / MX_ERR_ALIGN otherwise): head_dim == 128;
  * num_kv_heads divides num_q_heads; page_size a multiple of 128;

@@ -79,7 +79,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // scales span more than 236 codes cannot be brought in whole: its largest
 // block is kept exact and its blocks more than 2^236 below that one are
 // clamped up to the window's floor.
-// The NaN code 0xFF is kept, so its blocks decode to NaN.
+// The NaN code 0xFF counts as outside the window; the shift ignores it and
+// the decode writes its block as NaN.
 constexpr int kVFoldLo = 10, kVFoldHi = 246;
 __device__ __forceinline__ int v_key_shift(uint32_t w) {
   int lo = 255, hi = -1;
@@ -96,7 +97,53 @@ __device__ __forceinline__ int v_key_shift(uint32_t w) {
   return max(hi - kVFoldHi, min(lo - kVFoldLo, 0));
 }
 __device__ __forceinline__ uint32_t v_fold_code(uint32_t s, int r) {
-  return s == 0xFFu ? s : (uint32_t)min(max((int)s - r, kVFoldLo), kVFoldHi);
+  return (uint32_t)min(max((int)s - r, kVFoldLo), kVFoldHi);
+}
+
+// Work item lid -> (query tile qt, query head h, sequence s). Without a mask
+// the query tiles of one (sequence, head) share its keys, so they are kept
+// on one XCD (the 8 XCDs take work-groups round-robin). Under a causal mask
+// the work of a tile grows with its index, so all last tiles go first, then
+// the tiles before them, in plain dispatch order, which spreads every class
+// of tile evenly over the XCDs.
+__device__ __forceinline__ void tile_of(const AttnArgs& g, uint32_t lid, uint32_t& qt, uint32_t& h, uint32_t& s) {
+  if (g.causal) {
+    const uint32_t nsh = g.total_wg / g.q_tiles;  // (sequence, head) pairs
+    qt = g.q_tiles - 1 - lid / nsh;
+    h = (lid % nsh) % g.hq;
+    s = (lid % nsh) / g.hq;
+  } else {
+    const uint32_t l2 = g.total_wg % 8 == 0 ? (lid % 8) * (g.total_wg / 8) + lid / 8 : lid;
+    qt = l2 % g.q_tiles;
+    h = (l2 / g.q_tiles) % g.hq;
+    s = l2 / (g.q_tiles * g.hq);
+  }
+}
+// The sequence's key count L (returned), the keys the tile needs (kmax) and
+// the fewest any of its rows may use (kmin). Key counts fit in 31 bits
+// (checked on the host).
+__device__ __forceinline__ int tile_keys(const AttnArgs& g, uint32_t qt, uint32_t s, int& kmax, int& kmin) {
+  const int max_keys = (int)(g.pages_per_seq * (int64_t)g.page_size);
+  int L = g.lens[s];
+  L = L < 0 ? 0 : (L > max_keys ? max_keys : L);
+  const int q_len = (int)g.q_len;
+  const int q0 = (int)qt * kQT;
+  const int q_last = min(q0 + kQT - 1, q_len - 1);
+  kmax = L;
+  kmin = L;
+  if (g.causal) {
+    kmax = min(L, L - q_len + q_last + 1);
+    kmin = min(L, L - q_len + q0 + 1);
+  }
+  return L;
+}
+// some scale byte of w (the four head-dim blocks of one key) lies outside
+// the fold window or is the NaN code
+__device__ __forceinline__ bool v_word_outside(uint32_t w) {
+  bool out = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out |= ((w >> (8 * i)) & 0xFFu) - (uint32_t)kVFoldLo > (uint32_t)(kVFoldHi - kVFoldLo);
+  return out;
 }
 
 // The running softmax reference moves up only when a block's maximum
@@ -113,47 +160,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t VT[kHD * kVTRow];
   __shared__ __attribute__((aligned(16))) float VShift[SHIFTED ? kKB : 4];  // 2^r of each key (v_key_shift)
 
-  // ---- work item: (sequence, head, query tile). Without a mask the query
-  // tiles of one (sequence, head) share its keys, so they are kept on one XCD
-  // (the 8 XCDs take work-groups round-robin). Under a causal mask the work
-  // of a tile grows with its index, so all last tiles go first, then the
-  // tiles before them, in plain dispatch order, which spreads every class of
-  // tile evenly over the XCDs.
-  uint32_t qt, h, s;
-  {
-    const uint32_t lid = blockIdx.x;
-    if (g.causal) {
-      const uint32_t nsh = g.total_wg / g.q_tiles;  // (sequence, head) pairs
-      qt = g.q_tiles - 1 - lid / nsh;
-      h = (lid % nsh) % g.hq;
-      s = (lid % nsh) / g.hq;
-    } else {
-      const uint32_t l2 = g.total_wg % 8 == 0 ? (lid % 8) * (g.total_wg / 8) + lid / 8 : lid;
-      qt = l2 % g.q_tiles;
-      h = (l2 / g.q_tiles) % g.hq;
-      s = l2 / (g.q_tiles * g.hq);
-    }
-  }
-  const uint32_t hk = h / g.group;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
 
-  // key counts fit in 31 bits (checked on the host)
-  const int max_keys = (int)(g.pages_per_seq * (int64_t)g.page_size);
-  int L = g.lens[s];
-  L = L < 0 ? 0 : (L > max_keys ? max_keys : L);
+  // One tile: the 128 queries qt of (sequence s, query head h).
+  auto tile = [&](uint32_t qt, uint32_t h, uint32_t s) {
+  const uint32_t hk = h / g.group;
+
+  int kmax, kmin;
+  const int L = tile_keys(g, qt, s, kmax, kmin);
   const int q_len = (int)g.q_len;
   const int q0 = (int)qt * kQT;
-  const int q_last = min(q0 + kQT - 1, q_len - 1);
-  // keys the tile needs, and the fewest any of its rows may use
-  int kmax = L, kmin = L;
-  if (g.causal) {
-    kmax = min(L, L - q_len + q_last + 1);
-    kmin = min(L, L - q_len + q0 + 1);
-  }
   const int nblk = kmax > 0 ? (kmax + kKB - 1) / kKB : 0;
 
   // ---- this lane's query row (rows past q_len load the last row and store nothing)
@@ -165,21 +184,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   const int64_t out_row = tok * g.ld_o + (int64_t)h * kHD;
   const int32_t* tab = g.table + (int64_t)s * g.pages_per_seq;
 
-  // Does some V scale of the keys this tile reads lie outside the fold
-  // window? Such tiles are left to the SHIFTED instantiation of this kernel
-  // (launched after this one on the same stream), which moves part of those
-  // keys' scales onto P (v_key_shift); the plain one stays free of it.
-  bool v_out = false;
-  for (int j = tid; j < kmax; j += kAttnThreads) {
-    const int64_t slot = (int64_t)tab[j / g.page_size] * g.page_size + j % g.page_size;
-    const uint32_t w = *(const uint32_t*)(g.vs + (slot * g.hkv + hk) * (kHD / 32));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t c = (w >> (8 * i)) & 0xFFu;
-      v_out |= c != 0xFFu && (c < (uint32_t)kVFoldLo || c > (uint32_t)kVFoldHi);
-    }
-  }
-  if ((__syncthreads_or(v_out) != 0) != SHIFTED) return;
 
   if (nblk == 0) {  // no allowed key anywhere in the tile
     if (q_ok) {
@@ -276,14 +280,22 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
     const uint4 sb = *(const uint4*)&VSs[buf][v_key + 8];
     const uint32_t sw[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
     float sc[8];
+    bool vnan[8];
     if (!shifted) {
+      // scales inside the window decode exactly; a tile with any other is
+      // computed again by the shifted kernel
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sc[e] = scale_value((sw[e] >> (8 * db)) & 0xFFu);
+      for (int e = 0; e < 8; ++e) {
+        sc[e] = __uint_as_float(((sw[e] >> (8 * db)) & 0xFFu) << 23);
+        vnan[e] = false;
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        const uint32_t code = (sw[e] >> (8 * db)) & 0xFFu;
         const int r = v_key_shift(sw[e]);
-        sc[e] = scale_value(v_fold_code((sw[e] >> (8 * db)) & 0xFFu, r));
+        sc[e] = __uint_as_float(v_fold_code(code, r) << 23);
+        vnan[e] = code == 0xFFu;
         // the threads of head-dim block 0 publish the key's 2^r
         if (db == 0) VShift[v_key + (e & 3) + 8 * (e >> 2)] = __uint_as_float((uint32_t)(127 + r) << 23);
       }
@@ -295,6 +307,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
       for (int e = 0; e < 8; ++e) {
         lo[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)vraw[x][e], sc[e], false));
         hi[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)vraw[x][e], sc[e], true));
+        if (vnan[e]) lo[e] = hi[e] = 0x7FC07FC0u;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -430,9 +443,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   }
 
   // ---- epilogue: O = acc / l; element e of tile t is head-dim column
-  // 32t + 8(e/4) + 4lg + e%4.
+  // 32t + 8(e/4) + 4lg + e%4. (A tile that needs the shift is written again
+  // by the shifted kernel, which runs after this one on the stream.)
   if (!q_ok) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float inv = !(l_run <= 0.f) ? 1.f / l_run : 0.f;  // a NaN normaliser stays NaN
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -449,7 +463,47 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
       }
     }
   if (lg == 0 && g.lse)
-    g.lse[tok * g.hq + h] = l_run > 0.f ? (m_ref + __log2f(l_run)) * 0.69314718055994531f : -__builtin_inff();
+    g.lse[tok * g.hq + h] = !(l_run <= 0.f) ? (m_ref + __log2f(l_run)) * 0.69314718055994531f : -__builtin_inff();
+  };
+
+  if constexpr (!SHIFTED) {
+    uint32_t qt, h, s;
+    tile_of(g, blockIdx.x, qt, h, s);
+    tile(qt, h, s);
+  } else {
+    // One work-group per (sequence s, kv head hk): the first key j0 of the
+    // sequence with a V scale outside the fold window (or the NaN code); the
+    // tiles of the query heads on hk that read key j0 (kmax > j0) are the
+    // ones the plain kernel decoded inexactly, and they are computed again
+    // here, overwriting its output.
+    __shared__ int j_first;
+    const uint32_t s = blockIdx.x / g.hkv, hk = blockIdx.x % g.hkv;
+    const int max_keys = (int)(g.pages_per_seq * (int64_t)g.page_size);
+    int L = g.lens[s];
+    L = L < 0 ? 0 : (L > max_keys ? max_keys : L);
+    if (tid == 0) j_first = L;
+    __syncthreads();
+    const int32_t* tab = g.table + (int64_t)s * g.pages_per_seq;
+    for (int j = tid; j < L; j += kAttnThreads) {
+      const int64_t slot = (int64_t)tab[j / g.page_size] * g.page_size + j % g.page_size;
+      if (v_word_outside(*(const uint32_t*)(g.vs + (slot * g.hkv + hk) * (kHD / 32)))) {
+        atomicMin(&j_first, j);
+        break;
+      }
+    }
+    __syncthreads();
+    const int j0 = j_first;
+    if (j0 >= L) return;
+    for (uint32_t h = hk * g.group; h < (hk + 1) * g.group; ++h)
+      for (uint32_t qt = 0; qt < g.q_tiles; ++qt) {
+        int kmax, kmin;
+        tile_keys(g, qt, s, kmax, kmin);
+        if (kmax > j0) {
+          tile(qt, h, s);
+          __syncthreads();  // the next tile reuses the LDS buffers
+        }
+      }
+  }
 }
 
 }  // namespace
@@ -479,7 +533,7 @@ extern "C" mx_status_t mx_paged_attention(const mx_attention_desc_t* d, hipStrea
   if ((uintptr_t)d->out % oal != 0 || d->ld_o % 4 != 0 || ((uintptr_t)d->lse & 3u) != 0) return MX_ERR_ALIGN;
   const int64_t q_tiles = (d->q_len + kQT - 1) / kQT;
   const int64_t total = q_tiles * hq * d->num_seqs;
-  if (total >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
+  if (total >= ((int64_t)1 << 31) || d->num_seqs * hkv >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const mx_status_t dev = mx_host::check_device();
   if (dev != MX_OK) return dev;
 
@@ -493,14 +547,16 @@ extern "C" mx_status_t mx_paged_attention(const mx_attention_desc_t* d, hipStrea
   g.hq = (uint32_t)hq; g.hkv = (uint32_t)hkv; g.group = (uint32_t)(hq / hkv);
   g.causal = d->causal ? 1u : 0u; g.q_tiles = (uint32_t)q_tiles; g.total_wg = (uint32_t)total;
   g.c2 = d->sm_scale * 1.4426950408889634f;
-  // the plain kernel takes every tile whose V scales lie inside the fold
-  // window, the shifted one the rest (each tile decides the same way in both)
+  // the plain kernel computes every tile, decoding V with its scales as
+  // they are; the shifted one then computes again, and overwrites, every
+  // tile that reads a key with a V scale outside the fold window
+  const uint32_t shift_wg = (uint32_t)(d->num_seqs * hkv);  // one per (sequence, kv head)
   if (d->out_dtype == MX_BF16) {
     hipLaunchKernelGGL((attn_kernel<true, false>), dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
-    hipLaunchKernelGGL((attn_kernel<true, true>), dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
+    hipLaunchKernelGGL((attn_kernel<true, true>), dim3(shift_wg), dim3(kAttnThreads), 0, stream, g);
   } else {
     hipLaunchKernelGGL((attn_kernel<false, false>), dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
-    hipLaunchKernelGGL((attn_kernel<false, true>), dim3((uint32_t)total), dim3(kAttnThreads), 0, stream, g);
+    hipLaunchKernelGGL((attn_kernel<false, true>), dim3(shift_wg), dim3(kAttnThreads), 0, stream, g);
   }
   return mx_host::launch_status();
 }

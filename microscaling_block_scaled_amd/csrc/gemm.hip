@@ -73,21 +73,14 @@ __device__ __forceinline__ uint32_t load_scales4(const uint8_t* p, int64_t kt, i
   return v;
 }
 
-// FP32-accumulation mode: the per-lane record of a block whose scale lies
-// outside the fold window while it holds a non-zero code; the terms of such
-// blocks are replaced afterwards by an exact pass (exact_block16 / the
-// large-tile kernel's).
+// FP32-accumulation mode: the per-lane record of a block that needs the
+// exact pass (exact_flag); the terms of such blocks are replaced after the
+// main loop (exact_block16 / the large-tile kernel's pass).
 template <int FMT>
 __device__ __forceinline__ uint32_t unfolded_codes(uint32_t scale, uint2 w) {
-  return fold_excluded<FMT>(scale) ? ((w.x | w.y) & 0x7F7F7F7Fu) : 0u;
+  return exact_flag<FMT>(scale, w.x | w.y);
 }
 
-// fold_decode8 when `take`, else zeros (zero codes and a neutral scale: a
-// NaN scale would still give NaN)
-template <int FMT>
-__device__ __forceinline__ v8bf16 fold_decode8_or_zero(uint2 w, uint32_t s, bool take) {
-  return decode8_bf16<FMT>(take ? w : make_uint2(0u, 0u), take ? fold_scale<FMT>(s) : 1.f);
-}
 // -v, elementwise (sign bits flipped; exact)
 __device__ __forceinline__ v8bf16 neg_bf16x8(v8bf16 v) {
   uint4 u = __builtin_bit_cast(uint4, v);
@@ -120,19 +113,19 @@ __device__ __forceinline__ void exact_block16(const uint2 (&qa)[4], const uint32
   for (int i = 0; i < 4; ++i) {
     exa[i] = fold_excluded<AF>(ca[i]);
     exb[i] = fold_excluded<BF>(cb[i]);
-    b_all[i] = fold_decode8<BF>(qb[i], cb[i]);
-    b_ex[i] = fold_decode8_or_zero<BF>(qb[i], cb[i], exb[i]);
+    b_all[i] = exact_operand<BF>(qb[i], cb[i], true);
+    b_ex[i] = exact_operand<BF>(qb[i], cb[i], exb[i]);
   }
   const bool any_exb = __builtin_amdgcn_ballot_w64(exb[0] || exb[1] || exb[2] || exb[3]) != 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (__builtin_amdgcn_ballot_w64(exa[i]) != 0) {
-      const v8bf16 a1 = neg_bf16x8(fold_decode8_or_zero<AF>(qa[i], ca[i], exa[i]));
+      const v8bf16 a1 = neg_bf16x8(exact_operand<AF>(qa[i], ca[i], exa[i]));
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_all[j], a1, acc[i][j], 0, 0, 0);
     }
     if (any_exb) {
-      const v8bf16 a2 = neg_bf16x8(fold_decode8_or_zero<AF>(qa[i], ca[i], !exa[i]));
+      const v8bf16 a2 = neg_bf16x8(exact_operand<AF>(qa[i], ca[i], !exa[i]));
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b_ex[j], a2, acc[i][j], 0, 0, 0);
     }
@@ -831,15 +824,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   // byte 0 (after the shift by 8 lg) is the scale of the half's first
   // instruction and byte 2 that of its second.)
   uint4 sa4[4], sb4[4];
+  // FP32-accumulation mode: does some scale of the wave's rows in this group
+  // of stages lie outside its fold window? (lanes of the lower half test the
+  // A rows, lanes of the upper half the B rows; both halves hold the same
+  // rows.) Wave-uniform; each fragment set carries the answer of the group
+  // its scales came from (set_out).
+  bool grp_out = false;
+  bool set_out[2] = {false, false};
   auto read_scales = [&](int sbuf) {
     const uint32_t sh = MODE != kModeBF16 ? 8 * lg : 0;
+    uint32_t out = 0;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       uint4 va = *(const uint4*)(a_sc + sbuf * kScaleBuf + f * 32 * kScaleRow);
       uint4 vb = *(const uint4*)(b_sc + sbuf * kScaleBuf + f * 32 * kScaleRow);
       sa4[f] = make_uint4(va.x >> sh, va.y >> sh, va.z >> sh, va.w >> sh);
       sb4[f] = make_uint4(vb.x >> sh, vb.y >> sh, vb.z >> sh, vb.w >> sh);
+      if constexpr (MODE == kModeBF16) {
+        const uint4 v = lg ? vb : va;
+        const uint32_t lo = lg ? fold_lo<BFMT>() : fold_lo<AFMT>(), hi = lg ? fold_hi<BFMT>() : fold_hi<AFMT>();
+        out |= any_byte_outside(v.x, lo, hi) | any_byte_outside(v.y, lo, hi) | any_byte_outside(v.z, lo, hi) |
+               any_byte_outside(v.w, lo, hi);
+      }
     }
+    if constexpr (MODE == kModeBF16) grp_out = __builtin_amdgcn_ballot_w64(out != 0u) != 0;
   };
   auto word_of = [&](const uint4& w4, int k) -> uint32_t {
     return k == 0 ? w4.x : k == 1 ? w4.y : k == 2 ? w4.z : w4.w;
@@ -878,21 +886,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   // FP32-accumulation mode over the whole E8M0 range. A block whose scale
   // lies outside its fold window is folded inexactly (fold_decode8); it
   // matters only if it holds a non-zero code, and then the wave replaces its
-  // terms in the exact pass after the main loop. Per K half, lanes of the
-  // lower half test the two scale bytes of the wave's A rows, lanes of the
-  // upper half those of its B rows (both halves hold the same rows); only
-  // when some scale is outside do the lanes look at their codes. All-zero
-  // blocks (scale code 0) therefore never start the exact pass.
+  // terms in the exact pass after the main loop. Only in K halves whose
+  // group of scales has such a block (set_out) do the lanes look at their
+  // scales and codes, so all-zero blocks (scale code 0) never start the
+  // exact pass.
   bool needs_exact = false;
   auto check_half = [&](int set) {
     if constexpr (MODE == kModeBF16) {
-      const uint32_t lo = lg ? fold_lo<BFMT>() : fold_lo<AFMT>(), hi = lg ? fold_hi<BFMT>() : fold_hi<AFMT>();
-      const uint32_t s0 = (uint32_t)(lg ? sb[set][0] : sa[set][0]), s1 = (uint32_t)(lg ? sb[set][1] : sa[set][1]);
-      const uint32_t s2 = (uint32_t)(lg ? sb[set][2] : sa[set][2]), s3 = (uint32_t)(lg ? sb[set][3] : sa[set][3]);
-      // bytes 0-1 of each word are the scales of the half's two blocks
-      const uint32_t out = any_byte_outside(__builtin_amdgcn_perm(s1, s0, 0x05040100u), lo, hi) |
-                           any_byte_outside(__builtin_amdgcn_perm(s3, s2, 0x05040100u), lo, hi);
-      if (__builtin_amdgcn_ballot_w64(out != 0u) != 0) {
+      if (set_out[set]) {
         // branch-free (no short-circuit): divergent branches in the main
         // loop make the compiler move the accumulators out of registers
         uint32_t bad = 0;
@@ -901,10 +902,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
           for (int blk = 0; blk < 2; ++blk) {
             const v8i32 x = fa[set][f], y = fb[set][f];
-            const uint32_t nza = ((uint32_t)(x[4 * blk] | x[4 * blk + 1] | x[4 * blk + 2] | x[4 * blk + 3])) & 0x7F7F7F7Fu;
-            const uint32_t nzb = ((uint32_t)(y[4 * blk] | y[4 * blk + 1] | y[4 * blk + 2] | y[4 * blk + 3])) & 0x7F7F7F7Fu;
-            bad |= (fold_excluded<AFMT>(((uint32_t)sa[set][f] >> (8 * blk)) & 0xFFu) ? nza : 0u) |
-                   (fold_excluded<BFMT>(((uint32_t)sb[set][f] >> (8 * blk)) & 0xFFu) ? nzb : 0u);
+            const uint32_t ora = (uint32_t)(x[4 * blk] | x[4 * blk + 1] | x[4 * blk + 2] | x[4 * blk + 3]);
+            const uint32_t orb = (uint32_t)(y[4 * blk] | y[4 * blk + 1] | y[4 * blk + 2] | y[4 * blk + 3]);
+            bad |= exact_flag<AFMT>(((uint32_t)sa[set][f] >> (8 * blk)) & 0xFFu, ora) |
+                   exact_flag<BFMT>(((uint32_t)sb[set][f] >> (8 * blk)) & 0xFFu, orb);
           }
         needs_exact |= bad != 0u;
       }
@@ -950,7 +951,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
                                                                      sb[set][j], 0, sa[set][i]);
     } else {
       const int t = i;
-      if (t == 0) check_half(set);
       v8bf16 bb[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -982,6 +982,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   wait_vmcnt<16 + kPF>();  // scales and stage 0 landed; stage 1 may still be in flight
   barrier();
   read_scales(0);
+  set_out[0] = grp_out;
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     read_frag(a_row, sa4, 0, 0, 0, f, fa[0][f], sa[0][f]);
@@ -993,7 +994,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
     for (int u = 0; u < 4; ++u) {
       const int64_t s = s0 + u;
       const int buf = u & 1, sbuf = (int)((s / kG) & 1), sub = (int)(s % kG);
-      // ---- first half: MFMAs on set 0; set 1 <- second half of stage s
+      // ---- first half: MFMAs on set 0; set 1 <- second half of stage s.
+      // (The exactness test of a set sits where a scheduling barrier already
+      // splits the loop body: a branch inside an MFMA group would keep its
+      // LDS reads from interleaving with its MFMAs.)
+      check_half(0);
+      __builtin_amdgcn_sched_barrier(0);
+      set_out[1] = grp_out;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         read_frag(a_row, sa4, buf, sub, 1, i, fa[1][i], sa[1][i]);
@@ -1010,10 +1017,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
       // the next scale group was published by this barrier
       if (u % kG == kG - 1) read_scales(sbuf ^ 1);
       __builtin_amdgcn_sched_barrier(0);
+      check_half(1);
+      __builtin_amdgcn_sched_barrier(0);
       // ---- second half: MFMAs on set 1; set 0 <- first half of stage s+1.
       // The loads of stage s+2 are issued a quarter per MFMA group: a wave
       // issues in order, and 18 loads in a row would hold back its MFMAs.
       const int nbuf = buf ^ 1, nsub = (sub + 1) % kG;
+      set_out[0] = grp_out;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         read_frag(a_row, sa4, nbuf, nsub, 0, i, fa[0][i], sa[0][i]);
@@ -1081,10 +1091,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
         for (int f = 0; f < 4; ++f) {
           qa[f] = *(const uint4*)(a_base + ao[f] + 32 * b);
           qb[f] = *(const uint4*)(b_base + bo[f] + 32 * b);
-          nz |= fold_excluded<AFMT>(ca[f]) ? (qa[f].x | qa[f].y | qa[f].z | qa[f].w) : 0u;
-          nz |= fold_excluded<BFMT>(cb[f]) ? (qb[f].x | qb[f].y | qb[f].z | qb[f].w) : 0u;
+          nz |= exact_flag<AFMT>(ca[f], qa[f].x | qa[f].y | qa[f].z | qa[f].w);
+          nz |= exact_flag<BFMT>(cb[f], qb[f].x | qb[f].y | qb[f].z | qb[f].w);
         }
-        if (__builtin_amdgcn_ballot_w64((nz & 0x7F7F7F7Fu) != 0u) == 0) continue;
+        if (__builtin_amdgcn_ballot_w64(nz != 0u) == 0) continue;
         // take back the main loop's (folded) terms of the pairs the fold
         // does not cover: R1 = left-out A rows x every B row, R2 = the other
         // A rows x left-out B rows
@@ -1094,14 +1104,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
         for (int f = 0; f < 4; ++f) {
           exa[f] = fold_excluded<AFMT>(ca[f]);
           exb[f] = fold_excluded<BFMT>(cb[f]);
-          b0[f] = fold_decode8<BFMT>(make_uint2(qb[f].x, qb[f].y), cb[f]);
-          b1[f] = fold_decode8<BFMT>(make_uint2(qb[f].z, qb[f].w), cb[f]);
+          b0[f] = exact_operand<BFMT>(make_uint2(qb[f].x, qb[f].y), cb[f], true);
+          b1[f] = exact_operand<BFMT>(make_uint2(qb[f].z, qb[f].w), cb[f], true);
         }
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           if (__builtin_amdgcn_ballot_w64(exa[f]) == 0) continue;
-          const v8bf16 a0 = neg_bf16x8(fold_decode8_or_zero<AFMT>(make_uint2(qa[f].x, qa[f].y), ca[f], exa[f]));
-          const v8bf16 a1 = neg_bf16x8(fold_decode8_or_zero<AFMT>(make_uint2(qa[f].z, qa[f].w), ca[f], exa[f]));
+          const v8bf16 a0 = neg_bf16x8(exact_operand<AFMT>(make_uint2(qa[f].x, qa[f].y), ca[f], exa[f]));
+          const v8bf16 a1 = neg_bf16x8(exact_operand<AFMT>(make_uint2(qa[f].z, qa[f].w), ca[f], exa[f]));
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             acc[f][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0[j], a0, acc[f][j], 0, 0, 0);
@@ -1113,13 +1123,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             bon[j] = __builtin_amdgcn_ballot_w64(exb[j]) != 0;
-            b0[j] = fold_decode8_or_zero<BFMT>(make_uint2(qb[j].x, qb[j].y), cb[j], exb[j]);
-            b1[j] = fold_decode8_or_zero<BFMT>(make_uint2(qb[j].z, qb[j].w), cb[j], exb[j]);
+            b0[j] = exact_operand<BFMT>(make_uint2(qb[j].x, qb[j].y), cb[j], exb[j]);
+            b1[j] = exact_operand<BFMT>(make_uint2(qb[j].z, qb[j].w), cb[j], exb[j]);
           }
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
-            const v8bf16 a0 = neg_bf16x8(fold_decode8_or_zero<AFMT>(make_uint2(qa[f].x, qa[f].y), ca[f], !exa[f]));
-            const v8bf16 a1 = neg_bf16x8(fold_decode8_or_zero<AFMT>(make_uint2(qa[f].z, qa[f].w), ca[f], !exa[f]));
+            const v8bf16 a0 = neg_bf16x8(exact_operand<AFMT>(make_uint2(qa[f].x, qa[f].y), ca[f], !exa[f]));
+            const v8bf16 a1 = neg_bf16x8(exact_operand<AFMT>(make_uint2(qa[f].z, qa[f].w), ca[f], !exa[f]));
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               if (bon[j]) {

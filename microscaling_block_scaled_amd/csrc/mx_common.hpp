@@ -231,29 +231,34 @@ __device__ __forceinline__ v8bf16 decode8_bf16(uint2 w, float scale) {
 // exactly when s lies in [fold_lo, fold_hi]: E4M3 values run from 2^-9 to
 // 448 = 1.75 * 2^8, so 2^-9 * 2^(s - 127) >= 2^-126 needs s >= 10 and
 // 448 * 2^(s - 127) < 2^128 needs s <= 246; E5M2 values run from 2^-16 to
-// 1.75 * 2^15, giving [17, 239]. Blocks outside the window (and holding a
-// non-zero code) take an exact path instead: the codes alone, decoded
-// without a scale, go through the matrix instruction, and the block's
-// partial sum is scaled by 2^(sa + sb - 254) with ldexp, which is exact
-// until the f32 result itself under- or overflows.
+// 1.75 * 2^15, giving [17, 239]. The main loops fold every block; the terms
+// of blocks outside the window are replaced afterwards by an exact pass
+// (below).
 template <int FMT>
 constexpr uint32_t fold_lo() { return FMT == MX_E5M2 ? 17u : 10u; }
 template <int FMT>
 constexpr uint32_t fold_hi() { return FMT == MX_E5M2 ? 239u : 246u; }
 
-// A scale outside the fold window (the NaN code aside): its block's terms
-// are replaced by the exact pass. (Rows are left out of a pass by zeroing
-// their codes: the scaled conversions read only the exponent field of their
-// f32 scale operand, so a scale of 0.0 would act as 2^-127, not as 0.)
+// A scale outside the fold window, the NaN code 0xFF included: its block's
+// terms are replaced by the exact pass. (Rows are left out of a pass by
+// zeroing their codes: the scaled conversions read only the exponent field
+// of their f32 scale operand, so a scale of 0.0 would act as 2^-127, not as 0.)
 template <int FMT>
 __device__ __forceinline__ bool fold_excluded(uint32_t s) {
-  return s != 0xFFu && s - fold_lo<FMT>() > fold_hi<FMT>() - fold_lo<FMT>();
+  return s - fold_lo<FMT>() > fold_hi<FMT>() - fold_lo<FMT>();
+}
+// Non-zero when a block must go through the exact pass: its scale lies
+// outside the window and it holds a non-zero code (codes_or: the OR of some
+// of its code dwords), or its scale is the NaN code, which makes every
+// output it enters NaN whatever its codes.
+template <int FMT>
+__device__ __forceinline__ uint32_t exact_flag(uint32_t s, uint32_t codes_or) {
+  return fold_excluded<FMT>(s) ? (s == 0xFFu ? 1u : codes_or & 0x7F7F7F7Fu) : 0u;
 }
 
 // ---- the exact pass over blocks the fold leaves out.
 // Scale codes fall in 7 classes: 0 below the fold window, 1 its first codes
-// [lo, 33], 2-5 four near-equal parts of [34, hi], 6 above it (0xFF, the NaN
-// code, is folded and never reaches the pass). A term of a block pairs an A
+// [lo, 33], 2-5 four near-equal parts of [34, hi], 6 above it. A term of a block pairs an A
 // row of class x with a B row of class y; the main loop's fold is exact for
 // the pairs with x and y in 1..5. The pass takes back the main loop's terms
 // of every other pair (two passes of the folded operands, negated) and adds
@@ -263,7 +268,9 @@ __device__ __forceinline__ bool fold_excluded(uint32_t s) {
 // is unchanged. For every cell some shift w keeps both
 // folds inside their windows (checked at compile time below), except cells
 // whose terms cannot matter: all of them below 2^-160 (far under any f32
-// result they could change), or all of them beyond the f32 range.
+// result they could change), or all of them beyond the f32 range. Rows
+// under the NaN code take no cell: the take-back passes give them NaN
+// operands, which make their outputs NaN.
 template <int FMT>
 constexpr int exact_class_start(int c) {  // first code of class c (0..6); 7 -> 255
   return c == 0 ? 0 : c == 1 ? (int)fold_lo<FMT>() : c == 6 ? (int)fold_hi<FMT>() + 1 : c == 7 ? 255
@@ -309,19 +316,29 @@ struct ExactCells {
   }
 };
 
-// The scale the main loops fold a block with: 2^(s - 127), NaN for 0xFF, and
-// above the window the window's top (so the fold stays finite). Inside the
-// window the fold is exact; outside it the block is folded inexactly but
-// never enlarged, and the exact pass replaces its terms (exact ones added,
-// these subtracted).
+// The scale operand the main loops fold a block with: 2^(min(s, hi) - 127)
+// as an f32 whose only non-zero field is the exponent (s = 0 gives 0.0,
+// which the scaled conversions take as 2^-127). Inside the window the fold
+// is exact; outside it (the NaN code included) the block is folded
+// inexactly but never enlarged past the window, and the exact pass replaces
+// its terms.
 template <int FMT>
 __device__ __forceinline__ float fold_scale(uint32_t s) {
-  return s == 0xFFu ? __uint_as_float(0x7FC00000u) : scale_value(min(s, fold_hi<FMT>()));
+  return __uint_as_float(min(s, fold_hi<FMT>()) << 23);
 }
 // Eight codes of one block decoded with fold_scale.
 template <int FMT>
 __device__ __forceinline__ v8bf16 fold_decode8(uint2 w, uint32_t s) {
   return decode8_bf16<FMT>(w, fold_scale<FMT>(s));
+}
+// An operand of the exact pass's take-back: the block as the main loop
+// folded it when `take`, else zeros (zero codes and a neutral scale); a
+// block under the NaN scale code gives NaN.
+template <int FMT>
+__device__ __forceinline__ v8bf16 exact_operand(uint2 w, uint32_t s, bool take) {
+  const v8bf16 v = decode8_bf16<FMT>(take ? w : make_uint2(0u, 0u), take ? fold_scale<FMT>(s) : 1.f);
+  const uint4 nan = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+  return take && s == 0xFFu ? __builtin_bit_cast(v8bf16, nan) : v;
 }
 
 // Nonzero when some byte of w is below lo (lo <= 128): the borrow of a byte
@@ -336,13 +353,6 @@ __device__ __forceinline__ uint32_t any_byte_outside(uint32_t w, uint32_t lo, ui
 // Some of the element codes in the given dwords encode a non-zero value
 // (0x00 and 0x80 are the two zeros of E4M3 and E5M2).
 __device__ __forceinline__ bool codes_nonzero(uint32_t a, uint32_t b) { return ((a | b) & 0x7F7F7F7Fu) != 0u; }
-
-// One block's exact contribution: the unscaled partial sum times
-// 2^(sa + sb - 254); a NaN scale (0xFF) on either side makes it NaN.
-__device__ __forceinline__ float scaled_partial(float part, uint32_t sa, uint32_t sb) {
-  return (sa == 0xFFu || sb == 0xFFu) ? __uint_as_float(0x7FC00000u)
-                                       : __builtin_amdgcn_ldexpf(part, (int)(sa + sb) - 254);
-}
 
 // ---------------------------------------------------------------- LDS staging
 // 16-byte chunk permutation of a 128-byte LDS row: chunk ^ fperm(row) with

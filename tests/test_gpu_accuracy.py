@@ -1,24 +1,27 @@
-"""GPU accuracy of the block-scaled product on data that stresses it.
-
-Two things are checked here, each against the oracle on every output:
+"""GPU accuracy of the block-scaled product and of paged attention on data
+that stresses them, checked against the oracle on every output.
 
 1. The accumulation modes on data whose rounding errors cannot cancel:
    same-sign operands (|N(0,1)|) and heavy tails (Student-t, nu = 3), at
-   K = 2048 and K = 8192 with E4M3 operands, where MX_ACCUM_AUTO may pick the
-   scaled FP8 instruction. AUTO and FP32 must meet the product bound
-   |y - y_ref| <= 1e-5 * sum_k |a_k b_k| on every output; forced FP8 is held
-   to its own grouped bound (2^-10).
+   K = 2048 and K = 8192 with E4M3 operands. AUTO and FP32 must meet the
+   product bound |y - y_ref| <= 1e-5 * sum_k |a_k b_k| on every output;
+   forced FP8 is held to its own grouped bound (2^-10).
 
 2. The full E8M0 range [MXFP8 SM120 software support, §0.1: a finite scale
    is 2^k with -127 <= k <= 127]. Blocks with scale codes at both ends
-   (E4M3: 0, 1, 2, 3, 246, 247, 254; E5M2: 0..10 and 239..254) are mixed with
+   (E4M3: 0..3 and 246, 247, 254; E5M2: 0..10 and 239..254) are mixed with
    ordinary ones across the A and B operands (high scales of one operand
    meet low ones of the other, so the products stay in f32 range), in all
    three accumulation modes and on every kernel (row-panel, general,
-   large-tile). The bound
-   applies wherever the f32 result is representable at the bound's
-   resolution: 2^-100 <= sum |a b| <= 2^120 (smaller sums fall below the f32
-   grid, larger ones may overflow a partial sum).
+   large-tile). The bound applies wherever the f32 result is representable
+   at the bound's resolution: 2^-100 <= sum |a b| <= 2^120 (smaller sums fall
+   below the f32 grid, larger ones may overflow a partial sum).
+
+3. The NaN scale code [same section: E8M0 has one NaN code besides the
+   finite scales]: a block under 0xFF is NaN, so every output it enters is
+   NaN, also when its element codes are all zero.
+
+4. Paged attention with Q, K and V scales from both ends of the range.
 """
 import numpy as np
 import pytest
@@ -83,7 +86,6 @@ def test_accumulation_modes_on_hard_data(mx, oracle, dist, K):
 
 
 # --------------------------------------------------------------------------- 2. the whole E8M0 range
-EXTREME = {E4M3: [0, 1, 2, 3, 246, 247, 254], E5M2: list(range(0, 11)) + list(range(239, 255))}
 
 
 def _finite_codes(g, fmt, shape, small=False):
@@ -105,13 +107,26 @@ LOW = {E4M3: [0, 1, 2, 3], E5M2: list(range(0, 11))}
 HIGH = {E4M3: [246, 247, 254], E5M2: list(range(239, 255))}
 
 
-def _extreme_scales(g, fmt, shape):
-    """Half the blocks at the ends of the E8M0 range, half ordinary."""
-    ext = np.array(EXTREME[fmt], np.uint8)
-    s = g.integers(100, 155, shape).astype(np.uint8)
-    pick = g.random(shape) < 0.5
-    s[pick] = ext[g.integers(0, ext.size, int(pick.sum()))]
-    return s
+def _attention_v(g, vs_shape):
+    """E4M3 V scales and codes for the attention case. Per key and 32-wide
+    block the scale is low (0..3, 9, 10), high (246..254) or ordinary
+    (100..154), so most keys hold blocks from both ends; the high blocks hold
+    zero codes except for one element in 64 with a tiny magnitude (2^-9 ..
+    2^-7), so that an output column meets about one nonzero high value and W
+    stays within the range of the kernel's unnormalised sum."""
+    u = g.random(vs_shape)
+    vs = g.integers(100, 155, vs_shape).astype(np.uint8)
+    low = u < 0.3
+    high = (u >= 0.3) & (u < 0.55)
+    vs[low] = np.array([0, 1, 2, 3, 9, 10], np.uint8)[g.integers(0, 6, int(low.sum()))]
+    vs[high] = g.integers(246, 255, int(high.sum()))
+    vc = _finite_codes(g, E4M3, vs_shape[:-1] + (vs_shape[-1] * 32,))
+    big = np.repeat(high, 32, axis=-1)
+    nz = big & (g.random(big.shape) < 1 / 64)
+    tiny = np.array([1, 2, 3, 4, 0x81, 0x82, 0x83, 0x84], np.uint8)  # +-2^-9 .. +-2^-7
+    vc[big] = 0
+    vc[nz] = tiny[g.integers(0, tiny.size, int(nz.sum()))]
+    return vs, vc
 
 
 def _pick(g, shape, choices):
@@ -188,7 +203,36 @@ def test_extreme_scale_codes(mx, oracle, M, N, K, afmt, bfmt, accum):
     print("%s: worst |err|/T %.3g over %d representable outputs" % (what, worst, int(keep.sum())))
 
 
-# --------------------------------------------------------------------------- attention over the whole E8M0 range
+# --------------------------------------------------------------------------- 3. the NaN scale code
+@pytest.mark.parametrize("M,N,K", EXTREME_SHAPES)
+@pytest.mark.parametrize("afmt", [E4M3, E5M2])
+@pytest.mark.parametrize("accum", [AUTO, FP8, FP32])
+def test_nan_scale_code(mx, oracle, M, N, K, afmt, accum):
+    g = inputs.rng(7500 + M + N + K + afmt)
+    qa, sa = oracle.quantize_rows(inputs.normal_bf16(7501 + K + afmt, (M, K)), afmt)
+    qb, sb = oracle.quantize_rows(inputs.normal_bf16(7502 + K, (N, K)), E4M3)
+    kb = K // 32
+    ra, ba = g.choice(M, 3, replace=False), g.integers(0, kb, 3)
+    rb, bb = g.choice(N, 3, replace=False), g.integers(0, kb, 3)
+    sa[ra, ba] = 0xFF
+    sb[rb, bb] = 0xFF
+    qa[ra[0], 32 * ba[0]:32 * ba[0] + 32] = 0  # NaN scale over zero codes
+    qb[rb[0], 32 * bb[0]:32 * bb[0] + 32] = 0
+    y_ref, t_ref = oracle.gemm(qa, sa, afmt, qb, sb, E4M3)
+    nan_ref = np.isnan(y_ref)
+    assert nan_ref.sum() == 3 * N + 3 * M - 9  # three whole rows and three whole columns
+    what = "NaN scale %s x E4M3 %s %s" % (afmt, MODE_NAME[accum], (M, N, K))
+    rel = FP8_GROUPED_REL if accum == FP8 else REL_T
+    for f32 in (True, False):
+        y = _gemm(mx, qa, sa, qb, sb, afmt, E4M3, accum, f32=f32)
+        bad = np.isnan(y) != nan_ref
+        assert not bad.any(), "%s f32 %d: NaN pattern differs at %d outputs, first %s (got %r)" % (
+            what, f32, bad.sum(), tuple(np.argwhere(bad)[0]), y[bad][0])
+        assert_gemm_bound(y[~nan_ref], y_ref[~nan_ref], t_ref[~nan_ref], what + (" f32" if f32 else " bf16"),
+                          bf16_out=not f32, rel=rel)
+
+
+# --------------------------------------------------------------------------- 4. attention over the whole E8M0 range
 @pytest.mark.parametrize("causal", [False, True])
 def test_attention_extreme_scale_codes(mx, oracle, causal):
     """V blocks with scale codes from both ends of the E8M0 range mixed with
@@ -196,19 +240,15 @@ def test_attention_extreme_scale_codes(mx, oracle, causal):
     ends of the range in pairs whose products stay moderate (query block b at
     code c_b, key block b near 242 - c_b), so the scores are ordinary numbers
     computed from extreme operands. Checked on every output element whose
-    W = sum_j P_j |Vb_jd| is representable: 2^-100 <= W <= 2^100 (the
-    kernel forms the unnormalised sum of P_j * V_jd, with weights up to 2^8
-    over hundreds of keys, in f32 before dividing)."""
+    W = sum_j P_j |Vb_jd| satisfies 2^-100 <= W <= 2^110: the kernel forms the
+    unnormalised sum of P_j * V_jd with weights up to 2^8, so with at most
+    333 keys that sum stays below 2^8 * 2^8.4 * 2^110 < 2^127."""
     import math
-    from attn_util import assert_attention_bound, quantized_case, run_attention
+    from attn_util import assert_attention_bound, quantized_case, run_attention, small_weight_mass
     S, ql, lens, page, hq, hkv = 2, 200, [333, 256], 128, 2, 1
     c = quantized_case(oracle, 7400, S, ql, lens, page, hq, hkv, 128)
     g = inputs.rng(7401)
-    vs = _extreme_scales(g, E4M3, c["vs"].shape)
-    vc = _finite_codes(g, E4M3, c["vc"].shape)
-    big = np.repeat(vs >= 240, 32, axis=-1)
-    vc[big] = _finite_codes(g, E4M3, (int(big.sum()),), small=True)
-    c["vs"], c["vc"] = vs, vc
+    c["vs"], c["vc"] = _attention_v(g, c["vs"].shape)
     qbase = np.array([0, 2, 240, 242], np.int64)[g.integers(0, 4, 4)]
     jq = g.integers(0, 3, c["qs"].shape)
     jk = g.integers(0, 3, c["ks"].shape)
@@ -219,11 +259,67 @@ def test_attention_extreme_scale_codes(mx, oracle, causal):
     ref = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"], c["kv_lens"], ql,
                                  sm, causal)
     o_ref, w_ref = ref[0], ref[1]
-    keep = (w_ref >= 2.0 ** -100) & (w_ref <= 2.0 ** 100)
-    assert keep.mean() > 0.5, "too few representable outputs: %.2f" % keep.mean()
+    keep = (w_ref >= 2.0 ** -100) & (w_ref <= 2.0 ** 110)
+    assert keep.mean() > 0.9, "too few representable outputs: %.2f" % keep.mean()
+    small = small_weight_mass(oracle, c, sm, causal)
     for out_f32 in (True, False):
         o, lse = run_attention(mx, c, sm, causal, out_f32)
         k = keep if out_f32 else keep & (np.abs(o_ref) < 2.0 ** 126)
         worst = assert_attention_bound(o, lse, ref, sm, "extreme scales causal %d f32 %d" % (causal, out_f32),
-                                       out_f32=out_f32, keep=k)
+                                       out_f32=out_f32, keep=k, abs_extra=small)
         print("extreme scales causal %d f32 %d: worst |err|/W = %.3g" % (causal, out_f32, worst))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_nan_scale_codes(mx, oracle, causal):
+    """Scale code 0xFF in Q, K and V. A NaN query block makes its row NaN; a
+    NaN key block makes NaN every row that sees the key; a NaN value block
+    makes NaN its 32 output columns in every row that sees the key, and may
+    also do so in the rows of the same 128-query tile that the causal mask
+    hides it from (its zero weight times NaN is NaN inside the matrix
+    instruction). Every other output keeps the attention bound."""
+    import math
+    from attn_util import assert_attention_bound, quantized_case, run_attention
+    S, ql, lens, page, hq, hkv, D = 2, 200, [333, 256], 128, 2, 1, 128
+    c = quantized_case(oracle, 7600, S, ql, lens, page, hq, hkv, D)
+
+    def slot(s, j):
+        return int(c["table"][s, j // page]) * page + j % page
+
+    vs = c["vs"].reshape(-1, hkv, D // 32)
+    ks = c["ks"].reshape(-1, hkv, D // 32)
+    vkey, vblk = (0, 300), 1    # seen by queries >= 167 of sequence 0 under the mask
+    vs[slot(*vkey), 0, vblk] = 0xFF
+    ks[slot(1, 100), 0, 2] = 0xFF
+    c["qs"][7, 1, 0] = 0xFF     # token 7 (sequence 0), head 1
+    sm = 1.0 / math.sqrt(D)
+    ref = oracle.paged_attention(c["qc"], c["qs"], c["kc"], c["ks"], c["vc"], c["vs"], c["table"], c["kv_lens"], ql,
+                                 sm, causal)
+    o_ref, w_ref, lse_ref, tmax = ref
+    nan_ref = np.isnan(o_ref)
+    # where the kernel may also give NaN: the value block's columns in every
+    # row of a query tile that reads the key
+    T = S * ql
+    may = nan_ref.copy()
+    s, j = vkey
+    L = int(c["kv_lens"][s])
+    for qt in range((ql + 127) // 128):
+        q_last = min(qt * 128 + 127, ql - 1)
+        kmax = min(L, L - ql + q_last + 1) if causal else L
+        if j < kmax:
+            for tok in range(s * ql + qt * 128, s * ql + q_last + 1):
+                for h in range(hq):
+                    may[tok * hq + h, 32 * vblk:32 * vblk + 32] = True
+    assert nan_ref[:, 32 * vblk:32 * vblk + 32].any() and np.isnan(lse_ref).sum() > 0
+    rows_ok = ~np.isnan(lse_ref)
+    for out_f32 in (True, False):
+        o, lse = run_attention(mx, c, sm, causal, out_f32)
+        what = "NaN scale codes causal %d f32 %d" % (causal, out_f32)
+        got = np.isnan(o)
+        assert not (nan_ref & ~got).any(), "%s: %d outputs should be NaN, first %s" % (
+            what, (nan_ref & ~got).sum(), tuple(np.argwhere(nan_ref & ~got)[0]))
+        assert not (got & ~may).any(), "%s: %d outputs NaN where they should not be, first %s" % (
+            what, (got & ~may).sum(), tuple(np.argwhere(got & ~may)[0]))
+        assert np.all(np.isnan(lse[~rows_ok])), what + ": rows with a NaN score must have lse = NaN"
+        sub = (o_ref[rows_ok], w_ref[rows_ok], lse_ref[rows_ok], tmax[rows_ok])
+        assert_attention_bound(o[rows_ok], lse[rows_ok], sub, sm, what, out_f32=out_f32, keep=~may[rows_ok])
