@@ -77,8 +77,9 @@ typedef int32_t mx_status_t;
  * emax_elem = 2; a NaN/Inf block gets scale 0xFF and codes 0, E2M1 having no
  * NaN). Its codes are packed two per byte, element 2i in the low nibble, so
  * a row of `cols` elements holds cols/2 bytes and pitches stay in bytes.
- * E2M1 is accepted by mx_quantize, mx_dequantize and mx_gemm (see there);
- * the other entry points return MX_ERR_FORMAT for it. */
+ * E2M1 is accepted by mx_quantize, mx_quantize_colwise, mx_quantize_ex
+ * (1-D blocks), mx_dequantize, mx_gemm and mx_grouped_gemm (see there); the
+ * other entry points return MX_ERR_FORMAT for it. */
 typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2 } mx_fmt_t;
 /* High-precision data types of inputs and outputs. */
 typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype_t;
@@ -97,13 +98,14 @@ mx_status_t mx_quantize(const void* x, mx_dtype_t xdt, int64_t rows, int64_t col
                         uint8_t* q, int64_t ldq, uint8_t* s, int64_t lds, hipStream_t stream);
 
 /*
- * mx_quantize_colwise -- columnwise (32 x 1) MXFP8 quantization, stored
+ * mx_quantize_colwise -- columnwise (32 x 1) MX quantization, stored
  * transposed. Blocks are directional, so the second representation the
  * backward pass needs is quantized again from the high-precision input; a
  * transpose of the rowwise codes is not equivalent [SM120 §1.2, §1.3; GLOSS].
  *
  *   x    [rows x cols] input (xdt), pitch ldx >= cols
  *   qt   [cols x rows] codes out (qt[c][r] is element (r, c)), pitch ldq >= rows
+ *        (E2M1: rows/2 bytes per row, element r in nibble r % 2 of byte r/2)
  *   st   [cols x rows/32] scales out (st[c][r/32]), pitch lds >= rows/32
  * rows % 32 == 0. The result equals mx_quantize applied to x^T, so it is
  * directly a K-contiguous operand of mx_gemm with K = rows.
@@ -126,7 +128,7 @@ mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int
  *   blocks  MX_BLOCKS_1D: 1 x 32 blocks for the rowwise output and 32 x 1
  *           blocks for the colwise output, as mx_quantize / _colwise. With
  *           both outputs asked for, x is read once (rows % 32 == 0 and
- *           cols % 32 == 0; E4M3 / E5M2).
+ *           cols % 32 == 0; E4M3 / E5M2; E2M1 takes one pass per output).
  *           MX_BLOCKS_2D: one scale per 32 x 32 block (the 2-D weight
  *           quantization of [SM120 §1.3]), written in the MXFP8 layout: s
  *           repeats a block's scale on its 32 rows, st on its 32 columns, and
@@ -137,7 +139,7 @@ mx_status_t mx_quantize_colwise(const void* x, mx_dtype_t xdt, int64_t rows, int
  *   qt, st  colwise output stored transposed [cols x rows] / [cols x rows/32]
  *           (pitches ldqt, ldst), or both NULL. At least one pair is given.
  * Shapes, alignment and E2M1 packing follow mx_quantize / mx_quantize_colwise
- * (E2M1: rowwise 1-D only).
+ * (E2M1: 1-D blocks only).
  */
 typedef enum { MX_SCALE_FLOOR = 0, MX_SCALE_CEIL = 1 } mx_scale_rule_t;
 typedef enum { MX_BLOCKS_1D = 0, MX_BLOCKS_2D = 1 } mx_blocks_t;
@@ -268,14 +270,22 @@ mx_status_t mx_kv_quant_write(const void* k, const void* v, mx_dtype_t dt, int64
  *                    same kind of limited-precision accumulation in FP8 tensor
  *                    cores.
  *
- * MXFP4 (a_fmt = b_fmt = MX_E2M1; codes packed two per byte, lda/ldb in bytes
- * >= K/2): the scaled matrix instruction on the E2M1 codes (accum AUTO or
- * FP8, both exact here: a product of two E2M1 values has at most 4
- * significant bits, so a group of 8 fits the instruction's accumulator; FP32
- * is rejected with MX_ERR_FORMAT), on the large-tile kernel only:
- * K % 1024 == 0, M >= 256, N >= 256, no page table, 16-byte aligned code and
- * scale rows (MX_ERR_SHAPE / MX_ERR_ALIGN otherwise). E2M1 mixed with an FP8
- * format returns MX_ERR_FORMAT.
+ * E2M1 operands [NVFP4 §5.5; SM120 §0.3: the block-scaled instruction kind
+ * names A's and B's element formats separately]: MXFP4 x MXFP4, or E2M1 against
+ * E4M3 / E5M2 on either side; codes packed two per byte, so the E2M1
+ * operand's pitch is in bytes >= K/2. These products run on the scaled
+ * matrix instruction (accum AUTO or FP8; FP32 returns MX_ERR_FORMAT), on
+ * every shape mx_gemm takes (K % 32 == 0, any M and N, paged B included):
+ * MXFP4 x MXFP4 on the large-tile kernel when it fits (K % 1024 == 0,
+ * M >= 256, N >= 256, no page table, 16-byte aligned scale rows), otherwise
+ * on the general kernel. MXFP4 x MXFP4 is exact up to the FP32 sum over
+ * groups: a product of two E2M1 values has at most 4 significant bits, so
+ * each group of 8 fits the instruction's accumulator. A mixed product
+ * (up to 6 significant bits per product, exponents spread by the FP8
+ * operand) has the grouped accumulation of MX_ACCUM_FP8 above. Measured
+ * worst |err| / sum|a b| of mixed products: N(0,1) data 1.3e-5 at K = 96,
+ * 1.8e-6 at K = 1024, 1.2e-6 at K = 2048; codes drawn uniformly from every
+ * finite value 2.5e-4.
  */
 typedef enum { MX_ACCUM_AUTO = 0, MX_ACCUM_FP8 = 1, MX_ACCUM_FP32 = 2 } mx_accum_t;
 

@@ -125,14 +125,16 @@ def mx_quantize(x, fmt=MX_E4M3, q=None, s=None, stream=None):
 
 @_on_device_of_first_tensor
 def mx_quantize_colwise(x, fmt=MX_E4M3, qt=None, st=None, stream=None):
-    """Colwise MXFP8 quantization of x [rows, cols] (blocks of 32 down each
-    column), stored transposed -> (codes [cols, rows], scales [cols, rows/32])."""
+    """Colwise MX quantization of x [rows, cols] (blocks of 32 down each
+    column), stored transposed -> (codes [cols, rows] (E2M1: [cols, rows/2],
+    two per byte), scales [cols, rows/32])."""
     torch = _torch()
     _rowmajor(x, "x")
     rows, cols = x.shape
-    qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if qt is None else qt
+    rb = rows // 2 if fmt == MX_E2M1 else rows
+    qt = torch.empty((cols, rb), dtype=torch.uint8, device=x.device) if qt is None else qt
     st = torch.empty((cols, rows // BLOCK), dtype=torch.uint8, device=x.device) if st is None else st
-    _buf(qt, "qt", (cols, rows), torch.uint8, x)
+    _buf(qt, "qt", (cols, rb), torch.uint8, x)
     _buf(st, "st", (cols, rows // BLOCK), torch.uint8, x)
     check("mx_quantize_colwise", lib().mx_quantize_colwise(_p(x), _dtype_code(x), rows, cols, _ld(x), fmt,
                                                            _p(qt), _ld(qt), _p(st), _ld(st),
@@ -162,9 +164,10 @@ def mx_quantize_ex(x, fmt=MX_E4M3, rule=MX_SCALE_FLOOR, blocks=MX_BLOCKS_1D, row
     else:
         q = s = None
     if colwise:
-        qt = torch.empty((cols, rows), **u8) if qt is None else qt
+        rb = rows // 2 if fmt == MX_E2M1 else rows
+        qt = torch.empty((cols, rb), **u8) if qt is None else qt
         st = torch.empty((cols, rows // BLOCK), **u8) if st is None else st
-        _buf(qt, "qt", (cols, rows), torch.uint8, x)
+        _buf(qt, "qt", (cols, rb), torch.uint8, x)
         _buf(st, "st", (cols, rows // BLOCK), torch.uint8, x)
         d.qt, d.ldqt, d.st, d.ldst = _p(qt).value, _ld(qt), _p(st).value, _ld(st)
     else:

@@ -37,6 +37,9 @@ constexpr int kModeFP8 = 0;
 constexpr int kModeBF16 = 1;
 constexpr int kModeFP4 = 2;  // both operands E2M1 (MXFP4), large-tile kernel only
 constexpr int kMfmaFP4 = 4;  // the f8f6f4 instructions' format code for E2M1
+// an element format's code for the f8f6f4 instructions (E4M3 0, E5M2 1, E2M1 4)
+template <int FMT>
+constexpr int mfma_fmt() { return FMT == MX_E2M1 ? kMfmaFP4 : FMT; }
 
 constexpr int kThreads = 256;
 constexpr int kBK = 128;  // K bytes per step = 4 MX blocks
@@ -232,17 +235,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
   uint4 ra[CA], rb[CB];
   uint32_t rsa = 0, rsb = 0;
+  // A step covers kBK = 128 elements (4 blocks). An FP8 operand row gives
+  // them as 8 chunks of 16 bytes; an E2M1 one (two codes per byte) as
+  // chunks 0-3, one block each, and leaves chunks 4-7 unused.
+  auto load_chunk = [&](const uint8_t* row, int64_t kt, uint32_t ch, bool half) -> uint4 {
+    const int64_t e0 = kt * kBK + ch * (half ? 32 : 16);  // first element of the chunk
+    const int64_t off = half ? kt * (kBK / 2) + ch * 16 : e0;
+    return (row && (!half || ch < 4) && e0 < g.K) ? *(const uint4*)(row + off) : make_uint4(0, 0, 0, 0);
+  };
   auto load_global = [&](int64_t kt) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int64_t k0 = kt * kBK + a_ch[i] * 16;
-      ra[i] = (a_row[i] && k0 < g.K) ? *(const uint4*)(a_row[i] + k0) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < CA; ++i) ra[i] = load_chunk(a_row[i], kt, a_ch[i], AFMT == MX_E2M1);
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int64_t k0 = kt * kBK + b_ch[i] * 16;
-      rb[i] = (b_row[i] && k0 < g.K) ? *(const uint4*)(b_row[i] + k0) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < CB; ++i) rb[i] = load_chunk(b_row[i], kt, b_ch[i], BFMT == MX_E2M1);
     rsa = sa_row ? load_scales4(sa_row, kt, kblocks, dword_ok) : 0x7F7F7F7Fu;
     rsb = sb_row ? load_scales4(sb_row, kt, kblocks, dword_ok) : 0x7F7F7F7Fu;
   };
@@ -278,26 +283,32 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     if (kt + 1 < ksteps) load_global(kt + 1);
 
     if constexpr (MODE == kModeFP8) {
+      // Lane (r, g) supplies the scale of block g of its row. FP8 operand:
+      // k = 16g .. 16g+15 and 64+16g .. +15 (chunks g and g+4); E2M1
+      // operand: block g whole (chunk g, four of the eight registers).
+      auto frag = [&](const uint8_t* base, uint32_t row, bool half) -> v8i32 {
+        const uint4 lo = *(const uint4*)(base + swz(row, lg));
+        if (half) return v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+        const uint4 hi = *(const uint4*)(base + swz(row, lg + 4));
+        return v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      };
       v8i32 bf[FN];
       int bsc[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const uint32_t row = wn * WN + j * 16 + lr;
-        const uint4 lo = *(const uint4*)(&Bs[buf][swz(row, lg)]);
-        const uint4 hi = *(const uint4*)(&Bs[buf][swz(row, lg + 4)]);
-        bf[j] = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        bf[j] = frag(&Bs[buf][0], row, BFMT == MX_E2M1);
         bsc[j] = (int)(sBs[buf][row] >> (8 * lg));
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const uint32_t row = wm * WM + i * 16 + lr;
-        const uint4 lo = *(const uint4*)(&As[buf][swz(row, lg)]);
-        const uint4 hi = *(const uint4*)(&As[buf][swz(row, lg + 4)]);
-        const v8i32 af = v8i32{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const v8i32 af = frag(&As[buf][0], row, AFMT == MX_E2M1);
         const int asc = (int)(sAs[buf][row] >> (8 * lg));
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], BFMT, AFMT, 0, bsc[j], 0, asc);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], mfma_fmt<BFMT>(),
+                                                                       mfma_fmt<AFMT>(), 0, bsc[j], 0, asc);
       }
     } else {
       // one 32-K block per MFMA: lane (r, g) takes k = 32*kb + 8g .. +7, i.e.
@@ -1282,6 +1293,17 @@ mx_status_t launch(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, in
   hipLaunchKernelGGL((gemm_kernel<BM, BN, AF, BF, OUT, PAGED, MODE>), grid, dim3(kThreads), 0, st, g)
 #define MX_GEMM_OUT(AF, BF) \
   do { if (bf16out) MX_GEMM_LAUNCH(AF, BF, true); else MX_GEMM_LAUNCH(AF, BF, false); } while (0)
+  if constexpr (MODE == kModeFP8) {
+    // E2M1 operands, alone or against an FP8 format: scaled instruction only
+    if (af == MX_E2M1 || bf == MX_E2M1) {
+      if (af == MX_E2M1 && bf == MX_E2M1) MX_GEMM_OUT(MX_E2M1, MX_E2M1);
+      else if (af == MX_E2M1 && bf == MX_E4M3) MX_GEMM_OUT(MX_E2M1, MX_E4M3);
+      else if (af == MX_E2M1) MX_GEMM_OUT(MX_E2M1, MX_E5M2);
+      else if (af == MX_E4M3) MX_GEMM_OUT(MX_E4M3, MX_E2M1);
+      else MX_GEMM_OUT(MX_E5M2, MX_E2M1);
+      return mx_host::launch_status();
+    }
+  }
   if (af == MX_E4M3 && bf == MX_E4M3) MX_GEMM_OUT(MX_E4M3, MX_E4M3);
   else if (af == MX_E5M2 && bf == MX_E4M3) MX_GEMM_OUT(MX_E5M2, MX_E4M3);
   else if (af == MX_E4M3 && bf == MX_E5M2) MX_GEMM_OUT(MX_E4M3, MX_E5M2);
@@ -1295,14 +1317,13 @@ mx_status_t launch(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, in
 
 extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   if (!d) return MX_ERR_NULL;
-  const bool fp4 = d->a_fmt == MX_E2M1 || d->b_fmt == MX_E2M1;
-  if (fp4) {
-    // MXFP4 x MXFP4 only, on the large-tile kernel
-    if (d->a_fmt != MX_E2M1 || d->b_fmt != MX_E2M1 || d->accum == MX_ACCUM_FP32) return MX_ERR_FORMAT;
-  } else {
-    if (d->a_fmt != MX_E4M3 && d->a_fmt != MX_E5M2) return MX_ERR_FORMAT;
-    if (d->b_fmt != MX_E4M3 && d->b_fmt != MX_E5M2) return MX_ERR_FORMAT;
-  }
+  auto known = [](mx_fmt_t f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; };
+  if (!known(d->a_fmt) || !known(d->b_fmt)) return MX_ERR_FORMAT;
+  // an E2M1 operand (MXFP4 x MXFP4, or against E4M3 / E5M2) runs on the
+  // scaled matrix instruction only
+  const bool e2m1 = d->a_fmt == MX_E2M1 || d->b_fmt == MX_E2M1;
+  const bool fp4 = d->a_fmt == MX_E2M1 && d->b_fmt == MX_E2M1;
+  if (e2m1 && d->accum == MX_ACCUM_FP32) return MX_ERR_FORMAT;
   if (d->y_dtype != MX_F32 && d->y_dtype != MX_BF16) return MX_ERR_FORMAT;
   const int64_t M = d->M, N = d->N, K = d->K;
   if (M < 0 || N < 0 || K < 0 || K % kBlock != 0) return MX_ERR_SHAPE;
@@ -1313,14 +1334,13 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   if (M == 0 || N == 0) return mx_host::check_device();
   if (!d->y) return MX_ERR_NULL;
   if (K > 0 && (!d->a || !d->b || !d->sa || !d->sb)) return MX_ERR_NULL;
-  const int64_t krow = fp4 ? K / 2 : K;  // code bytes per operand row
-  if (d->lda < krow || d->ldb < krow || d->ldsa < K / kBlock || d->ldsb < K / kBlock || d->ldy < N)
+  // code bytes per operand row
+  const int64_t arow = d->a_fmt == MX_E2M1 ? K / 2 : K, brow = d->b_fmt == MX_E2M1 ? K / 2 : K;
+  if (d->lda < arow || d->ldb < brow || d->ldsa < K / kBlock || d->ldsb < K / kBlock || d->ldy < N)
     return MX_ERR_SHAPE;
   if (paged && (d->b_page_rows <= 0 || d->b_pages_per_seq <= 0 || (N + d->b_page_rows - 1) / d->b_page_rows > d->b_pages_per_seq))
     return MX_ERR_SHAPE;
   if (d->accum != MX_ACCUM_AUTO && d->accum != MX_ACCUM_FP8 && d->accum != MX_ACCUM_FP32) return MX_ERR_FORMAT;
-  // MXFP4 runs on the large-tile kernel only: its shape limits
-  if (fp4 && (paged || K % 1024 != 0 || M < 256 || N < 256)) return MX_ERR_SHAPE;
   const int64_t ysz = d->y_dtype == MX_F32 ? 4 : 2;
   if (!mx_host::aligned16(d->a) || !mx_host::aligned16(d->b) || d->lda % 16 || d->ldb % 16 ||
       ((uintptr_t)d->y % ysz) != 0)
@@ -1355,7 +1375,7 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
              (d->stride_y_inner * ysz) % 16 == 0) ? 1u : 0u;
   // MX_ACCUM_AUTO is the FP32-accumulation mode: the scaled FP8 instruction
   // meets 1e-5 * sum|a b| only on data whose errors cancel (see mx_accum_t)
-  const bool fp8 = d->accum == MX_ACCUM_FP8;
+  const bool fp8 = d->accum == MX_ACCUM_FP8 || e2m1;
 
   constexpr int BM = 128, BN = 128;
   g.tiles_m = (uint32_t)((M + BM - 1) / BM);
@@ -1368,8 +1388,9 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
                       d->ldsb % 16 == 0 && d->stride_sa_outer % 16 == 0 && d->stride_sa_inner % 16 == 0 &&
                       d->stride_sb_outer % 16 == 0 && d->stride_sb_inner % 16 == 0 && M >= 256 && N >= 256 &&
                       (M * d->lda) < ((int64_t)1 << 32) && (N * d->ldb) < ((int64_t)1 << 32);
-  if (fp4 && !big_ok) return MX_ERR_SHAPE;  // MXFP4 runs on the large-tile kernel only
-  if (big_ok) {
+  // MXFP4 x MXFP4 on the large-tile kernel where it fits; a mixed E2M1
+  // product, or any other shape, on the general kernel
+  if (big_ok && (fp4 || !e2m1)) {
     GemmArgs gb = g;
     gb.tiles_m = (uint32_t)((M + kFBM - 1) / kFBM);
     gb.tiles_n = (uint32_t)((N + kFBN - 1) / kFBN);

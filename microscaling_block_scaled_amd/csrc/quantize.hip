@@ -361,8 +361,29 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
       }
     }
     // encode: column c gets two dwords = rows 8b .. 8b+3 and 8b+4 .. 8b+7
+    // (E2M1: one dword, the 8 codes two per byte; a NaN block gets 0s)
 #pragma unroll
     for (int ci = 0; ci < 8; ++ci) {
+      if constexpr (FMT == MX_E2M1) {
+        const float div = scale_divisor(codes[ci]);
+        uint32_t d;
+        if constexpr (W == 4) {
+          const int p = ci >> 1;
+          const uint32_t sel = (ci & 1) ? 0x07060302u : 0x05040100u;
+          d = encode8_fp4_bf16(make_uint4(__builtin_amdgcn_perm(v[1][p], v[0][p], sel),
+                                          __builtin_amdgcn_perm(v[3][p], v[2][p], sel),
+                                          __builtin_amdgcn_perm(v[5][p], v[4][p], sel),
+                                          __builtin_amdgcn_perm(v[7][p], v[6][p], sel)), div);
+        } else {
+          d = encode8_fp4_f32(make_uint4(v[0][ci], v[1][ci], v[2][ci], v[3][ci]),
+                              make_uint4(v[4][ci], v[5][ci], v[6][ci], v[7][ci]), div);
+        }
+        if (codes[ci] == 0xFFu) d = 0u;
+        const uint32_t c = 8 * k + ci;
+        *(uint32_t*)(tile + col_lds_offset(c, 16 * wave + 4 * b)) = d;
+        if (b == 0) stile[c * 4 + wave] = (uint8_t)codes[ci];
+        continue;
+      }
       if (B2D && !qt) break;
       const float div = scale_divisor(codes[ci]);
       uint32_t d[2];
@@ -388,15 +409,18 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
   }
   if (B2D && !qt) return;  // uniform over the grid: rowwise output only
   __syncthreads();
-  // codes: 128 columns x 128 bytes = 1024 chunks of 16 bytes
+  // codes: 128 columns x 128 bytes = 1024 chunks of 16 bytes (E2M1: 64
+  // bytes, 512 chunks of one 32-row block each)
+  constexpr uint32_t kChunks = FMT == MX_E2M1 ? kColTileRows / 32 : kColTileRows / 16;  // per column
+  constexpr uint32_t kRowsPerChunk = kColTileRows / kChunks;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
+  for (uint32_t it = 0; it < kColTileCols * kChunks / kThreads; ++it) {
     const uint32_t id = threadIdx.x + kThreads * it;
-    const uint32_t c = id >> 3, m = id & 7;
-    const int64_t r = r0 + 16 * m;
+    const uint32_t c = id / kChunks, m = id % kChunks;
+    const int64_t r = r0 + kRowsPerChunk * m;
     if (c0 + c < cols && r < rows) {
       uint4 val = *(const uint4*)(tile + col_lds_offset(c, 16 * m));
-      *(uint4*)(qt + (c0 + c) * ldq + r) = val;
+      *(uint4*)(qt + (c0 + c) * ldq + (FMT == MX_E2M1 ? r / 2 : r)) = val;
     }
   }
   // rowwise scales (B2D / ROWS): row r's 4 blocks are 4 consecutive bytes of s2 row r0 + r
@@ -583,13 +607,15 @@ mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int6
   if (rows == 0 || cols == 0) {  // empty: no buffer, pitch or alignment matters
     if (rows < 0 || cols < 0) return MX_ERR_SHAPE;
     if (xdt != MX_F32 && xdt != MX_BF16) return MX_ERR_FORMAT;
-    if (fmt != MX_E4M3 && fmt != MX_E5M2) return MX_ERR_FORMAT;
+    if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1) return MX_ERR_FORMAT;
     return mx_host::check_device();
   }
   if (!x || !qt || !st) return MX_ERR_NULL;
-  mx_status_t rc = check_common(x, xdt, fmt, rows, cols, ldx);
+  if (fmt != MX_E4M3 && fmt != MX_E5M2 && fmt != MX_E2M1) return MX_ERR_FORMAT;
+  const bool fp4 = fmt == MX_E2M1;
+  mx_status_t rc = check_common(x, xdt, fp4 ? MX_E4M3 : fmt, rows, cols, ldx);
   if (rc != MX_OK) return rc;
-  if (rows % kBlock != 0 || ldq < rows || lds < rows / kBlock) return MX_ERR_SHAPE;
+  if (rows % kBlock != 0 || ldq < (fp4 ? rows / 2 : rows) || lds < rows / kBlock) return MX_ERR_SHAPE;
   if (!mx_host::aligned16(qt) || ldq % 16 != 0) return MX_ERR_ALIGN;
   if ((rc = mx_host::check_device()) != MX_OK) return rc;
   if (rows == 0 || cols == 0) return MX_OK;
@@ -609,9 +635,13 @@ mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int6
   hipLaunchKernelGGL((quant_cols_kernel<T, F, false, false>), grid, dim3(kThreads), lds_pad, stream, (const T*)x, rows, cols, ldx, \
                      qt, ldq, st, lds, (uint32_t)col_tiles, col_major, round_up, nullptr, 0, nullptr, 0)
   if (xdt == MX_BF16) {
-    if (fmt == MX_E5M2) MX_COLS_LAUNCH(uint16_t, MX_E5M2); else MX_COLS_LAUNCH(uint16_t, MX_E4M3);
+    if (fmt == MX_E5M2) MX_COLS_LAUNCH(uint16_t, MX_E5M2);
+    else if (fmt == MX_E2M1) MX_COLS_LAUNCH(uint16_t, MX_E2M1);
+    else MX_COLS_LAUNCH(uint16_t, MX_E4M3);
   } else {
-    if (fmt == MX_E5M2) MX_COLS_LAUNCH(float, MX_E5M2); else MX_COLS_LAUNCH(float, MX_E4M3);
+    if (fmt == MX_E5M2) MX_COLS_LAUNCH(float, MX_E5M2);
+    else if (fmt == MX_E2M1) MX_COLS_LAUNCH(float, MX_E2M1);
+    else MX_COLS_LAUNCH(float, MX_E4M3);
   }
 #undef MX_COLS_LAUNCH
   return mx_host::launch_status();
@@ -675,11 +705,11 @@ extern "C" mx_status_t mx_quantize_ex(const mx_quantize_desc_t* d, hipStream_t s
   if ((rowout && (!d->q || !d->s)) || (colout && (!d->qt || !d->st))) return MX_ERR_NULL;
   const uint32_t round_up = d->rule == MX_SCALE_CEIL ? 1u : 0u;
   if (d->blocks == MX_BLOCKS_2D) return quantize_tile_host(d, round_up, false, stream);
-  if (colout && d->fmt == MX_E2M1) return MX_ERR_FORMAT;
   // both 1-D orientations: one pass over x (~134 MB instead of ~203 MB of
   // traffic for an 8192 x 4096 bf16 input); x needs rows % 32 == 0 as for
-  // the colwise output alone, and cols % 32 == 0 as for the rowwise one
-  if (rowout && colout) return quantize_tile_host(d, round_up, true, stream);
+  // the colwise output alone, and cols % 32 == 0 as for the rowwise one.
+  // (MXFP4 takes the two single-orientation passes.)
+  if (rowout && colout && d->fmt != MX_E2M1) return quantize_tile_host(d, round_up, true, stream);
   mx_status_t rc = MX_OK;
   if (rowout)
     rc = quantize_rows_host(d->x, d->xdt, d->rows, d->cols, d->ldx, d->fmt, d->q, d->ldq, d->s, d->lds, round_up, stream);

@@ -125,14 +125,17 @@ def test_mxfp4_argument_errors_without_gpu(libmx):
             setattr(d, k, v)
         return d
 
-    assert g(ctypes.byref(desc(b_fmt=0, ldb=2048)), None) == -4     # E2M1 x E4M3
-    assert g(ctypes.byref(desc(accum=2)), None) == -4               # FP32-accumulation mode has no FP4 path
-    assert g(ctypes.byref(desc(K=1536, lda=768, ldb=768, ldsa=48, ldsb=48)), None) == -2  # K % 1024
-    assert g(ctypes.byref(desc(M=128)), None) == -2
+    assert g(ctypes.byref(desc(accum=2)), None) == -4               # FP32-accumulation mode has no E2M1 path
+    assert g(ctypes.byref(desc(b_fmt=0, ldb=2048, accum=2)), None) == -4  # nor for E2M1 x E4M3
+    assert g(ctypes.byref(desc(a_fmt=3)), None) == -4               # no such element format
     assert g(ctypes.byref(desc(lda=512)), None) == -2               # pitch below K/2 bytes
+    assert g(ctypes.byref(desc(b_fmt=0, ldb=1024)), None) == -2     # an E4M3 B row holds K bytes
+    assert g(ctypes.byref(desc(K=2064, lda=1040, ldb=1040, ldsa=65, ldsb=65)), None) == -2  # K % 32
     q = libmx.mx_quantize_colwise
     q.restype, q.argtypes = _lib.SIGNATURES["mx_quantize_colwise"]
-    assert q(0x10000, 1, 64, 64, 64, 2, 0x20000, 64, 0x30000, 2, None) == -4  # colwise MXFP4 not offered
+    assert q(0x10000, 1, 64, 64, 64, 2, 0x20000, 16, 0x30000, 2, None) == -2  # pitch below rows/2 bytes
+    assert q(0x10000, 1, 64, 64, 64, 2, 0x20008, 32, 0x30000, 2, None) == -3  # codes 16-byte aligned
+    assert q(0x10000, 1, 64, 64, 64, 3, 0x20000, 32, 0x30000, 2, None) == -4  # no such element format
 
 
 def test_scale_variant_argument_errors_without_gpu(libmx):
@@ -158,7 +161,7 @@ def test_scale_variant_argument_errors_without_gpu(libmx):
     assert f(ctypes.byref(desc(rule=2)), None) == -4
     assert f(ctypes.byref(desc(blocks=3)), None) == -4
     assert f(ctypes.byref(desc(fmt=2)), None) == -4                           # 2-D MXFP4 not offered
-    assert f(ctypes.byref(desc(blocks=0, fmt=2, q=None, s=None)), None) == -4  # colwise MXFP4 not offered
+    assert f(ctypes.byref(desc(blocks=0, fmt=2, q=None, s=None, ldqt=16)), None) == -2  # colwise MXFP4: rows/2 bytes
     assert f(ctypes.byref(desc(rows=48, ldqt=48)), None) == -2                # rows % 32
     assert f(ctypes.byref(desc(qt=0x40008)), None) == -3                      # transposed codes 16-aligned
     assert f(ctypes.byref(desc(ldq=32)), None) == -2

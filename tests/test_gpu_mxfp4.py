@@ -1,19 +1,25 @@
 """GPU parity of the MXFP4 path (E2M1 codes, E8M0 scale per 32) against the oracle.
 
 Codes (two per byte, element 2i in the low nibble) and scales must match the
-oracle bit for bit; dequantized values too. The product y = A * B^T of two
-MXFP4 operands must satisfy |y_gpu - y_ref| <= 1e-5 * sum_k |a_k b_k| per
-element (f32 output; bf16 output adds its own rounding, 2^-8 of |y|).
+oracle bit for bit, rowwise and colwise (stored transposed); dequantized
+values too. The product y = A * B^T of two MXFP4 operands must satisfy
+|y_gpu - y_ref| <= 1e-5 * sum_k |a_k b_k| per element (f32 output; bf16
+output adds its own rounding, 2^-8 of |y|), on the large-tile kernel and on
+every other shape (general kernel). A product of E2M1 with E4M3 / E5M2 runs
+on the same scaled instruction with the grouped accumulation of the FP8 mode
+and is held to that mode's bound (2^-10 * sum |a b|); the worst ratio found
+is printed.
 """
 import numpy as np
 import pytest
 
-from gpu_util import assert_bitexact, assert_gemm_bound, bf16_to_f64, dev, host
+from gpu_util import FP8_GROUPED_REL, assert_bitexact, assert_gemm_bound, bf16_to_f64, dev, host
 from microscaling_block_scaled_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-E2M1 = 2
+E4M3, E5M2, E2M1 = 0, 1, 2
+AUTO, FP8, FP32 = 0, 1, 2
 
 
 @pytest.fixture(scope="module")
@@ -136,3 +142,172 @@ def test_gemm_mxfp4_8192_cubed_sampled(mx, oracle):
     got = host(y[dev(mi), dev(ni)]).astype(np.float64)
     worst = assert_gemm_bound(got, y_ref, t_ref, "mxfp4 8192^3")
     print("mxfp4 8192^3: worst |err|/T = %.3g" % worst)
+
+
+# --------------------------------------------------------------------------- colwise MXFP4
+@pytest.mark.parametrize("rows,cols,seed", [(32, 8, 1), (64, 96, 2), (4096, 296, 3), (160, 1032, 4)])
+@pytest.mark.parametrize("f32", [False, True])
+def test_quantize_colwise_mxfp4(mx, oracle, rows, cols, seed, f32):
+    """Blocks of 32 down each column, stored transposed [cols, rows/2]: the
+    codes and scales of the oracle's colwise quantization, bit for bit (NaN,
+    Inf and all-zero column blocks included; column counts off the 128-column
+    tile; x's pitch 16-byte aligned as the colwise call requires)."""
+    x = inputs.normal_bf16(350 + seed, (rows, cols))
+    x[::29, :] = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(x[::29, :]) * np.float32(2.0 ** 9))
+    x[3, 0] = 0x7FC0                 # NaN in column block (0, 0)
+    if cols > 5:
+        x[rows - 1, 5] = 0x7F80      # +Inf in the last block of column 5
+        x[:32, cols - 1] = 0         # an all-zero block
+    if f32:
+        x = inputs.bf16_bits_to_f32(x) * np.float32(1.0 + 2.0 ** -12)
+    qt, st = mx.mx_quantize_colwise(dev(x, bf16=not f32), E2M1)
+    qo, so = oracle.quantize_cols(x, E2M1)
+    assert host(qt).shape == (cols, rows // 2)
+    assert_bitexact(host(st), so, "E2M1 colwise scales")
+    assert_bitexact(host(qt), qo, "E2M1 colwise codes")
+
+
+def test_quantize_ex_both_orientations_mxfp4(mx, oracle):
+    """mx_quantize_ex with both 1-D outputs in E2M1 (one pass per output)."""
+    x = inputs.normal_bf16(360, (256, 160))
+    q, s, qt, st = mx.mx_quantize_ex(dev(x, bf16=True), E2M1, rowwise=True, colwise=True)
+    qo, so = oracle.quantize_rows(x, E2M1)
+    qto, sto = oracle.quantize_cols(x, E2M1)
+    assert_bitexact(host(q), qo, "rowwise codes")
+    assert_bitexact(host(s), so, "rowwise scales")
+    assert_bitexact(host(qt), qto, "colwise codes")
+    assert_bitexact(host(st), sto, "colwise scales")
+
+
+def test_gemm_colwise_mxfp4_operands(mx, oracle):
+    """A weight-gradient-shaped product of two colwise MXFP4 operands:
+    dW [N, M] = G^T X with G [K, N] and X [K, M], both quantized down their
+    columns (K-contiguous after the transpose)."""
+    import torch
+    K, N, M = 1024, 320, 192
+    gx = inputs.normal_bf16(361, (K, N))
+    xx = inputs.normal_bf16(362, (K, M))
+    qg, sg = mx.mx_quantize_colwise(dev(gx, bf16=True), E2M1)
+    qx, sx = mx.mx_quantize_colwise(dev(xx, bf16=True), E2M1)
+    qgo, sgo = oracle.quantize_cols(gx, E2M1)
+    qxo, sxo = oracle.quantize_cols(xx, E2M1)
+    assert_bitexact(host(qg), qgo, "G^T codes")
+    assert_bitexact(host(qx), qxo, "X^T codes")
+    y_ref, t_ref = oracle.gemm(qgo, sgo, E2M1, qxo, sxo, E2M1)
+    y = mx.mx_gemm(qg, sg, qx, sx, a_fmt=E2M1, b_fmt=E2M1, out_dtype=torch.float32)
+    worst = assert_gemm_bound(host(y).astype(np.float64), y_ref, t_ref, "colwise mxfp4 product")
+    print("colwise MXFP4 G^T X %dx%dx%d: worst |err|/T = %.3g" % (N, M, K, worst))
+
+
+# --------------------------------------------------------------------------- MXFP4 products of any shape
+GENERAL_SHAPES = [(1, 1, 32), (64, 64, 128), (100, 37, 96), (130, 129, 160), (300, 257, 1056), (200, 600, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", GENERAL_SHAPES)
+@pytest.mark.parametrize("accum", [AUTO, FP8])
+def test_gemm_mxfp4_any_shape(mx, oracle, M, N, K, accum):
+    """Shapes the large-tile kernel does not take (K % 1024 != 0, M or N
+    below 256): the general kernel, exact up to the f32 sum."""
+    import torch
+    a = inputs.normal_bf16(370 + M + K, (M, K))
+    b = inputs.normal_bf16(371 + N + K, (N, K))
+    qa, sa = oracle.quantize_rows(a, E2M1)
+    qb, sb = oracle.quantize_rows(b, E2M1)
+    y_ref, t_ref = oracle.gemm(qa, sa, E2M1, qb, sb, E2M1)
+    what = "mxfp4 %dx%dx%d accum %d" % (M, N, K, accum)
+    y = mx.mx_gemm(dev(qa), dev(sa), dev(qb), dev(sb), a_fmt=E2M1, b_fmt=E2M1, out_dtype=torch.float32, accum=accum)
+    worst = assert_gemm_bound(host(y).astype(np.float64), y_ref, t_ref, what + " f32")
+    yb = mx.mx_gemm(dev(qa), dev(sa), dev(qb), dev(sb), a_fmt=E2M1, b_fmt=E2M1, out_dtype=torch.bfloat16,
+                    accum=accum)
+    assert_gemm_bound(bf16_to_f64(host(yb)), y_ref, t_ref, what + " bf16", bf16_out=True)
+    print("%s: worst |err|/T = %.3g" % (what, worst))
+
+
+# --------------------------------------------------------------------------- E2M1 x E4M3 / E5M2
+MIXED = [(E2M1, E4M3), (E2M1, E5M2), (E4M3, E2M1), (E5M2, E2M1)]
+MIXED_SHAPES = [(64, 64, 128), (300, 200, 96), (256, 512, 1024), (513, 1000, 2048)]
+
+
+@pytest.mark.parametrize("afmt,bfmt", MIXED)
+@pytest.mark.parametrize("M,N,K", MIXED_SHAPES)
+def test_gemm_e2m1_times_fp8(mx, oracle, afmt, bfmt, M, N, K):
+    import torch
+    a = inputs.normal_bf16(380 + M + 3 * afmt, (M, K))
+    b = inputs.normal_bf16(381 + N + 3 * bfmt, (N, K))
+    qa, sa = mx.mx_quantize(dev(a, bf16=True), afmt)
+    qb, sb = mx.mx_quantize(dev(b, bf16=True), bfmt)
+    qa_o, sa_o = oracle.quantize_rows(a, afmt)
+    qb_o, sb_o = oracle.quantize_rows(b, bfmt)
+    assert_bitexact(host(qa), qa_o, "A codes")
+    assert_bitexact(host(qb), qb_o, "B codes")
+    y_ref, t_ref = oracle.gemm(qa_o, sa_o, afmt, qb_o, sb_o, bfmt)
+    worst = 0.0
+    for accum in (AUTO, FP8):
+        what = "%d x %d %dx%dx%d accum %d" % (afmt, bfmt, M, N, K, accum)
+        y = mx.mx_gemm(qa, sa, qb, sb, a_fmt=afmt, b_fmt=bfmt, out_dtype=torch.float32, accum=accum)
+        worst = max(worst, assert_gemm_bound(host(y).astype(np.float64), y_ref, t_ref, what + " f32",
+                                             rel=FP8_GROUPED_REL))
+        yb = mx.mx_gemm(qa, sa, qb, sb, a_fmt=afmt, b_fmt=bfmt, out_dtype=torch.bfloat16, accum=accum)
+        assert_gemm_bound(bf16_to_f64(host(yb)), y_ref, t_ref, what + " bf16", bf16_out=True, rel=FP8_GROUPED_REL)
+    with pytest.raises(mx.MXError):
+        mx.mx_gemm(qa, sa, qb, sb, a_fmt=afmt, b_fmt=bfmt, out_dtype=torch.float32, accum=FP32)
+    print("E2M1 mixed %d x %d %dx%dx%d: worst |err|/T = %.3g" % (afmt, bfmt, M, N, K, worst))
+
+
+@pytest.mark.parametrize("afmt,bfmt", MIXED)
+def test_gemm_e2m1_times_fp8_random_codes(mx, oracle, afmt, bfmt):
+    """Codes drawn uniformly from every finite value of both formats and
+    scales from a wide range."""
+    import torch
+    g = inputs.rng(390 + afmt + 4 * bfmt)
+    M, N, K = 192, 320, 512
+
+    def codes(fmt, rows):
+        if fmt == E2M1:
+            return g.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+        c = g.integers(0, 256, (rows, K), dtype=np.uint8)
+        bad = (c & 0x7F) == 0x7F if fmt == E4M3 else (c & 0x7F) >= 0x7C  # NaN (and E5M2 Inf) codes
+        c[bad] ^= 0x08
+        return c
+
+    qa, qb = codes(afmt, M), codes(bfmt, N)
+    sa = g.integers(100, 150, (M, K // 32), dtype=np.uint8)
+    sb = g.integers(100, 150, (N, K // 32), dtype=np.uint8)
+    y_ref, t_ref = oracle.gemm(qa, sa, afmt, qb, sb, bfmt)
+    y = mx.mx_gemm(dev(qa), dev(sa), dev(qb), dev(sb), a_fmt=afmt, b_fmt=bfmt, out_dtype=torch.float32)
+    worst = assert_gemm_bound(host(y).astype(np.float64), y_ref, t_ref, "mixed random codes", rel=FP8_GROUPED_REL)
+    print("E2M1 mixed %d x %d random codes: worst |err|/T = %.3g" % (afmt, bfmt, worst))
+
+
+def test_gemm_e2m1_paged_b(mx, oracle):
+    """An E4M3 A against an E2M1 B read through a page table (rows of B in
+    pages of 64, pages out of order), N ragged."""
+    import ctypes
+    import torch
+    from microscaling_block_scaled_amd import _lib
+    M, N, K, page_rows = 96, 300, 256, 64
+    pages_per_seq = (N + page_rows - 1) // page_rows
+    n_pages = pages_per_seq + 3
+    g = inputs.rng(395)
+    table = g.permutation(n_pages)[:pages_per_seq].astype(np.int32)
+    a = inputs.normal_bf16(396, (M, K))
+    bpages = inputs.normal_bf16(397, (n_pages * page_rows, K))
+    qa, sa = oracle.quantize_rows(a, E4M3)
+    qbp, sbp = oracle.quantize_rows(bpages, E2M1)
+    rows = table[np.arange(N) // page_rows].astype(np.int64) * page_rows + np.arange(N) % page_rows
+    y_ref, t_ref = oracle.gemm(qa, sa, E4M3, np.ascontiguousarray(qbp[rows]), np.ascontiguousarray(sbp[rows]), E2M1)
+    dqa, dsa, dqb, dsb, dtab = dev(qa), dev(sa), dev(qbp), dev(sbp), dev(table)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    d = mx.mx_gemm_desc_t()
+    d.M, d.N, d.K = M, N, K
+    d.a, d.lda, d.sa, d.ldsa, d.a_fmt = dqa.data_ptr(), K, dsa.data_ptr(), K // 32, E4M3
+    d.b, d.ldb, d.sb, d.ldsb, d.b_fmt = dqb.data_ptr(), K // 2, dsb.data_ptr(), K // 32, E2M1
+    d.y, d.ldy, d.y_dtype = y.data_ptr(), N, 0
+    d.b_page_table = dtab.data_ptr()
+    d.b_pages_per_seq, d.b_page_rows = pages_per_seq, page_rows
+    d.b_page_stride, d.b_page_stride_s = page_rows * (K // 2), page_rows * (K // 32)
+    d.accum = AUTO
+    mx.mx_gemm_desc(d)
+    torch.cuda.synchronize()
+    worst = assert_gemm_bound(host(y).astype(np.float64), y_ref, t_ref, "paged E2M1 B", rel=FP8_GROUPED_REL)
+    print("paged E4M3 x E2M1: worst |err|/T = %.3g" % worst)
