@@ -159,6 +159,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   __shared__ __attribute__((aligned(16))) uint32_t VSs[2][kKB];
   __shared__ __attribute__((aligned(1024))) uint8_t VT[kHD * kVTRow];
   __shared__ __attribute__((aligned(16))) float VShift[SHIFTED ? kKB : 4];  // 2^r of each key (v_key_shift)
+  __shared__ __attribute__((aligned(16))) int32_t PageNext[2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,9 +224,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   // slots are consecutive.
   const uint32_t slot_bytes = g.hkv * kHD;        // code bytes per cache slot
   const uint32_t slot_sbytes = g.hkv * (kHD / 32); // scale bytes per cache slot
-  auto slot0_of = [&](int b) -> int64_t {
-    const uint32_t j = (uint32_t)b * kKB;
-    return (int64_t)tab[j / g.page_size] * g.page_size + j % g.page_size;
+  // The page of block b is fetched two blocks ahead, straight into LDS
+  // (PageNext[b & 1], 64 copies), so no register waits on its load.
+  auto page_of = [&](int b) -> int32_t { return tab[(uint32_t)b * kKB / g.page_size]; };
+  auto prefetch_page = [&](int b) {
+    if (wave == 0)
+      dma4(lds_off(&PageNext[b & 1][0]), 0u, uniform_ptr((const uint8_t*)(tab + (uint32_t)b * kKB / g.page_size)));
+  };
+  auto slot0_of = [&](int b, int32_t page) -> int64_t {
+    return (int64_t)page * g.page_size + ((uint32_t)b * kKB) % g.page_size;
   };
 
   // K code rows of this lane's 4 direct-to-LDS loads and the chunk each
@@ -247,8 +254,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   const uint32_t v_off0 = v_key * slot_bytes + 4 * gd0;
 
   uint32_t vraw[2][8];
-  auto issue_block = [&](int b, int buf) {
-    const int64_t slot0 = slot0_of(b);
+  auto issue_block = [&](int b, int buf, int32_t page) {
+    const int64_t slot0 = slot0_of(b, page);
     const uint32_t last = (uint32_t)min(kKB, kmax - b * kKB) - 1;
     const uint8_t* kbase = uniform_ptr(g.kc + (slot0 * g.hkv + hk) * kHD);
 #pragma unroll
@@ -331,7 +338,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
 
   const uint32_t fp = fperm(lr);
 
-  issue_block(0, 0);
+  issue_block(0, 0, page_of(0));
+  if (nblk > 1) prefetch_page(1);
 
   for (int b = 0; b < nblk; ++b) {
     const int buf = b & 1;
@@ -339,7 +347,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
     wait_lgkmcnt0();
     barrier();  // block b staged; V^T and buffer buf ^ 1 are free
     decode_v(buf, SHIFTED);
-    if (b + 1 < nblk) issue_block(b + 1, buf ^ 1);
+    if (b + 1 < nblk) {
+      // (landed: wave 0 waited for all its loads before the barrier above)
+      const int32_t page = __builtin_amdgcn_readfirstlane(PageNext[(b + 1) & 1][0]);
+      if (b + 2 < nblk) prefetch_page(b + 2);
+      issue_block(b + 1, buf ^ 1, page);
+    }
 
     // ---- S^T for this wave's 32 queries x 128 keys: 4 tiles of 32 keys,
     // accumulated over the two head-dim halves
