@@ -316,7 +316,12 @@ def quantize_rows_only(torch, mx, inputs, flush, stream, steps):
     qt, st = torch.empty((C, R), **u8), torch.empty((C, R // 32), **u8)
     q4 = torch.empty((R, C // 2), **u8)
     y = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    # a plain device copy moving as many bytes as a quantizer (reads and
+    # writes 51 MB): the rate this part sustains on a pure stream
+    cn = (3 * R * C + R * C // 32) // 2
+    csrc, cdst = torch.empty(cn, **u8), torch.empty(cn, **u8)
     calls = {
+        "device_copy_same_bytes": (lambda: cdst.copy_(csrc), 2 * cn),
         "rowwise": (lambda: mx.mx_quantize(X, mx.MX_E4M3, q=q, s=s), 3 * R * C + R * C // 32),
         "colwise": (lambda: mx.mx_quantize_colwise(X, mx.MX_E4M3, qt=qt, st=st), 3 * R * C + R * C // 32),
         "rows_and_cols_one_pass": (lambda: mx.mx_quantize_ex(X, mx.MX_E4M3, colwise=True, q=q, s=s, qt=qt, st=st),
