@@ -21,7 +21,11 @@ that stresses them, checked against the oracle on every output.
    finite scales]: a block under 0xFF is NaN, so every output it enters is
    NaN, also when its element codes are all zero.
 
-4. Paged attention with Q, K and V scales from both ends of the range.
+4. Paged attention with Q, K and V scales from both ends of the range, and
+   the NaN code in Q, K and V.
+
+5. The exact pass in the grouped product (large-tile kernel) and with B
+   read through a page table (row-panel and general kernels).
 """
 import numpy as np
 import pytest
@@ -323,3 +327,72 @@ def test_attention_nan_scale_codes(mx, oracle, causal):
         assert np.all(np.isnan(lse[~rows_ok])), what + ": rows with a NaN score must have lse = NaN"
         sub = (o_ref[rows_ok], w_ref[rows_ok], lse_ref[rows_ok], tmax[rows_ok])
         assert_attention_bound(o[rows_ok], lse[rows_ok], sub, sm, what, out_f32=out_f32, keep=~may[rows_ok])
+
+
+# --------------------------------------------------------------------------- the whole range in grouped and paged products
+@pytest.mark.parametrize("bfmt", [E4M3, E5M2])
+@pytest.mark.parametrize("accum", [AUTO, FP32])
+def test_grouped_extreme_scale_codes(mx, oracle, bfmt, accum):
+    """The exact pass of the large-tile kernel in grouped mode: each group's
+    rows and its own B drawn like the extreme-range pairs above, ragged and
+    empty groups, every representable output of every group."""
+    import torch
+    sizes, N, K, afmt = [300, 0, 17, 257, 40], 256, 1024, E4M3
+    g = inputs.rng(7700 + bfmt + 4 * accum)
+    parts = [_extreme_pair(g, afmt, bfmt, max(m, 1), N, K) for m in sizes]
+    qa = np.concatenate([p[0][:m] for p, m in zip(parts, sizes)])
+    sa = np.concatenate([p[1][:m] for p, m in zip(parts, sizes)])
+    qb = np.concatenate([p[2] for p in parts])
+    sb = np.concatenate([p[3] for p in parts])
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    G = len(sizes)
+    for f32 in (True, False):
+        dt = torch.float32 if f32 else torch.bfloat16
+        y = torch.zeros((int(off[-1]), N), dtype=dt, device="cuda")
+        mx.mx_grouped_gemm(dev(qa), dev(sa), dev(qb).view(G, N, K), dev(sb).view(G, N, K // 32), dev(off), a_fmt=afmt,
+                           b_fmt=bfmt, y=y, accum=accum)
+        yh = host(y)
+        yh = yh.astype(np.float64) if f32 else bf16_to_f64(yh)
+        for q in range(G):
+            r0, r1 = int(off[q]), int(off[q + 1])
+            if r1 == r0:
+                continue
+            y_ref, t_ref = oracle.gemm(qa[r0:r1], sa[r0:r1], afmt, qb[q * N:(q + 1) * N], sb[q * N:(q + 1) * N], bfmt)
+            keep = _representable(y_ref, t_ref)
+            if not f32:
+                keep &= np.abs(y_ref) < 2.0 ** 126
+            assert_gemm_bound(yh[r0:r1][keep], y_ref[keep], t_ref[keep], "grouped extreme group %d f32 %d" % (q, f32),
+                              bf16_out=not f32)
+
+
+@pytest.mark.parametrize("K,N", [(96, 300), (160, 129)])
+@pytest.mark.parametrize("afmt,bfmt", [(E4M3, E4M3), (E5M2, E4M3)])
+def test_paged_extreme_scale_codes(mx, oracle, K, N, afmt, bfmt):
+    """The exact pass with B read through a page table (the row-panel kernel
+    at K = 96, the general kernel at K = 160), FP32-accumulation mode."""
+    import torch
+    M, page_rows = 200, 64
+    pages_per_seq = (N + page_rows - 1) // page_rows
+    n_pages = pages_per_seq + 2
+    g = inputs.rng(7800 + K + N + afmt)
+    qa, sa, qbp, sbp = _extreme_pair(g, afmt, bfmt, M, n_pages * page_rows, K)
+    table = g.permutation(n_pages)[:pages_per_seq].astype(np.int32)
+    rows = table[np.arange(N) // page_rows].astype(np.int64) * page_rows + np.arange(N) % page_rows
+    y_ref, t_ref = oracle.gemm(qa, sa, afmt, np.ascontiguousarray(qbp[rows]), np.ascontiguousarray(sbp[rows]), bfmt)
+    keep = _representable(y_ref, t_ref)
+    assert keep.mean() > 0.5
+    dqa, dsa, dqb, dsb, dtab = dev(qa), dev(sa), dev(qbp), dev(sbp), dev(table)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    d = mx.mx_gemm_desc_t()
+    d.M, d.N, d.K = M, N, K
+    d.a, d.lda, d.sa, d.ldsa, d.a_fmt = dqa.data_ptr(), K, dsa.data_ptr(), K // 32, afmt
+    d.b, d.ldb, d.sb, d.ldsb, d.b_fmt = dqb.data_ptr(), K, dsb.data_ptr(), K // 32, bfmt
+    d.y, d.ldy, d.y_dtype = y.data_ptr(), N, 0
+    d.b_page_table = dtab.data_ptr()
+    d.b_pages_per_seq, d.b_page_rows = pages_per_seq, page_rows
+    d.b_page_stride, d.b_page_stride_s = page_rows * K, page_rows * (K // 32)
+    d.accum = FP32
+    mx.mx_gemm_desc(d)
+    torch.cuda.synchronize()
+    worst = assert_gemm_bound(host(y).astype(np.float64)[keep], y_ref[keep], t_ref[keep], "paged extreme K=%d" % K)
+    print("paged extreme K=%d N=%d %d x %d: worst |err|/T %.3g" % (K, N, afmt, bfmt, worst))
