@@ -35,7 +35,7 @@ from microscaling_block_scaled_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-E4M3, E5M2 = 0, 1
+E4M3, E5M2, E2M1 = 0, 1, 2
 AUTO, FP8, FP32 = 0, 1, 2
 MODE_NAME = {AUTO: "AUTO", FP8: "FP8", FP32: "FP32"}
 
@@ -208,27 +208,32 @@ def test_extreme_scale_codes(mx, oracle, M, N, K, afmt, bfmt, accum):
 
 
 # --------------------------------------------------------------------------- 3. the NaN scale code
+NAN_CASES = [(a, b, m) for a, b in [(E4M3, E4M3), (E5M2, E4M3), (E2M1, E2M1), (E2M1, E4M3), (E4M3, E2M1)]
+             for m in (AUTO, FP8, FP32) if not (m == FP32 and E2M1 in (a, b))]  # E2M1 has no FP32 mode
+
+
 @pytest.mark.parametrize("M,N,K", EXTREME_SHAPES)
-@pytest.mark.parametrize("afmt", [E4M3, E5M2])
-@pytest.mark.parametrize("accum", [AUTO, FP8, FP32])
-def test_nan_scale_code(mx, oracle, M, N, K, afmt, accum):
-    g = inputs.rng(7500 + M + N + K + afmt)
+@pytest.mark.parametrize("afmt,bfmt,accum", NAN_CASES)
+def test_nan_scale_code(mx, oracle, M, N, K, afmt, bfmt, accum):
+    g = inputs.rng(7500 + M + N + K + afmt + 3 * bfmt)
     qa, sa = oracle.quantize_rows(inputs.normal_bf16(7501 + K + afmt, (M, K)), afmt)
-    qb, sb = oracle.quantize_rows(inputs.normal_bf16(7502 + K, (N, K)), E4M3)
+    qb, sb = oracle.quantize_rows(inputs.normal_bf16(7502 + K + bfmt, (N, K)), bfmt)
     kb = K // 32
     ra, ba = g.choice(M, 3, replace=False), g.integers(0, kb, 3)
     rb, bb = g.choice(N, 3, replace=False), g.integers(0, kb, 3)
     sa[ra, ba] = 0xFF
     sb[rb, bb] = 0xFF
-    qa[ra[0], 32 * ba[0]:32 * ba[0] + 32] = 0  # NaN scale over zero codes
-    qb[rb[0], 32 * bb[0]:32 * bb[0] + 32] = 0
-    y_ref, t_ref = oracle.gemm(qa, sa, afmt, qb, sb, E4M3)
+    wa, wb = (16 if afmt == E2M1 else 32), (16 if bfmt == E2M1 else 32)  # code bytes per block
+    qa[ra[0], wa * ba[0]:wa * ba[0] + wa] = 0  # NaN scale over zero codes
+    qb[rb[0], wb * bb[0]:wb * bb[0] + wb] = 0
+    y_ref, t_ref = oracle.gemm(qa, sa, afmt, qb, sb, bfmt)
     nan_ref = np.isnan(y_ref)
     assert nan_ref.sum() == 3 * N + 3 * M - 9  # three whole rows and three whole columns
-    what = "NaN scale %s x E4M3 %s %s" % (afmt, MODE_NAME[accum], (M, N, K))
-    rel = FP8_GROUPED_REL if accum == FP8 else REL_T
+    what = "NaN scale %s x %s %s %s" % (afmt, bfmt, MODE_NAME[accum], (M, N, K))
+    exact = afmt == E2M1 and bfmt == E2M1
+    rel = FP8_GROUPED_REL if (accum == FP8 or E2M1 in (afmt, bfmt)) and not exact else REL_T
     for f32 in (True, False):
-        y = _gemm(mx, qa, sa, qb, sb, afmt, E4M3, accum, f32=f32)
+        y = _gemm(mx, qa, sa, qb, sb, afmt, bfmt, accum, f32=f32)
         bad = np.isnan(y) != nan_ref
         assert not bad.any(), "%s f32 %d: NaN pattern differs at %d outputs, first %s (got %r)" % (
             what, f32, bad.sum(), tuple(np.argwhere(bad)[0]), y[bad][0])
