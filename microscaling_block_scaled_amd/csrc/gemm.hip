@@ -896,11 +896,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
 
   // FP32-accumulation mode over the whole E8M0 range. A block whose scale
   // lies outside its fold window is folded inexactly (fold_decode8); it
-  // matters only if it holds a non-zero code, and then the wave replaces its
-  // terms in the exact pass after the main loop. Only in K halves whose
-  // group of scales has such a block (set_out) do the lanes look at their
-  // scales and codes, so all-zero blocks (scale code 0) never start the
-  // exact pass.
+  // matters only if it holds a non-zero code or its scale is the NaN code,
+  // and then the wave replaces its terms in the exact pass after the main
+  // loop (exact_flag). Only in K halves whose group of scales has a scale
+  // outside the window (set_out) do the lanes look at their scales and
+  // codes, so all-zero blocks (scale code 0) never start the exact pass.
   bool needs_exact = false;
   auto check_half = [&](int set) {
     if constexpr (MODE == kModeBF16) {
