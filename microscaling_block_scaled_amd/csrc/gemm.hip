@@ -312,15 +312,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       }
     } else {
       // one 32-K block per MFMA: lane (r, g) takes k = 32*kb + 8g .. +7, i.e.
-      // bytes 8*(g & 1) .. +7 of 16-byte chunk 2*kb + g/2 of its row
+      // bytes 8*(g & 1) .. +7 of 16-byte chunk 2*kb + g/2 of its row (E2M1:
+      // bytes 4g .. 4g+3 of chunk kb, the upper word zero)
+      auto codes8 = [&](const uint8_t* base, uint32_t row, int kb, bool half) -> uint2 {
+        if (half) return make_uint2(*(const uint32_t*)(base + swz(row, kb) + 4 * lg), 0u);
+        return *(const uint2*)(base + swz(row, 2 * kb + (lg >> 1)) + 8 * (lg & 1));
+      };
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const uint32_t chunk = 2 * kb + (lg >> 1), off = 8 * (lg & 1);
         v8bf16 bf[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const uint32_t row = wn * WN + j * 16 + lr;
-          const uint2 w = *(const uint2*)(&Bs[buf][swz(row, chunk) + off]);
+          const uint2 w = codes8(&Bs[buf][0], row, kb, BFMT == MX_E2M1);
           const uint32_t sc = (sBs[buf][row] >> (8 * kb)) & 0xFFu;
           unfolded |= unfolded_codes<BFMT>(sc, w);
           bf[j] = fold_decode8<BFMT>(w, sc);
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const uint32_t row = wm * WM + i * 16 + lr;
-          const uint2 w = *(const uint2*)(&As[buf][swz(row, chunk) + off]);
+          const uint2 w = codes8(&As[buf][0], row, kb, AFMT == MX_E2M1);
           const uint32_t sc = (sAs[buf][row] >> (8 * kb)) & 0xFFu;
           unfolded |= unfolded_codes<AFMT>(sc, w);
           const v8bf16 af = fold_decode8<AFMT>(w, sc);
@@ -350,12 +354,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       const uint8_t* br[4];
       const uint8_t* sar[4];
       const uint8_t* sbr[4];
+      // a lane's 8 codes of block b: 8 bytes at 32 b + 8 lg (E2M1: 4 bytes
+      // at 16 b + 4 lg)
+      constexpr int kAW = AFMT == MX_E2M1 ? 4 : 8, kBW = BFMT == MX_E2M1 ? 4 : 8;
+      auto codes_at = [](const uint8_t* p, int64_t b, int w) -> uint2 {
+        return w == 4 ? make_uint2(*(const uint32_t*)(p + 16 * b), 0u) : *(const uint2*)(p + 32 * b);
+      };
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + wm * WM + i * 16 + lr, n = n0 + wn * WN + i * 16 + lr;
-        ar[i] = m < g.M ? A + m * g.lda + 8 * lg : nullptr;
+        ar[i] = m < g.M ? A + m * g.lda + kAW * lg : nullptr;
         sar[i] = m < g.M ? SA + m * g.ldsa : nullptr;
-        br[i] = n < g.N ? b_row_ptr(n, B, g.ldb, g.page_stride) + 8 * lg : nullptr;
+        br[i] = n < g.N ? b_row_ptr(n, B, g.ldb, g.page_stride) + kBW * lg : nullptr;
         sbr[i] = n < g.N ? b_row_ptr(n, SB, g.ldsb, g.page_stride_s) : nullptr;
       }
       for (int64_t b = 0; b < kblocks; ++b) {
@@ -363,9 +373,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         uint32_t ca[4], cb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          qa[i] = ar[i] ? *(const uint2*)(ar[i] + 32 * b) : make_uint2(0, 0);
+          qa[i] = ar[i] ? codes_at(ar[i], b, kAW) : make_uint2(0, 0);
           ca[i] = sar[i] ? sar[i][b] : 127u;
-          qb[i] = br[i] ? *(const uint2*)(br[i] + 32 * b) : make_uint2(0, 0);
+          qb[i] = br[i] ? codes_at(br[i], b, kBW) : make_uint2(0, 0);
           cb[i] = sbr[i] ? sbr[i][b] : 127u;
         }
         exact_block16<AFMT, BFMT>(qa, ca, qb, cb, acc);
@@ -1293,16 +1303,14 @@ mx_status_t launch(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, in
   hipLaunchKernelGGL((gemm_kernel<BM, BN, AF, BF, OUT, PAGED, MODE>), grid, dim3(kThreads), 0, st, g)
 #define MX_GEMM_OUT(AF, BF) \
   do { if (bf16out) MX_GEMM_LAUNCH(AF, BF, true); else MX_GEMM_LAUNCH(AF, BF, false); } while (0)
-  if constexpr (MODE == kModeFP8) {
-    // E2M1 operands, alone or against an FP8 format: scaled instruction only
-    if (af == MX_E2M1 || bf == MX_E2M1) {
-      if (af == MX_E2M1 && bf == MX_E2M1) MX_GEMM_OUT(MX_E2M1, MX_E2M1);
-      else if (af == MX_E2M1 && bf == MX_E4M3) MX_GEMM_OUT(MX_E2M1, MX_E4M3);
-      else if (af == MX_E2M1) MX_GEMM_OUT(MX_E2M1, MX_E5M2);
-      else if (af == MX_E4M3) MX_GEMM_OUT(MX_E4M3, MX_E2M1);
-      else MX_GEMM_OUT(MX_E5M2, MX_E2M1);
-      return mx_host::launch_status();
-    }
+  // E2M1 operands, alone or against an FP8 format
+  if (af == MX_E2M1 || bf == MX_E2M1) {
+    if (af == MX_E2M1 && bf == MX_E2M1) MX_GEMM_OUT(MX_E2M1, MX_E2M1);
+    else if (af == MX_E2M1 && bf == MX_E4M3) MX_GEMM_OUT(MX_E2M1, MX_E4M3);
+    else if (af == MX_E2M1) MX_GEMM_OUT(MX_E2M1, MX_E5M2);
+    else if (af == MX_E4M3) MX_GEMM_OUT(MX_E4M3, MX_E2M1);
+    else MX_GEMM_OUT(MX_E5M2, MX_E2M1);
+    return mx_host::launch_status();
   }
   if (af == MX_E4M3 && bf == MX_E4M3) MX_GEMM_OUT(MX_E4M3, MX_E4M3);
   else if (af == MX_E5M2 && bf == MX_E4M3) MX_GEMM_OUT(MX_E5M2, MX_E4M3);
@@ -1319,11 +1327,9 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   if (!d) return MX_ERR_NULL;
   auto known = [](mx_fmt_t f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; };
   if (!known(d->a_fmt) || !known(d->b_fmt)) return MX_ERR_FORMAT;
-  // an E2M1 operand (MXFP4 x MXFP4, or against E4M3 / E5M2) runs on the
-  // scaled matrix instruction only
+  // an E2M1 operand: MXFP4 x MXFP4, or against E4M3 / E5M2
   const bool e2m1 = d->a_fmt == MX_E2M1 || d->b_fmt == MX_E2M1;
   const bool fp4 = d->a_fmt == MX_E2M1 && d->b_fmt == MX_E2M1;
-  if (e2m1 && d->accum == MX_ACCUM_FP32) return MX_ERR_FORMAT;
   if (d->y_dtype != MX_F32 && d->y_dtype != MX_BF16) return MX_ERR_FORMAT;
   const int64_t M = d->M, N = d->N, K = d->K;
   if (M < 0 || N < 0 || K < 0 || K % kBlock != 0) return MX_ERR_SHAPE;
@@ -1373,9 +1379,10 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
   g.scales_dword = (sa4 && sb4) ? 1u : 0u;
   g.y_vec = (mx_host::aligned16(d->y) && (d->ldy * ysz) % 16 == 0 && (d->stride_y_outer * ysz) % 16 == 0 &&
              (d->stride_y_inner * ysz) % 16 == 0) ? 1u : 0u;
-  // MX_ACCUM_AUTO is the FP32-accumulation mode: the scaled FP8 instruction
-  // meets 1e-5 * sum|a b| only on data whose errors cancel (see mx_accum_t)
-  const bool fp8 = d->accum == MX_ACCUM_FP8 || e2m1;
+  // MX_ACCUM_AUTO is the FP32-accumulation mode (the scaled FP8 instruction
+  // meets 1e-5 * sum|a b| only on data whose errors cancel, see mx_accum_t),
+  // except for MXFP4 x MXFP4, where the instruction is exact
+  const bool fp8 = d->accum == MX_ACCUM_FP8 || (d->accum == MX_ACCUM_AUTO && fp4);
 
   constexpr int BM = 128, BN = 128;
   g.tiles_m = (uint32_t)((M + BM - 1) / BM);
@@ -1388,9 +1395,9 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
                       d->ldsb % 16 == 0 && d->stride_sa_outer % 16 == 0 && d->stride_sa_inner % 16 == 0 &&
                       d->stride_sb_outer % 16 == 0 && d->stride_sb_inner % 16 == 0 && M >= 256 && N >= 256 &&
                       (M * d->lda) < ((int64_t)1 << 32) && (N * d->ldb) < ((int64_t)1 << 32);
-  // MXFP4 x MXFP4 on the large-tile kernel where it fits; a mixed E2M1
-  // product, or any other shape, on the general kernel
-  if (big_ok && (fp4 || !e2m1)) {
+  // MXFP4 x MXFP4 on the scaled instruction on the large-tile kernel where
+  // it fits; every other product with an E2M1 operand on the general kernel
+  if (big_ok && (!e2m1 || (fp4 && fp8))) {
     GemmArgs gb = g;
     gb.tiles_m = (uint32_t)((M + kFBM - 1) / kFBM);
     gb.tiles_n = (uint32_t)((N + kFBN - 1) / kFBN);
@@ -1399,7 +1406,7 @@ extern "C" mx_status_t mx_gemm(const mx_gemm_desc_t* d, hipStream_t stream) {
                : launch_big<kModeBF16>(gb, d->a_fmt, d->b_fmt, bf16out, bo * bi, stream);
   }
   // short reductions with at most 512 B rows: the row-panel kernel
-  const bool rowpanel_ok = !fp8 && K <= kBK && N <= kRPMaxN && d->lda % 8 == 0 && d->ldb % 16 == 0 &&
+  const bool rowpanel_ok = !fp8 && !e2m1 && K <= kBK && N <= kRPMaxN && d->lda % 8 == 0 && d->ldb % 16 == 0 &&
                            (paged ? d->b_page_stride % 16 == 0 : d->stride_b_outer % 16 == 0) &&
                            d->stride_b_inner % 16 == 0 && d->stride_a_outer % 8 == 0 && d->stride_a_inner % 8 == 0;
   if (rowpanel_ok)

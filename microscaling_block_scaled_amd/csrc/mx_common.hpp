@@ -207,11 +207,18 @@ __device__ __forceinline__ float scale_value(uint32_t code) {
   return code == 0xFFu ? __uint_as_float(0x7FC00000u) : __uint_as_float(code ? (code << 23) : 0x00400000u);
 }
 
-// Eight codes (two dwords) -> eight bf16 values times the block scale.
+// Eight codes -> eight bf16 values times the block scale: two dwords of
+// FP8 codes, or (E2M1) the eight nibbles of w.x, element 2i in the low
+// nibble of byte i.
 template <int FMT>
 __device__ __forceinline__ v8bf16 decode8_bf16(uint2 w, float scale) {
   v2bf16 r0, r1, r2, r3;
-  if constexpr (FMT == MX_E5M2) {
+  if constexpr (FMT == MX_E2M1) {
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.x, scale, 0);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.x, scale, 1);
+    r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.x, scale, 2);
+    r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w.x, scale, 3);
+  } else if constexpr (FMT == MX_E5M2) {
     r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.x, scale, false);
     r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.x, scale, true);
     r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w.y, scale, false);
@@ -231,13 +238,18 @@ __device__ __forceinline__ v8bf16 decode8_bf16(uint2 w, float scale) {
 // exactly when s lies in [fold_lo, fold_hi]: E4M3 values run from 2^-9 to
 // 448 = 1.75 * 2^8, so 2^-9 * 2^(s - 127) >= 2^-126 needs s >= 10 and
 // 448 * 2^(s - 127) < 2^128 needs s <= 246; E5M2 values run from 2^-16 to
-// 1.75 * 2^15, giving [17, 239]. The main loops fold every block; the terms
+// 1.75 * 2^15, giving [17, 239]; E2M1 values run from 2^-1 to 6 = 1.5 * 2^2,
+// giving [2, 252]. The main loops fold every block; the terms
 // of blocks outside the window are replaced afterwards by an exact pass
 // (below).
 template <int FMT>
-constexpr uint32_t fold_lo() { return FMT == MX_E5M2 ? 17u : 10u; }
+constexpr uint32_t fold_lo() { return FMT == MX_E5M2 ? 17u : FMT == MX_E2M1 ? 2u : 10u; }
 template <int FMT>
-constexpr uint32_t fold_hi() { return FMT == MX_E5M2 ? 239u : 246u; }
+constexpr uint32_t fold_hi() { return FMT == MX_E5M2 ? 239u : FMT == MX_E2M1 ? 252u : 246u; }
+// The bits of a code word that hold element magnitudes (a zero element of
+// either sign has none set): FP8 bytes, or E2M1 nibbles.
+template <int FMT>
+constexpr uint32_t code_mag_mask() { return FMT == MX_E2M1 ? 0x77777777u : 0x7F7F7F7Fu; }
 
 // A scale outside the fold window, the NaN code 0xFF included: its block's
 // terms are replaced by the exact pass. (Rows are left out of a pass by
@@ -253,7 +265,7 @@ __device__ __forceinline__ bool fold_excluded(uint32_t s) {
 // output it enters NaN whatever its codes.
 template <int FMT>
 __device__ __forceinline__ uint32_t exact_flag(uint32_t s, uint32_t codes_or) {
-  return fold_excluded<FMT>(s) ? (s == 0xFFu ? 1u : codes_or & 0x7F7F7F7Fu) : 0u;
+  return fold_excluded<FMT>(s) ? (s == 0xFFu ? 1u : codes_or & code_mag_mask<FMT>()) : 0u;
 }
 
 // ---- the exact pass over blocks the fold leaves out.
@@ -284,9 +296,9 @@ __device__ __forceinline__ uint32_t exact_class(uint32_t s) {
 }
 // log2 bounds of the largest and smallest non-zero element magnitude
 template <int FMT>
-constexpr int elem_log2_max() { return FMT == MX_E5M2 ? 16 : 9; }
+constexpr int elem_log2_max() { return FMT == MX_E5M2 ? 16 : FMT == MX_E2M1 ? 3 : 9; }
 template <int FMT>
-constexpr int elem_log2_min() { return FMT == MX_E5M2 ? -16 : -9; }
+constexpr int elem_log2_min() { return FMT == MX_E5M2 ? -16 : FMT == MX_E2M1 ? -1 : -9; }
 
 struct ExactCell { int x, y, w; };
 template <int AF, int BF>

@@ -125,8 +125,7 @@ def test_mxfp4_argument_errors_without_gpu(libmx):
             setattr(d, k, v)
         return d
 
-    assert g(ctypes.byref(desc(accum=2)), None) == -4               # FP32-accumulation mode has no E2M1 path
-    assert g(ctypes.byref(desc(b_fmt=0, ldb=2048, accum=2)), None) == -4  # nor for E2M1 x E4M3
+    assert g(ctypes.byref(desc(accum=3)), None) == -4               # no such accumulation mode
     assert g(ctypes.byref(desc(a_fmt=3)), None) == -4               # no such element format
     assert g(ctypes.byref(desc(lda=512)), None) == -2               # pitch below K/2 bytes
     assert g(ctypes.byref(desc(b_fmt=0, ldb=1024)), None) == -2     # an E4M3 B row holds K bytes

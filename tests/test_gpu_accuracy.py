@@ -94,8 +94,16 @@ def test_accumulation_modes_on_hard_data(mx, oracle, dist, K):
 
 def _finite_codes(g, fmt, shape, small=False):
     """Random element codes of finite values (no NaN / Inf codes); `small`
-    keeps magnitudes <= 0.25 so that blocks under the largest scales stay in
-    f32 range."""
+    keeps magnitudes <= 0.25 (E2M1: <= 1) so that blocks under the largest
+    scales stay in f32 range. E2M1: `shape` counts elements, two per byte."""
+    if fmt == E2M1:
+        pool = np.arange(16, dtype=np.uint8)
+        if small:
+            pool = pool[(pool & 7) <= 2]
+        shp = tuple(shape[:-1]) + (shape[-1] // 2,) if len(shape) > 0 else shape
+        lo = pool[g.integers(0, pool.size, shp)]
+        hi = pool[g.integers(0, pool.size, shp)]
+        return (lo | (hi << 4)).astype(np.uint8)
     if fmt == E4M3:
         pool = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
         lim = 0x28  # 0.25
@@ -107,8 +115,8 @@ def _finite_codes(g, fmt, shape, small=False):
     return pool[g.integers(0, pool.size, shape)]
 
 
-LOW = {E4M3: [0, 1, 2, 3], E5M2: list(range(0, 11))}
-HIGH = {E4M3: [246, 247, 254], E5M2: list(range(239, 255))}
+LOW = {E4M3: [0, 1, 2, 3], E5M2: list(range(0, 11)), E2M1: [0, 1, 2]}
+HIGH = {E4M3: [246, 247, 254], E5M2: list(range(239, 255)), E2M1: [252, 253, 254]}
 
 
 def _attention_v(g, vs_shape):
@@ -171,12 +179,23 @@ def _extreme_pair(g, afmt, bfmt, M, N, K):
 
     def codes(fmt, s, rows):
         q = _finite_codes(g, fmt, (rows, K))
-        # blocks under scales whose 2^(s - 127) * 448 (57344) would overflow f32 get small codes
-        big = np.repeat(s >= (240 if fmt == E4M3 else 232), 32, axis=1)
-        q[big] = _finite_codes(g, fmt, (int(big.sum()),), small=True)
+        # blocks under scales whose 2^(s - 127) * 448 (57344, 6) would overflow f32 get small codes
+        per = 16 if fmt == E2M1 else 32  # code bytes per block
+        big = np.repeat(s >= {E4M3: 240, E5M2: 232, E2M1: 250}[fmt], per, axis=1)
+        q[big] = _finite_codes(g, fmt, (int(big.sum()) * (2 if fmt == E2M1 else 1),), small=True)
         return q
 
     return codes(afmt, sa, M), sa, codes(bfmt, sb, N), sb
+
+
+def _mode_rel(afmt, bfmt, accum):
+    """The bound a product is held to: 1e-5 * sum|a b| in the FP32-
+    accumulation mode (AUTO's choice except for MXFP4 x MXFP4) and for
+    MXFP4 x MXFP4 on the instruction (exact), the grouped bound 2^-10 on the
+    scaled FP8 instruction otherwise."""
+    fp4 = afmt == E2M1 and bfmt == E2M1
+    on_instruction = accum == FP8 or (accum == AUTO and fp4)
+    return FP8_GROUPED_REL if on_instruction and not fp4 else REL_T
 
 
 def _representable(y_ref, t_ref):
@@ -189,7 +208,8 @@ EXTREME_SHAPES = [(300, 200, 96), (130, 129, 160), (256, 512, 512), (512, 256, 2
 
 
 @pytest.mark.parametrize("M,N,K", EXTREME_SHAPES)
-@pytest.mark.parametrize("afmt,bfmt", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)])
+@pytest.mark.parametrize("afmt,bfmt", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2), (E2M1, E2M1),
+                                       (E2M1, E4M3), (E5M2, E2M1)])
 @pytest.mark.parametrize("accum", [AUTO, FP8, FP32])
 def test_extreme_scale_codes(mx, oracle, M, N, K, afmt, bfmt, accum):
     g = inputs.rng(7300 + M + N + K + 10 * afmt + 20 * bfmt)
@@ -197,7 +217,7 @@ def test_extreme_scale_codes(mx, oracle, M, N, K, afmt, bfmt, accum):
     y_ref, t_ref = oracle.gemm(qa, sa, afmt, qb, sb, bfmt)
     keep = _representable(y_ref, t_ref)
     assert keep.mean() > 0.5, "too few representable outputs: %.2f" % keep.mean()
-    rel = FP8_GROUPED_REL if accum == FP8 else REL_T
+    rel = _mode_rel(afmt, bfmt, accum)
     what = "%s x %s %s %s" % (afmt, bfmt, MODE_NAME[accum], (M, N, K))
     y = _gemm(mx, qa, sa, qb, sb, afmt, bfmt, accum)
     worst = assert_gemm_bound(y[keep], y_ref[keep], t_ref[keep], what + " f32", rel=rel)
@@ -209,7 +229,7 @@ def test_extreme_scale_codes(mx, oracle, M, N, K, afmt, bfmt, accum):
 
 # --------------------------------------------------------------------------- 3. the NaN scale code
 NAN_CASES = [(a, b, m) for a, b in [(E4M3, E4M3), (E5M2, E4M3), (E2M1, E2M1), (E2M1, E4M3), (E4M3, E2M1)]
-             for m in (AUTO, FP8, FP32) if not (m == FP32 and E2M1 in (a, b))]  # E2M1 has no FP32 mode
+             for m in (AUTO, FP8, FP32)]
 
 
 @pytest.mark.parametrize("M,N,K", EXTREME_SHAPES)
@@ -230,8 +250,7 @@ def test_nan_scale_code(mx, oracle, M, N, K, afmt, bfmt, accum):
     nan_ref = np.isnan(y_ref)
     assert nan_ref.sum() == 3 * N + 3 * M - 9  # three whole rows and three whole columns
     what = "NaN scale %s x %s %s %s" % (afmt, bfmt, MODE_NAME[accum], (M, N, K))
-    exact = afmt == E2M1 and bfmt == E2M1
-    rel = FP8_GROUPED_REL if (accum == FP8 or E2M1 in (afmt, bfmt)) and not exact else REL_T
+    rel = _mode_rel(afmt, bfmt, accum)
     for f32 in (True, False):
         y = _gemm(mx, qa, sa, qb, sb, afmt, bfmt, accum, f32=f32)
         bad = np.isnan(y) != nan_ref
