@@ -656,6 +656,132 @@ constexpr uint32_t kScaleBuf = kFBM * kScaleRow;
 __device__ __forceinline__ void dma4(uint32_t lds, uint32_t off, const void* base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
 }
+// Origin of a large-tile work-group's 256 x 256 output tile. Work-groups
+// are dealt round-robin to the 8 XCDs, so tile ids are remapped to give each
+// XCD a contiguous band of tiles (shared panels stay in that XCD's L2),
+// walked in groups of 4 tile rows. In the grouped mode the grid has
+// ceil(M / 256) + groups row tiles; row tile t belongs to the group whose
+// tiles (ceil(rows / 256) each, offsets clamped to [0, M]) cover it, found
+// by every wave with a prefix sum over the groups, 64 at a time. Returns
+// false for the tiles past the last group's (their work-groups return
+// before any load or barrier).
+struct BigTile {
+  int64_t m0, n0, m_end, po, pi;
+  uint32_t tile_m, tile_n;
+};
+// (tile_m, tile_n) of work-group bid: XCD bands, then groups of 4 tile rows
+__device__ __forceinline__ void big_tile_coords(const GemmArgs& g, uint32_t bid, uint32_t& tile_m, uint32_t& tile_n) {
+  const uint32_t ntiles = g.tiles_m * g.tiles_n;
+  uint32_t lid = bid;
+  if (ntiles % 8 == 0) lid = (lid % 8) * (ntiles / 8) + lid / 8;
+  const uint32_t group = 4;
+  const uint32_t per_group = group * g.tiles_n;
+  const uint32_t first_m = (lid / per_group) * group;
+  const uint32_t gm = min(g.tiles_m - first_m, group);
+  tile_m = first_m + (lid % per_group) % gm;
+  tile_n = (lid % per_group) / gm;
+}
+__device__ __forceinline__ bool big_tile(const GemmArgs& g, int lane, BigTile& r) {
+  big_tile_coords(g, blockIdx.x, r.tile_m, r.tile_n);
+  r.n0 = (int64_t)r.tile_n * kFBN;
+  if (g.group_off == nullptr) {
+    r.m0 = (int64_t)r.tile_m * kFBM;
+    r.m_end = g.M;
+    const int64_t p = blockIdx.y;
+    r.po = p / g.batch_inner;
+    r.pi = p % g.batch_inner;
+    return true;
+  }
+  const uint32_t t = r.tile_m;
+  int64_t found = -1, lo_f = 0, hi_f = 0, first_tile = 0, prefix = 0;
+  for (uint32_t q0 = 0; q0 < g.groups && found < 0; q0 += 64) {
+    const uint32_t q = q0 + lane;
+    int64_t lo = 0, hi = 0;
+    if (q < g.groups) {
+      lo = min(max(g.group_off[q], (int64_t)0), g.M);
+      hi = min(max(g.group_off[q + 1], lo), g.M);
+    }
+    const int64_t nt = (hi - lo + kFBM - 1) / kFBM;
+    int64_t incl = nt;  // inclusive prefix of the tile counts across the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const int64_t chunk = __shfl(incl, 63);
+    if ((int64_t)t < prefix + chunk) {
+      const bool mine = (int64_t)t >= prefix + incl - nt && (int64_t)t < prefix + incl;
+      const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      found = q0 + src;
+      lo_f = __shfl(lo, src);
+      hi_f = __shfl(hi, src);
+      first_tile = prefix + __shfl(incl - nt, src);
+    }
+    prefix += chunk;
+  }
+  if (found < 0) return false;
+  r.m0 = lo_f + ((int64_t)t - first_tile) * kFBM;
+  r.m_end = hi_f;
+  r.po = found;
+  r.pi = 0;
+  return true;
+}
+
+// Store one 32 x 32 accumulator tile of v_mfma_*_32x32x* (lane (lr, lg)
+// holds row lr, columns 8 q + 4 lg .. +3 in elements 4 q .. 4 q + 3) at
+// output row m, columns nb .. nb + 31. Every lane takes part (the bf16 path
+// swaps dwords across lane halves); only lanes with mok store, and columns
+// at or past N are skipped.
+template <bool BF16OUT>
+__device__ __forceinline__ void store_tile32(const GemmArgs& g, uint8_t* Y, const v16f32& acc, int64_t m, bool mok,
+                                             int64_t nb, uint32_t lg) {
+  if constexpr (BF16OUT) {
+    uint16_t* row = (uint16_t*)Y + m * g.ldy;
+    uint32_t w[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[q][0] = pack_bf16x2_hw(acc[4 * q], acc[4 * q + 1]);
+      w[q][1] = pack_bf16x2_hw(acc[4 * q + 2], acc[4 * q + 3]);
+    }
+    if (g.y_vec && nb + 32 <= g.N) {
+      // Lanes l and l + 32 (same row) hold columns 16p + 4 lg .. and
+      // 16p + 8 + 4 lg ..; one lane swap per dword gives lane lg the 8
+      // consecutive columns 16p + 8 lg .. +7, stored as 16 bytes.
+#pragma unroll
+      for (int pq = 0; pq < 2; ++pq) {
+        const auto r0 = __builtin_amdgcn_permlane32_swap(w[2 * pq][0], w[2 * pq + 1][0], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(w[2 * pq][1], w[2 * pq + 1][1], false, false);
+        if (mok) *(uint4*)(row + nb + 16 * pq + 8 * lg) = make_uint4(r0[0], r1[0], r0[1], r1[1]);
+      }
+    } else if (mok) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = nb + 8 * q + 4 * lg;
+        if (g.y_vec && n + 3 < g.N) {
+          *(uint2*)(row + n) = make_uint2(w[q][0], w[q][1]);
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (n + e < g.N) row[n + e] = (uint16_t)(w[q][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  } else if (mok) {
+    float* row = (float*)Y + m * g.ldy;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = nb + 8 * q + 4 * lg;
+      const float v0 = acc[4 * q], v1 = acc[4 * q + 1], v2 = acc[4 * q + 2], v3 = acc[4 * q + 3];
+      if (g.y_vec && n + 3 < g.N) {
+        *(float4*)(row + n) = make_float4(v0, v1, v2, v3);
+      } else {
+        const float vv[4] = {v0, v1, v2, v3};
+        for (int e = 0; e < 4; ++e)
+          if (n + e < g.N) row[n + e] = vv[e];
+      }
+    }
+  }
+}
+
 template <int AFMT, int BFMT, bool BF16OUT, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t As[2][kCodeStage];
@@ -671,66 +797,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
 
-  int64_t m0, n0, m_end, po, pi;
-  // ---- tile id: XCD-contiguous bands, then groups of 4 tile rows (in the
-  // grouped mode over the grid of ceil(M / 256) + groups row tiles)
-  uint32_t tile_m, tile_n;
-  {
-    const uint32_t ntiles = g.tiles_m * g.tiles_n;
-    uint32_t lid = blockIdx.x;
-    if (ntiles % 8 == 0) lid = (lid % 8) * (ntiles / 8) + lid / 8;
-    const uint32_t group = 4;
-    const uint32_t per_group = group * g.tiles_n;
-    const uint32_t first_m = (lid / per_group) * group;
-    const uint32_t gm = min(g.tiles_m - first_m, group);
-    tile_m = first_m + (lid % per_group) % gm;
-    tile_n = (lid % per_group) / gm;
-  }
-  n0 = (int64_t)tile_n * kFBN;
-  if (g.group_off == nullptr) {
-    m0 = (int64_t)tile_m * kFBM;
-    m_end = g.M;
-    const int64_t p = blockIdx.y;
-    po = p / g.batch_inner;
-    pi = p % g.batch_inner;
-  } else {
-    // ---- grouped: row tile t belongs to the group whose tiles
-    // (ceil(rows / 256) each, offsets clamped to [0, M]) cover it; every wave
-    // finds it with a prefix sum over the groups, 64 at a time. Tiles past
-    // the last group's return before any load or barrier.
-    const uint32_t t = tile_m;
-    int64_t found = -1, lo_f = 0, hi_f = 0, first_tile = 0, prefix = 0;
-    for (uint32_t q0 = 0; q0 < g.groups && found < 0; q0 += 64) {
-      const uint32_t q = q0 + lane;
-      int64_t lo = 0, hi = 0;
-      if (q < g.groups) {
-        lo = min(max(g.group_off[q], (int64_t)0), g.M);
-        hi = min(max(g.group_off[q + 1], lo), g.M);
-      }
-      const int64_t nt = (hi - lo + kFBM - 1) / kFBM;
-      int64_t incl = nt;  // inclusive prefix of the tile counts across the wave
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int64_t v = __shfl_up(incl, d);
-        if (lane >= d) incl += v;
-      }
-      const int64_t chunk = __shfl(incl, 63);
-      if ((int64_t)t < prefix + chunk) {
-        const bool mine = (int64_t)t >= prefix + incl - nt && (int64_t)t < prefix + incl;
-        const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-        found = q0 + src;
-        lo_f = __shfl(lo, src);
-        hi_f = __shfl(hi, src);
-        first_tile = prefix + __shfl(incl - nt, src);
-      }
-      prefix += chunk;
-    }
-    if (found < 0) return;
-    m0 = lo_f + ((int64_t)t - first_tile) * kFBM;
-    m_end = hi_f;
-    po = found;
-    pi = 0;
-  }
+  BigTile tl;
+  if (!big_tile(g, lane, tl)) return;
+  const int64_t m0 = tl.m0, n0 = tl.n0, m_end = tl.m_end, po = tl.po, pi = tl.pi;
+  const uint32_t tile_m = tl.tile_m, tile_n = tl.tile_n;
   const uint8_t* A = g.a + po * g.sa_o + pi * g.sa_i;
   const uint8_t* SA = g.sa + po * g.ssa_o + pi * g.ssa_i;
   const uint8_t* B = g.b + po * g.sb_o + pi * g.sb_i;
@@ -1203,57 +1273,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = m0 + wm * 128 + i * 32 + lr;
-    const bool mok = m < m_end;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t nb = n0 + wn * 128 + j * 32;  // the lane's columns: nb + 8 q + 4 lg + 0..3
-      if constexpr (BF16OUT) {
-        uint16_t* row = (uint16_t*)Y + m * g.ldy;
-        uint32_t w[4][2];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          w[q][0] = pack_bf16x2_hw(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-          w[q][1] = pack_bf16x2_hw(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        }
-        if (g.y_vec && nb + 32 <= g.N) {
-          // Lanes l and l + 32 (same row) hold columns 16p + 4 lg .. and
-          // 16p + 8 + 4 lg ..; one lane swap per dword gives lane lg the 8
-          // consecutive columns 16p + 8 lg .. +7, stored as 16 bytes.
-#pragma unroll
-          for (int pq = 0; pq < 2; ++pq) {
-            const auto r0 = __builtin_amdgcn_permlane32_swap(w[2 * pq][0], w[2 * pq + 1][0], false, false);
-            const auto r1 = __builtin_amdgcn_permlane32_swap(w[2 * pq][1], w[2 * pq + 1][1], false, false);
-            if (mok) *(uint4*)(row + nb + 16 * pq + 8 * lg) = make_uint4(r0[0], r1[0], r0[1], r1[1]);
-          }
-        } else if (mok) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t n = nb + 8 * q + 4 * lg;
-            if (g.y_vec && n + 3 < g.N) {
-              *(uint2*)(row + n) = make_uint2(w[q][0], w[q][1]);
-            } else {
-              for (int e = 0; e < 4; ++e)
-                if (n + e < g.N) row[n + e] = (uint16_t)(w[q][e >> 1] >> (16 * (e & 1)));
-            }
-          }
-        }
-      } else if (mok) {
-        float* row = (float*)Y + m * g.ldy;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = nb + 8 * q + 4 * lg;
-          const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
-                      v3 = acc[i][j][4 * q + 3];
-          if (g.y_vec && n + 3 < g.N) {
-            *(float4*)(row + n) = make_float4(v0, v1, v2, v3);
-          } else {
-            const float vv[4] = {v0, v1, v2, v3};
-            for (int e = 0; e < 4; ++e)
-              if (n + e < g.N) row[n + e] = vv[e];
-          }
-        }
-      }
-    }
+    for (int j = 0; j < 4; ++j) store_tile32<BF16OUT>(g, Y, acc[i][j], m, m < m_end, n0 + wn * 128 + j * 32, lg);
   }
 }
 
