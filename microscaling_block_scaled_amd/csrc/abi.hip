@@ -6,9 +6,11 @@
 
 namespace {
 // Per-device answer of the architecture check, filled on first use and never
-// changed afterwards (0 = not yet known, 1 = gfx950, 2 = other).
+// changed afterwards (0 = not yet known, 1 = gfx950, 2 = other), and the
+// device's compute-unit count, filled with it.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
 
 const char* kReasonOk = "gfx950 device: MXFP8 quantize and scaled-MFMA GEMM available";
 const char* kReasonArch = "libmxfp8 is built for gfx950 (MI355X) only; this device is a different architecture";
@@ -21,6 +23,7 @@ int arch_state(int dev) {
   hipDeviceProp_t p;
   if (hipGetDeviceProperties(&p, dev) != hipSuccess) return 2;
   s = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  g_cu_count[dev].store(p.multiProcessorCount, std::memory_order_relaxed);
   g_arch_state[dev].store(s, std::memory_order_release);
   return s;
 }
@@ -31,6 +34,11 @@ mx_status_t check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return MX_ERR_DEVICE;
   return arch_state(dev) == 1 ? MX_OK : MX_ERR_DEVICE;
+}
+int cu_count() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || arch_state(dev) == 2) return 0;
+  return g_cu_count[dev].load(std::memory_order_relaxed);
 }
 }  // namespace mx_host
 

@@ -58,9 +58,6 @@ struct AttnArgs {
 // bank groups, so neither conflicts.
 __device__ __forceinline__ uint32_t vt_perm(uint32_t row) { return (row ^ (row >> 5)) & 15u; }
 
-__device__ __forceinline__ void dma4(uint32_t lds, uint32_t off, const void* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
-}
 
 // Buffer resource over [base, base + bytes): loads past the end return 0.
 constexpr int kBufferWord3 = 0x00020000;

@@ -652,10 +652,6 @@ constexpr uint32_t kCodeStage = kFBM * kFBK;   // bytes per operand per stage
 constexpr uint32_t kScaleRow = 16;             // scale bytes per row per scale group (4 FP8 / 2 FP4 stages)
 constexpr uint32_t kScaleBuf = kFBM * kScaleRow;
 
-// Direct global -> LDS load of one dword per lane.
-__device__ __forceinline__ void dma4(uint32_t lds, uint32_t off, const void* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
-}
 // Origin of a large-tile work-group's 256 x 256 output tile. Work-groups
 // are dealt round-robin to the 8 XCDs, so tile ids are remapped to give each
 // XCD a contiguous band of tiles (shared panels stay in that XCD's L2),
@@ -799,8 +795,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
 
   BigTile tl;
   if (!big_tile(g, lane, tl)) return;
-  const int64_t m0 = tl.m0, n0 = tl.n0, m_end = tl.m_end, po = tl.po, pi = tl.pi;
-  const uint32_t tile_m = tl.tile_m, tile_n = tl.tile_n;
+  int64_t m0 = tl.m0, n0 = tl.n0;
+  const int64_t m_end = tl.m_end, po = tl.po, pi = tl.pi;
+  uint32_t tile_m = tl.tile_m, tile_n = tl.tile_n;
   const uint8_t* A = g.a + po * g.sa_o + pi * g.sa_i;
   const uint8_t* SA = g.sa + po * g.ssa_o + pi * g.ssa_i;
   const uint8_t* B = g.b + po * g.sb_o + pi * g.sb_i;
@@ -851,41 +848,61 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   constexpr int kPF = MODE != kModeBF16 ? 1 : 0;
   __shared__ __attribute__((aligned(16))) uint8_t pf_sink[kPF ? 256 : 16];  // 64 lanes x 4 bytes
   const uint32_t pf_dst = lds_off(&pf_sink[0]);
-  const uint8_t* pf_base = wave < 2 ? a_base : b_base;
-  uint32_t pf_off;
-  {
-    const uint32_t tm_l = tile_m % 4, tn_l = tile_n % 8;
-    const uint32_t r = wave < 2 ? tn_l * 32 + 16 * wave + (lane & 15) : tm_l * 64 + 32 * (wave - 2) + (lane & 31);
-    const int64_t lastr = wave < 2 ? a_last : b_last;
-    pf_off = (uint32_t)min((int64_t)r, lastr) * (uint32_t)(wave < 2 ? g.lda : g.ldb);
-  }
+
+  // ---- Persistent walk. When every tile is whole (M and N multiples of 256,
+  // not grouped, one batch entry) the host may launch fewer work-groups than
+  // tiles; work-group b then computes tiles b, b + gridDim.x, ... (the same
+  // XCD band as with one tile per work-group). The prefetches of a tile's
+  // last 4 stages touch the next tile's first 4, and the next tile's first
+  // loads go out before this tile's epilogue stores, so its prologue runs
+  // under them. The load row offsets above hold for every whole tile. (The
+  // FP32-accumulation mode has no registers to spare for it.)
+  const bool walk = MODE != kModeBF16 && g.group_off == nullptr && gridDim.y == 1 && g.M % kFBM == 0 && g.N % kFBN == 0;
+  const uint32_t ntiles_all = g.tiles_m * g.tiles_n;
+  uint32_t bid = blockIdx.x;
+
+  // Prefetch addresses: a 32-bit lane offset (row and stage) from a wave-
+  // uniform base, which is the tile's first row, or when walking the
+  // operand's first row (every offset fits: on that path M * lda and
+  // N * ldb are below 2^32), so that the next tile needs no base of its own.
+  const uint8_t* pf_base = uniform_ptr(walk ? (wave < 2 ? A : B) : (wave < 2 ? a_base : b_base));
+  // the offset of this lane's prefetch row in tile (tm, tn) whose first rows
+  // are tm0 of A and tn0 of B
+  auto pf_row_off = [&](uint32_t tm, uint32_t tn, int64_t tm0, int64_t tn0) -> uint32_t {
+    const uint32_t r = wave < 2 ? (tn % 8) * 32 + 16 * wave + (lane & 15) : (tm % 4) * 64 + 32 * (wave - 2) + (lane & 31);
+    const int64_t origin = walk ? (wave < 2 ? tm0 : tn0) : 0;
+    return (uint32_t)(origin + min((int64_t)r, wave < 2 ? a_last : b_last)) * (uint32_t)(wave < 2 ? g.lda : g.ldb);
+  };
+  uint32_t pf_off = pf_row_off(tile_m, tile_n, m0, n0);
   auto issue_pf = [&](int64_t src) {
-    if constexpr (kPF) dma4(pf_dst, pf_off, pf_base + src * kFBK);
+    if constexpr (kPF) dma4(pf_dst, pf_off + (uint32_t)src * kFBK, pf_base);
   };
-  // codes of stage `src` into LDS buffer `buf`
-  auto issue_codes = [&](int64_t src, uint32_t buf) {
+
+  // Codes of stage `src`, rows 16q .. 16q + 15 of each wave's 64 for
+  // q in [q0, q1), into LDS buffer `buf` (buf, q0 and q1 are unrolled
+  // constants at every call, so each LDS address is a base plus an
+  // immediate).
+  auto issue_rows = [&](int64_t src, uint32_t buf, int q0, int q1) {
     const uint8_t* ab = a_base + src * kFBK;
     const uint8_t* bb = b_base + src * kFBK;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      dma16(a_dst + buf * kCodeStage + t * 8 * kFBK, a_off[t], ab);
-      dma16(b_dst + buf * kCodeStage + t * 8 * kFBK, b_off[t], bb);
+    for (int t = 2 * q0; t < 2 * q1; ++t) {
+      dma16_at(a_dst, buf * kCodeStage + t * 8 * kFBK, a_off[t], ab);
+      dma16_at(b_dst, buf * kCodeStage + t * 8 * kFBK, b_off[t], bb);
     }
   };
-  // a quarter of the codes of stage `src` (rows 16q .. 16q+15 of each wave's 64)
-  auto issue_codes_part = [&](int64_t src, uint32_t buf, int q) {
-    const uint8_t* ab = a_base + src * kFBK;
-    const uint8_t* bb = b_base + src * kFBK;
-#pragma unroll
-    for (int t = 2 * q; t < 2 * q + 2; ++t) {
-      dma16(a_dst + buf * kCodeStage + t * 8 * kFBK, a_off[t], ab);
-      dma16(b_dst + buf * kCodeStage + t * 8 * kFBK, b_off[t], bb);
-    }
-  };
+  auto issue_codes = [&](int64_t src, uint32_t buf) { issue_rows(src, buf, 0, 4); };
+  // a quarter of the codes of stage `src`
+  auto issue_codes_part = [&](int64_t src, uint32_t buf, int q) { issue_rows(src, buf, q, q + 1); };
+  // (the buffer of a scale group is a run-time value: the two addresses are
+  // formed here, and pass through an empty asm so that the compiler does
+  // not keep both buffers' addresses in scalar registers)
   auto issue_scales = [&](int64_t grp) {
     const uint32_t buf = (uint32_t)(grp & 1);
-    dma16(sa_dst + buf * kScaleBuf, sa_off, sa_base + grp * kScaleRow);
-    dma16(sb_dst + buf * kScaleBuf, sb_off, sb_base + grp * kScaleRow);
+    uint32_t la = sa_dst + buf * kScaleBuf, lb = sb_dst + buf * kScaleBuf;
+    asm volatile("" : "+s"(la), "+s"(lb));
+    dma16(la, sa_off, sa_base + grp * kScaleRow);
+    dma16(lb, sb_off, sb_base + grp * kScaleRow);
   };
 
   // ---- fragment reads: lane (lr, lg) of fragment f reads row base + 32 f;
@@ -1072,15 +1089,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   issue_pf(min((int64_t)3, last));
   wait_vmcnt<16 + kPF>();  // scales and stage 0 landed; stage 1 may still be in flight
   barrier();
-  read_scales(0);
-  set_out[0] = grp_out;
+  // a tile's first K half and scale group, from LDS buffer 0
+  auto read_first = [&]() {
+    read_scales(0);
+    set_out[0] = grp_out;
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    read_frag(a_row, sa4, 0, 0, 0, f, fa[0][f], sa[0][f]);
-    read_frag(b_row, sb4, 0, 0, 0, f, fb[0][f], sb[0][f]);
-  }
+    for (int f = 0; f < 4; ++f) {
+      read_frag(a_row, sa4, 0, 0, 0, f, fa[0][f], sa[0][f]);
+      read_frag(b_row, sb4, 0, 0, 0, f, fb[0][f], sb[0][f]);
+    }
+  };
+  read_first();
 
+  for (;;) {  // the tiles of this work-group
+  // the work-group's next tile, if any, and where the prefetches of this
+  // tile's last group go: that tile's stages 0 .. 3, or else this tile's
+  // last stage again
+  const bool has_next = walk && bid + gridDim.x < ntiles_all;
+  uint32_t ntm = 0, ntn = 0;
+  if (has_next) big_tile_coords(g, bid + gridDim.x, ntm, ntn);
+  const uint32_t pfn_off =
+      has_next ? pf_row_off(ntm, ntn, (int64_t)ntm * kFBM, (int64_t)ntn * kFBN) : pf_off + (uint32_t)last * kFBK;
+  const uint32_t pfn_step = has_next ? (uint32_t)kFBK : 0u;
   for (int64_t s0 = 0; s0 < nsteps; s0 += 4) {
+    // the prefetches of this group (stages s0 + 4 .. s0 + 7), chosen here,
+    // outside the scheduling regions below
+    const bool lastg = s0 + 4 >= nsteps;
+    const uint32_t pf_group = lastg ? pfn_off : pf_off + (uint32_t)(s0 + 4) * kFBK;
+    const uint32_t pf_gstep = lastg ? pfn_step : (uint32_t)kFBK;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t s = s0 + u;
@@ -1133,7 +1169,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      issue_pf(min(s + 4, last));
+      if constexpr (kPF) dma4(pf_dst, pf_group + (uint32_t)u * pf_gstep, pf_base);
     }
   }
   wait_vmcnt<0>();  // no load may still be writing LDS when the group ends
@@ -1268,19 +1304,66 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
     }
   }
 
+  // ---- the next tile's first loads go out before this tile's stores,
+  // once every wave is done with both LDS buffers
+  const int64_t em0 = m0, en0 = n0;
+  if (has_next) {
+    wait_lgkmcnt0();
+    barrier();
+    bid += gridDim.x;
+    tile_m = ntm;
+    tile_n = ntn;
+    m0 = (int64_t)tile_m * kFBM;
+    n0 = (int64_t)tile_n * kFBN;
+    a_base = uniform_ptr(A + m0 * g.lda);
+    b_base = uniform_ptr(B + n0 * g.ldb);
+    sa_base = uniform_ptr(SA + m0 * g.ldsa);
+    sb_base = uniform_ptr(SB + n0 * g.ldsb);
+    pf_off = pfn_off;
+    issue_scales(0);
+    issue_codes(0, 0);
+    issue_codes(1, 1);
+    issue_pf(min((int64_t)3, last));
+  }
+
   // ---- epilogue: lane owns y[m][n .. n+3] for 4 groups of n
   uint8_t* Y = (uint8_t*)g.y + (po * g.sy_o + pi * g.sy_i) * (BF16OUT ? 2 : 4);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + wm * 128 + i * 32 + lr;
+    const int64_t m = em0 + wm * 128 + i * 32 + lr;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) store_tile32<BF16OUT>(g, Y, acc[i][j], m, m < m_end, n0 + wn * 128 + j * 32, lg);
+    for (int j = 0; j < 4; ++j) store_tile32<BF16OUT>(g, Y, acc[i][j], m, m < m_end, en0 + wn * 128 + j * 32, lg);
   }
+  if (!has_next) break;
+
+  // ---- next tile: its first loads and this tile's stores (loads and
+  // stores share one counter and may complete out of order) have landed
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  needs_exact = false;
+  wait_vmcnt<0>();
+  barrier();
+  read_first();
+  }  // tiles
 }
 
 template <int MODE>
 mx_status_t launch_big(const GemmArgs& g, mx_fmt_t af, mx_fmt_t bf, bool bf16out, int64_t batch, hipStream_t st) {
-  const dim3 grid(g.tiles_m * g.tiles_n, (uint32_t)batch);
+  // The FP8 and FP4 modes walk the tiles with one work-group per CU (each
+  // computing every gridDim.x-th tile, which keeps the XCD bands when the
+  // CU count is a multiple of 8) when every tile is whole and there is one
+  // batch entry -- the same condition the kernel tests; otherwise one tile
+  // per work-group.
+  uint32_t wgs = g.tiles_m * g.tiles_n;
+  if (MODE != kModeBF16 && g.group_off == nullptr && batch == 1 && g.M % kFBM == 0 && g.N % kFBN == 0) {
+    const int cus = mx_host::cu_count();
+    if (cus >= 8 && cus % 8 == 0 && (uint32_t)cus < wgs) wgs = (uint32_t)cus;
+  }
+  const dim3 grid(wgs, (uint32_t)batch);
 #define MX_BIG_LAUNCH(AF, BF, OUT) \
   hipLaunchKernelGGL((gemm_big_kernel<AF, BF, OUT, MODE>), grid, dim3(kThreads), 0, st, g)
 #define MX_BIG_OUT(AF, BF) \

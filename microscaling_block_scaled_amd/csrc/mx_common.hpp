@@ -380,14 +380,29 @@ __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Direct global->LDS 16-byte loads: lane i's bytes land at M0 + 16i. The
-// address is a wave-uniform base (SGPR pair) plus a per-lane 32-bit offset.
-// They are issued as inline assembly so that the compiler does not add its
-// own drain of every outstanding load before each LDS read; completion is
-// tracked explicitly with wait_vmcnt before the barrier that publishes the
-// data. Nothing else in the kernels that use them touches M0.
+// Direct global->LDS loads: lane i's 16 (dma16) or 4 (dma4) bytes land at
+// M0 + 16i (4i). The address is a wave-uniform base (SGPR pair) plus a
+// per-lane 32-bit offset. They are issued as inline assembly so that the
+// compiler does not add its own drain of every outstanding load before each
+// LDS read; completion is tracked explicitly with wait_vmcnt before the
+// barrier that publishes the data. Nothing else in the kernels that use them
+// touches M0. An LDS-DMA load that reads M0 right after a scalar write of it
+// needs one wait state, which the compiler cannot insert inside the asm:
+// hence the s_nop.
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t off, const void* base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t off, const void* base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base) : "memory");
+}
+// dma16 with the LDS address given as a wave-uniform base plus an offset
+// that folds to a constant at compile time (an unrolled index): M0 is formed
+// inside the asm, so the compiler keeps no scalar register per distinct
+// address.
+__device__ __forceinline__ void dma16_at(uint32_t lds_base, uint32_t imm, uint32_t off, const void* base) {
+  asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3" ::"s"(lds_base), "i"(imm), "v"(off),
+               "s"(base)
+               : "memory", "scc");
 }
 // A pointer that is the same in every lane, moved to SGPRs once, so that
 // the per-stage address arithmetic stays on the scalar unit.
@@ -417,6 +432,7 @@ __device__ __forceinline__ float canon_nan(float f) { return f != f ? __uint_as_
 // ---------------------------------------------------------------- host side
 namespace mx_host {
 mx_status_t check_device();  // MX_OK when the current device is gfx950
+int cu_count();              // compute units of the current device (0 if unknown); cached with the check
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline mx_status_t launch_status() {
   return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_HIP;
