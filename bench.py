@@ -38,8 +38,10 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 / MXFP8 matrix peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 / MXFP4 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_8192_quantize_8192x4096.json")
-GEMM_SOURCE = os.path.join(ROOT, "microscaling_block_scaled_amd", "csrc", "gemm.hip")
-QUANT_SOURCE = os.path.join(ROOT, "microscaling_block_scaled_amd", "csrc", "quantize.hip")
+_CSRC = os.path.join(ROOT, "microscaling_block_scaled_amd", "csrc")
+# the sources each measured kernel is built from (its file and the shared header)
+GEMM_SOURCE = [os.path.join(_CSRC, "gemm.hip"), os.path.join(_CSRC, "mx_common.hpp")]
+QUANT_SOURCE = [os.path.join(_CSRC, "quantize.hip"), os.path.join(_CSRC, "mx_common.hpp")]
 
 
 def log(*a):
@@ -128,9 +130,13 @@ def copy_calibration(torch, steps):
     print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": steps}}))
 
 
-def _sha256(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def _sha256(paths):
+    """sha256 over the concatenated bytes of the files, in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def committed_traffic(key, source, sha_field):
