@@ -156,6 +156,46 @@ def test_large_tile_kernel(mx, oracle, M, N, K, afmt, bfmt):
     assert_gemm_bound(bf16_to_f64(yb), y_ref, t_ref, "fp32-accum bf16 %s" % ((M, N, K),), bf16_out=True)
 
 
+# Whole-tile shapes with more tiles than a 256-CU part has CUs, so the FP8
+# and FP4 modes walk tiles with one work-group per CU: 272 tiles leave 16
+# work-groups with a second tile. K = 512 is a single scale group per tile
+# (its last group is also its first), K = 1536 an odd number of groups.
+WALK_SHAPES = [(4352, 4096, 512), (4096, 4352, 1536)]
+
+
+def _sampled_rows(M, per_tile=3, seed=7):
+    """The first and last row of every 256-row tile and a few others."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for t0 in range(0, M, 256):
+        t1 = min(M, t0 + 256)
+        rows.update([t0, t1 - 1])
+        rows.update(int(r) for r in rng.integers(t0, t1, per_tile))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("M,N,K", WALK_SHAPES)
+@pytest.mark.parametrize("afmt,bfmt", [(E4M3, E4M3), (E5M2, E4M3)])
+def test_large_tile_kernel_walk(mx, oracle, M, N, K, afmt, bfmt):
+    """Every column of sampled rows of every row tile, against the oracle,
+    in the FP8 mode (walking) and the FP32-accumulation mode (one tile per
+    work-group), f32 and bf16 out."""
+    torch = _torch()
+    xa = inputs.normal_bf16(700 + K, (M, K))
+    xb = inputs.normal_bf16(800 + K, (N, K))
+    qa_o, sa_o = oracle.quantize_rows(xa, afmt)
+    qb_o, sb_o = oracle.quantize_rows(xb, bfmt)
+    rows = _sampled_rows(M)
+    y_ref, t_ref = oracle.gemm(qa_o[rows], sa_o[rows], afmt, qb_o, sb_o, bfmt)
+    qa, sa, qb, sb = dev(qa_o), dev(sa_o), dev(qb_o), dev(sb_o)
+    for accum, rel in ((FP8, FP8_GROUPED_REL), (FP32, REL_T)):
+        y = host(mx.mx_gemm(qa, sa, qb, sb, afmt, bfmt, out_dtype=torch.float32, accum=accum))[rows]
+        assert_gemm_bound(y, y_ref, t_ref, "walk f32 accum %d %s" % (accum, (M, N, K)), rel=rel)
+        yb = host(mx.mx_gemm(qa, sa, qb, sb, afmt, bfmt, out_dtype=torch.bfloat16, accum=accum))[rows]
+        assert_gemm_bound(bf16_to_f64(yb), y_ref, t_ref, "walk bf16 accum %d %s" % (accum, (M, N, K)),
+                          bf16_out=True, rel=rel)
+
+
 def test_large_tile_kernel_batched(mx, oracle):
     """Two problems of 256 x 512 x 512 in one call (batch strides)."""
     torch = _torch()

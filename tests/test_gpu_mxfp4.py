@@ -125,6 +125,29 @@ def test_gemm_mxfp4_varied_scales_and_extreme_codes(mx, oracle):
     assert_gemm_bound(host(y).astype(np.float64), y_ref, t_ref, "mxfp4 random codes")
 
 
+def test_gemm_mxfp4_walk(mx, oracle):
+    """4352 x 4096 x 1024 MXFP4: 272 whole tiles, more than a 256-CU part
+    has CUs, so the large-tile kernel walks tiles (16 work-groups take a
+    second one); every column of the first and last row of each row tile
+    and of 3 others against the oracle, f32 and bf16 out."""
+    import torch
+    M, N, K = 4352, 4096, 1024
+    a = inputs.normal_bf16(380, (M, K))
+    b = inputs.normal_bf16(381, (N, K))
+    qa_o, sa_o = oracle.quantize_rows(a, E2M1)
+    qb_o, sb_o = oracle.quantize_rows(b, E2M1)
+    g = inputs.rng(382)
+    rows = sorted({r for t0 in range(0, M, 256) for r in [t0, t0 + 255] + list(g.integers(t0, t0 + 256, 3))})
+    rows = np.array(rows)
+    y_ref, t_ref = oracle.gemm(qa_o[rows], sa_o[rows], E2M1, qb_o, sb_o, E2M1)
+    qa, sa, qb, sb = dev(qa_o), dev(sa_o), dev(qb_o), dev(sb_o)
+    y = host(mx.mx_gemm(qa, sa, qb, sb, a_fmt=E2M1, b_fmt=E2M1, out_dtype=torch.float32))[rows]
+    worst = assert_gemm_bound(y.astype(np.float64), y_ref, t_ref, "mxfp4 walk f32")
+    yb = host(mx.mx_gemm(qa, sa, qb, sb, a_fmt=E2M1, b_fmt=E2M1, out_dtype=torch.bfloat16))[rows]
+    assert_gemm_bound(bf16_to_f64(yb), y_ref, t_ref, "mxfp4 walk bf16", bf16_out=True)
+    print("mxfp4 walk %dx%dx%d: worst |err|/T = %.3g" % (M, N, K, worst))
+
+
 @pytest.mark.slow
 def test_gemm_mxfp4_8192_cubed_sampled(mx, oracle):
     """M = N = K = 8192 MXFP4 (the GEMM workload's inputs quantized to E2M1),
