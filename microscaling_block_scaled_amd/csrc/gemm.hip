@@ -613,7 +613,8 @@ __global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uin
 }
 
 // ---------------------------------------------------------------------------
-// Main-loop kernel for large aligned problems (FP8 accumulation path).
+// Main-loop kernel for large aligned problems, in the FP8, FP32-accumulation
+// and FP4 modes.
 //
 // Tile 256 x 256 per workgroup, 4 waves of 128 x 128, built from
 // v_mfma_scale_f32_32x32x64_f8f6f4 (K = 64 per issue = 2 MX blocks). K
@@ -629,7 +630,9 @@ __global__ __launch_bounds__(kThreads) void gemm_rowpanel_kernel(GemmArgs g, uin
 // so the fragment reads are free of bank conflicts. Rows past M or N are
 // clamped to the last row for loading and skipped on store. Work-groups are
 // dealt round-robin to the 8 XCDs, so tile ids are remapped to give each XCD
-// a contiguous band of tiles (shared panels stay in that XCD's L2).
+// a contiguous band of tiles (shared panels stay in that XCD's L2). With
+// whole tiles the FP8 and FP4 modes run one work-group per CU, each walking
+// tiles (see "Persistent walk" in the kernel).
 // Requires K % 512 == 0 and 16-byte aligned scale rows.
 //
 // FP4 mode (both operands MXFP4, codes two per byte): a 128-byte stage holds
@@ -1081,7 +1084,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
   // of a stage of MFMA work to land. The loop body has
   // no branches (a branch lets the compiler sink MFMAs past the barrier):
   // past the last stage the loads repeat the last stage into the free
-  // buffer and the extra fragment reads are discarded.
+  // buffer and the extra fragment reads are discarded (a walking work-group
+  // then loads the next tile's first stages after the loop).
   const int64_t last = nsteps - 1;
   issue_scales(0);
   issue_codes(0, 0);
