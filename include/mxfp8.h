@@ -24,10 +24,10 @@
  * Conventions shared by every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller. The library
  *     allocates no memory and keeps no pointer after returning. Its only
- *     global state is a per-device cache of the architecture check (filled
- *     atomically on the first call on each device, never changed after), so
- *     calls from several threads and on different streams may run
- *     concurrently.
+ *     global state is a per-device cache of the architecture check and the
+ *     device's compute-unit count (filled atomically on the first call on
+ *     each device, never changed after), so calls from several threads and
+ *     on different streams may run concurrently.
  *   - Work is enqueued on `stream` (asynchronous; no implicit sync). Argument
  *     errors are detected on the host before anything is launched and are
  *     returned synchronously; then nothing is written. A launch failure
