@@ -196,6 +196,35 @@ def test_large_tile_kernel_walk(mx, oracle, M, N, K, afmt, bfmt):
                           bf16_out=True, rel=rel)
 
 
+@pytest.mark.parametrize("afmt,bfmt", [(E4M3, E5M2), (E5M2, E5M2)])
+def test_large_tile_kernel_walk_padded(mx, oracle, afmt, bfmt):
+    """A walking shape (4352 x 4096 x 1024, 272 tiles) with every pitch
+    padded: codes and scales of A and B and the output rows (f32 and bf16);
+    sampled rows of every row tile against the oracle and the padding left
+    as it was."""
+    torch = _torch()
+    M, N, K = 4352, 4096, 1024
+    xa = inputs.normal_bf16(900, (M, K))
+    xb = inputs.normal_bf16(901, (N, K))
+    qa_o, sa_o = oracle.quantize_rows(xa, afmt)
+    qb_o, sb_o = oracle.quantize_rows(xb, bfmt)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    A = torch.zeros((M, K + 64), **u8); B = torch.zeros((N, K + 128), **u8)
+    SA = torch.zeros((M, K // 32 + 16), **u8); SB = torch.zeros((N, K // 32 + 32), **u8)
+    A[:, :K] = dev(qa_o); B[:, :K] = dev(qb_o); SA[:, :K // 32] = dev(sa_o); SB[:, :K // 32] = dev(sb_o)
+    rows = _sampled_rows(M)
+    y_ref, t_ref = oracle.gemm(qa_o[rows], sa_o[rows], afmt, qb_o, sb_o, bfmt)
+    for dt in (torch.float32, torch.bfloat16):
+        Y = torch.full((M, N + 64), -7.0, dtype=dt, device="cuda")
+        mx.mx_gemm(A[:, :K], SA[:, :K // 32], B[:, :K], SB[:, :K // 32], afmt, bfmt, y=Y[:, :N], accum=FP8)
+        Yh = host(Y)
+        got = bf16_to_f64(Yh[rows, :N]) if dt == torch.bfloat16 else Yh[rows, :N]
+        assert_gemm_bound(got, y_ref, t_ref, "walk padded %s" % dt, bf16_out=dt == torch.bfloat16,
+                          rel=FP8_GROUPED_REL)
+        pad = bf16_to_f64(Yh[:, N:]) if dt == torch.bfloat16 else Yh[:, N:]
+        assert np.all(pad == -7.0)
+
+
 def test_large_tile_kernel_batched(mx, oracle):
     """Two problems of 256 x 512 x 512 in one call (batch strides)."""
     torch = _torch()
