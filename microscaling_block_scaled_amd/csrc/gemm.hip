@@ -1213,7 +1213,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
         for (int f = 0; f < 4; ++f) {
           ca[f] = sa_base[sao[f] + b];
           cb[f] = sb_base[sbo[f] + b];
-          any |= fold_excluded<AFMT>(ca[f]) | fold_excluded<BFMT>(cb[f]);
+          any |= (fold_excluded<AFMT>(ca[f]) ? 1 : 0) | (fold_excluded<BFMT>(cb[f]) ? 1 : 0);  // no short circuit
         }
         if (__builtin_amdgcn_ballot_w64(any) == 0) continue;
         uint4 qa[4], qb[4];
