@@ -253,6 +253,37 @@ def test_large_tile_kernel_batched(mx, oracle):
         assert_gemm_bound(yh[b], y_ref, t_ref, "batch %d" % b, rel=FP8_GROUPED_REL)
 
 
+def test_large_tile_kernel_batched_whole_tiles(mx, oracle):
+    """Two problems of 4352 x 4096 x 512 in one call: whole tiles and more
+    of them than a 256-CU part has CUs, but a batch does not walk (one tile
+    per work-group); sampled rows of every row tile of both problems."""
+    torch = _torch()
+    Bt, M, N, K = 2, 4352, 4096, 512
+    xa = inputs.normal_bf16(53, (Bt * M, K))
+    xb = inputs.normal_bf16(54, (Bt * N, K))
+    qa_o, sa_o = oracle.quantize_rows(xa, E4M3)
+    qb_o, sb_o = oracle.quantize_rows(xb, E4M3)
+    qa, sa, qb, sb = dev(qa_o), dev(sa_o), dev(qb_o), dev(sb_o)
+    y = torch.empty((Bt, M, N), dtype=torch.bfloat16, device="cuda")
+    d = mx.mx_gemm_desc_t()
+    d.M, d.N, d.K = M, N, K
+    d.a, d.lda, d.sa, d.ldsa, d.a_fmt = qa.data_ptr(), K, sa.data_ptr(), K // 32, E4M3
+    d.b, d.ldb, d.sb, d.ldsb, d.b_fmt = qb.data_ptr(), K, sb.data_ptr(), K // 32, E4M3
+    d.y, d.ldy, d.y_dtype = y.data_ptr(), N, mx.MX_BF16
+    d.batch_outer, d.batch_inner = Bt, 1
+    d.stride_a_outer, d.stride_sa_outer = M * K, M * K // 32
+    d.stride_b_outer, d.stride_sb_outer = N * K, N * K // 32
+    d.stride_y_outer = M * N
+    d.accum = FP8
+    mx.mx_gemm_desc(d)
+    yh = host(y)
+    rows = _sampled_rows(M)
+    for b in range(Bt):
+        y_ref, t_ref = oracle.gemm(qa_o[b * M + rows], sa_o[b * M + rows], E4M3,
+                                   qb_o[b * N:(b + 1) * N], sb_o[b * N:(b + 1) * N], E4M3)
+        assert_gemm_bound(bf16_to_f64(yh[b][rows]), y_ref, t_ref, "batch %d" % b, bf16_out=True, rel=FP8_GROUPED_REL)
+
+
 def test_padded_pitches_and_unaligned_scale_rows(mx, oracle):
     """Leading dimensions larger than the rows, and K/32 not a multiple of 4
     (scale rows not dword aligned)."""
