@@ -458,20 +458,35 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnArgs g) {
   if (!q_ok) return;
   const float inv = !(l_run <= 0.f) ? 1.f / l_run : 0.f;  // a NaN normaliser stays NaN
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (BF16OUT) {
+      // Lanes l and l + 32 (the same query) hold columns 8r + 4lg .. +3 of
+      // each r; one lane swap per dword gives lane lg the 8 consecutive
+      // columns 16p + 8lg .. +7 of each pair p of r, stored as 16 bytes
+      uint32_t w[4][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t d = 32 * t + 8 * r + 4 * lg;
-      const float v0 = o_acc[t][4 * r] * inv, v1 = o_acc[t][4 * r + 1] * inv;
-      const float v2 = o_acc[t][4 * r + 2] * inv, v3 = o_acc[t][4 * r + 3] * inv;
-      if constexpr (BF16OUT) {
-        const uint32_t w0 = f32_to_bf16_rne(canon_nan(v0)) | (f32_to_bf16_rne(canon_nan(v1)) << 16);
-        const uint32_t w1 = f32_to_bf16_rne(canon_nan(v2)) | (f32_to_bf16_rne(canon_nan(v3)) << 16);
-        *(uint2*)((uint16_t*)g.out + out_row + d) = make_uint2(w0, w1);
-      } else {
+      for (int r = 0; r < 4; ++r) {
+        const float v0 = o_acc[t][4 * r] * inv, v1 = o_acc[t][4 * r + 1] * inv;
+        const float v2 = o_acc[t][4 * r + 2] * inv, v3 = o_acc[t][4 * r + 3] * inv;
+        w[r][0] = f32_to_bf16_rne(canon_nan(v0)) | (f32_to_bf16_rne(canon_nan(v1)) << 16);
+        w[r][1] = f32_to_bf16_rne(canon_nan(v2)) | (f32_to_bf16_rne(canon_nan(v3)) << 16);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const auto r0 = __builtin_amdgcn_permlane32_swap(w[2 * p][0], w[2 * p + 1][0], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(w[2 * p][1], w[2 * p + 1][1], false, false);
+        *(uint4*)((uint16_t*)g.out + out_row + 32 * t + 16 * p + 8 * lg) = make_uint4(r0[0], r1[0], r0[1], r1[1]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t d = 32 * t + 8 * r + 4 * lg;
+        const float v0 = o_acc[t][4 * r] * inv, v1 = o_acc[t][4 * r + 1] * inv;
+        const float v2 = o_acc[t][4 * r + 2] * inv, v3 = o_acc[t][4 * r + 3] * inv;
         *(float4*)((float*)g.out + out_row + d) = make_float4(v0, v1, v2, v3);
       }
     }
+  }
   if (lg == 0 && g.lse)
     g.lse[tok * g.hq + h] = !(l_run <= 0.f) ? (m_ref + __log2f(l_run)) * 0.69314718055994531f : -__builtin_inff();
   };
