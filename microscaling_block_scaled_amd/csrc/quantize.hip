@@ -456,7 +456,9 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(const InT* __restr
 // A positive normal power of two 2^(E - 127) has code E (its exponent field);
 // 2^-127 is the f32 subnormal 0x00400000 and has code 0; anything else
 // (another subnormal, a significand other than 1, zero, negative, Inf, NaN)
-// gets 0xFF. One thread writes the 4 codes of one source scale.
+// gets 0xFF. A thread converts 4 consecutive source scales of a row (one
+// 16-byte load and one 16-byte store of 16 codes) when the rows and pitches
+// allow it, else one.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t e8m0_of_pow2_bits(uint32_t b) {
   const uint32_t E = (b >> 23) & 0xFFu, m = b & 0x7FFFFFu;
@@ -465,15 +467,24 @@ __device__ __forceinline__ uint32_t e8m0_of_pow2_bits(uint32_t b) {
   return m == 0x400000u ? 0u : 0xFFu;
 }
 
+template <int V>
 __global__ __launch_bounds__(kThreads) void scale_bcast_kernel(const float* __restrict__ s_in, int64_t ld_in,
                                                                uint32_t layout, uint32_t n, FastDiv per_row,
                                                                uint8_t* __restrict__ out, int64_t ld_out) {
+  // thread i: V consecutive source scales of one row (group cg of row r)
   const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= n) return;
-  const uint32_t r = per_row.div(i), cb = i - r * per_row.d;
+  const uint32_t r = per_row.div(i), cg = i - r * per_row.d;
   const int64_t src_row = layout ? r / 128 : r;
-  const uint32_t code = e8m0_of_pow2_bits(__float_as_uint(s_in[src_row * ld_in + cb]));
-  *(uint32_t*)(out + (int64_t)r * ld_out + 4 * (int64_t)cb) = code * 0x01010101u;
+  const float* src = s_in + src_row * ld_in + (int64_t)V * cg;
+  uint8_t* dst = out + (int64_t)r * ld_out + 4 * (int64_t)V * cg;
+  if constexpr (V == 1) {
+    *(uint32_t*)dst = e8m0_of_pow2_bits(__float_as_uint(*src)) * 0x01010101u;
+  } else {
+    const uint4 w = *(const uint4*)src;
+    *(uint4*)dst = make_uint4(e8m0_of_pow2_bits(w.x) * 0x01010101u, e8m0_of_pow2_bits(w.y) * 0x01010101u,
+                              e8m0_of_pow2_bits(w.z) * 0x01010101u, e8m0_of_pow2_bits(w.w) * 0x01010101u);
+  }
 }
 
 mx_status_t check_common(const void* x, mx_dtype_t xdt, mx_fmt_t fmt, int64_t rows, int64_t cols, int64_t ldx) {
@@ -729,10 +740,22 @@ extern "C" mx_status_t mx_scale_broadcast(const float* s_in, int64_t ld_in, mx_b
   mx_status_t rc;
   if ((rc = mx_host::check_device()) != MX_OK) return rc;
   if (rows == 0 || cols == 0) return MX_OK;
-  const int64_t n = rows * (cols / 128);
-  if (n >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
-  hipLaunchKernelGGL(scale_bcast_kernel, dim3((uint32_t)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
-                     s_in, ld_in, layout == MX_BCAST_128X128 ? 1u : 0u, (uint32_t)n,
-                     FastDiv::make((uint32_t)(cols / 128)), out, ld_out);
+  const int64_t per_row = cols / 128;
+  if (rows * per_row >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
+  // four source scales per thread (one 16-byte load, one 16-byte store) when
+  // the rows and pitches allow it, else one
+  const bool v4 = per_row % 4 == 0 && ld_in % 4 == 0 && ld_out % 16 == 0 && mx_host::aligned16(s_in) &&
+                  mx_host::aligned16(out);
+  const uint32_t layout_flag = layout == MX_BCAST_128X128 ? 1u : 0u;
+  if (v4) {
+    const int64_t n = rows * (per_row / 4);
+    hipLaunchKernelGGL(scale_bcast_kernel<4>, dim3((uint32_t)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, s_in, ld_in, layout_flag, (uint32_t)n, FastDiv::make((uint32_t)(per_row / 4)), out,
+                       ld_out);
+  } else {
+    const int64_t n = rows * per_row;
+    hipLaunchKernelGGL(scale_bcast_kernel<1>, dim3((uint32_t)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, s_in, ld_in, layout_flag, (uint32_t)n, FastDiv::make((uint32_t)per_row), out, ld_out);
+  }
   return mx_host::launch_status();
 }

@@ -216,3 +216,19 @@ def test_scale_broadcast_strided(mx, oracle):
     want = oracle.scale_broadcast(s_in[:, :4], 0, 64, 512)
     assert_bitexact(host(out[:, :16]), want, "broadcast into a wider array")
     assert (host(out[:, 16:]) == 0x5A).all()
+
+
+def test_scale_broadcast_strided_four_per_thread(mx, oracle):
+    """Padded pitches on the path that converts 4 source scales per thread
+    (a multiple of 4 scales per row, 4-scale and 16-byte pitches): both
+    layouts, bytes past the output pitch untouched."""
+    import torch
+    for layout in (0, 1):
+        rows = 300
+        sr = rows if layout == 0 else (rows + 127) // 128
+        s_in = broadcast_scales(770 + layout, (sr, 36))
+        out = torch.full((rows, 144), 0x5A, dtype=torch.uint8, device="cuda")
+        mx.mx_scale_broadcast(dev(s_in)[:, :32], rows, 32 * 128, layout=layout, out=out[:, :128])
+        want = oracle.scale_broadcast(s_in[:, :32], layout, rows, 32 * 128)
+        assert_bitexact(host(out[:, :128]), want, "broadcast, 4 per thread, layout %d" % layout)
+        assert (host(out[:, 128:]) == 0x5A).all()
