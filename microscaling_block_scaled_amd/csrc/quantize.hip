@@ -637,11 +637,13 @@ mx_status_t quantize_cols_host(const void* x, mx_dtype_t xdt, int64_t rows, int6
   const uint32_t col_major = col_tiles >= 64 ? 1u : 0u;
   // With 8 work-groups per CU, grids of up to 2048 tiles are resident all at
   // once, so every work-group reads, then writes, in step with the others.
-  // 20000 bytes of unused dynamic LDS leave 4 per CU and stagger them. The
-  // 4096-tile threshold is measured, not derived: 8192 x 4096 (2048 tiles)
-  // 25.1 -> 24.2 us, 14336 x 4096 (3584) 37.7 -> 37.3 us, 16384 x 4096 (4096)
-  // 42.5 -> 42.3 us; on 16384 x 14336 (14336 tiles) it measured 1.2 % slower.
-  const uint32_t lds_pad = row_tiles * col_tiles <= 4096 ? 20000u : 0u;
+  // Unused dynamic LDS limits how many fit per CU and staggers them: 20000
+  // bytes (4 per CU) measured 8192 x 4096 (2048 tiles) 25.1 -> 24.2 us,
+  // 14336 x 4096 (3584) 37.7 -> 37.3 us, 16384 x 4096 (4096) 42.5 -> 42.3 us,
+  // and 1.2 % slower on 16384 x 14336 (14336 tiles); 12000 bytes (5 per CU)
+  // then 24.2 -> 23.5 us and 37.8 -> 37.5 us, while 3 and 6 per CU were
+  // slower. The 4096-tile threshold is measured, not derived.
+  const uint32_t lds_pad = row_tiles * col_tiles <= 4096 ? 12000u : 0u;
 #define MX_COLS_LAUNCH(T, F)                                                                                        \
   hipLaunchKernelGGL((quant_cols_kernel<T, F, false, false>), grid, dim3(kThreads), lds_pad, stream, (const T*)x, rows, cols, ldx, \
                      qt, ldq, st, lds, (uint32_t)col_tiles, col_major, round_up, nullptr, 0, nullptr, 0)
@@ -677,7 +679,9 @@ mx_status_t quantize_tile_host(const mx_quantize_desc_t* d, uint32_t round_up, b
   if (row_tiles * col_tiles >= ((int64_t)1 << 31)) return MX_ERR_SHAPE;
   const dim3 grid((uint32_t)(row_tiles * col_tiles));
   const uint32_t col_major = col_tiles >= 64 ? 1u : 0u;
-  const uint32_t lds_pad = row_tiles * col_tiles <= 4096 ? 20000u : 0u;  // as in the colwise call
+  // 4 per CU here (as first measured for the colwise call): 5 per CU measured
+  // 1.7 % slower on the 2-D blocks of 14336 x 4096 and no different one-pass
+  const uint32_t lds_pad = row_tiles * col_tiles <= 4096 ? 20000u : 0u;
 #define MX_TILE_LAUNCH(T, F, B2D, ROWS)                                                                            \
   hipLaunchKernelGGL((quant_cols_kernel<T, F, B2D, ROWS>), grid, dim3(kThreads), lds_pad, stream, (const T*)d->x, d->rows, \
                      d->cols, d->ldx, d->qt, d->ldqt, d->st, d->ldst, (uint32_t)col_tiles, col_major, round_up,  \
